@@ -1,0 +1,159 @@
+/*
+ * libmla — absorbed Multi-head Latent Attention decode with decoupled RoPE, for MI355X (gfx950).
+ *
+ * The four compute calls follow the inference flow of one new token in
+ * "Decoupled RoPE · MLA Part 2" (agent.namiai.tech), §5: append the token's latent c and its
+ * rotated position key to the cache, absorb the content query through W_UK, score every cached
+ * row with q~·c + q_R·k_R, softmax, sum the latents, and project once through W_UV.
+ *
+ * Conventions shared by every call
+ *  - Ownership: every data pointer is device memory allocated and owned by the caller. The
+ *    library never allocates, frees or synchronises; each call only enqueues kernels on
+ *    `stream` (a hipStream_t; NULL means the legacy default stream) and returns.
+ *  - Layout: row-major and contiguous. Weights keep the nn.Linear [out, in] layout, viewed per
+ *    head ("从零理解 MLA", section "矩阵吸收" code note on the weight view).
+ *  - Storage dtype: `cfg->dtype` is the dtype of the cache, the weights, q_nope/q_rope,
+ *    q_packed and o. Latent outputs z and lse are always float32. Arithmetic accumulates in
+ *    float32; RoPE angles are formed and reduced in float64.
+ *  - Cache: token p of sequence b is row (seq_off[b] + p); a row is
+ *    [c (d_latent) ; RoPE_p(k_R) (d_rope)], latent first ("从零理解 MLA", section "解耦 RoPE",
+ *    absorbed_step, where the cached entry is the concatenation of c_kv and the rotated k_r).
+ *  - RoPE: consecutive pairs (2j, 2j+1) of a position vector at position p are turned by
+ *    p·theta_j, theta_j = rope_base^(-2j/d_rope) ("Decoupled RoPE · MLA Part 2", §4 and §7).
+ *  - Device metadata (seq_off, len_before, seq_len, q_pos) is trusted: the caller guarantees
+ *    slab capacity, 0 < n_q <= seq_len[b] <= max_seq_len, and positions within int32.
+ *  - Errors: arguments are validated before anything is launched; a failing check returns a
+ *    status, launches nothing and writes nothing. A failed launch returns MLA_ERR_HIP.
+ *    mla_last_error() gives the calling thread's detail text for the last non-OK status.
+ *    Faults inside a kernel surface at the caller's next synchronisation.
+ *  - Empty work (batch == 0, n_new == 0, n_rows == 0) is valid and launches nothing.
+ *  - Outputs must not alias inputs; only `cache` is read-write.
+ */
+#ifndef MLA_H
+#define MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mla_status {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = 1, /* null pointer, negative size, inconsistent shape, bad scale/base */
+  MLA_ERR_UNSUPPORTED = 2, /* dims or dtype outside what the compiled kernels cover */
+  MLA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than mla_decode_attn_workspace_size */
+  MLA_ERR_HIP = 4          /* a HIP runtime call or launch failed; see mla_last_error() */
+} mla_status;
+
+typedef enum mla_dtype { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
+
+/* Shape and numeric parameters of one MLA layer. 40 bytes, no padding surprises. */
+typedef struct mla_config {
+  int32_t n_heads;     /* H: attention heads (128 for DeepSeek-V2/V3) */
+  int32_t d_nope;      /* per-head content query/key width d_h (128) */
+  int32_t d_latent;    /* latent width d_c (512) */
+  int32_t d_rope;      /* decoupled position width d_R (64); even, may be 0 */
+  int32_t d_v;         /* per-head value width (128) */
+  int32_t dtype;       /* mla_dtype of stored tensors */
+  double rope_base;    /* RoPE base (10000); > 0 */
+  float softmax_scale; /* score scale, 1/sqrt(d_nope + d_rope) in the pages' models; > 0 */
+  int32_t reserved;    /* must be 0 */
+} mla_config;
+
+/* Library version string, e.g. "mla 0.1.0 gfx950". */
+const char* mla_version(void);
+
+/* Static text for a status code. */
+const char* mla_status_string(mla_status status);
+
+/* Detail text of the calling thread's last non-OK status ("" if none). */
+const char* mla_last_error(void);
+
+/*
+ * mla_rope_append — cache append ("Decoupled RoPE · MLA Part 2", §3.4: a key's position part is
+ * rotated once, when the token is first computed, and stored rotated; §5 steps 2–3).
+ *
+ * For b < batch and i < n_new, with p = len_before[b] + i:
+ *   cache[seq_off[b] + p] = [ c_new[b, i, :] ; RoPE_p(k_rope_new[b, i, :]) ]
+ *  c_new       [batch, n_new, d_latent]  storage dtype, device
+ *  k_rope_new  [batch, n_new, d_rope]    storage dtype, device, unrotated
+ *  cache       rows of d_latent + d_rope storage-dtype elements, device, written
+ *  seq_off     int64 [batch] device: first cache row of each sequence's slab
+ *  len_before  int32 [batch] device: tokens already cached (position of the first new token)
+ */
+mla_status mla_rope_append(const mla_config* cfg, int32_t batch, int32_t n_new,
+                           const void* c_new, const void* k_rope_new, void* cache,
+                           const int64_t* seq_off, const int32_t* len_before, void* stream);
+
+/*
+ * mla_absorb_q — query absorption ("从零理解 MLA", section "矩阵吸收": the content logit
+ * q_C·(W_UK,i c) equals (W_UK,i^T q_C)·c; "Decoupled RoPE · MLA Part 2", §5 step 4).
+ *
+ * For r < n_rows, head i < H:
+ *   q_packed[r, i, 0:d_latent]               = W_UK,i^T q_nope[r, i, :]
+ *   q_packed[r, i, d_latent:d_latent+d_rope] = RoPE_{q_pos[r]}(q_rope[r, i, :])
+ *  q_nope    [n_rows, H, d_nope]   storage dtype, device
+ *  q_rope    [n_rows, H, d_rope]   storage dtype, device, unrotated
+ *  q_pos     int32 [n_rows] device: position of each query row
+ *  w_uk      [H, d_nope, d_latent] storage dtype, device (nn.Linear(d_latent, H*d_nope).weight)
+ *  q_packed  [n_rows, H, d_latent + d_rope] storage dtype, device, written
+ */
+mla_status mla_absorb_q(const mla_config* cfg, int32_t n_rows, const void* q_nope, const void* q_rope,
+                        const int32_t* q_pos, const void* w_uk, void* q_packed, void* stream);
+
+/*
+ * Bytes of device workspace mla_decode_attn needs for these sizes (0 when no split-K partials
+ * are needed). n_splits = 0 selects the library's choice. Returns 0 for invalid arguments.
+ */
+size_t mla_decode_attn_workspace_size(const mla_config* cfg, int32_t batch, int32_t n_q,
+                                      int32_t max_seq_len, int32_t n_splits);
+
+/*
+ * mla_decode_attn — latent attention over the packed cache (scores, mask, softmax, latent sum;
+ * "Decoupled RoPE · MLA Part 2", §3.2 and §5 steps 4–5; value = the latent part of the same
+ * cached row, "从零理解 MLA", section "矩阵吸收").
+ *
+ * Query row t of sequence b sits at position seq_len[b] - n_q + t and sees keys
+ * j <= seq_len[b] - n_q + t (the causal mask with diagonal offset S - L, "从零理解 MLA",
+ * section "KV Cache"); for decode (n_q = 1) that is every cached key including itself.
+ *   s_j   = softmax_scale * <q_packed[b, t, i, :], cache[seq_off[b] + j, :]>   (d_latent + d_rope)
+ *   z     = sum_j softmax(s)_j * cache[seq_off[b] + j, 0:d_latent]
+ *   lse   = ln sum_j exp(s_j)
+ *  q_packed  [batch, n_q, H, d_latent + d_rope] storage dtype, device
+ *  cache     packed rows (see top), device, read
+ *  seq_off   int64 [batch] device;  seq_len int32 [batch] device: keys incl. the n_q new ones
+ *  max_seq_len  host upper bound of seq_len (grid sizing)
+ *  n_splits  split-K chunks per sequence (0 = library choice); results do not depend on it
+ *            beyond float32 summation order
+ *  workspace device scratch of at least mla_decode_attn_workspace_size(...) bytes (may be
+ *            NULL when that size is 0); contents need no initialisation
+ *  z         float32 [batch, n_q, H, d_latent] device, written
+ *  lse       float32 [batch, n_q, H] device, written; may be NULL
+ */
+mla_status mla_decode_attn(const mla_config* cfg, int32_t batch, int32_t n_q, const void* q_packed,
+                           const void* cache, const int64_t* seq_off, const int32_t* seq_len,
+                           int32_t max_seq_len, int32_t n_splits, void* workspace,
+                           size_t workspace_bytes, float* z, float* lse, void* stream);
+
+/*
+ * mla_out_proj — output projection in latent space ("从零理解 MLA", section "矩阵吸收",
+ * output-side equation o_i = W_UV,i z_i; "Decoupled RoPE · MLA Part 2", §5 step 5).
+ *
+ * For r < n_rows, head i:  o[r, i, :] = W_UV,i z[r, i, :]
+ *  z     float32 [n_rows, H, d_latent] device
+ *  w_uv  [H, d_v, d_latent] storage dtype, device (nn.Linear(d_latent, H*d_v).weight)
+ *  o     [n_rows, H, d_v] storage dtype, device, written
+ *  d_model, w_o, u: the optional W_O projection u = W_O concat_i(o_i) is not provided by this
+ *        version; pass d_model = 0, w_o = NULL, u = NULL (anything else returns
+ *        MLA_ERR_UNSUPPORTED).
+ */
+mla_status mla_out_proj(const mla_config* cfg, int32_t n_rows, const float* z, const void* w_uv,
+                        void* o, int32_t d_model, const void* w_o, void* u, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H */

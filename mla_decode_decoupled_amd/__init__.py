@@ -1,0 +1,16 @@
+"""MI355X-native absorbed MLA decode with decoupled RoPE.
+
+The compute path is libmla.so (HIP kernels for gfx950, C ABI in include/mla.h);
+``ops`` holds thin torch wrappers with the same names as the C entry points.
+"""
+
+from .ops import (  # noqa: F401
+    make_config,
+    storage_dtype,
+    mla_rope_append,
+    mla_absorb_q,
+    mla_decode_attn_workspace_size,
+    mla_decode_attn,
+    mla_out_proj,
+    version,
+)

@@ -1,0 +1,188 @@
+// C-ABI entry points of libmla: argument validation, split planning and dispatch.
+// Nothing here allocates or synchronises; every launch goes to the caller's stream.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/mla.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+mla_status fail(mla_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+mla_status ok() {
+  g_err[0] = '\0';
+  return MLA_OK;
+}
+
+mla_status from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(MLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Shared checks on the layer description.
+mla_status check_cfg(const mla_config* cfg, mla::LayerDims* L) {
+  if (cfg == nullptr) return fail(MLA_ERR_INVALID_ARG, "cfg is NULL");
+  if (cfg->reserved != 0) return fail(MLA_ERR_INVALID_ARG, "cfg->reserved must be 0");
+  if (cfg->n_heads < 1 || cfg->d_nope < 1 || cfg->d_latent < 1 || cfg->d_v < 1 || cfg->d_rope < 0)
+    return fail(MLA_ERR_INVALID_ARG, "dims must be positive (d_rope >= 0): H=%d d_nope=%d d_latent=%d d_rope=%d d_v=%d",
+                cfg->n_heads, cfg->d_nope, cfg->d_latent, cfg->d_rope, cfg->d_v);
+  if (cfg->d_rope % 2 != 0) return fail(MLA_ERR_INVALID_ARG, "d_rope must be even, got %d", cfg->d_rope);
+  if (cfg->dtype != MLA_F32 && cfg->dtype != MLA_BF16) return fail(MLA_ERR_INVALID_ARG, "unknown dtype %d", cfg->dtype);
+  if (!(cfg->softmax_scale > 0.0f) || !isfinite(cfg->softmax_scale))
+    return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  if (!(cfg->rope_base > 0.0) || !isfinite(cfg->rope_base)) return fail(MLA_ERR_INVALID_ARG, "rope_base must be finite and > 0");
+  if ((int64_t)cfg->d_latent + cfg->d_rope > mla::kGenericMaxRow)
+    return fail(MLA_ERR_UNSUPPORTED, "d_latent + d_rope = %d exceeds %d", cfg->d_latent + cfg->d_rope, mla::kGenericMaxRow);
+  if (cfg->d_nope > mla::kGenericMaxNope)
+    return fail(MLA_ERR_UNSUPPORTED, "d_nope = %d exceeds %d", cfg->d_nope, mla::kGenericMaxNope);
+  L->n_heads = cfg->n_heads;
+  L->d_nope = cfg->d_nope;
+  L->d_latent = cfg->d_latent;
+  L->d_rope = cfg->d_rope;
+  L->d_v = cfg->d_v;
+  L->rope_base = cfg->rope_base;
+  L->softmax_scale = cfg->softmax_scale;
+  return MLA_OK;
+}
+
+// Chunking of the keys for split-K. n_splits = 0 picks ~512 keys per chunk (at most kMaxSplits).
+mla_status plan_splits(int32_t max_seq_len, int32_t n_splits, mla::SplitPlan* plan) {
+  if (n_splits < 0 || n_splits > mla::kMaxSplits)
+    return fail(MLA_ERR_INVALID_ARG, "n_splits must be in [0, %d], got %d", mla::kMaxSplits, n_splits);
+  int n = n_splits;
+  if (n == 0) {
+    n = (max_seq_len + 511) / 512;
+    if (n > 64) n = 64;
+    if (n < 1) n = 1;
+  }
+  if (n > max_seq_len) n = max_seq_len;
+  plan->chunk_len = (max_seq_len + n - 1) / n;
+  plan->n_chunks = (max_seq_len + plan->chunk_len - 1) / plan->chunk_len;
+  return MLA_OK;
+}
+
+size_t attn_workspace_bytes(const mla::LayerDims& L, int batch, int n_q, const mla::SplitPlan& plan) {
+  if (plan.n_chunks <= 1) return 0;
+  const size_t slots = (size_t)batch * n_q * L.n_heads * plan.n_chunks;
+  return slots * ((size_t)L.d_latent + 2) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_version(void) { return "mla 0.1.0 gfx950"; }
+
+const char* mla_status_string(mla_status s) {
+  switch (s) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG: invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: shape or dtype not supported";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace missing or too small";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP: HIP runtime error";
+  }
+  return "unknown mla_status";
+}
+
+const char* mla_last_error(void) { return g_err; }
+
+mla_status mla_rope_append(const mla_config* cfg, int32_t batch, int32_t n_new, const void* c_new,
+                           const void* k_rope_new, void* cache, const int64_t* seq_off, const int32_t* len_before,
+                           void* stream) {
+  mla::LayerDims L;
+  mla_status s = check_cfg(cfg, &L);
+  if (s != MLA_OK) return s;
+  if (batch < 0 || n_new < 0) return fail(MLA_ERR_INVALID_ARG, "batch and n_new must be >= 0");
+  if (batch == 0 || n_new == 0) return ok();
+  if (batch > 65535) return fail(MLA_ERR_UNSUPPORTED, "batch %d exceeds 65535", batch);
+  if (!c_new || !cache || !seq_off || !len_before || (L.d_rope > 0 && !k_rope_new))
+    return fail(MLA_ERR_INVALID_ARG, "NULL pointer argument");
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = cfg->dtype == MLA_F32
+                     ? mla::launch_rope_append_generic<float>(L, batch, n_new, c_new, k_rope_new, cache, seq_off, len_before, st)
+                     : mla::launch_rope_append_generic<__bf16>(L, batch, n_new, c_new, k_rope_new, cache, seq_off, len_before, st);
+  return from_hip(e, "mla_rope_append launch");
+}
+
+mla_status mla_absorb_q(const mla_config* cfg, int32_t n_rows, const void* q_nope, const void* q_rope,
+                        const int32_t* q_pos, const void* w_uk, void* q_packed, void* stream) {
+  mla::LayerDims L;
+  mla_status s = check_cfg(cfg, &L);
+  if (s != MLA_OK) return s;
+  if (n_rows < 0) return fail(MLA_ERR_INVALID_ARG, "n_rows must be >= 0");
+  if (n_rows == 0) return ok();
+  if (L.n_heads > 65535) return fail(MLA_ERR_UNSUPPORTED, "n_heads %d exceeds 65535", L.n_heads);
+  if (!q_nope || !q_pos || !w_uk || !q_packed || (L.d_rope > 0 && !q_rope))
+    return fail(MLA_ERR_INVALID_ARG, "NULL pointer argument");
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = cfg->dtype == MLA_F32
+                     ? mla::launch_absorb_q_generic<float>(L, n_rows, q_nope, q_rope, q_pos, w_uk, q_packed, st)
+                     : mla::launch_absorb_q_generic<__bf16>(L, n_rows, q_nope, q_rope, q_pos, w_uk, q_packed, st);
+  return from_hip(e, "mla_absorb_q launch");
+}
+
+size_t mla_decode_attn_workspace_size(const mla_config* cfg, int32_t batch, int32_t n_q, int32_t max_seq_len,
+                                      int32_t n_splits) {
+  mla::LayerDims L;
+  if (check_cfg(cfg, &L) != MLA_OK) return 0;
+  if (batch <= 0 || n_q <= 0 || max_seq_len < n_q) return 0;
+  mla::SplitPlan plan;
+  if (plan_splits(max_seq_len, n_splits, &plan) != MLA_OK) return 0;
+  return attn_workspace_bytes(L, batch, n_q, plan);
+}
+
+mla_status mla_decode_attn(const mla_config* cfg, int32_t batch, int32_t n_q, const void* q_packed, const void* cache,
+                           const int64_t* seq_off, const int32_t* seq_len, int32_t max_seq_len, int32_t n_splits,
+                           void* workspace, size_t workspace_bytes, float* z, float* lse, void* stream) {
+  mla::LayerDims L;
+  mla_status s = check_cfg(cfg, &L);
+  if (s != MLA_OK) return s;
+  if (batch < 0 || n_q < 0) return fail(MLA_ERR_INVALID_ARG, "batch and n_q must be >= 0");
+  if (batch == 0 || n_q == 0) return ok();
+  if (max_seq_len < n_q) return fail(MLA_ERR_INVALID_ARG, "max_seq_len (%d) must be >= n_q (%d)", max_seq_len, n_q);
+  if ((int64_t)batch * n_q > 65535) return fail(MLA_ERR_UNSUPPORTED, "batch * n_q exceeds 65535");
+  if (L.n_heads > 65535) return fail(MLA_ERR_UNSUPPORTED, "n_heads %d exceeds 65535", L.n_heads);
+  if (!q_packed || !cache || !seq_off || !seq_len || !z) return fail(MLA_ERR_INVALID_ARG, "NULL pointer argument");
+  mla::SplitPlan plan;
+  s = plan_splits(max_seq_len, n_splits, &plan);
+  if (s != MLA_OK) return s;
+  const size_t need = attn_workspace_bytes(L, batch, n_q, plan);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(MLA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu%s", need, workspace_bytes,
+                workspace ? "" : " (NULL)");
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = cfg->dtype == MLA_F32
+                     ? mla::launch_attn_generic<float>(L, batch, n_q, q_packed, cache, seq_off, seq_len, plan, workspace, z, lse, st)
+                     : mla::launch_attn_generic<__bf16>(L, batch, n_q, q_packed, cache, seq_off, seq_len, plan, workspace, z, lse, st);
+  return from_hip(e, "mla_decode_attn launch");
+}
+
+mla_status mla_out_proj(const mla_config* cfg, int32_t n_rows, const float* z, const void* w_uv, void* o,
+                        int32_t d_model, const void* w_o, void* u, void* stream) {
+  mla::LayerDims L;
+  mla_status s = check_cfg(cfg, &L);
+  if (s != MLA_OK) return s;
+  if (n_rows < 0) return fail(MLA_ERR_INVALID_ARG, "n_rows must be >= 0");
+  if (w_o != nullptr || u != nullptr || d_model != 0)
+    return fail(MLA_ERR_UNSUPPORTED, "the W_O projection is not provided; pass d_model = 0, w_o = u = NULL");
+  if (n_rows == 0) return ok();
+  if (L.n_heads > 65535) return fail(MLA_ERR_UNSUPPORTED, "n_heads %d exceeds 65535", L.n_heads);
+  if (!z || !w_uv || !o) return fail(MLA_ERR_INVALID_ARG, "NULL pointer argument");
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = cfg->dtype == MLA_F32 ? mla::launch_out_proj_generic<float>(L, n_rows, z, w_uv, o, st)
+                                       : mla::launch_out_proj_generic<__bf16>(L, n_rows, z, w_uv, o, st);
+  return from_hip(e, "mla_out_proj launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,44 @@
+// Host-side launcher interface shared by the C-ABI layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla {
+
+struct LayerDims {
+  int n_heads, d_nope, d_latent, d_rope, d_v;
+  double rope_base;
+  float softmax_scale;
+};
+
+// How one sequence's keys are cut into split-K chunks: chunk k covers keys
+// [k * chunk_len, (k + 1) * chunk_len) of the visible range.
+struct SplitPlan {
+  int n_chunks;
+  int chunk_len;
+};
+
+constexpr int kMaxSplits = 256;
+
+// Largest row (d_latent + d_rope) and d_nope the generic kernels accept.
+constexpr int kGenericMaxRow = 1024;
+constexpr int kGenericMaxNope = 256;
+
+template <typename T>
+hipError_t launch_rope_append_generic(const LayerDims& L, int batch, int n_new, const void* c_new, const void* k_new,
+                                      void* cache, const int64_t* seq_off, const int32_t* len_before,
+                                      hipStream_t stream);
+template <typename T>
+hipError_t launch_absorb_q_generic(const LayerDims& L, int n_rows, const void* q_nope, const void* q_rope,
+                                   const int32_t* q_pos, const void* w_uk, void* q_packed, hipStream_t stream);
+template <typename T>
+hipError_t launch_attn_generic(const LayerDims& L, int batch, int n_q, const void* q_packed, const void* cache,
+                               const int64_t* seq_off, const int32_t* seq_len, const SplitPlan& plan, void* workspace,
+                               float* z, float* lse, hipStream_t stream);
+template <typename T>
+hipError_t launch_out_proj_generic(const LayerDims& L, int n_rows, const float* z, const void* w_uv, void* o,
+                                   hipStream_t stream);
+
+}  // namespace mla

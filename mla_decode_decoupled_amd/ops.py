@@ -1,0 +1,148 @@
+"""Torch-facing wrappers with the C-ABI's names (include/mla.h).
+
+Each wrapper checks dtype, device, contiguity and shapes, raises ValueError on
+a mismatch, and otherwise passes raw device pointers and the current HIP stream
+to libmla. Nothing here computes any part of the attention.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import MLA_BF16, MLA_F32, MlaConfig, check, lib
+
+_DT = {MLA_F32: torch.float32, MLA_BF16: torch.bfloat16}
+
+
+def make_config(n_heads: int, d_nope: int, d_latent: int, d_rope: int, d_v: int, dtype: str = "bf16",
+                rope_base: float = 10000.0, softmax_scale: Optional[float] = None) -> MlaConfig:
+    """Layer description; softmax_scale defaults to 1/sqrt(d_nope + d_rope)."""
+    code = {"f32": MLA_F32, "float32": MLA_F32, "bf16": MLA_BF16, "bfloat16": MLA_BF16}[dtype]
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d_nope + d_rope)
+    return MlaConfig(n_heads, d_nope, d_latent, d_rope, d_v, code, float(rope_base), float(softmax_scale), 0)
+
+
+def storage_dtype(cfg: MlaConfig) -> torch.dtype:
+    return _DT[cfg.dtype]
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t: torch.Tensor):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def mla_rope_append(cfg: MlaConfig, c_new: torch.Tensor, k_rope_new: torch.Tensor, cache: torch.Tensor,
+                    seq_off: torch.Tensor, len_before: torch.Tensor) -> None:
+    """cache[seq_off[b] + len_before[b] + i] = [c_new[b, i] ; RoPE(k_rope_new[b, i])]."""
+    dt = storage_dtype(cfg)
+    if c_new.dim() != 3:
+        raise ValueError("c_new must be [batch, n_new, d_latent]")
+    B, n_new = c_new.shape[0], c_new.shape[1]
+    dev = c_new.device
+    _need(c_new, "c_new", dt, (B, n_new, cfg.d_latent))
+    _need(k_rope_new, "k_rope_new", dt, (B, n_new, cfg.d_rope), dev)
+    _need(cache, "cache", dt, None, dev)
+    if cache.dim() != 2 or cache.shape[1] != cfg.d_latent + cfg.d_rope:
+        raise ValueError("cache must be [rows, d_latent + d_rope]")
+    _need(seq_off, "seq_off", torch.int64, (B,), dev)
+    _need(len_before, "len_before", torch.int32, (B,), dev)
+    check(lib.mla_rope_append(cfg, B, n_new, _ptr(c_new), _ptr(k_rope_new), _ptr(cache), _ptr(seq_off),
+                              _ptr(len_before), _stream(cache)), "mla_rope_append")
+
+
+def mla_absorb_q(cfg: MlaConfig, q_nope: torch.Tensor, q_rope: torch.Tensor, q_pos: torch.Tensor,
+                 w_uk: torch.Tensor, q_packed: torch.Tensor) -> None:
+    """q_packed[r, i] = [W_UK,i^T q_nope[r, i] ; RoPE_{q_pos[r]}(q_rope[r, i])]."""
+    dt = storage_dtype(cfg)
+    H = cfg.n_heads
+    R = q_nope.shape[0] if q_nope.dim() == 3 else -1
+    dev = q_nope.device
+    _need(q_nope, "q_nope", dt, (R, H, cfg.d_nope))
+    _need(q_rope, "q_rope", dt, (R, H, cfg.d_rope), dev)
+    _need(q_pos, "q_pos", torch.int32, (R,), dev)
+    _need(w_uk, "w_uk", dt, (H, cfg.d_nope, cfg.d_latent), dev)
+    _need(q_packed, "q_packed", dt, (R, H, cfg.d_latent + cfg.d_rope), dev)
+    check(lib.mla_absorb_q(cfg, R, _ptr(q_nope), _ptr(q_rope), _ptr(q_pos), _ptr(w_uk), _ptr(q_packed),
+                           _stream(q_packed)), "mla_absorb_q")
+
+
+def mla_decode_attn_workspace_size(cfg: MlaConfig, batch: int, n_q: int, max_seq_len: int, n_splits: int = 0) -> int:
+    return int(lib.mla_decode_attn_workspace_size(cfg, batch, n_q, max_seq_len, n_splits))
+
+
+def mla_decode_attn(cfg: MlaConfig, q_packed: torch.Tensor, cache: torch.Tensor, seq_off: torch.Tensor,
+                    seq_len: torch.Tensor, max_seq_len: int, z: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                    n_splits: int = 0, workspace: Optional[torch.Tensor] = None) -> None:
+    """Latent attention of q_packed [batch, n_q, H, d_latent + d_rope] over the cache; writes z (and lse)."""
+    dt = storage_dtype(cfg)
+    H, row = cfg.n_heads, cfg.d_latent + cfg.d_rope
+    if q_packed.dim() != 4:
+        raise ValueError("q_packed must be [batch, n_q, H, d_latent + d_rope]")
+    B, n_q = q_packed.shape[0], q_packed.shape[1]
+    dev = q_packed.device
+    _need(q_packed, "q_packed", dt, (B, n_q, H, row))
+    _need(cache, "cache", dt, None, dev)
+    _need(seq_off, "seq_off", torch.int64, (B,), dev)
+    _need(seq_len, "seq_len", torch.int32, (B,), dev)
+    _need(z, "z", torch.float32, (B, n_q, H, cfg.d_latent), dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, n_q, H), dev)
+    ws_bytes = 0
+    if workspace is not None:
+        _need(workspace, "workspace", workspace.dtype, None, dev)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    check(lib.mla_decode_attn(cfg, B, n_q, _ptr(q_packed), _ptr(cache), _ptr(seq_off), _ptr(seq_len),
+                              int(max_seq_len), int(n_splits), _ptr(workspace), ws_bytes, _ptr(z), _ptr(lse),
+                              _stream(z)), "mla_decode_attn")
+
+
+def mla_out_proj(cfg: MlaConfig, z: torch.Tensor, w_uv: torch.Tensor, o: torch.Tensor) -> None:
+    """o[r, i] = W_UV,i z[r, i]."""
+    dt = storage_dtype(cfg)
+    H = cfg.n_heads
+    R = z.shape[0] if z.dim() == 3 else -1
+    dev = z.device
+    _need(z, "z", torch.float32, (R, H, cfg.d_latent))
+    _need(w_uv, "w_uv", dt, (H, cfg.d_v, cfg.d_latent), dev)
+    _need(o, "o", dt, (R, H, cfg.d_v), dev)
+    check(lib.mla_out_proj(cfg, R, _ptr(z), _ptr(w_uv), _ptr(o), 0, None, None, _stream(o)), "mla_out_proj")
+
+
+def version() -> str:
+    return lib.mla_version().decode()
+
+
+__all__ = [
+    "make_config",
+    "storage_dtype",
+    "mla_rope_append",
+    "mla_absorb_q",
+    "mla_decode_attn_workspace_size",
+    "mla_decode_attn",
+    "mla_out_proj",
+    "version",
+    "_lib",
+]

@@ -1,0 +1,129 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol the header declares, and
+rejects bad arguments with the documented status before launching anything."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from mla_decode_decoupled_amd import _lib
+from mla_decode_decoupled_amd._lib import (MLA_BF16, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE,
+                                           MLA_F32, MLA_OK, MlaConfig, lib)
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "mla.h")
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation first
+
+
+def _declared():
+    text = open(HEADER).read()
+    return set(re.findall(r"^\s*(?:const char\*|mla_status|size_t)\s+(mla_\w+)\s*\(", text, re.M))
+
+
+def test_header_symbols_exported():
+    names = _declared()
+    assert {"mla_rope_append", "mla_absorb_q", "mla_decode_attn", "mla_out_proj",
+            "mla_decode_attn_workspace_size", "mla_status_string", "mla_last_error", "mla_version"} <= names
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in _lib.SIGNATURES, n
+
+
+def test_config_struct_layout():
+    assert ctypes.sizeof(MlaConfig) == 40
+    assert MlaConfig.rope_base.offset == 24 and MlaConfig.softmax_scale.offset == 32
+
+
+def cfg(**kw):
+    base = dict(n_heads=128, d_nope=128, d_latent=512, d_rope=64, d_v=128, dtype=MLA_BF16, rope_base=10000.0,
+                softmax_scale=0.0721687836, reserved=0)
+    base.update(kw)
+    return MlaConfig(**base)
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(n_heads=0), MLA_ERR_INVALID_ARG),
+    (dict(d_latent=-1), MLA_ERR_INVALID_ARG),
+    (dict(d_rope=7), MLA_ERR_INVALID_ARG),
+    (dict(dtype=9), MLA_ERR_INVALID_ARG),
+    (dict(softmax_scale=0.0), MLA_ERR_INVALID_ARG),
+    (dict(softmax_scale=float("nan")), MLA_ERR_INVALID_ARG),
+    (dict(rope_base=-1.0), MLA_ERR_INVALID_ARG),
+    (dict(reserved=1), MLA_ERR_INVALID_ARG),
+    (dict(d_latent=2048), MLA_ERR_UNSUPPORTED),
+    (dict(d_nope=512), MLA_ERR_UNSUPPORTED),
+])
+def test_bad_config_rejected_by_every_call(bad, code):
+    c = cfg(**bad)
+    assert lib.mla_rope_append(c, 1, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == code
+    assert lib.mla_absorb_q(c, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == code
+    assert lib.mla_decode_attn(c, 1, 1, FAKE, FAKE, FAKE, FAKE, 10, 0, None, 0, FAKE, None, None) == code
+    assert lib.mla_out_proj(c, 1, FAKE, FAKE, FAKE, 0, None, None, None) == code
+    assert lib.mla_decode_attn_workspace_size(c, 1, 1, 10, 0) == 0
+    assert lib.mla_last_error() != b""
+
+
+def test_null_config():
+    assert lib.mla_absorb_q(None, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == MLA_ERR_INVALID_ARG
+    assert b"NULL" in lib.mla_last_error()
+
+
+def test_null_pointers_and_negative_sizes():
+    c = cfg()
+    assert lib.mla_rope_append(c, 1, 1, None, FAKE, FAKE, FAKE, FAKE, None) == MLA_ERR_INVALID_ARG
+    assert lib.mla_rope_append(c, -1, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == MLA_ERR_INVALID_ARG
+    assert lib.mla_absorb_q(c, 2, FAKE, FAKE, None, FAKE, FAKE, None) == MLA_ERR_INVALID_ARG
+    assert lib.mla_absorb_q(c, -2, FAKE, FAKE, FAKE, FAKE, FAKE, None) == MLA_ERR_INVALID_ARG
+    assert lib.mla_decode_attn(c, 1, 1, FAKE, None, FAKE, FAKE, 10, 0, None, 0, FAKE, None, None) == MLA_ERR_INVALID_ARG
+    assert lib.mla_decode_attn(c, 1, 1, FAKE, FAKE, FAKE, FAKE, 10, 0, None, 0, None, None, None) == MLA_ERR_INVALID_ARG
+    assert lib.mla_out_proj(c, 1, None, FAKE, FAKE, 0, None, None, None) == MLA_ERR_INVALID_ARG
+
+
+def test_decode_attn_shape_rules():
+    c = cfg()
+    # max_seq_len below n_q
+    assert lib.mla_decode_attn(c, 1, 8, FAKE, FAKE, FAKE, FAKE, 4, 0, None, 0, FAKE, None, None) == MLA_ERR_INVALID_ARG
+    # split count outside [0, 256]
+    assert lib.mla_decode_attn(c, 1, 1, FAKE, FAKE, FAKE, FAKE, 4096, 999, None, 0, FAKE, None, None) == MLA_ERR_INVALID_ARG
+    assert lib.mla_decode_attn(c, 1, 1, FAKE, FAKE, FAKE, FAKE, 4096, -1, None, 0, FAKE, None, None) == MLA_ERR_INVALID_ARG
+
+
+def test_workspace_rules():
+    c = cfg()
+    need = lib.mla_decode_attn_workspace_size(c, 4, 1, 131073, 64)
+    assert need > 0
+    assert need == lib.mla_decode_attn_workspace_size(c, 4, 1, 131073, 64)
+    assert lib.mla_decode_attn(c, 4, 1, FAKE, FAKE, FAKE, FAKE, 131073, 64, None, need, FAKE, None, None) == MLA_ERR_WORKSPACE
+    assert lib.mla_decode_attn(c, 4, 1, FAKE, FAKE, FAKE, FAKE, 131073, 64, FAKE, need - 1, FAKE, None, None) == MLA_ERR_WORKSPACE
+    # a single split needs no workspace
+    assert lib.mla_decode_attn_workspace_size(c, 1, 1, 100, 1) == 0
+
+
+def test_w_o_projection_not_provided():
+    c = cfg()
+    assert lib.mla_out_proj(c, 1, FAKE, FAKE, FAKE, 7168, FAKE, FAKE, None) == MLA_ERR_UNSUPPORTED
+    assert lib.mla_out_proj(c, 1, FAKE, FAKE, FAKE, 0, None, FAKE, None) == MLA_ERR_UNSUPPORTED
+
+
+def test_empty_work_returns_ok_without_launch():
+    c = cfg(dtype=MLA_F32)
+    assert lib.mla_rope_append(c, 0, 5, None, None, None, None, None, None) == MLA_OK
+    assert lib.mla_absorb_q(c, 0, None, None, None, None, None, None) == MLA_OK
+    assert lib.mla_decode_attn(c, 0, 1, None, None, None, None, 0, 0, None, 0, None, None, None) == MLA_OK
+    assert lib.mla_out_proj(c, 0, None, None, None, 0, None, None, None) == MLA_OK
+    assert lib.mla_last_error() == b""
+
+
+def test_status_strings():
+    for s in range(5):
+        assert lib.mla_status_string(s).startswith(b"MLA_")
+    assert b"gfx950" in lib.mla_version()
+
+
+def test_python_wrappers_validate_before_calling():
+    torch = pytest.importorskip("torch")
+    import mla_decode_decoupled_amd as mla
+    c = mla.make_config(4, 16, 32, 8, 16, "f32")
+    with pytest.raises(ValueError):
+        mla.mla_absorb_q(c, torch.zeros(1, 4, 16), torch.zeros(1, 4, 8), torch.zeros(1, dtype=torch.int32),
+                         torch.zeros(4, 16, 32), torch.zeros(1, 4, 40))   # host tensors are refused

@@ -1,0 +1,246 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle, on the same seeded inputs.
+
+Bar (per output): fp32 storage -> max|err| <= 1e-5; bf16 storage -> max|err| <= 2e-2 and
+rel-L2 <= 1e-2. Cache latents are copies and must match bit for bit; rotated position keys
+must sit within one bf16 rounding (2^-8 relative) or float32 rounding of the fp64 value.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle as O  # noqa: E402
+from mla_workloads import CONFIGS, MLAConfig  # noqa: E402
+from mla_workloads import generate as G  # noqa: E402
+
+from .gpu_pipeline import assert_close, host_inputs, lib_config, np32, run_pipeline, tdev  # noqa: E402
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def _oracle(hi, b, heads=None, rows=None, scale=None):
+    cfg = hi.cfg
+    return O.explicit_attention(hi.c[b], hi.k_pre[b], hi.q_nope[b], hi.q_rope[b], hi.w_uk, hi.w_uv,
+                                scale=cfg.softmax_scale if scale is None else scale, base=cfg.rope_base,
+                                heads=heads, rows=rows)
+
+
+def _check_cache(run, hi, b):
+    cfg = hi.cfg
+    n = int(hi.lens[b])
+    off = int(run.seq_off[b].item())
+    rows = np32(run.cache[off:off + n])
+    assert np.array_equal(rows[:, :cfg.d_latent], hi.c[b].astype(np.float64)), "latent rows must be exact copies"
+    k_ref = O.rope_rotate(hi.k_pre[b], np.arange(n), cfg.rope_base)
+    rel = 2.0 ** -8 if cfg.dtype == "bf16" else 2.0 ** -23
+    err = np.abs(rows[:, cfg.d_latent:] - k_ref)
+    assert np.all(err <= rel * np.abs(k_ref) + 1e-7), f"rotated keys: max err {err.max():.3e}"
+
+
+def _check_qpacked(run, hi, b, rows=None):
+    cfg = hi.cfg
+    n = int(hi.lens[b])
+    rows = np.arange(cfg.n_q) if rows is None else np.asarray(rows)
+    pos = n - cfg.n_q + rows
+    ref = O.packed_query(hi.q_nope[b][rows], hi.q_rope[b][rows], pos, hi.w_uk, cfg.rope_base)
+    assert_close(np32(run.q_packed[b][rows]), ref, cfg.dtype, f"q_packed[{b}]")
+
+
+def _check_outputs(run, hi, b, heads=None, rows=None, scale=None):
+    cfg = hi.cfg
+    ref = _oracle(hi, b, heads=heads, rows=rows, scale=scale)
+    sel_r = np.arange(cfg.n_q) if rows is None else np.asarray(rows)
+    sel_h = np.arange(cfg.n_heads) if heads is None else np.asarray(heads)
+    z = np32(run.z[b])[sel_r][:, sel_h]
+    lse = np32(run.lse[b])[sel_r][:, sel_h]
+    o = np32(run.o[b])[sel_r][:, sel_h]
+    stats = {
+        "z": assert_close(z, ref["z"], cfg.dtype, f"z[{b}]"),
+        "lse": assert_close(lse, ref["lse"], cfg.dtype, f"lse[{b}]"),
+        "o": assert_close(o, ref["o"], cfg.dtype, f"o[{b}]"),
+    }
+    print(f"seq {b}: " + ", ".join(f"{k} max {v['max_err']:.2e} relL2 {v['rel_l2']:.2e}" for k, v in stats.items()),
+          flush=True)
+    return stats
+
+
+# ------------------------------------------------------------------ the five workloads
+def test_tiny_fp32_all_outputs():
+    hi = host_inputs(CONFIGS[0])
+    run = run_pipeline(hi)
+    _check_cache(run, hi, 0)
+    _check_qpacked(run, hi, 0)
+    _check_outputs(run, hi, 0)
+
+
+def test_v3_decode_4k_all_heads():
+    hi = host_inputs(CONFIGS[1])
+    run = run_pipeline(hi)
+    _check_cache(run, hi, 0)
+    _check_qpacked(run, hi, 0)
+    _check_outputs(run, hi, 0)
+
+
+@pytest.mark.parametrize("n_splits", [1, 3, 64])
+def test_split_count_does_not_change_results(n_splits):
+    hi = host_inputs(CONFIGS[1])
+    base = run_pipeline(hi, n_splits=9)
+    other = run_pipeline(hi, n_splits=n_splits)
+    dz = np.abs(np32(other.z) - np32(base.z)).max()
+    dl = np.abs(np32(other.lse) - np32(base.lse)).max()
+    assert dz <= 1e-5 and dl <= 1e-5, (dz, dl)
+
+
+def test_ragged_batch_sampled():
+    cfg = CONFIGS[2]
+    hi = host_inputs(cfg)
+    run = run_pipeline(hi)
+    lens = hi.lens
+    picks = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 17})
+    heads = [0, 63, 127]
+    for b in picks:
+        _check_cache(run, hi, b)
+        _check_qpacked(run, hi, b)
+        _check_outputs(run, hi, b, heads=heads)
+    # a sequence computed alone equals the same sequence inside the batch
+    b = picks[-1]
+    alone = host_inputs(MLAConfig(**{**cfg.__dict__, "batch": 1}), lens=[int(lens[b])])
+    alone.c, alone.k_pre = [hi.c[b]], [hi.k_pre[b]]
+    alone.q_nope, alone.q_rope = hi.q_nope[b:b + 1], hi.q_rope[b:b + 1]
+    run1 = run_pipeline(alone)
+    assert np.abs(np32(run1.z[0]) - np32(run.z[b])).max() <= 1e-5
+    assert np.abs(np32(run1.lse[0]) - np32(run.lse[b])).max() <= 1e-5
+
+
+@pytest.mark.slow
+def test_long_context_128k_sampled():
+    cfg = CONFIGS[3]
+    hi = host_inputs(cfg)
+    run = run_pipeline(hi, n_splits=cfg.n_splits)
+    _check_cache(run, hi, 0)
+    _check_qpacked(run, hi, 3)
+    _check_outputs(run, hi, 0, heads=[5, 100])
+    _check_outputs(run, hi, 3, heads=[64])
+
+
+@pytest.mark.slow
+def test_chunked_prefill_sampled():
+    cfg = CONFIGS[4]
+    hi = host_inputs(cfg)
+    run = run_pipeline(hi)
+    _check_cache(run, hi, 1)
+    _check_qpacked(run, hi, 1, rows=[0, 1, 1000, 2047])
+    _check_outputs(run, hi, 1, heads=[0, 127], rows=[0, 1, 1000, 2047])
+    _check_outputs(run, hi, 0, heads=[64], rows=[2047, 5])
+
+
+# ------------------------------------------------------------------------ edge cases
+def _small_cfg(cid, dtype, n_q=1, batch=1, fixed_len=40, H=4, d_c=32, d_r=8, d=16, rms=False):
+    return MLAConfig(cid=cid, name="small", batch=batch, n_heads=H, d_model=64, q_lora=None, d_latent=d_c,
+                     d_rope=d_r, d_nope=d, d_v=d, n_q=n_q, dtype=dtype, fixed_len=fixed_len, latent_rms_norm=rms)
+
+
+def test_hand_worked_example_on_gpu():
+    """The page's 3-token example run through the four calls (scale 1)."""
+    with open(os.path.join(os.path.dirname(__file__), "golden", "decoupled_rope_hand_example.json")) as f:
+        g = json.load(f)
+    cfg = _small_cfg(200, "f32", fixed_len=3, H=2, d_c=2, d_r=2, d=2)
+    hi = host_inputs(cfg)
+    hi.c = [np.array([[1, 0], [0, 1], [0.5, 0.5]], dtype=np.float32)]
+    hi.k_pre = [np.asarray(g["expected_k_rope_pre"], dtype=np.float32)]
+    hi.q_nope = np.array([[[[1, 0], [0, 1]]]], dtype=np.float32)
+    hi.q_rope = np.asarray(g["expected_q_rope_pre"], dtype=np.float32)[None, None]
+    hi.w_uk = np.asarray(g["constructed"]["w_uk"], dtype=np.float32)
+    hi.w_uv = np.asarray(g["constructed"]["w_uv"], dtype=np.float32)
+    run = run_pipeline(hi, scale=1.0)
+    rows = np32(run.cache)
+    assert np.max(np.abs(rows[:, 2:] - np.asarray(g["expected_k_rot"]))) <= g["printed_precision"]
+    qp = np32(run.q_packed[0, 0])
+    assert np.max(np.abs(qp[:, 2:] - np.asarray(g["expected_q_rot"]))) <= g["printed_precision"]
+    # lse of the page's total scores (printed to 3 decimals, so 3 * 5e-4 slack)
+    tot = np.asarray(g["expected_total_scores"])
+    lse_page = np.log(np.exp(tot).sum(axis=1))
+    assert np.max(np.abs(np32(run.lse[0, 0]) - lse_page)) <= 1.5e-3
+    _check_outputs(run, hi, 0, scale=1.0)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_single_key_sequence(dtype):
+    cfg = _small_cfg(201, dtype, fixed_len=1)
+    hi = host_inputs(cfg)
+    run = run_pipeline(hi)
+    assert np.array_equal(np32(run.z[0, 0]), np.broadcast_to(hi.c[0][0].astype(np.float64), (4, 32)))
+    _check_outputs(run, hi, 0)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prefill_from_empty_cache(dtype):
+    """n_q = seq_len: the square causal mask of a full forward."""
+    cfg = _small_cfg(202, dtype, n_q=37, fixed_len=37)
+    hi = host_inputs(cfg)
+    run = run_pipeline(hi)
+    _check_cache(run, hi, 0)
+    _check_qpacked(run, hi, 0)
+    _check_outputs(run, hi, 0)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_ragged_small_many_splits(dtype):
+    cfg = _small_cfg(203, dtype, batch=5, fixed_len=None, n_q=3)
+    cfg = MLAConfig(**{**cfg.__dict__, "ragged_range": (0, 300)})
+    hi = host_inputs(cfg)
+    run = run_pipeline(hi, n_splits=16)
+    for b in range(5):
+        _check_cache(run, hi, b)
+        _check_outputs(run, hi, b)
+
+
+def test_multi_step_decode_matches_oracle_each_step():
+    """Append-then-attend over several consecutive tokens, one call sequence per token."""
+    import mla_decode_decoupled_amd as mla
+    cfg = _small_cfg(204, "f32", fixed_len=24)
+    hi = host_inputs(cfg)
+    lc = lib_config(cfg)
+    H = cfg.n_heads
+    n_total = 24
+    cache = torch.full((n_total, cfg.row), float("nan"), dtype=torch.float32, device="cuda")
+    seq_off = torch.zeros(1, dtype=torch.int64, device="cuda")
+    qn_all = G._normal(cfg, G.TensorId.Q_NOPE, (n_total, H, cfg.d_nope), 1.0, 7)
+    qr_all = G._normal(cfg, G.TensorId.Q_ROPE, (n_total, H, cfg.d_rope), 1.0, 7)
+    w_uk, w_uv = tdev(hi.w_uk, torch.float32), tdev(hi.w_uv, torch.float32)
+    for t in range(n_total):
+        mla.mla_rope_append(lc, tdev(hi.c[0][None, t:t + 1], torch.float32),
+                            tdev(hi.k_pre[0][None, t:t + 1], torch.float32), cache, seq_off,
+                            torch.full((1,), t, dtype=torch.int32, device="cuda"))
+        qp = torch.empty((1, H, cfg.row), dtype=torch.float32, device="cuda")
+        mla.mla_absorb_q(lc, tdev(qn_all[t:t + 1], torch.float32), tdev(qr_all[t:t + 1], torch.float32),
+                         torch.full((1,), t, dtype=torch.int32, device="cuda"), w_uk, qp)
+        z = torch.empty((1, 1, H, cfg.d_latent), dtype=torch.float32, device="cuda")
+        lse = torch.empty((1, 1, H), dtype=torch.float32, device="cuda")
+        mla.mla_decode_attn(lc, qp.view(1, 1, H, cfg.row), cache, seq_off,
+                            torch.full((1,), t + 1, dtype=torch.int32, device="cuda"), t + 1, z, lse)
+        o = torch.empty((1, H, cfg.d_v), dtype=torch.float32, device="cuda")
+        mla.mla_out_proj(lc, z.view(1, H, cfg.d_latent), w_uv, o)
+        ref = O.explicit_attention(hi.c[0][:t + 1], hi.k_pre[0][:t + 1], qn_all[t:t + 1], qr_all[t:t + 1],
+                                   hi.w_uk, hi.w_uv, scale=cfg.softmax_scale, base=cfg.rope_base)
+        assert_close(np32(o)[0], ref["o"][0], "f32", f"o step {t}")
+        assert_close(np32(z)[0, 0], ref["z"][0], "f32", f"z step {t}")
+
+
+def test_empty_work_is_a_noop():
+    import mla_decode_decoupled_amd as mla
+    from mla_decode_decoupled_amd import _lib
+    cfg = lib_config(_small_cfg(205, "f32"))
+    z = torch.full((1, 1, 4, 32), 7.0, device="cuda")
+    st = _lib.lib.mla_decode_attn(cfg, 0, 1, None, None, None, None, 10, 0, None, 0, z.data_ptr(), None, None)
+    assert st == _lib.MLA_OK
+    st = _lib.lib.mla_rope_append(cfg, 3, 0, None, None, None, None, None, None)
+    assert st == _lib.MLA_OK
+    torch.cuda.synchronize()
+    assert torch.all(z == 7.0)
