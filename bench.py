@@ -1,0 +1,262 @@
+#!/usr/bin/env python3
+"""Benchmark of one absorbed-MLA decode step on one MI355X.
+
+A step is one pass of the whole hot path over one batch: mla_rope_append (the
+new tokens), mla_absorb_q, mla_decode_attn (+ split-K merge) and mla_out_proj,
+all through the C ABI. The default workload is the DeepSeek-V3-shaped decode
+step (batch 1, 128 heads, 512-dim latent, 64-dim position part, 4096 cached
+tokens + 1 new, bf16). Inputs are seeded synthetic data of that shape and live
+in HBM before timing starts. Unless --hot is given, every step reads its own
+copy of the cache, weights and queries (copies rotated so the working set is
+at least 1 GiB, four times the 256 MB last-level cache), so the bytes really
+come from HBM.
+
+Prints one JSON line (rank 0) with throughput, a roofline object for the
+dominant kernel (HIP events around its launches inside the timed region) and
+the fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=1, help="workload id (1 = V3 decode, batch 1, S=4096)")
+    ap.add_argument("--n-splits", type=int, default=0, help="split-K chunks per sequence (0 = library choice)")
+    ap.add_argument("--hot", action="store_true", help="reuse one copy of every input (cache-hot numbers)")
+    ap.add_argument("--copies", type=int, default=0, help="input copies to rotate (0 = enough for 1 GiB)")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0, help="budget for the CPU oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--verbose", action="store_true")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus_requested": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mla_decode_decoupled_amd as mla
+    from mla_workloads import get_config
+    from mla_workloads import generate as G
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = get_config(args.config)
+    lc = mla.make_config(cfg.n_heads, cfg.d_nope, cfg.d_latent, cfg.d_rope, cfg.d_v, cfg.dtype, cfg.rope_base)
+    dt = mla.storage_dtype(lc)
+    esz = 2 if cfg.dtype == "bf16" else 4
+    B, n_q, H, row = cfg.batch, cfg.n_q, cfg.n_heads, cfg.row
+    lens = G.seq_lens(cfg)
+    R = B * n_q
+    max_len = int(lens.max())
+    n_splits = args.n_splits or cfg.n_splits
+
+    # ------------------------------------------------------------------ inputs (host, seeded)
+    t0 = time.time()
+    c_host = [G.cache_latent(cfg, b, int(lens[b])) for b in range(B)]
+    k_host = [G.cache_rope_pre(cfg, b, int(lens[b])) for b in range(B)]
+    qn_host = np.stack([G.query_nope(cfg, b) for b in range(B)]).reshape(R, H, cfg.d_nope)
+    qr_host = np.stack([G.query_rope_pre(cfg, b) for b in range(B)]).reshape(R, H, cfg.d_rope)
+    wuk_host, wuv_host = G.weight_uk(cfg), G.weight_uv(cfg)
+    up = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(dt)  # noqa: E731
+
+    offs = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    seq_off = torch.from_numpy(offs).to(dev)
+    seq_len = torch.from_numpy(lens.astype(np.int32)).to(dev)
+    len_before = torch.from_numpy((lens - n_q).astype(np.int32)).to(dev)
+    q_pos = torch.from_numpy(np.concatenate([np.arange(int(l) - n_q, int(l)) for l in lens]).astype(np.int32)).to(dev)
+    c_new = up(np.stack([c_host[b][int(lens[b]) - n_q:] for b in range(B)]))
+    k_new = up(np.stack([k_host[b][int(lens[b]) - n_q:] for b in range(B)]))
+
+    # one copy: cache (history appended by the library itself), weights, queries
+    cache0 = torch.empty((int(lens.sum()), row), dtype=dt, device=dev)
+    for b in range(B):
+        h = int(lens[b]) - n_q
+        if h > 0:
+            mla.mla_rope_append(lc, up(c_host[b][None, :h]), up(k_host[b][None, :h]), cache0, seq_off[b:b + 1],
+                                torch.zeros(1, dtype=torch.int32, device=dev))
+    wuk0, wuv0 = up(wuk_host), up(wuv_host)
+    qn0, qr0 = up(qn_host), up(qr_host)
+    per_copy = (cache0.numel() + wuk0.numel() + wuv0.numel() + qn0.numel() + qr0.numel()) * esz
+    if args.hot:
+        n_copies = 1
+    else:
+        n_copies = args.copies or max(1, min(64, math.ceil((1 << 30) / per_copy)))
+    copies = [(cache0, wuk0, wuv0, qn0, qr0)]
+    for _ in range(n_copies - 1):
+        copies.append(tuple(t.clone() for t in copies[0]))
+    # outputs and workspace (shared by all copies)
+    q_packed = torch.empty((R, H, row), dtype=dt, device=dev)
+    z = torch.empty((B, n_q, H, cfg.d_latent), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, n_q, H), dtype=torch.float32, device=dev)
+    o = torch.empty((R, H, cfg.d_v), dtype=dt, device=dev)
+    ws_bytes = mla.mla_decode_attn_workspace_size(lc, B, n_q, max_len, n_splits)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    setup_s = time.time() - t0
+
+    stream = torch.cuda.current_stream(dev)
+    ev = {k: [] for k in ("append", "absorb", "attn", "proj")}
+
+    def step(i, timed):
+        cache, wuk, wuv, qn, qr = copies[i % n_copies]
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if timed else None
+        if timed:
+            marks[0].record(stream)
+        mla.mla_rope_append(lc, c_new, k_new, cache, seq_off, len_before)
+        if timed:
+            marks[1].record(stream)
+        mla.mla_absorb_q(lc, qn, qr, q_pos, wuk, q_packed)
+        if timed:
+            marks[2].record(stream)
+        mla.mla_decode_attn(lc, q_packed.view(B, n_q, H, row), cache, seq_off, seq_len, max_len, z, lse,
+                            n_splits=n_splits, workspace=ws)
+        if timed:
+            marks[3].record(stream)
+        mla.mla_out_proj(lc, z.view(R, H, cfg.d_latent), wuv, o)
+        if timed:
+            marks[4].record(stream)
+            for j, k in enumerate(("append", "absorb", "attn", "proj")):
+                ev[k].append((marks[j], marks[j + 1]))
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    # whole-step timing without per-kernel events
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        step(i, False)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(stop)
+    ms_step = ms_total / args.steps
+    # per-kernel timing pass (events between the calls), same rotation
+    for i in range(args.steps):
+        step(i, True)
+    torch.cuda.synchronize()
+    per_kernel_ms = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in ev.items()}
+
+    # ------------------------------------------------------------------ algorithmic work
+    keys = int(lens.sum())
+    if n_q == 1:
+        vis_pairs = keys
+    else:
+        vis_pairs = int(sum(n_q * (int(l) - n_q) + n_q * (n_q + 1) // 2 for l in lens))
+    attn_bytes = keys * row * esz + R * H * row * esz + R * H * cfg.d_latent * 4 + R * H * 4
+    attn_flops = 2 * H * (row + cfg.d_latent) * vis_pairs
+    kernel_bytes = {
+        "append": R * (cfg.d_latent + cfg.d_rope) * esz + R * row * esz,
+        "absorb": H * cfg.d_nope * cfg.d_latent * esz + R * H * (cfg.d_nope + cfg.d_rope) * esz + R * H * row * esz,
+        "attn": attn_bytes,
+        "proj": H * cfg.d_v * cfg.d_latent * esz + R * H * cfg.d_latent * 4 + R * H * cfg.d_v * esz,
+    }
+    dominant = max(per_kernel_ms, key=per_kernel_ms.get)
+    if dominant == "attn":
+        t_bw, t_mf = attn_bytes / (HBM_PEAK_GBS * 1e9), attn_flops / (BF16_PEAK_TFLOPS * 1e12)
+        bound = "hbm" if t_bw >= t_mf else "mfma"
+    else:
+        bound = "hbm"
+    dom_s = per_kernel_ms[dominant] * 1e-3
+    if bound == "hbm":
+        achieved, peak, unit = kernel_bytes[dominant] / dom_s / 1e9, HBM_PEAK_GBS, "GB/s"
+    else:
+        achieved, peak, unit = attn_flops / dom_s / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s"
+
+    tokens_per_s = R / (ms_step * 1e-3)
+
+    # ------------------------------------------------------------------ CPU oracle baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, c_host, k_host, qn_host, qr_host, wuk_host, wuv_host, lens, args.cpu_seconds)
+
+    out = {
+        "metric": "MLA decode tokens/s + achieved HBM GB/s (H=128, d_c=512, S=4K-128K)",
+        "value": round(tokens_per_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) inputs, N(0,1/fan_in) weights, RMS-normalised latent)",
+        "config": {"workload": cfg.name, "batch": B, "n_q": n_q, "heads": H, "d_latent": cfg.d_latent,
+                   "d_rope": cfg.d_rope, "d_nope": cfg.d_nope, "d_v": cfg.d_v,
+                   "seq_len_keys": int(max_len) if len(set(lens.tolist())) == 1 else [int(lens.min()), int(lens.max())],
+                   "n_splits": n_splits, "cold_copies": n_copies, "parallelism": "single GPU"},
+        "roofline": {"kernel": {"attn": "mla_decode_attn", "absorb": "mla_absorb_q", "proj": "mla_out_proj",
+                                "append": "mla_rope_append"}[dominant],
+                     "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": kernel_bytes[dominant],
+                     "avg_launch_ms": round(per_kernel_ms[dominant], 6)},
+        "kernels_ms": {k: round(v, 6) for k, v in per_kernel_ms.items()},
+        "attn_gbs": round(attn_bytes / (per_kernel_ms["attn"] * 1e-3) / 1e9, 2),
+        "attn_tflops": round(attn_flops / (per_kernel_ms["attn"] * 1e-3) / 1e12, 3),
+        "cpu_baseline": cpu,
+    }
+    if args.verbose:
+        print(f"setup {setup_s:.1f}s, copies {n_copies} x {per_copy / 1e6:.1f} MB", file=sys.stderr)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(cfg, c_host, k_host, qn_host, qr_host, wuk_host, wuv_host, lens, budget_s):
+    """The fp64 oracle on the host cores over a bounded sample of the same workload."""
+    import numpy as np
+
+    import oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    H, n_q = cfg.n_heads, cfg.n_q
+    # sample: sequence 0, its query rows, heads taken in order until the time budget is used
+    b = 0
+    qn = qn_host[b * n_q:(b + 1) * n_q]
+    qr = qr_host[b * n_q:(b + 1) * n_q]
+    rows = list(range(n_q)) if n_q <= 4 else [0, n_q // 2, n_q - 1]
+    t0 = time.perf_counter()
+    heads_done = 0
+    while heads_done < H and (time.perf_counter() - t0) < budget_s:
+        hs = list(range(heads_done, min(H, heads_done + 8)))
+        O.explicit_attention(c_host[b], k_host[b], qn, qr, wuk_host, wuv_host, scale=cfg.softmax_scale,
+                             base=cfg.rope_base, heads=hs, rows=rows)
+        heads_done += len(hs)
+    el = time.perf_counter() - t0
+    # scale the sample (heads_done of H heads, len(rows) of n_q rows) to whole query tokens
+    tokens = (heads_done / H) * len(rows)
+    return {"value": round(tokens / el, 4), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"sequence 0 ({int(lens[0])} keys), {len(rows)} query row(s), {heads_done}/{H} heads, "
+                      f"{el:.1f} s fp64 non-absorbed oracle; tokens/s scaled to all heads"}
+
+
+if __name__ == "__main__":
+    main()

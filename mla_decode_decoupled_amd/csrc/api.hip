@@ -56,21 +56,35 @@ mla_status check_cfg(const mla_config* cfg, mla::LayerDims* L) {
   return MLA_OK;
 }
 
-// Chunking of the keys for split-K. n_splits = 0 picks ~512 keys per chunk (at most kMaxSplits).
-mla_status plan_splits(int32_t max_seq_len, int32_t n_splits, mla::SplitPlan* plan) {
+// Chunking of the keys for split-K. With n_splits = 0 the library picks: for the MFMA kernel about
+// one workgroup per CU over the whole batch, but never chunks shorter than 256 keys (each chunk
+// writes a 128 x 512 fp32 partial); for the generic kernel ~512 keys per chunk. At most 64.
+mla_status plan_splits(int32_t max_seq_len, int32_t n_splits, int64_t rows, bool fast, mla::SplitPlan* plan) {
   if (n_splits < 0 || n_splits > mla::kMaxSplits)
     return fail(MLA_ERR_INVALID_ARG, "n_splits must be in [0, %d], got %d", mla::kMaxSplits, n_splits);
-  int n = n_splits;
+  int64_t n = n_splits;
   if (n == 0) {
-    n = (max_seq_len + 511) / 512;
+    if (fast) {
+      const int64_t by_cu = 256 / (rows > 0 ? rows : 1);
+      const int64_t by_len = max_seq_len / 256;
+      n = by_cu < by_len ? by_cu : by_len;
+    } else {
+      n = (max_seq_len + 511) / 512;
+    }
     if (n > 64) n = 64;
     if (n < 1) n = 1;
   }
   if (n > max_seq_len) n = max_seq_len;
-  plan->chunk_len = (max_seq_len + n - 1) / n;
+  plan->chunk_len = (int)((max_seq_len + n - 1) / n);
   plan->n_chunks = (max_seq_len + plan->chunk_len - 1) / plan->chunk_len;
   return MLA_OK;
 }
+
+bool use_fast_attn(const mla_config* cfg, const mla::LayerDims& L) {
+  return cfg->dtype == MLA_BF16 && mla::attn_fast_supported(L);
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 size_t attn_workspace_bytes(const mla::LayerDims& L, int batch, int n_q, const mla::SplitPlan& plan) {
   if (plan.n_chunks <= 1) return 0;
@@ -138,7 +152,7 @@ size_t mla_decode_attn_workspace_size(const mla_config* cfg, int32_t batch, int3
   if (check_cfg(cfg, &L) != MLA_OK) return 0;
   if (batch <= 0 || n_q <= 0 || max_seq_len < n_q) return 0;
   mla::SplitPlan plan;
-  if (plan_splits(max_seq_len, n_splits, &plan) != MLA_OK) return 0;
+  if (plan_splits(max_seq_len, n_splits, (int64_t)batch * n_q, use_fast_attn(cfg, L), &plan) != MLA_OK) return 0;
   return attn_workspace_bytes(L, batch, n_q, plan);
 }
 
@@ -154,17 +168,22 @@ mla_status mla_decode_attn(const mla_config* cfg, int32_t batch, int32_t n_q, co
   if ((int64_t)batch * n_q > 65535) return fail(MLA_ERR_UNSUPPORTED, "batch * n_q exceeds 65535");
   if (L.n_heads > 65535) return fail(MLA_ERR_UNSUPPORTED, "n_heads %d exceeds 65535", L.n_heads);
   if (!q_packed || !cache || !seq_off || !seq_len || !z) return fail(MLA_ERR_INVALID_ARG, "NULL pointer argument");
+  const bool fast = use_fast_attn(cfg, L);
   mla::SplitPlan plan;
-  s = plan_splits(max_seq_len, n_splits, &plan);
+  s = plan_splits(max_seq_len, n_splits, (int64_t)batch * n_q, fast, &plan);
   if (s != MLA_OK) return s;
   const size_t need = attn_workspace_bytes(L, batch, n_q, plan);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))
     return fail(MLA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu%s", need, workspace_bytes,
                 workspace ? "" : " (NULL)");
   hipStream_t st = (hipStream_t)stream;
-  hipError_t e = cfg->dtype == MLA_F32
-                     ? mla::launch_attn_generic<float>(L, batch, n_q, q_packed, cache, seq_off, seq_len, plan, workspace, z, lse, st)
-                     : mla::launch_attn_generic<__bf16>(L, batch, n_q, q_packed, cache, seq_off, seq_len, plan, workspace, z, lse, st);
+  hipError_t e;
+  if (fast && aligned16(q_packed) && aligned16(cache) && aligned16(z) && aligned16(workspace))
+    e = mla::launch_attn_fast(L, batch, n_q, q_packed, cache, seq_off, seq_len, plan, workspace, z, lse, st);
+  else if (cfg->dtype == MLA_F32)
+    e = mla::launch_attn_generic<float>(L, batch, n_q, q_packed, cache, seq_off, seq_len, plan, workspace, z, lse, st);
+  else
+    e = mla::launch_attn_generic<__bf16>(L, batch, n_q, q_packed, cache, seq_off, seq_len, plan, workspace, z, lse, st);
   return from_hip(e, "mla_decode_attn launch");
 }
 

@@ -279,8 +279,12 @@ hipError_t launch_attn_generic(const LayerDims& L, int batch, int n_q, const voi
                      plan.n_chunks, part_acc, part_ml, z, lse);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.n_chunks == 1) return e;
-  hipLaunchKernelGGL(attn_merge, dim3(batch * n_q * L.n_heads), dim3(256), 0, stream, part_acc, part_ml,
-                     plan.n_chunks, L.d_latent, z, lse);
+  return launch_attn_merge(batch * n_q * L.n_heads, plan.n_chunks, L.d_latent, part_acc, part_ml, z, lse, stream);
+}
+
+hipError_t launch_attn_merge(int n_rowheads, int n_chunks, int d_latent, const float* part_acc, const float* part_ml,
+                             float* z, float* lse, hipStream_t stream) {
+  hipLaunchKernelGGL(attn_merge, dim3(n_rowheads), dim3(256), 0, stream, part_acc, part_ml, n_chunks, d_latent, z, lse);
   return hipGetLastError();
 }
 

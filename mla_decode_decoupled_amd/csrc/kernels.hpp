@@ -41,4 +41,13 @@ template <typename T>
 hipError_t launch_out_proj_generic(const LayerDims& L, int n_rows, const float* z, const void* w_uv, void* o,
                                    hipStream_t stream);
 
+hipError_t launch_attn_merge(int n_rowheads, int n_chunks, int d_latent, const float* part_acc, const float* part_ml,
+                             float* z, float* lse, hipStream_t stream);
+
+// MFMA path for the DeepSeek-V2/V3 shape (H 128, d_latent 512, d_rope 64, bf16)
+bool attn_fast_supported(const LayerDims& L);
+hipError_t launch_attn_fast(const LayerDims& L, int batch, int n_q, const void* q_packed, const void* cache,
+                            const int64_t* seq_off, const int32_t* seq_len, const SplitPlan& plan, void* workspace,
+                            float* z, float* lse, hipStream_t stream);
+
 }  // namespace mla

@@ -60,7 +60,7 @@ class DeviceRun:
 
 
 def run_pipeline(hi: HostInputs, n_splits: int = 0, scale: Optional[float] = None,
-                 append_history_per_seq: bool = True, lib_cfg=None) -> DeviceRun:
+                 lib_cfg=None, max_len: Optional[int] = None) -> DeviceRun:
     """Cache the history, then one step: append the n_q new tokens, absorb, attend, project."""
     cfg = hi.cfg
     lc = lib_config(cfg, scale) if lib_cfg is None else lib_cfg
@@ -92,7 +92,7 @@ def run_pipeline(hi: HostInputs, n_splits: int = 0, scale: Optional[float] = Non
                      tdev(hi.q_rope.reshape(R, H, cfg.d_rope), dt), q_pos, tdev(hi.w_uk, dt), q_packed)
     z = torch.empty((B, n_q, H, cfg.d_latent), dtype=torch.float32, device="cuda")
     lse = torch.empty((B, n_q, H), dtype=torch.float32, device="cuda")
-    max_len = int(lens.max())
+    max_len = int(lens.max()) if max_len is None else int(max_len)
     ws_bytes = mla.mla_decode_attn_workspace_size(lc, B, n_q, max_len, n_splits)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
     mla.mla_decode_attn(lc, q_packed.view(B, n_q, H, cfg.row), cache, seq_off, seq_len, max_len, z, lse,

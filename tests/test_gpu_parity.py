@@ -87,20 +87,34 @@ def test_v3_decode_4k_all_heads():
     _check_outputs(run, hi, 0)
 
 
-@pytest.mark.parametrize("n_splits", [1, 3, 64])
-def test_split_count_does_not_change_results(n_splits):
-    hi = host_inputs(CONFIGS[1])
+@pytest.mark.parametrize("cid,n_splits", [(0, 1), (0, 7), (1, 1), (1, 3), (1, 64)])
+def test_split_count_does_not_change_results(cid, n_splits):
+    """fp32: only the float32 summation order changes -> 1e-5.
+
+    bf16: each chunk rounds its probabilities to bf16 relative to its own reference max, so the
+    rounding (at most 2^-9 relative per weight, independent across keys) differs between split
+    counts; the latent sum inherits ~1e-3 relative noise. Bound: rel-L2 <= 5e-3, max <= 2e-3.
+    The log-sum-exp is accumulated in float32 either way -> 1e-5.
+    """
+    hi = host_inputs(CONFIGS[cid])
     base = run_pipeline(hi, n_splits=9)
     other = run_pipeline(hi, n_splits=n_splits)
-    dz = np.abs(np32(other.z) - np32(base.z)).max()
+    zb, zo = np32(base.z), np32(other.z)
+    dz = np.abs(zo - zb).max()
+    rel = np.linalg.norm(zo - zb) / np.linalg.norm(zb)
     dl = np.abs(np32(other.lse) - np32(base.lse)).max()
-    assert dz <= 1e-5 and dl <= 1e-5, (dz, dl)
+    print(f"split {n_splits} vs 9: max|dz| {dz:.2e} rel-L2 {rel:.2e} max|dlse| {dl:.2e}", flush=True)
+    assert dl <= 1e-5
+    if CONFIGS[cid].dtype == "f32":
+        assert dz <= 1e-5
+    else:
+        assert dz <= 2e-3 and rel <= 5e-3
 
 
 def test_ragged_batch_sampled():
     cfg = CONFIGS[2]
     hi = host_inputs(cfg)
-    run = run_pipeline(hi)
+    run = run_pipeline(hi, n_splits=4)
     lens = hi.lens
     picks = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 17})
     heads = [0, 63, 127]
@@ -108,14 +122,15 @@ def test_ragged_batch_sampled():
         _check_cache(run, hi, b)
         _check_qpacked(run, hi, b)
         _check_outputs(run, hi, b, heads=heads)
-    # a sequence computed alone equals the same sequence inside the batch
+    # a sequence computed alone (same chunking) equals the same sequence inside the batch, bit for bit
     b = picks[-1]
     alone = host_inputs(MLAConfig(**{**cfg.__dict__, "batch": 1}), lens=[int(lens[b])])
     alone.c, alone.k_pre = [hi.c[b]], [hi.k_pre[b]]
     alone.q_nope, alone.q_rope = hi.q_nope[b:b + 1], hi.q_rope[b:b + 1]
-    run1 = run_pipeline(alone)
-    assert np.abs(np32(run1.z[0]) - np32(run.z[b])).max() <= 1e-5
-    assert np.abs(np32(run1.lse[0]) - np32(run.lse[b])).max() <= 1e-5
+    run1 = run_pipeline(alone, n_splits=4, max_len=int(lens.max()))
+    assert np.array_equal(np32(run1.z[0]), np32(run.z[b]))
+    assert np.array_equal(np32(run1.lse[0]), np32(run.lse[b]))
+    assert np.array_equal(np32(run1.o[0]), np32(run.o[b]))
 
 
 @pytest.mark.slow
