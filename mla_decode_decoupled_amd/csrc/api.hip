@@ -140,9 +140,13 @@ mla_status mla_absorb_q(const mla_config* cfg, int32_t n_rows, const void* q_nop
   if (!q_nope || !q_pos || !w_uk || !q_packed || (L.d_rope > 0 && !q_rope))
     return fail(MLA_ERR_INVALID_ARG, "NULL pointer argument");
   hipStream_t st = (hipStream_t)stream;
-  hipError_t e = cfg->dtype == MLA_F32
-                     ? mla::launch_absorb_q_generic<float>(L, n_rows, q_nope, q_rope, q_pos, w_uk, q_packed, st)
-                     : mla::launch_absorb_q_generic<__bf16>(L, n_rows, q_nope, q_rope, q_pos, w_uk, q_packed, st);
+  hipError_t e;
+  if (cfg->dtype == MLA_BF16 && mla::proj_fast_supported(L) && aligned16(w_uk))
+    e = mla::launch_absorb_q_fast(L, n_rows, q_nope, q_rope, q_pos, w_uk, q_packed, st);
+  else if (cfg->dtype == MLA_F32)
+    e = mla::launch_absorb_q_generic<float>(L, n_rows, q_nope, q_rope, q_pos, w_uk, q_packed, st);
+  else
+    e = mla::launch_absorb_q_generic<__bf16>(L, n_rows, q_nope, q_rope, q_pos, w_uk, q_packed, st);
   return from_hip(e, "mla_absorb_q launch");
 }
 
@@ -199,8 +203,13 @@ mla_status mla_out_proj(const mla_config* cfg, int32_t n_rows, const float* z, c
   if (L.n_heads > 65535) return fail(MLA_ERR_UNSUPPORTED, "n_heads %d exceeds 65535", L.n_heads);
   if (!z || !w_uv || !o) return fail(MLA_ERR_INVALID_ARG, "NULL pointer argument");
   hipStream_t st = (hipStream_t)stream;
-  hipError_t e = cfg->dtype == MLA_F32 ? mla::launch_out_proj_generic<float>(L, n_rows, z, w_uv, o, st)
-                                       : mla::launch_out_proj_generic<__bf16>(L, n_rows, z, w_uv, o, st);
+  hipError_t e;
+  if (cfg->dtype == MLA_BF16 && mla::proj_fast_supported(L) && aligned16(w_uv) && aligned16(z))
+    e = mla::launch_out_proj_fast(L, n_rows, z, w_uv, o, st);
+  else if (cfg->dtype == MLA_F32)
+    e = mla::launch_out_proj_generic<float>(L, n_rows, z, w_uv, o, st);
+  else
+    e = mla::launch_out_proj_generic<__bf16>(L, n_rows, z, w_uv, o, st);
   return from_hip(e, "mla_out_proj launch");
 }
 

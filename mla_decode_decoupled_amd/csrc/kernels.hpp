@@ -50,4 +50,12 @@ hipError_t launch_attn_fast(const LayerDims& L, int batch, int n_q, const void* 
                             const int64_t* seq_off, const int32_t* seq_len, const SplitPlan& plan, void* workspace,
                             float* z, float* lse, hipStream_t stream);
 
+// GEMV-style projections for the DeepSeek-V2/V3 shape (H 128, d_nope = d_v 128, d_latent 512,
+// d_rope 64, bf16)
+bool proj_fast_supported(const LayerDims& L);
+hipError_t launch_absorb_q_fast(const LayerDims& L, int n_rows, const void* q_nope, const void* q_rope,
+                                const int32_t* q_pos, const void* w_uk, void* q_packed, hipStream_t stream);
+hipError_t launch_out_proj_fast(const LayerDims& L, int n_rows, const float* z, const void* w_uv, void* o,
+                                hipStream_t stream);
+
 }  // namespace mla

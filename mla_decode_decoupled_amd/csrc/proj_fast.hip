@@ -1,0 +1,194 @@
+// Query absorption and latent output projection for the DeepSeek-V2/V3 shape
+// (128 heads, d_nope = d_v = 128, d_latent = 512, d_rope = 64, bf16 weights).
+//
+// At decode batch sizes both calls are matrix-vector products whose cost is reading the
+// per-head weights once (W_UK and W_UV are 16.8 MB each in bf16), so the kernels are built for
+// HBM streaming: every lane issues 16-byte weight loads, a workgroup owns one 64 KB weight slab,
+// and the 256 workgroups cover the chip once. Query rows are processed kRowBlock at a time
+// against the same weight registers.
+//
+//   absorb: q~[r, i, c] = sum_a W_UK[i, a, c] q_nope[r, i, a]   ("从零理解 MLA", section "矩阵吸收")
+//   out:    o[r, i, v]  = sum_c W_UV[i, v, c] z[r, i, c]        (same section, output side)
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace mla {
+namespace proj {
+
+constexpr int H = 128;
+constexpr int DN = 128;   // d_nope = d_v
+constexpr int DC = 512;
+constexpr int DR = 64;
+constexpr int ROW = DC + DR;
+constexpr int kRowBlock = 4;
+
+__device__ __forceinline__ void unpack8(const i32x4 v, float* f) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t u = (uint32_t)v[e];
+    f[2 * e] = __uint_as_float(u << 16);
+    f[2 * e + 1] = __uint_as_float(u & 0xFFFF0000u);
+  }
+}
+
+// grid (H, 2 column halves, row blocks); 256 threads: column group cg = t % 32 (8 columns),
+// row group ag = t / 32 (16 rows a of W_UK[i]). Partial sums over the 8 row groups meet in LDS.
+__global__ void __launch_bounds__(256) absorb_q_gemv(const bf16* __restrict__ q_nope, const bf16* __restrict__ q_rope,
+                                                     const int32_t* __restrict__ q_pos, const bf16* __restrict__ w_uk,
+                                                     bf16* __restrict__ q_packed, int n_rows, double base) {
+  __shared__ float qs[kRowBlock][DN];
+  __shared__ float red[8][kRowBlock][256 + 4];
+  const int i = blockIdx.x, half = blockIdx.y;
+  const int r0 = blockIdx.z * kRowBlock;
+  const int nr = min(kRowBlock, n_rows - r0);
+  const int t = threadIdx.x, cg = t & 31, ag = t >> 5;
+
+  // weights first: 16 independent 16-byte loads per lane
+  const bf16* wp = w_uk + ((size_t)i * DN + ag * 16) * DC + half * 256 + cg * 8;
+  i32x4 wv[16];
+#pragma unroll
+  for (int a = 0; a < 16; ++a) wv[a] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(wp + (size_t)a * DC));
+  for (int e = t; e < kRowBlock * DN; e += 256) {
+    const int rr = e / DN, a = e % DN;
+    qs[rr][a] = rr < nr ? (float)q_nope[((size_t)(r0 + rr) * H + i) * DN + a] : 0.0f;
+  }
+  __syncthreads();
+
+  float acc[kRowBlock][8];
+#pragma unroll
+  for (int rr = 0; rr < kRowBlock; ++rr)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[rr][e] = 0.0f;
+#pragma unroll
+  for (int a = 0; a < 16; ++a) {
+    float w[8];
+    unpack8(wv[a], w);
+#pragma unroll
+    for (int rr = 0; rr < kRowBlock; ++rr) {
+      const float q = qs[rr][ag * 16 + a];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[rr][e] = fmaf(w[e], q, acc[rr][e]);
+    }
+  }
+#pragma unroll
+  for (int rr = 0; rr < kRowBlock; ++rr)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[ag][rr][cg * 8 + e] = acc[rr][e];
+  __syncthreads();
+  // thread t sums column t (0..255) over the 8 row groups for each row
+  for (int rr = 0; rr < nr; ++rr) {
+    float s = 0.0f;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) s += red[g][rr][t];
+    q_packed[((size_t)(r0 + rr) * H + i) * ROW + half * 256 + t] = (bf16)s;
+  }
+  if (half == 0) {  // rotate the position part of these rows
+    for (int e = t; e < nr * (DR / 2); e += 256) {
+      const int rr = e / (DR / 2), j = e % (DR / 2);
+      const size_t r = (size_t)(r0 + rr);
+      const bf16* src = q_rope + (r * H + i) * DR;
+      double s, co;
+      rope_sincos(base, j, DR, q_pos[r], &s, &co);
+      const double x0 = (float)src[2 * j], x1 = (float)src[2 * j + 1];
+      bf16* dst = q_packed + (r * H + i) * ROW + DC;
+      dst[2 * j] = from_f64<bf16>(x0 * co - x1 * s);
+      dst[2 * j + 1] = from_f64<bf16>(x0 * s + x1 * co);
+    }
+  }
+}
+
+// grid (H, 4 quarters of the 128 outputs, row blocks); 4 waves, wave w owns 8 outputs
+// v = 32 q + 8 w + j. Lane l holds latent columns 8l..8l+7, so one 16-byte load per lane covers a
+// whole 512-wide weight row; the 8 per-lane dot products are then reduced across the wave by
+// a reduce-scatter butterfly (each halving step keeps half the outputs), 10 exchanges per row.
+__global__ void __launch_bounds__(256) out_proj_gemv(const float* __restrict__ z, const bf16* __restrict__ w_uv,
+                                                     bf16* __restrict__ o, int n_rows) {
+  const int i = blockIdx.x, quarter = blockIdx.y;
+  const int r0 = blockIdx.z * kRowBlock;
+  const int nr = min(kRowBlock, n_rows - r0);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int v0 = quarter * 32 + w * 8;
+
+  i32x4 wv[8];
+  const bf16* wp = w_uv + ((size_t)i * DN + v0) * DC + lane * 8;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) wv[j] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(wp + (size_t)j * DC));
+
+  for (int rr = 0; rr < nr; ++rr) {
+    const float* zp = z + ((size_t)(r0 + rr) * H + i) * DC + lane * 8;
+    const f32x4 za = *reinterpret_cast<const f32x4*>(zp);
+    const f32x4 zb = *reinterpret_cast<const f32x4*>(zp + 4);
+    float d[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float wf[8];
+      unpack8(wv[j], wf);
+      float s = wf[0] * za[0];
+      s = fmaf(wf[1], za[1], s);
+      s = fmaf(wf[2], za[2], s);
+      s = fmaf(wf[3], za[3], s);
+      s = fmaf(wf[4], zb[0], s);
+      s = fmaf(wf[5], zb[1], s);
+      s = fmaf(wf[6], zb[2], s);
+      s = fmaf(wf[7], zb[3], s);
+      d[j] = s;
+    }
+    // reduce-scatter: after exchanging with lane ^ 32 keep outputs 0-3 (low half) or 4-7 (high
+    // half), then ^16 keeps 2, ^8 keeps 1; lanes with equal bits 5..3 now hold one output each.
+    {
+      const bool hi = lane & 32;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float send = hi ? d[j] : d[j + 4];
+        const float recv = __shfl_xor(send, 32, 64);
+        d[j] = (hi ? d[j + 4] : d[j]) + recv;
+      }
+    }
+    {
+      const bool hi = lane & 16;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float send = hi ? d[j] : d[j + 2];
+        const float recv = __shfl_xor(send, 16, 64);
+        d[j] = (hi ? d[j + 2] : d[j]) + recv;
+      }
+    }
+    float s;
+    {
+      const bool hi = lane & 8;
+      const float send = hi ? d[0] : d[1];
+      s = (hi ? d[1] : d[0]) + __shfl_xor(send, 8, 64);
+    }
+    s += __shfl_xor(s, 4, 64);
+    s += __shfl_xor(s, 2, 64);
+    s += __shfl_xor(s, 1, 64);
+    // lane bits: b5 -> output bit 2, b4 -> bit 1, b3 -> bit 0
+    const int j = ((lane >> 5) & 1) * 4 + ((lane >> 4) & 1) * 2 + ((lane >> 3) & 1);
+    if ((lane & 7) == 0) o[((size_t)(r0 + rr) * H + i) * DN + v0 + j] = (bf16)s;
+  }
+}
+
+}  // namespace proj
+
+bool proj_fast_supported(const LayerDims& L) {
+  return L.n_heads == proj::H && L.d_nope == proj::DN && L.d_v == proj::DN && L.d_latent == proj::DC &&
+         L.d_rope == proj::DR;
+}
+
+hipError_t launch_absorb_q_fast(const LayerDims& L, int n_rows, const void* q_nope, const void* q_rope,
+                                const int32_t* q_pos, const void* w_uk, void* q_packed, hipStream_t stream) {
+  const int rb = (n_rows + proj::kRowBlock - 1) / proj::kRowBlock;
+  hipLaunchKernelGGL(proj::absorb_q_gemv, dim3(proj::H, 2, rb), dim3(256), 0, stream, (const bf16*)q_nope,
+                     (const bf16*)q_rope, q_pos, (const bf16*)w_uk, (bf16*)q_packed, n_rows, L.rope_base);
+  return hipGetLastError();
+}
+
+hipError_t launch_out_proj_fast(const LayerDims& L, int n_rows, const float* z, const void* w_uv, void* o,
+                                hipStream_t stream) {
+  const int rb = (n_rows + proj::kRowBlock - 1) / proj::kRowBlock;
+  hipLaunchKernelGGL(proj::out_proj_gemv, dim3(proj::H, 4, rb), dim3(256), 0, stream, z, (const bf16*)w_uv, (bf16*)o,
+                     n_rows);
+  return hipGetLastError();
+}
+
+}  // namespace mla
