@@ -44,7 +44,62 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="budget for the CPU oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--verbose", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="instead of the step: time a plain 1 GiB device copy (the reference kernel that scales "
+                         "the FETCH_SIZE / WRITE_SIZE counters to bytes)")
     return ap.parse_args()
+
+
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_attn_v3_decode_s4k_counters.md")
+TRAFFIC_SOURCES = [os.path.join(ROOT, "mla_decode_decoupled_amd", "csrc", f)
+                   for f in ("api.hip", "generic.hip", "decode_fast.hip")]
+
+
+def sources_sha() -> str:
+    """Hash of the sources that decide what the attention kernels read and write."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str, n_splits: int, cold: bool):
+    """HBM bytes per mla_decode_attn call from the committed counter summary (FETCH_SIZE and
+    WRITE_SIZE, each scaled by the plain-copy calibration), or None when the summary is missing,
+    was taken on another workload, or the kernels changed since it was taken."""
+    try:
+        text = open(COUNTERS_FILE).read()
+        block = text.split("```json", 1)[1].split("```", 1)[0]
+        rec = json.loads(block)
+    except (OSError, IndexError, ValueError):
+        return None
+    if (rec.get("workload") != workload or rec.get("n_splits") != n_splits or not cold
+            or rec.get("source_sha") != sources_sha()):
+        return None
+    return rec.get("traffic_bytes_per_call")
+
+
+def copy_calibration(args):
+    """One plain device-to-device copy kernel of known size, repeated: the counters read for it
+    give the factor between FETCH_SIZE / WRITE_SIZE and the bytes really moved."""
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    reps = 5
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / reps
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "reps": reps, "ms_per_copy": round(ms, 4),
+                      "gbs_read_plus_write": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
 def main():
@@ -53,6 +108,10 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus_requested": args.gpus}))
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration(args)
+        return
 
     import numpy as np
     import torch
@@ -213,7 +272,8 @@ def main():
         "roofline": {"kernel": {"attn": "mla_decode_attn", "absorb": "mla_absorb_q", "proj": "mla_out_proj",
                                 "append": "mla_rope_append"}[dominant],
                      "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "frac": round(achieved / peak, 4),
+                     "traffic": recorded_traffic(cfg.name, n_splits, not args.hot) if dominant == "attn" else None,
                      "algorithmic_bytes_per_launch": kernel_bytes[dominant],
                      "avg_launch_ms": round(per_kernel_ms[dominant], 6)},
         "kernels_ms": {k: round(v, 6) for k, v in per_kernel_ms.items()},
@@ -244,18 +304,20 @@ def cpu_baseline(cfg, c_host, k_host, qn_host, qr_host, wuk_host, wuv_host, lens
     qr = qr_host[b * n_q:(b + 1) * n_q]
     rows = list(range(n_q)) if n_q <= 4 else [0, n_q // 2, n_q - 1]
     t0 = time.perf_counter()
-    heads_done = 0
-    while heads_done < H and (time.perf_counter() - t0) < budget_s:
-        hs = list(range(heads_done, min(H, heads_done + 8)))
+    heads_done = 0   # head evaluations, cycling over the heads in groups of 8 until the budget is used
+    while (time.perf_counter() - t0) < budget_s:
+        h0 = heads_done % H
+        hs = list(range(h0, min(H, h0 + 8)))
         O.explicit_attention(c_host[b], k_host[b], qn, qr, wuk_host, wuv_host, scale=cfg.softmax_scale,
                              base=cfg.rope_base, heads=hs, rows=rows)
         heads_done += len(hs)
     el = time.perf_counter() - t0
-    # scale the sample (heads_done of H heads, len(rows) of n_q rows) to whole query tokens
+    # scale the sample (heads_done head evaluations of len(rows) query rows) to whole query tokens
     tokens = (heads_done / H) * len(rows)
     return {"value": round(tokens / el, 4), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"sequence 0 ({int(lens[0])} keys), {len(rows)} query row(s), {heads_done}/{H} heads, "
-                      f"{el:.1f} s fp64 non-absorbed oracle; tokens/s scaled to all heads"}
+            "sample": f"sequence 0 ({int(lens[0])} keys), {len(rows)} query row(s), {heads_done} head evaluations "
+                      f"({heads_done / H:.1f} x all {H} heads) in {el:.1f} s of the fp64 non-absorbed oracle; "
+                      f"tokens/s = whole-token equivalents / s"}
 
 
 if __name__ == "__main__":

@@ -15,7 +15,8 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_PATH = os.path.join(PKG_DIR, "libmla.so")
 SOURCES = ["api.hip", "generic.hip", "decode_fast.hip", "proj_fast.hip"]
 
-# Packed-FP32 instructions are switched off for every device pass (build flags).
+# Packed-FP32 instructions (v_pk_*_f32) are switched off for every device pass: the compiler
+# otherwise forms them from plain float code, and the kernels are validated without them.
 HIP_FLAGS = [
     "--offload-arch=gfx950",
     "-O3",

@@ -182,34 +182,84 @@ __global__ void __launch_bounds__(256) attn_partial_generic(const T* __restrict_
 
 // Log-sum-exp merge of split-K partials of one (query row, head): with M = max_k m_k,
 // z = sum_k 2^(m_k - M) acc_k / sum_k 2^(m_k - M) l_k. Chunks that saw no key (l_k = 0) are
-// skipped, so an empty chunk never produces NaN.
+// skipped (their accumulator is never read), so an empty chunk never produces NaN.
+//
+// The merge is a pure stream over the partials, so it is written for memory-level parallelism:
+// wave 0 first compacts the live chunks and their weights into LDS, then the 4 waves split the
+// live chunks round-robin, every lane reading V consecutive floats of each chunk row with all of a
+// batch of 8 chunk loads in flight before the first is used; the 4 wave sums meet in LDS.
+constexpr int kMergeWaves = 4;
+constexpr int kMergeBatch = 8;
+
+template <int V>
 __global__ void __launch_bounds__(256) attn_merge(const float* __restrict__ part_acc, const float* __restrict__ part_ml,
                                                   int n_chunks, int d_latent, float* __restrict__ z,
                                                   float* __restrict__ lse) {
-  __shared__ float wts[kMaxSplits];
+  typedef __attribute__((__vector_size__(V * sizeof(float)))) float vec;
+  extern __shared__ __attribute__((aligned(16))) float merge_smem[];
+  float* red = merge_smem;                                       // [kMergeWaves][d_latent]
+  float* wts = red + kMergeWaves * d_latent;                     // [kMaxSplits] live weights
+  int* idx = reinterpret_cast<int*>(wts + kMaxSplits);           // [kMaxSplits] live chunk ids
+  __shared__ int n_live;
   __shared__ float total;
   const size_t rh = blockIdx.x;
-  const float* ml = part_ml + rh * n_chunks * 2;
-  if (threadIdx.x == 0) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (w == 0) {
+    const float* ml = part_ml + rh * n_chunks * 2;
     float M = -INFINITY;
-    for (int k = 0; k < n_chunks; ++k)
+    for (int k = lane; k < n_chunks; k += 64)
       if (ml[2 * k + 1] > 0.0f) M = fmaxf(M, ml[2 * k]);
+    M = warp_max(M);
     float L = 0.0f;
-    for (int k = 0; k < n_chunks; ++k) {
-      const float w = ml[2 * k + 1] > 0.0f ? exp2f(ml[2 * k] - M) : 0.0f;
-      wts[k] = w;
-      L += w * ml[2 * k + 1];
+    int base = 0;
+    for (int k0 = 0; k0 < n_chunks; k0 += 64) {
+      const int k = k0 + lane;
+      const float m = k < n_chunks ? ml[2 * k] : 0.0f;
+      const float l = k < n_chunks ? ml[2 * k + 1] : 0.0f;
+      const bool live = l > 0.0f;
+      const uint64_t mask = __ballot(live);
+      if (live) {
+        const int pos = base + __popcll(mask & ((1ull << lane) - 1ull));
+        const float wk = exp2f(m - M);
+        wts[pos] = wk;
+        idx[pos] = k;
+        L = fmaf(wk, l, L);
+      }
+      base += __popcll(mask);
     }
-    total = L;
-    if (lse != nullptr) lse[rh] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
+    L = warp_sum(L);
+    if (lane == 0) {
+      n_live = base;
+      total = L;
+      if (lse != nullptr) lse[rh] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
+    }
+  }
+  __syncthreads();
+  const int live = n_live;
+  const float* acc = part_acc + rh * n_chunks * (size_t)d_latent;
+  for (int c = lane * V; c < d_latent; c += 64 * V) {
+    vec s = {};
+    for (int q0 = w; q0 < live; q0 += kMergeWaves * kMergeBatch) {
+      vec x[kMergeBatch];
+#pragma unroll
+      for (int u = 0; u < kMergeBatch; ++u) {
+        const int q = q0 + u * kMergeWaves;
+        if (q < live) x[u] = *reinterpret_cast<const vec*>(acc + (size_t)idx[q] * d_latent + c);
+      }
+#pragma unroll
+      for (int u = 0; u < kMergeBatch; ++u) {
+        const int q = q0 + u * kMergeWaves;
+        if (q < live) s += wts[q] * x[u];
+      }
+    }
+    *reinterpret_cast<vec*>(red + w * d_latent + c) = s;
   }
   __syncthreads();
   const float inv = total > 0.0f ? 1.0f / total : 0.0f;
-  const float* acc = part_acc + rh * n_chunks * d_latent;
   for (int c = threadIdx.x; c < d_latent; c += blockDim.x) {
     float s = 0.0f;
-    for (int k = 0; k < n_chunks; ++k)
-      if (wts[k] != 0.0f) s = fmaf(wts[k], acc[(size_t)k * d_latent + c], s);
+#pragma unroll
+    for (int g = 0; g < kMergeWaves; ++g) s += red[g * d_latent + c];
     z[rh * d_latent + c] = s * inv;
   }
 }
@@ -284,7 +334,13 @@ hipError_t launch_attn_generic(const LayerDims& L, int batch, int n_q, const voi
 
 hipError_t launch_attn_merge(int n_rowheads, int n_chunks, int d_latent, const float* part_acc, const float* part_ml,
                              float* z, float* lse, hipStream_t stream) {
-  hipLaunchKernelGGL(attn_merge, dim3(n_rowheads), dim3(256), 0, stream, part_acc, part_ml, n_chunks, d_latent, z, lse);
+  const size_t smem = (size_t)kMergeWaves * d_latent * sizeof(float) + kMaxSplits * (sizeof(float) + sizeof(int));
+  if (d_latent % 4 == 0 && ((uintptr_t)part_acc & 15u) == 0)
+    hipLaunchKernelGGL(attn_merge<4>, dim3(n_rowheads), dim3(64 * kMergeWaves), smem, stream, part_acc, part_ml,
+                       n_chunks, d_latent, z, lse);
+  else
+    hipLaunchKernelGGL(attn_merge<1>, dim3(n_rowheads), dim3(64 * kMergeWaves), smem, stream, part_acc, part_ml,
+                       n_chunks, d_latent, z, lse);
   return hipGetLastError();
 }
 

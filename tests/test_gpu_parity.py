@@ -248,6 +248,44 @@ def test_multi_step_decode_matches_oracle_each_step():
         assert_close(np32(z)[0, 0], ref["z"][0], "f32", f"z step {t}")
 
 
+@pytest.mark.parametrize("n_splits", [1, 3])
+def test_later_scores_far_above_the_first_tile(n_splits):
+    """A chunk whose later keys score far above its first tile (by more than 64 in log2 units)
+    must still match the oracle: the fast kernel's fixed per-chunk reference cannot hold those
+    probabilities, so it has to fall back to its exact online-softmax path.
+
+    Construction (bf16 fast shape, 232 keys): keys 0..31 have zero latent and zero position key
+    (score 0); keys 32.. all carry the same latent c* = sign(q~ of head 0), and every position
+    part is zero. Head 0 then scores its later keys at scale * sum|q~| (about 100 in natural
+    units), every other head at a moderate value; each head's softmax has two levels, which keeps
+    the comparison well conditioned."""
+    cfg = CONFIGS[1]
+    n = 32 + 200
+    hi = host_inputs(cfg, lens=[n])
+    hi.q_rope = np.zeros_like(hi.q_rope)
+    hi.k_pre = [np.zeros_like(hi.k_pre[0])]
+    q_abs = O.absorb_query(hi.q_nope[0], hi.w_uk)[0]           # [H, d_c], row 0
+    star = np.where(q_abs[0] >= 0, 1.0, -1.0).astype(np.float32)
+    c = np.zeros((n, cfg.d_latent), np.float32)
+    c[32:] = star
+    hi.c = [c]
+    scale = 0.5
+    jump_log2 = scale * float(q_abs[0] @ star) * math.log2(math.e)
+    assert jump_log2 > 2 * 64, f"construction must exceed the kernel's headroom: {jump_log2:.1f}"
+    run = run_pipeline(hi, n_splits=n_splits, scale=scale)
+    ref = _oracle(hi, 0, scale=scale)
+    assert_close(np32(run.z[0]), ref["z"], cfg.dtype, "z")
+    assert_close(np32(run.o[0]), ref["o"], cfg.dtype, "o")
+    # lse reaches ~100 here, so it carries the score error of q_packed's bf16 storage:
+    # |ds| <= scale * sum_c |q~_c c_c| * 2^-9 (half an ulp per element), on top of the usual bar.
+    bound = scale * np.abs(q_abs) @ np.abs(star) * 2.0 ** -9 + 2e-2       # per head
+    err = np.abs(np32(run.lse[0, 0]) - ref["lse"][0])
+    assert np.all(err <= bound), f"lse: max err {err.max():.3e}, worst margin {(err - bound).max():.3e}"
+    # head 0 puts all its weight on the later keys: z = c* up to exp(-jump)
+    assert np.max(np.abs(np32(run.z[0, 0, 0]) - star)) <= 1e-3
+
+
+
 def test_empty_work_is_a_noop():
     import mla_decode_decoupled_amd as mla
     from mla_decode_decoupled_amd import _lib
