@@ -43,6 +43,8 @@
 // are waited for with lgkmcnt in issue order, chained MFMAs use exactly the same accumulator (no
 // wait states needed), an operand ring slot is only rewritten after the MFMA reading it has
 // issued, and 20 wait states separate the last score MFMA from VALU reads of its result.
+#include <cstddef>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -65,6 +67,8 @@ constexpr int DMA_PER_WAVE = SLOTS_PER_WAVE / 64;         // 9 instructions
 constexpr int P_STRIDE = 80;            // bytes per head row of P (64 + 16 pad: conflict-free b128 reads)
 constexpr int QR_STRIDE = 144;          // bytes per head row of the position queries (128 + 16 pad)
 constexpr float HEADROOM = 64.0f;       // log2 units: P values stay <= 2^64
+constexpr int QS_STRIDE = 1024 + 16;    // bytes per staged query row (latent part + pad)
+constexpr int ES_STRIDE = 512 + 4;      // floats per staged output row (+ pad)
 
 static_assert(TILE_SLOTS % (WAVES * 64) == 0, "tile must split into whole DMA instructions");
 static_assert(ROW_CHUNKS % 8 == 0, "swizzle groups of 8 chunks");
@@ -76,6 +80,10 @@ struct Smem {
   float lsum[H];
   int restart[WAVES];
 };
+// Query staging (before the loop) and output staging (after it) reuse tiles, P and the position
+// queries; both stop short of lsum, which the epilogue still reads.
+static_assert(H * QS_STRIDE <= offsetof(Smem, lsum), "query staging must end before lsum");
+static_assert(64 * ES_STRIDE * 4 <= offsetof(Smem, lsum), "output staging must end before lsum");
 
 typedef int v16i __attribute__((vector_size(64)));
 
@@ -237,57 +245,39 @@ decode_attn_fast(const bf16* __restrict__ q_packed, const bf16* __restrict__ cac
     }
   };
 
-  // ---- queries of this wave's 32 heads. Latent part: 32 B fragments (8 bf16 per lane:
-  // dims 16s + 8g .. +7 of head 32w + l32) loaded straight into v[128:255]. Position part: LDS.
+  // ---- queries of this wave's 32 heads (32w .. 32w+31).
+  // Latent part: 32 B fragments (8 bf16 per lane: dims 16s + 8g .. +7 of head 32w + l32) for
+  // v[128:255]. Loaded straight from global memory, every instruction would touch 32 rows 1152 B
+  // apart, so the rows are staged through LDS instead: each wave copies its 32 rows with 1 KB
+  // direct global->LDS loads (8 whole cache lines each) into slots QS_STRIDE bytes apart (the
+  // 16-byte pad puts the 16 heads of one LDS phase on 16 different bank groups), then reads its
+  // fragments. The staging area is the first tile buffers, free until the first tile DMA.
+  // Position part: 4 fragments per lane, kept in LDS and read by every score phase.
   const int qhead = w * 32 + l32;
   const bf16* qrow = q_packed + (rh0 + qhead) * ROW + 8 * g;
+  const uint32_t qstage = (uint32_t)(uintptr_t)MLA_LDS(unsigned char, &sm.tile[0][0]) + w * 32 * QS_STRIDE;
+  {
+    const unsigned char* qw = reinterpret_cast<const unsigned char*>(q_packed + (rh0 + w * 32) * ROW) + 16 * lane;
+#pragma unroll 4
+    for (int i = 0; i < 32; ++i) dma16(qw + i * ROW_BYTES, __builtin_amdgcn_readfirstlane(qstage + i * QS_STRIDE));
+  }
+  bf16x8 qr_frag[DR / 16];
+#pragma unroll
+  for (int s = 0; s < DR / 16; ++s) qr_frag[s] = *reinterpret_cast<const bf16x8*>(qrow + DC + 16 * s);
+  wait_vmcnt_0();   // the staged rows and the position fragments are in
   v16i q0, q1, q2, q3, q4, q5, q6, q7;
   asm volatile(
-      "global_load_dwordx4 v[128:131], %[a], off offset:0\n\t"
-      "global_load_dwordx4 v[132:135], %[a], off offset:32\n\t"
-      "global_load_dwordx4 v[136:139], %[a], off offset:64\n\t"
-      "global_load_dwordx4 v[140:143], %[a], off offset:96\n\t"
-      "global_load_dwordx4 v[144:147], %[a], off offset:128\n\t"
-      "global_load_dwordx4 v[148:151], %[a], off offset:160\n\t"
-      "global_load_dwordx4 v[152:155], %[a], off offset:192\n\t"
-      "global_load_dwordx4 v[156:159], %[a], off offset:224\n\t"
-      "global_load_dwordx4 v[160:163], %[a], off offset:256\n\t"
-      "global_load_dwordx4 v[164:167], %[a], off offset:288\n\t"
-      "global_load_dwordx4 v[168:171], %[a], off offset:320\n\t"
-      "global_load_dwordx4 v[172:175], %[a], off offset:352\n\t"
-      "global_load_dwordx4 v[176:179], %[a], off offset:384\n\t"
-      "global_load_dwordx4 v[180:183], %[a], off offset:416\n\t"
-      "global_load_dwordx4 v[184:187], %[a], off offset:448\n\t"
-      "global_load_dwordx4 v[188:191], %[a], off offset:480\n\t"
-      "global_load_dwordx4 v[192:195], %[a], off offset:512\n\t"
-      "global_load_dwordx4 v[196:199], %[a], off offset:544\n\t"
-      "global_load_dwordx4 v[200:203], %[a], off offset:576\n\t"
-      "global_load_dwordx4 v[204:207], %[a], off offset:608\n\t"
-      "global_load_dwordx4 v[208:211], %[a], off offset:640\n\t"
-      "global_load_dwordx4 v[212:215], %[a], off offset:672\n\t"
-      "global_load_dwordx4 v[216:219], %[a], off offset:704\n\t"
-      "global_load_dwordx4 v[220:223], %[a], off offset:736\n\t"
-      "global_load_dwordx4 v[224:227], %[a], off offset:768\n\t"
-      "global_load_dwordx4 v[228:231], %[a], off offset:800\n\t"
-      "global_load_dwordx4 v[232:235], %[a], off offset:832\n\t"
-      "global_load_dwordx4 v[236:239], %[a], off offset:864\n\t"
-      "global_load_dwordx4 v[240:243], %[a], off offset:896\n\t"
-      "global_load_dwordx4 v[244:247], %[a], off offset:928\n\t"
-      "global_load_dwordx4 v[248:251], %[a], off offset:960\n\t"
-      "global_load_dwordx4 v[252:255], %[a], off offset:992\n\t"
-      "s_waitcnt vmcnt(0)"
+@QLOAD_ASM@
       : "=&{v[128:143]}"(q0), "=&{v[144:159]}"(q1), "=&{v[160:175]}"(q2), "=&{v[176:191]}"(q3),
         "=&{v[192:207]}"(q4), "=&{v[208:223]}"(q5), "=&{v[224:239]}"(q6), "=&{v[240:255]}"(q7)
-      : [a] "v"(qrow)
+      : [a] "v"(qstage + l32 * QS_STRIDE + 16 * g)
       : "memory");
+  lds_barrier();   // every wave holds its fragments: the staging area is free for the tiles
 #pragma unroll
   for (int s = 0; s < DR / 16; ++s)
-    *reinterpret_cast<bf16x8*>(sm.qrope + qhead * QR_STRIDE + (2 * s + g) * 16) =
-        *reinterpret_cast<const bf16x8*>(qrow + DC + 16 * s);
-  wait_vmcnt_0();   // nothing of the queries in flight once the tile DMA starts
+    *reinterpret_cast<bf16x8*>(sm.qrope + qhead * QR_STRIDE + (2 * s + g) * 16) = qr_frag[s];
 
-  if (threadIdx.x < WAVES) sm.restart[threadIdx.x] = 0;
-  bool overflowed = false;
+  bool ovf = false;   // this wave saw a score far above its reference (uniform)
 
   // O^T accumulators: [col block cb][head block hb], 16 fp32 each, zeroed in AGPRs by MFMAs of
   // zero operands (a plain zero initialisation would be built in VGPRs first and copied over)
@@ -336,18 +326,43 @@ decode_attn_fast(const bf16* __restrict__ q_packed, const bf16* __restrict__ cac
 
   auto tile_lds = [&](int tile) { return (uint32_t)(uintptr_t)MLA_LDS(unsigned char, sm.tile[tile % NBUF]); };
 
-  // scores of one tile into v[112:127]
+  // Scores of one tile into v[112:127]. The same asm block issues the DMA of the tile after it
+  // (9 global_load_lds spread between the MFMAs, so the VMEM issue overlaps the matrix work).
+  // That tile's buffer held tile - 2, which every wave finished reading before the barrier that
+  // opened this iteration. With no tile left to load, the DMA reads this query row's packed
+  // queries (valid memory of H * ROW_BYTES bytes) into that buffer, which is not read again.
+  const unsigned char* qbytes = reinterpret_cast<const unsigned char*>(q_packed + rh0 * ROW);
   auto scores = [&](int tile, f32x16& sacc) {
     const uint32_t tb = tile_lds(tile);
+    const int dt = tile + 1;
+    const int key0 = j0 + dt * TILE;
+    const unsigned char* src = dt < n_tiles ? kv + (int64_t)key0 * ROW_BYTES : qbytes;
+    uint32_t o[DMA_PER_WAVE];
+#pragma unroll
+    for (int it = 0; it < DMA_PER_WAVE; ++it) o[it] = dma_off[it];
+    if (dt < n_tiles && key0 + TILE > j1) {  // tail tile: rows past the end re-read the last valid row
+      const int last = j1 - 1 - key0;
+#pragma unroll
+      for (int it = 0; it < DMA_PER_WAVE; ++it) {
+        const int r = dma_off[it] / ROW_BYTES;
+        o[it] = dma_off[it] - (r > last ? r - last : 0) * ROW_BYTES;
+      }
+    }
+    const uint64_t sb = (uint64_t)(uintptr_t)src;
+    const uint64_t sbase = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(sb >> 32)) << 32) |
+                           (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)sb);
+    const uint32_t sdst = __builtin_amdgcn_readfirstlane(tile_lds(dt) + (w * SLOTS_PER_WAVE) * 16);
     asm volatile(
 @QK_ASM@
         : "=&{v[112:127]}"(sacc)
         : [k0] "v"(tb + qk_off[0]), [k1] "v"(tb + qk_off[1]), [k2] "v"(tb + qk_off[2]), [k3] "v"(tb + qk_off[3]),
           [qr] "v"(qr_addr), "{v[128:143]}"(q0), "{v[144:159]}"(q1), "{v[160:175]}"(q2), "{v[176:191]}"(q3),
-          "{v[192:207]}"(q4), "{v[208:223]}"(q5), "{v[224:239]}"(q6), "{v[240:255]}"(q7)
+          "{v[192:207]}"(q4), "{v[208:223]}"(q5), "{v[224:239]}"(q6), "{v[240:255]}"(q7),
+          [b] "s"(sbase), [m] "s"(sdst), [o0] "v"(o[0]), [o1] "v"(o[1]), [o2] "v"(o[2]), [o3] "v"(o[3]),
+          [o4] "v"(o[4]), [o5] "v"(o[5]), [o6] "v"(o[6]), [o7] "v"(o[7]), [o8] "v"(o[8])
         : "v80", "v81", "v82", "v83", "v84", "v85", "v86", "v87", "v88", "v89", "v90", "v91", "v92", "v93", "v94",
           "v95", "v96", "v97", "v98", "v99", "v100", "v101", "v102", "v103", "v104", "v105", "v106", "v107", "v108",
-          "v109", "v110", "v111");
+          "v109", "v110", "v111", "memory", "m0");
   };
 
   // softmax of one tile in C++ (first tile: fixes the reference; partial tail tile: masks keys
@@ -364,7 +379,7 @@ decode_attn_fast(const bf16* __restrict__ q_packed, const bf16* __restrict__ cac
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
     if (m_ref == -INFINITY) m_ref = tmax;
-    if (__any(tmax > m_ref + HEADROOM) && lane == 0) sm.restart[w] = 1;
+    ovf |= __any(tmax > m_ref + HEADROOM);
     float psum = 0.0f;
     uint32_t pk[8];
 #pragma unroll
@@ -396,7 +411,7 @@ decode_attn_fast(const bf16* __restrict__ q_packed, const bf16* __restrict__ cac
         : "v80", "v81", "v82", "v83", "v84", "v85", "v86", "v87", "v88", "v89", "v90", "v91", "v92", "v93", "v94",
           "v95", "v96", "v97", "v98", "v99", "v100", "v101", "v102", "v103", "v104", "v105", "v106", "v107", "v108",
           "v109", "v110", "v111", "memory");
-    if (__any(mx * scale_log2 > m_ref + HEADROOM) && lane == 0) sm.restart[w] = 1;
+    ovf |= __any(mx * scale_log2 > m_ref + HEADROOM);
   };
 
   // ---- the loop. Iteration t >= 0: P.V of tile t fused with the softmax of tile t+1 (its scores
@@ -406,11 +421,6 @@ decode_attn_fast(const bf16* __restrict__ q_packed, const bf16* __restrict__ cac
   for (int tile = -1; tile < n_tiles; ++tile) {
     wait_vmcnt_0();   // tile t+1 (the only DMA in flight) landed
     lds_barrier();    // P(t) and tile t+1 visible to all waves; iteration t-1 finished everywhere
-    if (__builtin_amdgcn_readfirstlane(sm.restart[0] | sm.restart[1] | sm.restart[2] | sm.restart[3]) != 0) {
-      overflowed = true;   // a score far above the reference: leave for the exact path (see header)
-      break;
-    }
-    if (tile + 2 < n_tiles) issue_tile(tile + 2);   // into the buffer of tile t-1
     f32x16 sacc;
     if (tile + 1 < n_tiles) scores(tile + 1, sacc);
     if (tile < 0) {
@@ -429,6 +439,12 @@ decode_attn_fast(const bf16* __restrict__ q_packed, const bf16* __restrict__ cac
     pv_softmax(tile, sacc);
   }
 
+  // A score far above the reference makes later probabilities overflow (inf / NaN in the
+  // accumulator, harmless to the hardware); the loop still runs to its end, and the chunk is then
+  // recomputed by the exact path. The flags meet in LDS once, after the loop.
+  if (lane == 0) sm.restart[w] = ovf ? 1 : 0;
+  __syncthreads();
+  const bool overflowed = (sm.restart[0] | sm.restart[1] | sm.restart[2] | sm.restart[3]) != 0;
   if (overflowed) {
     wait_vmcnt_0();   // no DMA may still target LDS
     __syncthreads();
@@ -443,43 +459,54 @@ decode_attn_fast(const bf16* __restrict__ q_packed, const bf16* __restrict__ cac
   // ---- per-head totals: combine the two key halves, publish for every wave
   l_run += __shfl_xor(l_run, 32, 64);
   if (g == 0) sm.lsum[w * 32 + l32] = l_run;
-  __syncthreads();
-  const f32x16* oacc[4][4] = {{&o00, &o01, &o02, &o03}, {&o10, &o11, &o12, &o13},
-                              {&o20, &o21, &o22, &o23}, {&o30, &o31, &o32, &o33}};
-  if (n_chunks == 1) {
-    if (lse != nullptr && g == 0) lse[rh0 + w * 32 + l32] = (m_ref + log2f(l_run)) * kLn2;
-#pragma unroll
-    for (int hb = 0; hb < 4; ++hb) {
-      const int head = hb * 32 + l32;
-      const float inv = 1.0f / sm.lsum[head];
-      float* dst = z + (rh0 + head) * DC + 128 * w + 4 * g;
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const f32x16& o = *oacc[cb][hb];
-          f32x4 v = {o[4 * j] * inv, o[4 * j + 1] * inv, o[4 * j + 2] * inv, o[4 * j + 3] * inv};
-          *reinterpret_cast<f32x4*>(dst + 32 * cb + 8 * j) = v;
-        }
-    }
-  } else {
-    if (g == 0) {
+  if (g == 0) {
+    if (n_chunks == 1) {
+      if (lse != nullptr) lse[rh0 + w * 32 + l32] = (m_ref + log2f(l_run)) * kLn2;
+    } else {
       float* ml = part_ml + ((rh0 + w * 32 + l32) * n_chunks + k) * 2;
       ml[0] = m_ref;
       ml[1] = l_run;
     }
+  }
+
+  // ---- O^T out through LDS, 64 heads per round. Written straight from the accumulator layout,
+  // every store would touch 32 rows; staged, each wave writes whole 2 KB rows (one chunk's
+  // partial, or z = O / l when the chunk is the whole sequence) with contiguous 1 KB stores.
+  float* stage = reinterpret_cast<float*>(smem_raw);   // [64][ES_STRIDE]
+  const f32x16* oacc[4][4] = {{&o00, &o01, &o02, &o03}, {&o10, &o11, &o12, &o13},
+                              {&o20, &o21, &o22, &o23}, {&o30, &o31, &o32, &o33}};
 #pragma unroll
-    for (int hb = 0; hb < 4; ++hb) {
-      const int head = hb * 32 + l32;
-      float* dst = part_acc + ((rh0 + head) * n_chunks + k) * (size_t)DC + 128 * w + 4 * g;
+  for (int half = 0; half < 2; ++half) {
+    __syncthreads();   // the loop (or the previous round's reads) finished everywhere; lsum visible
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      float* row = stage + (hh * 32 + l32) * ES_STRIDE + 128 * w + 4 * g;
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const f32x16& o = *oacc[cb][hb];
-          f32x4 v = {o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]};
-          *reinterpret_cast<f32x4*>(dst + 32 * cb + 8 * j) = v;
+          const f32x16& o = *oacc[cb][2 * half + hh];
+          *reinterpret_cast<f32x4*>(row + 32 * cb + 8 * j) = f32x4{o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]};
         }
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int i = 0; i < 16; ++i) {
+      const int hl = 16 * w + i;
+      const size_t head = (size_t)(64 * half + hl);
+      f32x4 va = *reinterpret_cast<const f32x4*>(stage + hl * ES_STRIDE + 4 * lane);
+      f32x4 vb = *reinterpret_cast<const f32x4*>(stage + hl * ES_STRIDE + 256 + 4 * lane);
+      float* dst;
+      if (n_chunks == 1) {
+        const float inv = 1.0f / sm.lsum[head];
+        va *= inv;
+        vb *= inv;
+        dst = z + (rh0 + head) * DC;
+      } else {
+        dst = part_acc + ((rh0 + head) * n_chunks + k) * (size_t)DC;
+      }
+      *reinterpret_cast<f32x4*>(dst + 4 * lane) = va;
+      *reinterpret_cast<f32x4*>(dst + 256 + 4 * lane) = vb;
     }
   }
 }
