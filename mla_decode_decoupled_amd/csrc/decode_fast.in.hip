@@ -9,40 +9,44 @@
 // both contractions.
 //
 // One workgroup (4 waves, one per SIMD) takes one (query row, split chunk) and walks the chunk
-// in tiles of 32 keys:
-//   * tiles stream HBM -> LDS with direct 16-byte global_load_lds, three buffers, two tiles in
-//     flight. The global addresses are permuted so that LDS holds an XOR-swizzled layout
-//     (16-byte chunk c of row r sits at c ^ f(r) within its group of 8), which makes both LDS read
-//     patterns below bank-conflict free;
-//   * scores: wave w owns heads 32w..32w+31 and computes S^T[32 keys x 32 heads] = K Q_w^T with
-//     36 chained MFMA 32x32x16 over the 576 dims. The latent part of its queries stays in VGPRs
-//     for the whole chunk, the 64-dim position part is read from LDS;
+// in tiles of 32 keys. Wave w owns heads 32w..32w+31 from end to end:
+//   * tiles stream HBM -> LDS with direct 16-byte global_load_lds into four buffers, two tiles in
+//     flight while two are being computed on. The global addresses are permuted so that LDS holds
+//     an XOR-swizzled layout (16-byte chunk c of row r sits at c ^ f(r) within its group of 8),
+//     which makes both LDS read patterns below bank-conflict free;
+//   * scores: S^T[32 keys x 32 heads] = K Q_w^T with 36 chained MFMA 32x32x16 over the 576 dims.
+//     The latent part of the wave's queries stays in VGPRs for the whole chunk, the 64-dim
+//     position part is read from LDS. The key rows of the A operand are taken in the order pi
+//     (below), so that each lane's 16 score registers are exactly the keys its P.V operand needs;
 //   * softmax per head in log2 units against a fixed reference: m_ref is the head's max over the
 //     chunk's first tile and probabilities are 2^(s - m_ref). Softmax is exact for any reference,
-//     so the accumulator is never rescaled. Overflow is impossible while every later score stays
-//     below m_ref + 64; if one does not, the workgroup leaves the MFMA loop and recomputes its
-//     chunk with exact_chunk(), a slow VALU online softmax (correct for any input, never taken
-//     on realistic scores). Keys more than 126 below the reference lose weight under 2^-126
-//     relative to the first tile's largest key;
-//   * P (bf16) goes to LDS; wave w then owns latent columns 128w..128w+127 for all 128 heads and
-//     computes O^T += V^T P^T, reading V^T straight from the row-major tile with the gfx950
-//     transpose read ds_read_b64_tr_b16. V is read from LDS once per workgroup.
-// The loop is software-pipelined with one barrier per tile: iteration t computes the scores of
-// tile t+1, then runs the P.V MFMAs of tile t with the softmax VALU work of tile t+1 interleaved
-// between them (P is double-buffered in LDS), so the exponentials hide under the MFMAs.
-// The chunk result is either final (one chunk: z = O / l, lse) or a split-K partial (O, m, l)
-// that attn_merge combines by log-sum-exp.
+//     so the accumulator is never rescaled. A score above m_ref + 64 sets a flag; after the loop
+//     the workgroup then recomputes its chunk with exact_chunk(), a slow VALU online softmax
+//     (correct for any input, never taken on realistic scores). Keys more than 126 below the
+//     reference lose weight under 2^-126 relative to the first tile's largest key;
+//   * P (bf16) stays in registers: O^T[512 x 32 heads] += V^T P^T with 32 MFMAs, the B operand
+//     straight from the softmax registers and V^T read from the row-major tile with the gfx950
+//     transpose read ds_read_b64_tr_b16. No wave waits for another wave's probabilities.
+// The loop is software-pipelined with one barrier per tile (the tile buffers are shared):
+// iteration t computes the scores of tile t+1 (and issues the DMA of tile t+3), then runs the
+// P.V MFMAs of tile t with the softmax VALU work of tile t+1 interleaved between them, so the
+// exponentials hide under the MFMAs. The chunk result is either final (one chunk: z = O / l,
+// lse) or a split-K partial (O, m, l) that attn_merge_frag combines by log-sum-exp.
 //
 // Register plan (per lane, 512 = 256 VGPRs + 256 AGPRs with one wave per SIMD):
-//   a[0:255]    O^T accumulator, 16 blocks of 32x32 fp32 (asm operands constrained to AGPRs)
+//   a[0:255]    O^T accumulator, 16 blocks of 32 latent columns x 32 heads, fp32
 //   v[128:255]  latent queries, 32 MFMA B fragments (pinned by physical-register constraints)
-//   v[112:127]  score accumulator S^T; v[80:111] operand rings of the two MFMA phases
-//   v[0:79]     everything the compiler allocates (addresses, softmax, DMA offsets)
+//   v[112:127]  score accumulator S^T, softmax in place
+//   v[80:87]    P of the tile being accumulated (two B fragments of 16 keys), carried between
+//               the asm blocks as a pinned value
+//   v[88:111]   operand rings of the two MFMA phases
+//   v[0:79]     everything the compiler allocates (addresses, softmax state, DMA offsets)
 // The two MFMA phases are inline asm because at this occupancy the compiler's allocator spills
 // whatever split it picks. Hazards it cannot see inside asm are handled explicitly: LDS operands
 // are waited for with lgkmcnt in issue order, chained MFMAs use exactly the same accumulator (no
-// wait states needed), an operand ring slot is only rewritten after the MFMA reading it has
-// issued, and 20 wait states separate the last score MFMA from VALU reads of its result.
+// wait states needed), an operand register is only rewritten after the MFMA reading it has
+// issued (plus wait states where a VALU op rewrites it), and 20 wait states separate the last
+// score MFMA from VALU reads of its result.
 #include <cstddef>
 
 #include "common.hpp"
@@ -58,34 +62,34 @@ constexpr int ROW = DC + DR;            // 576 elements
 constexpr int ROW_BYTES = ROW * 2;      // 1152
 constexpr int ROW_CHUNKS = ROW_BYTES / 16;  // 72 chunks of 16 bytes
 constexpr int TILE = 32;                // keys per tile
-constexpr int NBUF = 3;
+constexpr int NBUF = 4;                 // tile buffers: two being computed on, two in flight
 constexpr int TILE_BYTES = TILE * ROW_BYTES;              // 36864
 constexpr int TILE_SLOTS = TILE * ROW_CHUNKS;             // 2304 16-byte slots
 constexpr int WAVES = 4;
 constexpr int SLOTS_PER_WAVE = TILE_SLOTS / WAVES;        // 576
 constexpr int DMA_PER_WAVE = SLOTS_PER_WAVE / 64;         // 9 instructions
-constexpr int P_STRIDE = 80;            // bytes per head row of P (64 + 16 pad: conflict-free b128 reads)
-constexpr int QR_STRIDE = 144;          // bytes per head row of the position queries (128 + 16 pad)
 constexpr float HEADROOM = 64.0f;       // log2 units: P values stay <= 2^64
 constexpr int QS_STRIDE = 1024 + 16;    // bytes per staged query row (latent part + pad)
-constexpr int ES_STRIDE = 512 + 4;      // floats per staged output row (+ pad)
+constexpr int ES_STRIDE = 256 + 4;      // floats per staged half output row (+ pad)
 
 static_assert(TILE_SLOTS % (WAVES * 64) == 0, "tile must split into whole DMA instructions");
 static_assert(ROW_CHUNKS % 8 == 0, "swizzle groups of 8 chunks");
 
+// LDS (160 KB, all of it): four tile buffers, then the position queries laid out chunk-major
+// ([8 chunks of 16 B][128 heads]) so that 16 heads reading the same chunk hit 16 bank groups.
+// The query staging before the loop and the output staging after it reuse the tile buffers;
+// the overflow flags sit in the last kilobyte of the tile area, clear of both stagings.
 struct Smem {
   unsigned char tile[NBUF][TILE_BYTES];
-  unsigned char p[2][H * P_STRIDE];     // double-buffered: tile t read while tile t+1 is written
-  unsigned char qrope[H * QR_STRIDE];
-  float lsum[H];
-  int restart[WAVES];
+  unsigned char qrope[DR * 2 / 16][H][16];
 };
-// Query staging (before the loop) and output staging (after it) reuse tiles, P and the position
-// queries; both stop short of lsum, which the epilogue still reads.
-static_assert(H * QS_STRIDE <= offsetof(Smem, lsum), "query staging must end before lsum");
-static_assert(64 * ES_STRIDE * 4 <= offsetof(Smem, lsum), "output staging must end before lsum");
+constexpr int FLAGS_OFF = NBUF * TILE_BYTES - 1024;
+static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget");
+static_assert(H * QS_STRIDE <= FLAGS_OFF, "query staging must end before the flags");
+static_assert(H * ES_STRIDE * 4 <= FLAGS_OFF, "output staging must end before the flags");
 
 typedef int v16i __attribute__((vector_size(64)));
+typedef int v8i __attribute__((vector_size(32)));
 
 // LDS has 64 banks of 4 bytes and serves 16 lanes of a 16-byte read per cycle. A cache row is
 // 1152 bytes (= 128 mod 256), so rows of equal parity share bank offsets; swz() is injective on
@@ -94,6 +98,16 @@ typedef int v16i __attribute__((vector_size(64)));
 __device__ __forceinline__ int swz(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
 // physical 16-byte chunk of logical chunk c in tile row r (an involution)
 __device__ __forceinline__ int phys_chunk(int c, int r) { return (c & ~7) | ((c ^ swz(r)) & 7); }
+// Key order of the score operand: A row r = 8j + 4h + i holds key pi(r) = 16(j/2) + 8h + 4(j%2) + i.
+// The MFMA result then gives the lane of key half h the 16 keys 8h..8h+7 and 16+8h..16+8h+7,
+// which are its B fragments of the two 16-key steps of P.V. pi maps rows 0-15 and 16-31 onto
+// themselves, so the bank pattern of the score reads does not change.
+__device__ __forceinline__ int key_of_row(int r) {
+  const int j = r >> 3, h = (r >> 2) & 1, i = r & 3;
+  return 16 * (j >> 1) + 8 * h + 4 * (j & 1) + i;
+}
+// key held in score register rr (0..15) by a lane of key half g
+__device__ __forceinline__ int key_of_reg(int rr, int g) { return key_of_row(8 * (rr >> 2) + 4 * g + (rr & 3)); }
 
 // Workgroup barrier for LDS traffic only. __syncthreads() carries a workgroup fence, and because
 // the tile DMA writes LDS the fence would wait for every DMA in flight (vmcnt(0)), which would
@@ -102,13 +116,7 @@ __device__ __forceinline__ int phys_chunk(int c, int r) { return (c & ~7) | ((c 
 // accesses across the barrier.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// One 16-byte-per-lane HBM -> LDS copy: lane l's 16 bytes land at lds_base + 16 * l. Written as
-// inline asm so the compiler does not treat later LDS reads of *other* tile buffers as possibly
-// aliasing this in-flight write (it would insert vmcnt(0) before them). The instruction has no
-// register results; completion is tracked with explicit vmcnt waits. One wait state separates the
-// M0 write from the LDS-DMA instruction that reads it.
-// Nothing else in this kernel uses M0 (the compiler warns that it does not track a clobber of
-// that reserved register, so this must stay true).
+// one 16-byte-per-lane direct global->LDS load: lane l writes LDS bytes lds_base + 16 l
 __device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gaddr), "s"(lds_base)
                : "memory", "m0");
@@ -116,6 +124,18 @@ __device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_base) {
 
 __device__ __forceinline__ void wait_vmcnt_9() { __builtin_amdgcn_s_waitcnt((9 & 15) | (7 << 4) | (15 << 8)); }
 __device__ __forceinline__ void wait_vmcnt_0() { __builtin_amdgcn_s_waitcnt((0) | (7 << 4) | (15 << 8)); }
+
+// Split-K partials of the fast path are stored in the accumulator's own register order, so the
+// attention kernel writes them with whole 1 KB stores straight from the accumulators and the merge
+// reads them the same way. Per (query row, chunk) one block of H * DC floats:
+//   [head block hb][col block cb (16)][row group j][lane][4]
+// holds O^T[col][head] for col = 32cb + 8j + 4(lane / 32) + e, head = 32hb + lane % 32.
+constexpr int PART_FLOATS = H * DC;   // per (query row, chunk)
+__device__ __forceinline__ int frag_offset(int head, int col) {
+  const int cb = col >> 5, j = (col >> 3) & 3, g = (col >> 2) & 1, e = col & 3;
+  const int hb = head >> 5, lane = 32 * g + (head & 31);
+  return (((hb * 16 + cb) * 4 + j) * 64 + lane) * 4 + e;
+}
 
 // Exact fallback for one (query row, chunk): per head, a float32 online softmax that rescales
 // its running sum and latent accumulator at every block of 256 keys. Same outputs as the MFMA
@@ -173,21 +193,24 @@ __device__ __noinline__ void exact_chunk(const bf16* __restrict__ q_packed, cons
       if (lse != nullptr && tid == 0) lse[rh] = (m + log2f(l)) * kLn2;
     } else {
       const size_t slot = rh * n_chunks + k;
-      part_acc[slot * DC + tid] = acc0;
-      part_acc[slot * DC + tid + 256] = acc1;
+      float* blk = part_acc + ((rh0 / H) * n_chunks + k) * (size_t)PART_FLOATS;
+      blk[frag_offset(h, tid)] = acc0;
+      blk[frag_offset(h, tid + 256)] = acc1;
       if (tid == 0) {
         part_ml[slot * 2 + 0] = m;
         part_ml[slot * 2 + 1] = l;
       }
     }
+    __syncthreads();
   }
 }
 
-__global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
-decode_attn_fast(const bf16* __restrict__ q_packed, const bf16* __restrict__ cache,
-                 const int64_t* __restrict__ seq_off, const int32_t* __restrict__ seq_len, int n_q, float scale_log2,
-                 int chunk_len, int n_chunks, float* __restrict__ part_acc, float* __restrict__ part_ml,
-                 float* __restrict__ z, float* __restrict__ lse) {
+// grid (n_chunks, batch * n_q), 256 threads, sizeof(Smem) dynamic LDS
+__global__ void __launch_bounds__(256)
+    decode_attn_fast(const bf16* __restrict__ q_packed, const bf16* __restrict__ cache,
+                     const int64_t* __restrict__ seq_off, const int32_t* __restrict__ seq_len, int n_q, float scale_log2,
+                     int chunk_len, int n_chunks, float* __restrict__ part_acc, float* __restrict__ part_ml,
+                     float* __restrict__ z, float* __restrict__ lse) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
 
@@ -209,6 +232,8 @@ decode_attn_fast(const bf16* __restrict__ q_packed, const bf16* __restrict__ cac
   }
   const int n_tiles = (j1 - j0 + TILE - 1) / TILE;
   const unsigned char* kv = reinterpret_cast<const unsigned char*>(cache + seq_off[b] * (int64_t)ROW);
+  // always-valid DMA source for "no tile left": this query row's packed queries (H * ROW_BYTES bytes)
+  const unsigned char* qbytes = reinterpret_cast<const unsigned char*>(q_packed + rh0 * ROW);
 
   // ---- DMA plan: slot (row r, physical chunk p) of the LDS tile is filled from logical chunk
   // phys_chunk(p, r) of key r: dma_off = r * ROW_BYTES + 16 * phys_chunk(p, r).
@@ -219,30 +244,39 @@ decode_attn_fast(const bf16* __restrict__ q_packed, const bf16* __restrict__ cac
     const int r = slot / ROW_CHUNKS, p = slot % ROW_CHUNKS;
     dma_off[it] = r * ROW_BYTES + phys_chunk(p, r) * 16;
   }
-  auto issue_tile = [&](int tile) {
+  auto tile_lds = [&](int tile) { return (uint32_t)(uintptr_t)MLA_LDS(unsigned char, sm.tile[tile % NBUF]); };
+  // DMA source of tile `tile` and this lane's nine offsets. Rows of a tail tile past the end
+  // re-read the last valid row (their scores are masked); a tile past the chunk reads qbytes.
+  auto dma_plan = [&](int tile, uint32_t* o) -> const unsigned char* {
     const int key0 = j0 + tile * TILE;
-    const unsigned char* src0 = kv + (int64_t)key0 * ROW_BYTES;
-    const uint32_t dst = (uint32_t)(uintptr_t)MLA_LDS(unsigned char, sm.tile[tile % NBUF] + (w * SLOTS_PER_WAVE) * 16);
-    if (key0 + TILE <= j1) {  // full tile: SGPR base + 32-bit lane offsets, no VALU work
-      const uint64_t sb = (uint64_t)(uintptr_t)src0;
-      const uint64_t sbase = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(sb >> 32)) << 32) |
-                             (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)sb);
-      const uint32_t sdst = __builtin_amdgcn_readfirstlane(dst);
-      asm volatile(
-@DMA_ASM@
-          ::[b] "s"(sbase), [m] "s"(sdst), [o0] "v"(dma_off[0]), [o1] "v"(dma_off[1]), [o2] "v"(dma_off[2]),
-          [o3] "v"(dma_off[3]), [o4] "v"(dma_off[4]), [o5] "v"(dma_off[5]), [o6] "v"(dma_off[6]),
-          [o7] "v"(dma_off[7]), [o8] "v"(dma_off[8])
-          : "memory", "m0");
-    } else {  // tail tile: rows past the end re-read the last valid row (their scores are masked)
+#pragma unroll
+    for (int it = 0; it < DMA_PER_WAVE; ++it) o[it] = dma_off[it];
+    if (tile >= n_tiles) return qbytes;
+    if (key0 + TILE > j1) {
       const int last = j1 - 1 - key0;
 #pragma unroll
       for (int it = 0; it < DMA_PER_WAVE; ++it) {
         const int r = dma_off[it] / ROW_BYTES;
-        const int off = dma_off[it] - (r > last ? r - last : 0) * ROW_BYTES;
-        dma16(src0 + off, __builtin_amdgcn_readfirstlane(dst + it * 64 * 16));
+        o[it] = dma_off[it] - (r > last ? r - last : 0) * ROW_BYTES;
       }
     }
+    return kv + (int64_t)key0 * ROW_BYTES;
+  };
+  auto sgpr_ptr = [](const void* p) {
+    const uint64_t sb = (uint64_t)(uintptr_t)p;
+    return ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(sb >> 32)) << 32) |
+           (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)sb);
+  };
+  // stand-alone tile DMA (prologue): nine 1 KB instructions per wave into the tile's buffer
+  auto issue_tile = [&](int tile) {
+    uint32_t o[DMA_PER_WAVE];
+    const uint64_t sbase = sgpr_ptr(dma_plan(tile, o));
+    const uint32_t sdst = __builtin_amdgcn_readfirstlane(tile_lds(tile) + (w * SLOTS_PER_WAVE) * 16);
+    asm volatile(
+@DMA_ASM@
+        ::[b] "s"(sbase), [m] "s"(sdst), [o0] "v"(o[0]), [o1] "v"(o[1]), [o2] "v"(o[2]), [o3] "v"(o[3]),
+        [o4] "v"(o[4]), [o5] "v"(o[5]), [o6] "v"(o[6]), [o7] "v"(o[7]), [o8] "v"(o[8])
+        : "memory", "m0");
   };
 
   // ---- queries of this wave's 32 heads (32w .. 32w+31).
@@ -251,7 +285,7 @@ decode_attn_fast(const bf16* __restrict__ q_packed, const bf16* __restrict__ cac
   // apart, so the rows are staged through LDS instead: each wave copies its 32 rows with 1 KB
   // direct global->LDS loads (8 whole cache lines each) into slots QS_STRIDE bytes apart (the
   // 16-byte pad puts the 16 heads of one LDS phase on 16 different bank groups), then reads its
-  // fragments. The staging area is the first tile buffers, free until the first tile DMA.
+  // fragments. The staging area is the tile buffers, free until the first tile DMA.
   // Position part: 4 fragments per lane, kept in LDS and read by every score phase.
   const int qhead = w * 32 + l32;
   const bf16* qrow = q_packed + (rh0 + qhead) * ROW + 8 * g;
@@ -261,10 +295,10 @@ decode_attn_fast(const bf16* __restrict__ q_packed, const bf16* __restrict__ cac
 #pragma unroll 4
     for (int i = 0; i < 32; ++i) dma16(qw + i * ROW_BYTES, __builtin_amdgcn_readfirstlane(qstage + i * QS_STRIDE));
   }
-  bf16x8 qr_frag[DR / 16];
 #pragma unroll
-  for (int s = 0; s < DR / 16; ++s) qr_frag[s] = *reinterpret_cast<const bf16x8*>(qrow + DC + 16 * s);
-  wait_vmcnt_0();   // the staged rows and the position fragments are in
+  for (int s = 0; s < DR / 16; ++s)   // chunk 2s + g of the position part, chunk-major layout
+    *reinterpret_cast<bf16x8*>(&sm.qrope[2 * s + g][qhead][0]) = *reinterpret_cast<const bf16x8*>(qrow + DC + 16 * s);
+  wait_vmcnt_0();   // the staged rows are in
   v16i q0, q1, q2, q3, q4, q5, q6, q7;
   asm volatile(
 @QLOAD_ASM@
@@ -273,18 +307,21 @@ decode_attn_fast(const bf16* __restrict__ q_packed, const bf16* __restrict__ cac
       : [a] "v"(qstage + l32 * QS_STRIDE + 16 * g)
       : "memory");
   lds_barrier();   // every wave holds its fragments: the staging area is free for the tiles
-#pragma unroll
-  for (int s = 0; s < DR / 16; ++s)
-    *reinterpret_cast<bf16x8*>(sm.qrope + qhead * QR_STRIDE + (2 * s + g) * 16) = qr_frag[s];
+  issue_tile(0);
+  issue_tile(1);   // past the chunk when it has one tile: then a harmless read of qbytes
 
   bool ovf = false;   // this wave saw a score far above its reference (uniform)
 
-  // O^T accumulators: [col block cb][head block hb], 16 fp32 each, zeroed in AGPRs by MFMAs of
-  // zero operands (a plain zero initialisation would be built in VGPRs first and copied over)
-  f32x16 o00, o01, o02, o03, o10, o11, o12, o13, o20, o21, o22, o23, o30, o31, o32, o33;
+  // O^T accumulators: latent col block cb (32 columns) x this wave's 32 heads, 16 fp32 each,
+  // zeroed in AGPRs by MFMAs of zero operands (a plain zero initialisation would be built in
+  // VGPRs first and copied over)
+  f32x16 oc0, oc1, oc2, oc3, oc4, oc5, oc6, oc7, oc8, oc9, oc10, oc11, oc12, oc13, oc14, oc15;
   {
+    // The zero operand is written by VALU just before: wait states before an MFMA reads it (the
+    // compiler does not pad hazards into inline asm).
     const bf16x8 zf = {};
     asm volatile(
+        "s_nop 7\n\t"
         "v_mfma_f32_32x32x16_bf16 %0, %[z], %[z], 0\n\tv_mfma_f32_32x32x16_bf16 %1, %[z], %[z], 0\n\t"
         "v_mfma_f32_32x32x16_bf16 %2, %[z], %[z], 0\n\tv_mfma_f32_32x32x16_bf16 %3, %[z], %[z], 0\n\t"
         "v_mfma_f32_32x32x16_bf16 %4, %[z], %[z], 0\n\tv_mfma_f32_32x32x16_bf16 %5, %[z], %[z], 0\n\t"
@@ -293,21 +330,25 @@ decode_attn_fast(const bf16* __restrict__ q_packed, const bf16* __restrict__ cac
         "v_mfma_f32_32x32x16_bf16 %10, %[z], %[z], 0\n\tv_mfma_f32_32x32x16_bf16 %11, %[z], %[z], 0\n\t"
         "v_mfma_f32_32x32x16_bf16 %12, %[z], %[z], 0\n\tv_mfma_f32_32x32x16_bf16 %13, %[z], %[z], 0\n\t"
         "v_mfma_f32_32x32x16_bf16 %14, %[z], %[z], 0\n\tv_mfma_f32_32x32x16_bf16 %15, %[z], %[z], 0"
-        : "=a"(o00), "=a"(o01), "=a"(o02), "=a"(o03), "=a"(o10), "=a"(o11), "=a"(o12), "=a"(o13),
-          "=a"(o20), "=a"(o21), "=a"(o22), "=a"(o23), "=a"(o30), "=a"(o31), "=a"(o32), "=a"(o33)
+        : "=a"(oc0), "=a"(oc1), "=a"(oc2), "=a"(oc3), "=a"(oc4), "=a"(oc5), "=a"(oc6), "=a"(oc7),
+          "=a"(oc8), "=a"(oc9), "=a"(oc10), "=a"(oc11), "=a"(oc12), "=a"(oc13), "=a"(oc14), "=a"(oc15)
         : [z] "v"(zf));
   }
 
   float m_ref = -INFINITY;  // per lane: head 32w + l32 (both lane halves agree); set by the first tile
   float l_run = 0.0f;       // per lane: sum over this lane's half of the keys
+  v8i pfr;                  // P of the tile being accumulated: bf16 pairs, keys 16s + 8g + e
 
   // per-lane LDS byte offsets
-  // scores: A operand row = key l32, logical chunk 2s + g -> phys (s/4)*8 + ((2(s%4)+g) ^ swz(l32))
+  // scores: A operand row l32 = key pi(l32), logical chunk 2s + g -> phys (s/4)*8 + ((2(s%4)+g) ^ swz(key))
   uint32_t qk_off[4];
+  {
+    const int key = key_of_row(l32);
 #pragma unroll
-  for (int s4 = 0; s4 < 4; ++s4) qk_off[s4] = l32 * ROW_BYTES + (((2 * s4 + g) ^ swz(l32)) & 7) * 16;
-  const uint32_t qr_addr = (uint32_t)(uintptr_t)MLA_LDS(unsigned char, sm.qrope + qhead * QR_STRIDE + 16 * g);
-  // values: transpose reads. lane = 16q + L; row = 16s + 8g + 4h + L/4; col = 128w + 32cb + 16(q&1) + 4(L&3)
+    for (int s4 = 0; s4 < 4; ++s4) qk_off[s4] = key * ROW_BYTES + (((2 * s4 + g) ^ swz(key)) & 7) * 16;
+  }
+  const uint32_t qr_addr = (uint32_t)(uintptr_t)MLA_LDS(unsigned char, &sm.qrope[g][qhead][0]);
+  // values: transpose reads. lane = 16q + L; row = 16s + 8g + 4h + L/4; col = 32cb + 16(q&1) + 4(L&3)
   const int q16 = lane >> 4, L = lane & 15;
   uint32_t pv_off[2][2];  // [cb & 1][h]
 #pragma unroll
@@ -317,114 +358,84 @@ decode_attn_fast(const bf16* __restrict__ q_packed, const bf16* __restrict__ cac
       const int row = 8 * g + 4 * h + (L >> 2);
       const int clow = 4 * cbo + 2 * (q16 & 1) + ((L >> 1) & 1);  // logical chunk & 7
       const int ph = (clow ^ swz(row)) & 7;
-      pv_off[cbo][h] = row * ROW_BYTES + (16 * w) * 16 + ph * 16 + (L & 1) * 8;
+      pv_off[cbo][h] = row * ROW_BYTES + ph * 16 + (L & 1) * 8;
     }
-  const uint32_t p_base = (uint32_t)(uintptr_t)MLA_LDS(unsigned char, &sm.p[0][0]);
-  const uint32_t p_wr = p_base + (w * 32 + l32) * P_STRIDE + 4 * g * 2;   // + 16 * j for key block j
-  const uint32_t p_rd = p_base + l32 * P_STRIDE + 8 * g * 2;
-  constexpr uint32_t P_BUF = H * P_STRIDE;
 
-  auto tile_lds = [&](int tile) { return (uint32_t)(uintptr_t)MLA_LDS(unsigned char, sm.tile[tile % NBUF]); };
-
-  // Scores of one tile into v[112:127]. The same asm block issues the DMA of the tile after it
-  // (9 global_load_lds spread between the MFMAs, so the VMEM issue overlaps the matrix work).
-  // That tile's buffer held tile - 2, which every wave finished reading before the barrier that
-  // opened this iteration. With no tile left to load, the DMA reads this query row's packed
-  // queries (valid memory of H * ROW_BYTES bytes) into that buffer, which is not read again.
-  const unsigned char* qbytes = reinterpret_cast<const unsigned char*>(q_packed + rh0 * ROW);
+  // Scores of one tile into v[112:127]. The same asm block issues the DMA of the tile two
+  // after it (9 global_load_lds spread between the MFMAs, so the VMEM issue overlaps the matrix
+  // work). That tile's buffer held the tile before the one being accumulated, which every wave
+  // finished reading before the barrier that opened this iteration.
   auto scores = [&](int tile, f32x16& sacc) {
     const uint32_t tb = tile_lds(tile);
-    const int dt = tile + 1;
-    const int key0 = j0 + dt * TILE;
-    const unsigned char* src = dt < n_tiles ? kv + (int64_t)key0 * ROW_BYTES : qbytes;
+    const int dt = tile + 2;
     uint32_t o[DMA_PER_WAVE];
-#pragma unroll
-    for (int it = 0; it < DMA_PER_WAVE; ++it) o[it] = dma_off[it];
-    if (dt < n_tiles && key0 + TILE > j1) {  // tail tile: rows past the end re-read the last valid row
-      const int last = j1 - 1 - key0;
-#pragma unroll
-      for (int it = 0; it < DMA_PER_WAVE; ++it) {
-        const int r = dma_off[it] / ROW_BYTES;
-        o[it] = dma_off[it] - (r > last ? r - last : 0) * ROW_BYTES;
-      }
-    }
-    const uint64_t sb = (uint64_t)(uintptr_t)src;
-    const uint64_t sbase = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(sb >> 32)) << 32) |
-                           (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)sb);
+    const uint64_t sbase = sgpr_ptr(dma_plan(dt, o));
     const uint32_t sdst = __builtin_amdgcn_readfirstlane(tile_lds(dt) + (w * SLOTS_PER_WAVE) * 16);
     asm volatile(
 @QK_ASM@
         : "=&{v[112:127]}"(sacc)
         : [k0] "v"(tb + qk_off[0]), [k1] "v"(tb + qk_off[1]), [k2] "v"(tb + qk_off[2]), [k3] "v"(tb + qk_off[3]),
           [qr] "v"(qr_addr), "{v[128:143]}"(q0), "{v[144:159]}"(q1), "{v[160:175]}"(q2), "{v[176:191]}"(q3),
-          "{v[192:207]}"(q4), "{v[208:223]}"(q5), "{v[224:239]}"(q6), "{v[240:255]}"(q7),
+          "{v[192:207]}"(q4), "{v[208:223]}"(q5), "{v[224:239]}"(q6), "{v[240:255]}"(q7), "{v[80:87]}"(pfr),
           [b] "s"(sbase), [m] "s"(sdst), [o0] "v"(o[0]), [o1] "v"(o[1]), [o2] "v"(o[2]), [o3] "v"(o[3]),
           [o4] "v"(o[4]), [o5] "v"(o[5]), [o6] "v"(o[6]), [o7] "v"(o[7]), [o8] "v"(o[8])
-        : "v80", "v81", "v82", "v83", "v84", "v85", "v86", "v87", "v88", "v89", "v90", "v91", "v92", "v93", "v94",
-          "v95", "v96", "v97", "v98", "v99", "v100", "v101", "v102", "v103", "v104", "v105", "v106", "v107", "v108",
-          "v109", "v110", "v111", "memory", "m0");
+        : "v88", "v89", "v90", "v91", "v92", "v93", "v94", "v95", "v96", "v97", "v98", "v99", "v100", "v101",
+          "v102", "v103", "v104", "v105", "v106", "v107", "v108", "v109", "v110", "v111", "memory", "m0");
   };
 
-  // softmax of one tile in C++ (first tile: fixes the reference; partial tail tile: masks keys
-  // past the end). Writes the tile's P buffer and flags a score far above the reference.
-  auto softmax_masked = [&](int tile, f32x16 sacc) {
-    const int key0 = j0 + tile * TILE;
+  // softmax of the chunk's first tile in C++: fixes the reference, masks keys past the end of a
+  // tail tile, and leaves P in the B-operand registers.
+  auto softmax_first = [&](f32x16 sacc) {
     float tmax = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int kk = 8 * (r >> 2) + 4 * g + (r & 3);
-      const float sv = (key0 + kk < j1) ? sacc[r] * scale_log2 : -INFINITY;
+      const float sv = (j0 + key_of_reg(r, g) < j1) ? sacc[r] * scale_log2 : -INFINITY;
       sacc[r] = sv;
       tmax = fmaxf(tmax, sv);
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    if (m_ref == -INFINITY) m_ref = tmax;
-    ovf |= __any(tmax > m_ref + HEADROOM);
+    m_ref = tmax;
     float psum = 0.0f;
-    uint32_t pk[8];
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
       const float p0 = exp2f(sacc[r] - m_ref), p1 = exp2f(sacc[r + 1] - m_ref);
       psum += p0 + p1;
-      pk[r / 2] = (uint32_t)__builtin_bit_cast(unsigned short, (bf16)p0) |
-                  ((uint32_t)__builtin_bit_cast(unsigned short, (bf16)p1) << 16);
+      pfr[r / 2] = (int)((uint32_t)__builtin_bit_cast(unsigned short, (bf16)p0) |
+                         ((uint32_t)__builtin_bit_cast(unsigned short, (bf16)p1) << 16));
     }
     l_run += psum;
-    unsigned char* pw = &sm.p[tile & 1][0] + (w * 32 + l32) * P_STRIDE + 4 * g * 2;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) *reinterpret_cast<uint2*>(pw + 16 * j) = make_uint2(pk[2 * j], pk[2 * j + 1]);
   };
 
-  // P.V of tile t with the softmax of the full tile t+1 (scores in v[112:127]) interleaved
+  // P.V of tile t (P in v[80:87]) with the softmax of tile t+1 (scores in v[112:127])
+  // interleaved; leaves P of tile t+1 in v[80:87].
   auto pv_softmax = [&](int tile, f32x16& sacc) {
     const uint32_t tb = tile_lds(tile);
     float mx;
     asm volatile(
 @PVSM_ASM@
-        : [o00] "+a"(o00), [o01] "+a"(o01), [o02] "+a"(o02), [o03] "+a"(o03), [o10] "+a"(o10), [o11] "+a"(o11),
-          [o12] "+a"(o12), [o13] "+a"(o13), [o20] "+a"(o20), [o21] "+a"(o21), [o22] "+a"(o22), [o23] "+a"(o23),
-          [o30] "+a"(o30), [o31] "+a"(o31), [o32] "+a"(o32), [o33] "+a"(o33), [l] "+v"(l_run), [mx] "=&v"(mx),
-          "+{v[112:127]}"(sacc)
-        : [p] "v"(p_rd + (tile & 1) * P_BUF), [v00] "v"(tb + pv_off[0][0]), [v01] "v"(tb + pv_off[0][1]),
-          [v10] "v"(tb + pv_off[1][0]), [v11] "v"(tb + pv_off[1][1]), [sc] "s"(scale_log2), [nm] "v"(-m_ref),
-          [pw] "v"(p_wr + ((tile + 1) & 1) * P_BUF)
-        : "v80", "v81", "v82", "v83", "v84", "v85", "v86", "v87", "v88", "v89", "v90", "v91", "v92", "v93", "v94",
-          "v95", "v96", "v97", "v98", "v99", "v100", "v101", "v102", "v103", "v104", "v105", "v106", "v107", "v108",
-          "v109", "v110", "v111", "memory");
+        : [o0] "+a"(oc0), [o1] "+a"(oc1), [o2] "+a"(oc2), [o3] "+a"(oc3), [o4] "+a"(oc4), [o5] "+a"(oc5),
+          [o6] "+a"(oc6), [o7] "+a"(oc7), [o8] "+a"(oc8), [o9] "+a"(oc9), [o10] "+a"(oc10), [o11] "+a"(oc11),
+          [o12] "+a"(oc12), [o13] "+a"(oc13), [o14] "+a"(oc14), [o15] "+a"(oc15), [l] "+v"(l_run), [mx] "=&v"(mx),
+          "+{v[112:127]}"(sacc), "+{v[80:87]}"(pfr)
+        : [v00] "v"(tb + pv_off[0][0]), [v01] "v"(tb + pv_off[0][1]), [v10] "v"(tb + pv_off[1][0]),
+          [v11] "v"(tb + pv_off[1][1]), [sc] "s"(scale_log2), [nm] "v"(-m_ref)
+        : "v88", "v89", "v90", "v91", "v92", "v93", "v94", "v95", "v96", "v97", "v98", "v99", "v100", "v101",
+          "v102", "v103", "v104", "v105", "v106", "v107", "v108", "v109", "v110", "v111", "memory");
     ovf |= __any(mx * scale_log2 > m_ref + HEADROOM);
   };
 
   // ---- the loop. Iteration t >= 0: P.V of tile t fused with the softmax of tile t+1 (its scores
   // computed just before); iteration -1 only scores tile 0 and fixes the reference in C++.
   // Exactly one site per asm phase keeps the register assignment simple for the compiler.
-  issue_tile(0);
+  // Every score phase issues exactly one tile DMA (a harmless one past the chunk), so at the top
+  // of each iteration the newest nine loads of this wave belong to the tile after next.
   for (int tile = -1; tile < n_tiles; ++tile) {
-    wait_vmcnt_0();   // tile t+1 (the only DMA in flight) landed
-    lds_barrier();    // P(t) and tile t+1 visible to all waves; iteration t-1 finished everywhere
+    wait_vmcnt_9();   // tile t+1 landed; tile t+2 may still be in flight
+    lds_barrier();    // tile t+1 visible to all waves; iteration t-1 finished everywhere
     f32x16 sacc;
     if (tile + 1 < n_tiles) scores(tile + 1, sacc);
     if (tile < 0) {
-      softmax_masked(0, sacc);
+      softmax_first(sacc);
       continue;
     }
     if (tile + 1 >= n_tiles) {
@@ -434,80 +445,168 @@ decode_attn_fast(const bf16* __restrict__ q_packed, const bf16* __restrict__ cac
       const int key0 = j0 + (tile + 1) * TILE;
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (key0 + 8 * (r >> 2) + 4 * g + (r & 3) >= j1) sacc[r] = -INFINITY;
+        if (key0 + key_of_reg(r, g) >= j1) sacc[r] = -INFINITY;
     }
     pv_softmax(tile, sacc);
   }
+  wait_vmcnt_0();   // the trailing DMAs (past the chunk) have landed; LDS is free
 
   // A score far above the reference makes later probabilities overflow (inf / NaN in the
   // accumulator, harmless to the hardware); the loop still runs to its end, and the chunk is then
   // recomputed by the exact path. The flags meet in LDS once, after the loop.
-  if (lane == 0) sm.restart[w] = ovf ? 1 : 0;
+  int* flags = reinterpret_cast<int*>(smem_raw + FLAGS_OFF);
+  if (lane == 0) flags[w] = ovf ? 1 : 0;
   __syncthreads();
-  const bool overflowed = (sm.restart[0] | sm.restart[1] | sm.restart[2] | sm.restart[3]) != 0;
+  const bool overflowed = (flags[0] | flags[1] | flags[2] | flags[3]) != 0;
   if (overflowed) {
-    wait_vmcnt_0();   // no DMA may still target LDS
     __syncthreads();
     exact_chunk(q_packed, kv, rh0, j0, j1, scale_log2, n_chunks, k, part_acc, part_ml, z, lse, smem_raw);
     return;
   }
   // the accumulator is read by VALU below: 20 wait states after the last MFMA
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3"
-               : "+a"(o00), "+a"(o01), "+a"(o02), "+a"(o03), "+a"(o10), "+a"(o11), "+a"(o12), "+a"(o13),
-                 "+a"(o20), "+a"(o21), "+a"(o22), "+a"(o23), "+a"(o30), "+a"(o31), "+a"(o32), "+a"(o33));
+               : "+a"(oc0), "+a"(oc1), "+a"(oc2), "+a"(oc3), "+a"(oc4), "+a"(oc5), "+a"(oc6), "+a"(oc7),
+                 "+a"(oc8), "+a"(oc9), "+a"(oc10), "+a"(oc11), "+a"(oc12), "+a"(oc13), "+a"(oc14), "+a"(oc15));
 
-  // ---- per-head totals: combine the two key halves, publish for every wave
+  // ---- per-head totals: combine the two key halves of this lane's head
   l_run += __shfl_xor(l_run, 32, 64);
-  if (g == 0) sm.lsum[w * 32 + l32] = l_run;
   if (g == 0) {
     if (n_chunks == 1) {
-      if (lse != nullptr) lse[rh0 + w * 32 + l32] = (m_ref + log2f(l_run)) * kLn2;
+      if (lse != nullptr) lse[rh0 + qhead] = (m_ref + log2f(l_run)) * kLn2;
     } else {
-      float* ml = part_ml + ((rh0 + w * 32 + l32) * n_chunks + k) * 2;
+      float* ml = part_ml + ((rh0 + qhead) * n_chunks + k) * 2;
       ml[0] = m_ref;
       ml[1] = l_run;
     }
   }
+  const f32x16* oacc[16] = {&oc0, &oc1, &oc2, &oc3, &oc4, &oc5, &oc6, &oc7,
+                            &oc8, &oc9, &oc10, &oc11, &oc12, &oc13, &oc14, &oc15};
+  if (n_chunks > 1) {
+    // ---- partial: 64 stores of 1 KB per wave, straight from the accumulators (layout above)
+    float* blk = part_acc + ((size_t)bt * n_chunks + k) * PART_FLOATS + (size_t)w * (PART_FLOATS / 4) + 4 * lane;
+#pragma unroll
+    for (int cb = 0; cb < 16; ++cb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x16& o = *oacc[cb];
+        *reinterpret_cast<f32x4*>(blk + (cb * 4 + j) * 256) = f32x4{o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]};
+      }
+    return;
+  }
 
-  // ---- O^T out through LDS, 64 heads per round. Written straight from the accumulator layout,
-  // every store would touch 32 rows; staged, each wave writes whole 2 KB rows (one chunk's
-  // partial, or z = O / l when the chunk is the whole sequence) with contiguous 1 KB stores.
-  float* stage = reinterpret_cast<float*>(smem_raw);   // [64][ES_STRIDE]
-  const f32x16* oacc[4][4] = {{&o00, &o01, &o02, &o03}, {&o10, &o11, &o12, &o13},
-                              {&o20, &o21, &o22, &o23}, {&o30, &o31, &o32, &o33}};
+  // ---- z = O / l of this wave's 32 heads, through this wave's own slice of LDS, one half of the
+  // columns at a time: written straight from the accumulator layout, every store would touch 32
+  // rows; transposed, each store writes 1 KB of one head's row. No other wave touches the slice.
+  const float inv = 1.0f / l_run;
+  float* stage = reinterpret_cast<float*>(smem_raw) + w * 32 * ES_STRIDE;   // [32 heads][ES_STRIDE]
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
-    __syncthreads();   // the loop (or the previous round's reads) finished everywhere; lsum visible
+    float* row = stage + l32 * ES_STRIDE + 4 * g;
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      float* row = stage + (hh * 32 + l32) * ES_STRIDE + 128 * w + 4 * g;
+    for (int cb = 0; cb < 8; ++cb)
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const f32x16& o = *oacc[cb][2 * half + hh];
-          *reinterpret_cast<f32x4*>(row + 32 * cb + 8 * j) = f32x4{o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]};
-        }
-    }
-    __syncthreads();
-#pragma unroll 4
-    for (int i = 0; i < 16; ++i) {
-      const int hl = 16 * w + i;
-      const size_t head = (size_t)(64 * half + hl);
-      f32x4 va = *reinterpret_cast<const f32x4*>(stage + hl * ES_STRIDE + 4 * lane);
-      f32x4 vb = *reinterpret_cast<const f32x4*>(stage + hl * ES_STRIDE + 256 + 4 * lane);
-      float* dst;
-      if (n_chunks == 1) {
-        const float inv = 1.0f / sm.lsum[head];
-        va *= inv;
-        vb *= inv;
-        dst = z + (rh0 + head) * DC;
-      } else {
-        dst = part_acc + ((rh0 + head) * n_chunks + k) * (size_t)DC;
+      for (int j = 0; j < 4; ++j) {
+        const f32x16& o = *oacc[8 * half + cb];
+        *reinterpret_cast<f32x4*>(row + 32 * cb + 8 * j) =
+            f32x4{o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]} * inv;
       }
-      *reinterpret_cast<f32x4*>(dst + 4 * lane) = va;
-      *reinterpret_cast<f32x4*>(dst + 256 + 4 * lane) = vb;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's writes land before its reads
+#pragma unroll 4
+    for (int i = 0; i < 32; ++i) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(stage + i * ES_STRIDE + 4 * lane);
+      *reinterpret_cast<f32x4*>(z + (rh0 + w * 32 + i) * DC + 256 * half + 4 * lane) = v;
     }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads done before the next half's writes
+  }
+}
+
+// Log-sum-exp merge of the split-K partials of the fast path (layout above). One workgroup per
+// (query row, head block hb, col block cb): 32 heads x 32 latent columns, each lane owning one
+// head and 16 columns. With M = max_k m_k over live chunks (m in log2 units),
+// z = sum_k 2^(m_k - M) O_k / sum_k 2^(m_k - M) l_k. The (m, l) pairs of the 32 heads are first
+// turned into weights in LDS, so the stream over the partials has no global-memory dependency:
+// the 4 waves take the chunks round-robin, two chunks (8 coalesced 1 KB loads) per step, and
+// meet in LDS. A chunk with l = 0 saw no key (it is empty for every head) and is not read.
+__global__ void __launch_bounds__(256) attn_merge_frag(const float* __restrict__ part_acc,
+                                                       const float* __restrict__ part_ml, int n_chunks,
+                                                       float* __restrict__ z, float* __restrict__ lse) {
+  extern __shared__ __attribute__((aligned(16))) float2 wl[];   // [32 heads][n_chunks]: (weight, l)
+  __shared__ f32x4 red[3][4][64];
+  __shared__ float mh[32], lh[32];
+  const int bt = blockIdx.y, slab = blockIdx.x;   // slab = hb * 16 + cb
+  const int hb = slab >> 4, cb = slab & 15;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int g = lane >> 5, hl = lane & 31;
+  const float2* ml = reinterpret_cast<const float2*>(part_ml) + ((size_t)bt * H + 32 * hb) * n_chunks;
+  for (int e = tid; e < 32 * n_chunks; e += 256) wl[e] = ml[e];
+  __syncthreads();
+  {  // per head: M over live chunks (8 lanes per head), then the weights and their l-weighted sum
+    const int h = tid >> 3, sub = tid & 7;
+    float M = -INFINITY;
+    for (int kk = sub; kk < n_chunks; kk += 8) {
+      const float2 v = wl[h * n_chunks + kk];
+      if (v.y > 0.0f) M = fmaxf(M, v.x);
+    }
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+    float Lsum = 0.0f;
+    for (int kk = sub; kk < n_chunks; kk += 8) {
+      float2 v = wl[h * n_chunks + kk];
+      v.x = v.y > 0.0f ? exp2f(v.x - M) : 0.0f;
+      Lsum = fmaf(v.x, v.y, Lsum);
+      wl[h * n_chunks + kk] = v;
+    }
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) Lsum += __shfl_xor(Lsum, o, 64);
+    if (sub == 0) {
+      mh[h] = M;
+      lh[h] = Lsum;
+    }
+  }
+  __syncthreads();
+  const float* base = part_acc + (size_t)bt * n_chunks * PART_FLOATS + (size_t)slab * 1024 + 4 * lane;
+  const float2* wrow = wl + hl * n_chunks;
+  f32x4 acc[4] = {};
+  for (int k0 = wv; k0 < n_chunks; k0 += 8) {
+    const int k1 = k0 + 4;
+    const bool live0 = wl[k0].y > 0.0f;                      // head 0's l: the same for every head
+    const bool live1 = k1 < n_chunks && wl[k1].y > 0.0f;
+    f32x4 x0[4], x1[4];
+    if (live0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x0[j] = *reinterpret_cast<const f32x4*>(base + (size_t)k0 * PART_FLOATS + j * 256);
+    }
+    if (live1) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x1[j] = *reinterpret_cast<const f32x4*>(base + (size_t)k1 * PART_FLOATS + j * 256);
+    }
+    if (live0) {
+      const float wk = wrow[k0].x;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] += wk * x0[j];
+    }
+    if (live1) {
+      const float wk = wrow[k1].x;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] += wk * x1[j];
+    }
+  }
+  if (wv > 0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) red[wv - 1][j][lane] = acc[j];
+  }
+  __syncthreads();
+  if (wv == 0) {
+#pragma unroll
+    for (int u = 0; u < 3; ++u)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] += red[u][j][lane];
+    const size_t rh = (size_t)bt * H + 32 * hb + hl;
+    const float inv = 1.0f / lh[hl];
+    float* dst = z + rh * DC + 32 * cb + 4 * g;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<f32x4*>(dst + 8 * j) = acc[j] * inv;
+    if (lse != nullptr && cb == 0 && g == 0) lse[rh] = (mh[hl] + log2f(lh[hl])) * kLn2;
   }
 }
 
@@ -521,11 +620,15 @@ hipError_t launch_attn_fast(const LayerDims& L, int batch, int n_q, const void* 
                             const int64_t* seq_off, const int32_t* seq_len, const SplitPlan& plan, void* workspace,
                             float* z, float* lse, hipStream_t stream) {
   float* part_acc = (float*)workspace;
-  float* part_ml = plan.n_chunks > 1 ? part_acc + (size_t)batch * n_q * fast::H * plan.n_chunks * fast::DC : nullptr;
+  float* part_ml =
+      plan.n_chunks > 1 ? part_acc + (size_t)batch * n_q * plan.n_chunks * fast::PART_FLOATS : nullptr;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)fast::decode_attn_fast, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)sizeof(fast::Smem));
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute((const void*)fast::attn_merge_frag, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            32 * kMaxSplits * (int)sizeof(float2));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
@@ -535,7 +638,10 @@ hipError_t launch_attn_fast(const LayerDims& L, int batch, int n_q, const void* 
                      plan.n_chunks, part_acc, part_ml, z, lse);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.n_chunks == 1) return e;
-  return launch_attn_merge(batch * n_q * fast::H, plan.n_chunks, fast::DC, part_acc, part_ml, z, lse, stream);
+  const size_t merge_lds = (size_t)32 * plan.n_chunks * sizeof(float2);
+  hipLaunchKernelGGL(fast::attn_merge_frag, dim3(64, batch * n_q), dim3(256), merge_lds, stream, part_acc, part_ml,
+                     plan.n_chunks, z, lse);
+  return hipGetLastError();
 }
 
 }  // namespace mla

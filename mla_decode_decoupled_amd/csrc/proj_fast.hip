@@ -48,6 +48,20 @@ __global__ void __launch_bounds__(256) absorb_q_gemv(const bf16* __restrict__ q_
   i32x4 wv[16];
 #pragma unroll
   for (int a = 0; a < 16; ++a) wv[a] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(wp + (size_t)a * DC));
+  // while they are in flight: rotate the position part of these rows (blocks of the first half)
+  if (half == 0) {
+    for (int e = t; e < nr * (DR / 2); e += 256) {
+      const int rr = e / (DR / 2), j = e % (DR / 2);
+      const size_t r = (size_t)(r0 + rr);
+      const bf16* src = q_rope + (r * H + i) * DR;
+      double sn, co;
+      rope_sincos(base, j, DR, q_pos[r], &sn, &co);
+      const double x0 = (float)src[2 * j], x1 = (float)src[2 * j + 1];
+      bf16* dst = q_packed + (r * H + i) * ROW + DC;
+      dst[2 * j] = from_f64<bf16>(x0 * co - x1 * sn);
+      dst[2 * j + 1] = from_f64<bf16>(x0 * sn + x1 * co);
+    }
+  }
   for (int e = t; e < kRowBlock * DN; e += 256) {
     const int rr = e / DN, a = e % DN;
     qs[rr][a] = rr < nr ? (float)q_nope[((size_t)(r0 + rr) * H + i) * DN + a] : 0.0f;
@@ -81,19 +95,6 @@ __global__ void __launch_bounds__(256) absorb_q_gemv(const bf16* __restrict__ q_
 #pragma unroll
     for (int g = 0; g < 8; ++g) s += red[g][rr][t];
     q_packed[((size_t)(r0 + rr) * H + i) * ROW + half * 256 + t] = (bf16)s;
-  }
-  if (half == 0) {  // rotate the position part of these rows
-    for (int e = t; e < nr * (DR / 2); e += 256) {
-      const int rr = e / (DR / 2), j = e % (DR / 2);
-      const size_t r = (size_t)(r0 + rr);
-      const bf16* src = q_rope + (r * H + i) * DR;
-      double s, co;
-      rope_sincos(base, j, DR, q_pos[r], &s, &co);
-      const double x0 = (float)src[2 * j], x1 = (float)src[2 * j + 1];
-      bf16* dst = q_packed + (r * H + i) * ROW + DC;
-      dst[2 * j] = from_f64<bf16>(x0 * co - x1 * s);
-      dst[2 * j + 1] = from_f64<bf16>(x0 * s + x1 * co);
-    }
   }
 }
 
