@@ -141,7 +141,11 @@ mla_status mla_absorb_q(const mla_config* cfg, int32_t n_rows, const void* q_nop
     return fail(MLA_ERR_INVALID_ARG, "NULL pointer argument");
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
-  if (cfg->dtype == MLA_BF16 && mla::proj_fast_supported(L) && aligned16(w_uk))
+  if (n_rows > 65535 * 4) return fail(MLA_ERR_UNSUPPORTED, "n_rows %d exceeds %d", n_rows, 65535 * 4);
+  const bool fast = cfg->dtype == MLA_BF16 && mla::proj_fast_supported(L) && aligned16(w_uk);
+  if (fast && n_rows >= mla::kGemmMinRows && aligned16(q_nope) && aligned16(q_rope) && aligned16(q_packed))
+    e = mla::launch_absorb_q_gemm(L, n_rows, q_nope, q_rope, q_pos, w_uk, q_packed, st);
+  else if (fast)
     e = mla::launch_absorb_q_fast(L, n_rows, q_nope, q_rope, q_pos, w_uk, q_packed, st);
   else if (cfg->dtype == MLA_F32)
     e = mla::launch_absorb_q_generic<float>(L, n_rows, q_nope, q_rope, q_pos, w_uk, q_packed, st);
@@ -204,7 +208,11 @@ mla_status mla_out_proj(const mla_config* cfg, int32_t n_rows, const float* z, c
   if (!z || !w_uv || !o) return fail(MLA_ERR_INVALID_ARG, "NULL pointer argument");
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
-  if (cfg->dtype == MLA_BF16 && mla::proj_fast_supported(L) && aligned16(w_uv) && aligned16(z))
+  if (n_rows > 65535 * 4) return fail(MLA_ERR_UNSUPPORTED, "n_rows %d exceeds %d", n_rows, 65535 * 4);
+  const bool fast = cfg->dtype == MLA_BF16 && mla::proj_fast_supported(L) && aligned16(w_uv) && aligned16(z);
+  if (fast && n_rows >= mla::kGemmMinRows)
+    e = mla::launch_out_proj_gemm(L, n_rows, z, w_uv, o, st);
+  else if (fast)
     e = mla::launch_out_proj_fast(L, n_rows, z, w_uv, o, st);
   else if (cfg->dtype == MLA_F32)
     e = mla::launch_out_proj_generic<float>(L, n_rows, z, w_uv, o, st);

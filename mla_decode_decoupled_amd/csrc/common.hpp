@@ -38,11 +38,28 @@ template <> __device__ __forceinline__ bf16 from_f64<bf16>(double x) {
   return (bf16)f;
 }
 
-// theta_j = base^(-2j/d) and the rotation angle p * theta_j, both in float64 so that the
-// angle keeps full precision at positions up to 2^31 (float32 would lose ~0.016 rad at 131072).
-__device__ __forceinline__ void rope_sincos(double base, int j, int d_rope, int64_t pos, double* s, double* c) {
-  const double theta = pow(base, -2.0 * (double)j / (double)d_rope);
+// RoPE frequency theta_j = base^(-2j/d), in float64.
+__device__ __forceinline__ double rope_theta(double base, int j, int d_rope) {
+  return pow(base, -2.0 * (double)j / (double)d_rope);
+}
+
+// sin and cos of pos * theta entirely in float64 (float32 storage, where the rotated values must
+// come out correctly rounded).
+__device__ __forceinline__ void rope_sincos_f64(double theta, int64_t pos, double* s, double* c) {
   sincos((double)pos * theta, s, c);
+}
+
+// sin and cos of the angle pos * theta. The angle is formed and reduced to [-pi, pi] in float64,
+// so positions up to 2^31 keep full precision (a float32 angle would be off by up to 0.008 rad
+// at position 131072); the reduced angle is then evaluated in float32, whose error (~1e-7) is far
+// below the bf16 / fp32 rounding of the rotated values.
+__device__ __forceinline__ void rope_sincos(double theta, int64_t pos, float* s, float* c) {
+  constexpr double kTwoPiHi = 6.283185307179586;        // 2 pi rounded to float64
+  constexpr double kTwoPiLo = 2.4492935982947064e-16;   // 2 pi - kTwoPiHi
+  const double a = (double)pos * theta;
+  const double k = rint(a * 0.15915494309189535);        // a / (2 pi)
+  const double r = fma(-k, kTwoPiLo, fma(-k, kTwoPiHi, a));
+  sincosf((float)r, s, c);
 }
 
 __device__ __forceinline__ float warp_sum(float v) {

@@ -22,13 +22,16 @@ __global__ void __launch_bounds__(128) rope_append_kernel(const T* __restrict__ 
   const T* sc = c_new + tok * d_latent;
   for (int c = threadIdx.x; c < d_latent; c += blockDim.x) dst[c] = sc[c];
   const T* sk = k_new + tok * d_rope;
+  // cached keys are rotated in float64 and rounded once, so a stored row is exactly the rounding
+  // of the true rotated value
   for (int j = threadIdx.x; j < d_rope / 2; j += blockDim.x) {
     double s, co;
-    rope_sincos(base, j, d_rope, p, &s, &co);
+    rope_sincos_f64(rope_theta(base, j, d_rope), p, &s, &co);
     const double x0 = to_f32(sk[2 * j]), x1 = to_f32(sk[2 * j + 1]);
     dst[d_latent + 2 * j] = from_f64<T>(x0 * co - x1 * s);
     dst[d_latent + 2 * j + 1] = from_f64<T>(x0 * s + x1 * co);
   }
+
 }
 
 // ----------------------------------------------------------------------------- absorb
@@ -72,7 +75,7 @@ __global__ void __launch_bounds__(256) absorb_q_generic(const T* __restrict__ q_
       const size_t r = (size_t)(r0 + rr);
       const T* src = q_rope + (r * H + i) * d_rope;
       double s, co;
-      rope_sincos(base, j, d_rope, q_pos[r], &s, &co);
+      rope_sincos_f64(rope_theta(base, j, d_rope), q_pos[r], &s, &co);
       const double x0 = to_f32(src[2 * j]), x1 = to_f32(src[2 * j + 1]);
       T* dst = q_packed + (r * H + i) * row + d_latent;
       dst[2 * j] = from_f64<T>(x0 * co - x1 * s);

@@ -57,5 +57,11 @@ hipError_t launch_absorb_q_fast(const LayerDims& L, int n_rows, const void* q_no
                                 const int32_t* q_pos, const void* w_uk, void* q_packed, hipStream_t stream);
 hipError_t launch_out_proj_fast(const LayerDims& L, int n_rows, const float* z, const void* w_uv, void* o,
                                 hipStream_t stream);
+// MFMA GEMM forms of the same two projections (same shape), for many query rows at once
+constexpr int kGemmMinRows = 16;
+hipError_t launch_absorb_q_gemm(const LayerDims& L, int n_rows, const void* q_nope, const void* q_rope,
+                                const int32_t* q_pos, const void* w_uk, void* q_packed, hipStream_t stream);
+hipError_t launch_out_proj_gemm(const LayerDims& L, int n_rows, const float* z, const void* w_uv, void* o,
+                                hipStream_t stream);
 
 }  // namespace mla

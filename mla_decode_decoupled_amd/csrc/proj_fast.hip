@@ -54,12 +54,12 @@ __global__ void __launch_bounds__(256) absorb_q_gemv(const bf16* __restrict__ q_
       const int rr = e / (DR / 2), j = e % (DR / 2);
       const size_t r = (size_t)(r0 + rr);
       const bf16* src = q_rope + (r * H + i) * DR;
-      double sn, co;
-      rope_sincos(base, j, DR, q_pos[r], &sn, &co);
-      const double x0 = (float)src[2 * j], x1 = (float)src[2 * j + 1];
+      float sn, co;
+      rope_sincos(rope_theta(base, j, DR), q_pos[r], &sn, &co);
+      const float x0 = (float)src[2 * j], x1 = (float)src[2 * j + 1];
       bf16* dst = q_packed + (r * H + i) * ROW + DC;
-      dst[2 * j] = from_f64<bf16>(x0 * co - x1 * sn);
-      dst[2 * j + 1] = from_f64<bf16>(x0 * sn + x1 * co);
+      dst[2 * j] = (bf16)(x0 * co - x1 * sn);
+      dst[2 * j + 1] = (bf16)(x0 * sn + x1 * co);
     }
   }
   for (int e = t; e < kRowBlock * DN; e += 256) {

@@ -1,0 +1,308 @@
+// Query absorption and latent output projection as per-head MFMA GEMMs, for many query rows
+// at once (batched decode, chunked prefill) at the DeepSeek-V2/V3 shape (128 heads,
+// d_nope = d_v = 128, d_latent = 512, d_rope = 64, bf16 weights).
+//
+//   absorb: q~[r, i, :] = q_nope[r, i, :] W_UK[i]      ([R x 128] x [128 x 512] per head)
+//   out:    o[r, i, :]  = z[r, i, :] W_UV[i]^T         ([R x 512] x [512 x 128] per head)
+// ("从零理解 MLA", section "矩阵吸收": the content query is carried into the latent space through
+// W_UK, and the latent attention output comes back through W_UV.)
+//
+// A workgroup owns one head and 64 query rows; the weight slab of that head is read once per
+// workgroup, so weights are re-read only R / 64 times. Both contractions run on
+// v_mfma_f32_32x32x16_bf16 with fp32 accumulation. The absorbed query is rounded to bf16 once, as
+// q_packed is stored. z is float32: it enters the MFMA as two bf16 parts (hi = bf16(z),
+// lo = bf16(z - hi)), whose products with the bf16 weight are exact, so o keeps float32-level
+// accuracy before its final rounding.
+//
+// Every operand reaches LDS through direct 1 KB global->LDS loads of whole row segments (an
+// MFMA fragment loaded straight from global memory would touch 32 rows per instruction); rows
+// are XOR-swizzled by 16-byte piece so that the 16 rows read together by a fragment load fall on
+// distinct bank groups.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace mla {
+namespace gemm {
+
+constexpr int H = 128;
+constexpr int DN = 128;   // d_nope = d_v
+constexpr int DC = 512;
+constexpr int DR = 64;
+constexpr int ROW = DC + DR;
+constexpr int BM = 64;    // query rows per workgroup
+
+typedef __bf16 bf16x8e __attribute__((ext_vector_type(8)));
+typedef short i16x4e __attribute__((ext_vector_type(4)));
+typedef float f32x16e __attribute__((ext_vector_type(16)));
+
+// one 16-byte-per-lane direct global->LDS load: lane l writes LDS bytes lds_base + 16 l
+__device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gaddr), "s"(lds_base)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ f32x16e mfma(bf16x8e a, bf16x8e b, f32x16e c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)MLA_LDS(const char, p); }
+
+// B operand (16 k x 32 n) of a row-major bf16 tile T[k][n] in LDS (row stride `stride` bytes),
+// k-step s, column block nb, via two transpose reads. Lane l = 16q + L (g = l / 32) gets
+// T[16s + 8g + e][32nb + l % 32] for e = 0..7: source lane L of each 16-lane group points at
+// row 16s + 8g + 4h + L/4, columns 32nb + 16(q & 1) + 4(L & 3) .. +3, for the halves h = 0, 1.
+__device__ __forceinline__ bf16x8e tr_fragment(const unsigned char* tile, int stride, int s, int nb, int lane) {
+  const int g = lane >> 5, q = lane >> 4, L = lane & 15;
+  const int col = 32 * nb + 16 * (q & 1) + 4 * (L & 3);
+  i16x4e h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4e*)MLA_LDS(unsigned char, tile + (16 * s + 8 * g + (L >> 2)) * stride + 2 * col));
+  i16x4e h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4e*)MLA_LDS(unsigned char, tile + (16 * s + 8 * g + 4 + (L >> 2)) * stride + 2 * col));
+  const i16x4e h[2] = {h0, h1};
+  return __builtin_bit_cast(bf16x8e, h);
+}
+
+// ---------------------------------------------------------------- absorb
+// grid (ceil(R / 64), H), 256 threads. LDS: W_UK[i] (128 x 512 bf16, rows padded to 1088 B: four
+// consecutive rows then start 16 banks apart, so the 32 lanes of a transpose read hit distinct
+// banks), the 64 q_nope rows (256 B each, 16-byte pieces XOR-swizzled by row), the RoPE
+// frequencies; the output tile reuses the weight area.
+constexpr int WK_STRIDE = DC * 2 + 64;        // 1088
+constexpr int A_OFF = DN * WK_STRIDE;         // 139264
+constexpr int THETA_OFF = A_OFF + BM * DN * 2;  // 155648
+constexpr int ABSORB_LDS = THETA_OFF + (DR / 2) * 8;
+constexpr int OUT_STRIDE = DC * 2 + 16;       // staged output rows (bf16)
+static_assert(BM * OUT_STRIDE <= A_OFF, "output tile must fit the weight area");
+
+__global__ void __launch_bounds__(256) absorb_q_gemm(const bf16* __restrict__ q_nope, const bf16* __restrict__ q_rope,
+                                                     const int32_t* __restrict__ q_pos, const bf16* __restrict__ w_uk,
+                                                     bf16* __restrict__ q_packed, int n_rows, double base) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int i = blockIdx.y, r0 = blockIdx.x * BM;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
+  const int nr = min(BM, n_rows - r0);
+  double* theta = reinterpret_cast<double*>(smem + THETA_OFF);
+
+  // W_UK[i]: one 1 KB row per instruction (wave w: rows w, w+4, ..)
+  {
+    const unsigned char* wsrc = reinterpret_cast<const unsigned char*>(w_uk + (size_t)i * DN * DC) + 16 * lane;
+    const uint32_t lds0 = lds_addr(smem);
+#pragma unroll 8
+    for (int row = w; row < DN; row += 4)
+      dma16(wsrc + (size_t)row * DC * 2, __builtin_amdgcn_readfirstlane(lds0 + row * WK_STRIDE));
+  }
+  // q_nope rows: four 256 B rows per instruction; lane l fills row 4q + l/16, slot l%16 with
+  // piece (l%16) ^ (row & 15). Rows past the end repeat the last row (never stored).
+  {
+    const uint32_t lds0 = lds_addr(smem + A_OFF);
+#pragma unroll
+    for (int q = w; q < BM / 4; q += 4) {
+      const int row = 4 * q + (lane >> 4), slot = lane & 15;
+      const int rs = min(row, nr - 1);
+      const bf16* src = q_nope + ((size_t)(r0 + rs) * H + i) * DN + 8 * (slot ^ (row & 15));
+      dma16(src, __builtin_amdgcn_readfirstlane(lds0 + q * 1024));
+    }
+  }
+  if (t < DR / 2) theta[t] = rope_theta(base, t, DR);
+  __builtin_amdgcn_s_waitcnt(0);   // vmcnt 0: this wave's rows have landed
+  __syncthreads();
+
+  // position part of these rows, one thread per (row, 16 pairs): float64-reduced angle, float32
+  // rotation; the 64 bytes of a row half are loaded and stored as four 16-byte pieces
+  if (t < 2 * nr) {
+    const int rr = t >> 1, hj = t & 1;
+    const size_t r = (size_t)(r0 + rr);
+    const int64_t pos = q_pos[r];
+    const i32x4* src = reinterpret_cast<const i32x4*>(q_rope + (r * H + i) * DR + 32 * hj);
+    i32x4 x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x[u] = src[u];
+    i32x4 y[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {   // one pair (2j, 2j+1) per 32-bit word
+        const int j = 16 * hj + 4 * u + e;
+        float sn, co;
+        rope_sincos(theta[j], pos, &sn, &co);
+        const uint32_t wd = (uint32_t)x[u][e];
+        const float x0 = __uint_as_float(wd << 16), x1 = __uint_as_float(wd & 0xFFFF0000u);
+        const bf16 y0 = (bf16)(x0 * co - x1 * sn), y1 = (bf16)(x0 * sn + x1 * co);
+        y[u][e] = (int)((uint32_t)__builtin_bit_cast(unsigned short, y0) |
+                        ((uint32_t)__builtin_bit_cast(unsigned short, y1) << 16));
+      }
+    i32x4* dst = reinterpret_cast<i32x4*>(q_packed + (r * H + i) * ROW + DC + 32 * hj);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) dst[u] = y[u];
+  }
+
+  // wave w: output columns 128w .. 128w + 127 (4 blocks of 32) x both row blocks
+  f32x16e acc[2][4];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) acc[rb][nb] = f32x16e{};
+#pragma unroll 2
+  for (int s = 0; s < DN / 16; ++s) {
+    bf16x8e a[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int m = 32 * rb + l32;
+      a[rb] = *reinterpret_cast<const bf16x8e*>(smem + A_OFF + m * (DN * 2) + 16 * ((2 * s + g) ^ (m & 15)));
+    }
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const bf16x8e b = tr_fragment(smem, WK_STRIDE, s, 4 * w + nb, lane);
+      acc[0][nb] = mfma(a[0], b, acc[0][nb]);
+      acc[1][nb] = mfma(a[1], b, acc[1][nb]);
+    }
+  }
+  __syncthreads();   // every wave is done with W: the area takes the output tile
+
+  // D layout: lane holds column 32nb' + l32 (nb' = 4w + nb) of rows 32rb + 8j + 4g + e
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = 32 * rb + 8 * j + 4 * g + e, col = 128 * w + 32 * nb + l32;
+          *reinterpret_cast<bf16*>(smem + row * OUT_STRIDE + 2 * col) = (bf16)acc[rb][nb][4 * j + e];
+        }
+  __syncthreads();
+  // whole 1 KB rows out: 64 rows x 64 pieces of 16 bytes
+  for (int p = t; p < nr * (DC / 8); p += 256) {
+    const int row = p / (DC / 8), ch = p % (DC / 8);
+    *reinterpret_cast<i32x4*>(q_packed + ((size_t)(r0 + row) * H + i) * ROW + ch * 8) =
+        *reinterpret_cast<const i32x4*>(smem + row * OUT_STRIDE + ch * 16);
+  }
+}
+
+// ---------------------------------------------------------------- output projection
+// grid (ceil(R / 64), H), 256 threads. The latent dimension is taken in two halves of 256; per
+// half LDS holds W_UV[i][:, half] (128 rows of 512 B) and the 64 z rows' half (64 rows of 1 KB
+// float32, then split in place into bf16 hi / lo parts), both XOR-swizzled by 16-byte piece. Wave w computes outputs v = 32w .. 32w + 31 for
+// all 64 rows.
+constexpr int KH = DC / 2;                    // latent columns per half
+constexpr int WV_ROW = KH * 2;                // 512 B
+constexpr int Z_ROW = KH * 4;                 // 1024 B
+constexpr int Z_OFF = DN * WV_ROW;            // 65536
+constexpr int OUTP_LDS = Z_OFF + BM * Z_ROW;  // 131072
+
+__global__ void __launch_bounds__(256) out_proj_gemm(const float* __restrict__ z, const bf16* __restrict__ w_uv,
+                                                     bf16* __restrict__ o, int n_rows) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int i = blockIdx.y, r0 = blockIdx.x * BM;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
+  const int nr = min(BM, n_rows - r0);
+  const uint32_t lds_w = lds_addr(smem), lds_z = lds_addr(smem + Z_OFF);
+
+  f32x16e acc[2] = {f32x16e{}, f32x16e{}};
+  for (int kh = 0; kh < 2; ++kh) {
+    if (kh > 0) __syncthreads();   // the previous half is no longer read
+    // W_UV rows: two 512 B rows per instruction, lane l -> row 2q + l/32, slot (l%32) holds
+    // piece (l%32) ^ (row & 15)
+#pragma unroll 4
+    for (int q = w; q < DN / 2; q += 4) {
+      const int row = 2 * q + (lane >> 5), slot = lane & 31;
+      const bf16* src = w_uv + ((size_t)i * DN + row) * DC + kh * KH + 8 * (slot ^ (row & 15));
+      dma16(src, __builtin_amdgcn_readfirstlane(lds_w + q * 1024));
+    }
+    // z rows: one 1 KB row half per instruction, slot l holds piece l ^ (row & 15); rows past
+    // the end repeat the last row (their outputs are not written)
+#pragma unroll 4
+    for (int row = w; row < BM; row += 4) {
+      const int rs = min(row, nr - 1);
+      const float* src = z + ((size_t)(r0 + rs) * H + i) * DC + kh * KH + 4 * (lane ^ (row & 15));
+      dma16(src, __builtin_amdgcn_readfirstlane(lds_z + row * Z_ROW));
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // vmcnt 0: this wave's rows have landed
+    __syncthreads();
+    // each 16-byte piece of 4 floats becomes [hi0..hi3 | lo0..lo3] in bf16, in place (a thread
+    // reads and rewrites only its own pieces): hi = bf16(z), lo = bf16(z - hi)
+    for (int pc = t; pc < BM * (Z_ROW / 16); pc += 256) {
+      unsigned char* at = smem + Z_OFF + pc * 16;
+      const f32x4 zv = *reinterpret_cast<const f32x4*>(at);
+      uint32_t hw[2], lw[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const bf16 h0 = (bf16)zv[2 * e], h1 = (bf16)zv[2 * e + 1];
+        const bf16 l0 = (bf16)(zv[2 * e] - (float)h0), l1 = (bf16)(zv[2 * e + 1] - (float)h1);
+        hw[e] = (uint32_t)__builtin_bit_cast(unsigned short, h0) | ((uint32_t)__builtin_bit_cast(unsigned short, h1) << 16);
+        lw[e] = (uint32_t)__builtin_bit_cast(unsigned short, l0) | ((uint32_t)__builtin_bit_cast(unsigned short, l1) << 16);
+      }
+      *reinterpret_cast<i32x4*>(at) = i32x4{(int)hw[0], (int)hw[1], (int)lw[0], (int)lw[1]};
+    }
+    __syncthreads();
+
+    const int v = 32 * w + l32;
+#pragma unroll 2
+    for (int s = 0; s < KH / 16; ++s) {
+      // B: W_UV[i][v][16s + 8g .. +7] = logical piece 2s + g of row v
+      const bf16x8e b = *reinterpret_cast<const bf16x8e*>(smem + v * WV_ROW + 16 * ((2 * s + g) ^ (v & 15)));
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        // A: z[m][16s + 8g .. +7] = logical float pieces 2(2s + g) and 2(2s + g) + 1 of row m
+        const int m = 32 * rb + l32;
+        const int p0 = 2 * (2 * s + g);
+        const unsigned char* q0 = smem + Z_OFF + m * Z_ROW + 16 * (p0 ^ (m & 15));
+        const unsigned char* q1 = smem + Z_OFF + m * Z_ROW + 16 * ((p0 + 1) ^ (m & 15));
+        typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
+        const i32x2 h0 = *reinterpret_cast<const i32x2*>(q0), h1 = *reinterpret_cast<const i32x2*>(q1);
+        const i32x2 l0 = *reinterpret_cast<const i32x2*>(q0 + 8), l1 = *reinterpret_cast<const i32x2*>(q1 + 8);
+        const i32x2 hh[2] = {h0, h1}, ll[2] = {l0, l1};
+        acc[rb] = mfma(__builtin_bit_cast(bf16x8e, hh), b, acc[rb]);
+        acc[rb] = mfma(__builtin_bit_cast(bf16x8e, ll), b, acc[rb]);
+      }
+    }
+  }
+  // D layout: lane holds output v = 32w + l32 of rows 32rb + 8j + 4g + e
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 32 * rb + 8 * j + 4 * g + e;
+        if (row < nr) o[((size_t)(r0 + row) * H + i) * DN + 32 * w + l32] = (bf16)acc[rb][4 * j + e];
+      }
+}
+
+}  // namespace gemm
+
+hipError_t launch_absorb_q_gemm(const LayerDims& L, int n_rows, const void* q_nope, const void* q_rope,
+                                const int32_t* q_pos, const void* w_uk, void* q_packed, hipStream_t stream) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)gemm::absorb_q_gemm, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       gemm::ABSORB_LDS);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const dim3 grid((n_rows + gemm::BM - 1) / gemm::BM, gemm::H);   // row tiles of one head run together
+  hipLaunchKernelGGL(gemm::absorb_q_gemm, grid, dim3(256), gemm::ABSORB_LDS, stream, (const bf16*)q_nope,
+                     (const bf16*)q_rope, q_pos, (const bf16*)w_uk, (bf16*)q_packed, n_rows, L.rope_base);
+  return hipGetLastError();
+}
+
+hipError_t launch_out_proj_gemm(const LayerDims& L, int n_rows, const float* z, const void* w_uv, void* o,
+                                hipStream_t stream) {
+  (void)L;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)gemm::out_proj_gemm, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       gemm::OUTP_LDS);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const dim3 grid((n_rows + gemm::BM - 1) / gemm::BM, gemm::H);   // row tiles of one head run together
+  hipLaunchKernelGGL(gemm::out_proj_gemm, grid, dim3(256), gemm::OUTP_LDS, stream, z, (const bf16*)w_uv, (bf16*)o,
+                     n_rows);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -14,6 +14,7 @@ import pytest
 
 torch = pytest.importorskip("torch")
 
+import mla_decode_decoupled_amd as mla  # noqa: E402
 import oracle as O  # noqa: E402
 from mla_workloads import CONFIGS, MLAConfig  # noqa: E402
 from mla_workloads import generate as G  # noqa: E402
@@ -122,15 +123,25 @@ def test_ragged_batch_sampled():
         _check_cache(run, hi, b)
         _check_qpacked(run, hi, b)
         _check_outputs(run, hi, b, heads=heads)
-    # a sequence computed alone (same chunking) equals the same sequence inside the batch, bit for bit
+    # a sequence attended alone (same chunking, same packed queries) equals the same sequence
+    # inside the batch, bit for bit: no other sequence leaks into its result. (The projections
+    # take a different path for 1 row than for 64, so the packed queries are passed over.)
     b = picks[-1]
     alone = host_inputs(MLAConfig(**{**cfg.__dict__, "batch": 1}), lens=[int(lens[b])])
     alone.c, alone.k_pre = [hi.c[b]], [hi.k_pre[b]]
     alone.q_nope, alone.q_rope = hi.q_nope[b:b + 1], hi.q_rope[b:b + 1]
     run1 = run_pipeline(alone, n_splits=4, max_len=int(lens.max()))
-    assert np.array_equal(np32(run1.z[0]), np32(run.z[b]))
-    assert np.array_equal(np32(run1.lse[0]), np32(run.lse[b]))
-    assert np.array_equal(np32(run1.o[0]), np32(run.o[b]))
+    lc = lib_config(cfg)
+    max_len = int(lens.max())
+    z1 = torch.empty_like(run1.z)
+    lse1 = torch.empty_like(run1.lse)
+    ws = torch.empty(max(mla.mla_decode_attn_workspace_size(lc, 1, 1, max_len, 4), 1), dtype=torch.uint8,
+                     device="cuda")
+    mla.mla_decode_attn(lc, run.q_packed[b:b + 1].contiguous(), run1.cache, run1.seq_off, run1.seq_len, max_len,
+                        z1, lse1, n_splits=4, workspace=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(np32(z1[0]), np32(run.z[b]))
+    assert np.array_equal(np32(lse1[0]), np32(run.lse[b]))
 
 
 @pytest.mark.slow
@@ -153,6 +164,22 @@ def test_chunked_prefill_sampled():
     _check_qpacked(run, hi, 1, rows=[0, 1, 1000, 2047])
     _check_outputs(run, hi, 1, heads=[0, 127], rows=[0, 1, 1000, 2047])
     _check_outputs(run, hi, 0, heads=[64], rows=[2047, 5])
+
+
+@pytest.mark.parametrize("n_q", [15, 16, 100])
+def test_projection_row_counts(n_q):
+    """DeepSeek shape with a few query rows: 15 rows take the matrix-vector projections, 16 and
+    100 the MFMA GEMMs (100 leaves a partial 64-row tile). Every row and head of q_packed and o,
+    and z of every row for a subset of heads, against the oracle."""
+    cfg = MLAConfig(**{**CONFIGS[1].__dict__, "cid": 210 + n_q, "n_q": n_q, "fixed_len": n_q + 200})
+    hi = host_inputs(cfg)
+    run = run_pipeline(hi)
+    _check_qpacked(run, hi, 0)
+    _check_outputs(run, hi, 0, heads=[0, 31, 64, 127])
+    # o for every head: the projection of the GPU's own z (isolates the output projection)
+    z = np32(run.z[0])
+    o_ref = O.latent_out_projection(z, hi.w_uv)
+    assert_close(np32(run.o[0]), o_ref, cfg.dtype, "o from GPU z")
 
 
 # ------------------------------------------------------------------------ edge cases
