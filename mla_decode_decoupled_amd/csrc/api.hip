@@ -77,6 +77,8 @@ mla_status plan_splits(int32_t max_seq_len, int32_t n_splits, int64_t rows, bool
   if (n > max_seq_len) n = max_seq_len;
   plan->chunk_len = (int)((max_seq_len + n - 1) / n);
   plan->n_chunks = (max_seq_len + plan->chunk_len - 1) / plan->chunk_len;
+  plan->fast_mode = plan->fast_grid_x = plan->fast_slots = 0;
+  if (fast) mla::attn_fast_plan((int)rows, n_splits, plan);
   return MLA_OK;
 }
 
@@ -86,10 +88,14 @@ bool use_fast_attn(const mla_config* cfg, const mla::LayerDims& L) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-size_t attn_workspace_bytes(const mla::LayerDims& L, int batch, int n_q, const mla::SplitPlan& plan) {
-  if (plan.n_chunks <= 1) return 0;
-  const size_t slots = (size_t)batch * n_q * L.n_heads * plan.n_chunks;
-  return slots * ((size_t)L.d_latent + 2) * sizeof(float);
+// Workspace: the generic kernels' partials ([row, head, chunk] x (d_latent + 2) floats) or, for the
+// MFMA path, its partial slots; a shape that takes the MFMA path may still fall back to the
+// generic kernels (unaligned pointers), so it is sized for both.
+size_t attn_workspace_bytes(const mla::LayerDims& L, int batch, int n_q, const mla::SplitPlan& plan, bool fast) {
+  size_t generic = 0;
+  if (plan.n_chunks > 1) generic = (size_t)batch * n_q * L.n_heads * plan.n_chunks * ((size_t)L.d_latent + 2) * sizeof(float);
+  const size_t fastb = fast ? mla::attn_fast_workspace_bytes(plan, batch * n_q) : 0;
+  return generic > fastb ? generic : fastb;
 }
 
 }  // namespace
@@ -161,7 +167,7 @@ size_t mla_decode_attn_workspace_size(const mla_config* cfg, int32_t batch, int3
   if (batch <= 0 || n_q <= 0 || max_seq_len < n_q) return 0;
   mla::SplitPlan plan;
   if (plan_splits(max_seq_len, n_splits, (int64_t)batch * n_q, use_fast_attn(cfg, L), &plan) != MLA_OK) return 0;
-  return attn_workspace_bytes(L, batch, n_q, plan);
+  return attn_workspace_bytes(L, batch, n_q, plan, use_fast_attn(cfg, L));
 }
 
 mla_status mla_decode_attn(const mla_config* cfg, int32_t batch, int32_t n_q, const void* q_packed, const void* cache,
@@ -180,7 +186,7 @@ mla_status mla_decode_attn(const mla_config* cfg, int32_t batch, int32_t n_q, co
   mla::SplitPlan plan;
   s = plan_splits(max_seq_len, n_splits, (int64_t)batch * n_q, fast, &plan);
   if (s != MLA_OK) return s;
-  const size_t need = attn_workspace_bytes(L, batch, n_q, plan);
+  const size_t need = attn_workspace_bytes(L, batch, n_q, plan, fast);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))
     return fail(MLA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu%s", need, workspace_bytes,
                 workspace ? "" : " (NULL)");

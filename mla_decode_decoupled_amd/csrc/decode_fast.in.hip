@@ -137,12 +137,76 @@ __device__ __forceinline__ int frag_offset(int head, int col) {
   return (((hb * 16 + cb) * 4 + j) * 64 + lane) * 4 + e;
 }
 
+// ---- How the keys are cut into chunks (one workgroup each).
+// FIXED: the caller's n_splits, chunk k of row bt covers keys [k L, (k + 1) L) with
+//   L = ceil(max_seq_len / n_splits); partial slot bt * n_splits + k.
+// BALANCED (batch * n_q <= kBalanceRows): one grid of kBalanceGrid workgroups over the whole batch.
+//   Every row's visible keys are cut into chunks of Q tiles, Q = max(kMinTiles,
+//   ceil(T / (kBalanceGrid - rows))) for T tiles in all, so no chunk is longer than the share of
+//   one workgroup, whatever the mix of lengths; the chunks of all rows are numbered in row order
+//   and chunk number = workgroup = partial slot.
+// PER_ROW: one chunk per row (many rows already fill the chip).
+enum ChunkMode { FIXED = 0, BALANCED = 1, PER_ROW = 2 };
+constexpr int kBalanceGrid = 256;
+constexpr int kBalanceRows = 128;
+constexpr int kMinTiles = 4;
+
+struct Chunk {
+  int bt, k, nck, slot, j0, j1;
+};
+
+// BALANCED plan, computed by every lane of wave 0 for all rows (rows <= 128: two per lane): the
+// chunk of `target` (a workgroup index), or of row `target_row` when target < 0. Returns false
+// when `target` lies past the last chunk.
+__device__ bool balanced_chunk(const int32_t* __restrict__ seq_len, int n_q, int rows, int target, int target_row,
+                               Chunk* out) {
+  const int lane = threadIdx.x & 63;
+  int nvis[2], tiles[2];
+  int64_t tsum = 0;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int r = lane + 64 * u;
+    nvis[u] = r < rows ? seq_len[r / n_q] - n_q + (r % n_q) + 1 : 0;
+    tiles[u] = (nvis[u] + TILE - 1) / TILE;
+    tsum += tiles[u];
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) tsum += __shfl_xor(tsum, o, 64);
+  const int64_t share = (tsum + (kBalanceGrid - rows) - 1) / (kBalanceGrid - rows);
+  const int q = (int)max((int64_t)kMinTiles, share);
+  bool found = false;
+  int carry = 0;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int nck = (tiles[u] + q - 1) / q;
+    int incl = nck;   // inclusive prefix over the 64 lanes of this round
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
+    }
+    const int first = carry + incl - nck;
+    const int r = lane + 64 * u;
+    const bool mine = r < rows && (target >= 0 ? (target >= first && target < first + nck) : r == target_row);
+    const uint64_t hit = __ballot(mine);
+    if (hit) {
+      const int src = __ffsll((unsigned long long)hit) - 1;
+      const int f = __shfl(first, src, 64), n = __shfl(nck, src, 64), nv = __shfl(nvis[u], src, 64);
+      const int k = target >= 0 ? target - f : 0;
+      *out = Chunk{src + 64 * u, k, n, target >= 0 ? target : f, k * q * TILE, min((k + 1) * q * TILE, nv)};
+      found = true;
+    }
+    carry += __shfl(incl, 63, 64);
+  }
+  return found;
+}
+
 // Exact fallback for one (query row, chunk): per head, a float32 online softmax that rescales
 // its running sum and latent accumulator at every block of 256 keys. Same outputs as the MFMA
 // path (final z/lse with one chunk, otherwise a partial in log2 units). Kept out of line so the
 // MFMA loop's register allocation does not see it.
 __device__ __noinline__ void exact_chunk(const bf16* __restrict__ q_packed, const unsigned char* __restrict__ kv,
-                                         size_t rh0, int j0, int j1, float scale_log2, int n_chunks, int k,
+                                         size_t rh0, int j0, int j1, float scale_log2, int n_chunks, int slot,
                                          float* __restrict__ part_acc, float* __restrict__ part_ml,
                                          float* __restrict__ z, float* __restrict__ lse, unsigned char* smem) {
   float* qs = reinterpret_cast<float*>(smem);   // [ROW]
@@ -192,44 +256,62 @@ __device__ __noinline__ void exact_chunk(const bf16* __restrict__ q_packed, cons
       z[rh * DC + tid + 256] = acc1 / l;
       if (lse != nullptr && tid == 0) lse[rh] = (m + log2f(l)) * kLn2;
     } else {
-      const size_t slot = rh * n_chunks + k;
-      float* blk = part_acc + ((rh0 / H) * n_chunks + k) * (size_t)PART_FLOATS;
+      float* blk = part_acc + (size_t)slot * PART_FLOATS;
       blk[frag_offset(h, tid)] = acc0;
       blk[frag_offset(h, tid + 256)] = acc1;
       if (tid == 0) {
-        part_ml[slot * 2 + 0] = m;
-        part_ml[slot * 2 + 1] = l;
+        part_ml[((size_t)slot * H + h) * 2 + 0] = m;
+        part_ml[((size_t)slot * H + h) * 2 + 1] = l;
       }
     }
     __syncthreads();
   }
 }
 
-// grid (n_chunks, batch * n_q), 256 threads, sizeof(Smem) dynamic LDS
+// grid: FIXED (n_splits, rows), BALANCED (kBalanceGrid), PER_ROW (rows); 256 threads,
+// sizeof(Smem) dynamic LDS
 __global__ void __launch_bounds__(256)
     decode_attn_fast(const bf16* __restrict__ q_packed, const bf16* __restrict__ cache,
-                     const int64_t* __restrict__ seq_off, const int32_t* __restrict__ seq_len, int n_q, float scale_log2,
-                     int chunk_len, int n_chunks, float* __restrict__ part_acc, float* __restrict__ part_ml,
-                     float* __restrict__ z, float* __restrict__ lse) {
+                     const int64_t* __restrict__ seq_off, const int32_t* __restrict__ seq_len, int n_q, int rows,
+                     float scale_log2, int mode, int n_splits, int chunk_len, float* __restrict__ part_acc,
+                     float* __restrict__ part_ml, int2* __restrict__ row_chunks, float* __restrict__ z,
+                     float* __restrict__ lse) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
-
-  const int k = blockIdx.x, bt = blockIdx.y;
-  const int b = bt / n_q, t = bt % n_q;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 5, l32 = lane & 31;
-  const int n_vis = seq_len[b] - n_q + t + 1;
-  const int j0 = k * chunk_len;
-  const int j1 = min(j0 + chunk_len, n_vis);
-  const size_t rh0 = (size_t)bt * H;
 
-  if (j0 >= j1) {  // empty chunk (only possible with several chunks): contributes nothing
-    if (threadIdx.x < H) {
-      part_ml[((rh0 + threadIdx.x) * n_chunks + k) * 2 + 0] = -INFINITY;
-      part_ml[((rh0 + threadIdx.x) * n_chunks + k) * 2 + 1] = 0.0f;
+  // ---- this workgroup's chunk
+  Chunk ch;
+  if (mode == FIXED) {
+    const int bt = blockIdx.y, k = blockIdx.x;
+    const int n_vis = seq_len[bt / n_q] - n_q + (bt % n_q) + 1;
+    ch = Chunk{bt, k, (n_vis + chunk_len - 1) / chunk_len, bt * n_splits + k, k * chunk_len,
+               min((k + 1) * chunk_len, n_vis)};
+    if (ch.j0 >= ch.j1) return;   // past the row's last chunk: nothing to do, nothing written
+  } else if (mode == PER_ROW) {
+    const int bt = blockIdx.x;
+    ch = Chunk{bt, 0, 1, 0, 0, seq_len[bt / n_q] - n_q + (bt % n_q) + 1};
+  } else {
+    Chunk* shared_ch = reinterpret_cast<Chunk*>(smem_raw + FLAGS_OFF + 64);
+    if (w == 0) {
+      Chunk c;
+      const bool found = balanced_chunk(seq_len, n_q, rows, (int)blockIdx.x, -1, &c);
+      if (lane == 0) {
+        if (!found) c.nck = 0;
+        *shared_ch = c;
+      }
     }
-    return;
+    __syncthreads();
+    ch = *shared_ch;
+    if (ch.nck == 0) return;   // the plan has fewer chunks than the grid
   }
+  const int bt = ch.bt, j0 = ch.j0, j1 = ch.j1, n_chunks = ch.nck;
+  const int b = bt / n_q;
+  const size_t rh0 = (size_t)bt * H;
+  // every row's first chunk publishes where the row's partials are (first slot, count; count 1
+  // means the row is written directly), so the merge never reads an entry of an earlier call
+  if (row_chunks != nullptr && ch.k == 0 && threadIdx.x == 0) row_chunks[bt] = make_int2(ch.slot, n_chunks);
   const int n_tiles = (j1 - j0 + TILE - 1) / TILE;
   const unsigned char* kv = reinterpret_cast<const unsigned char*>(cache + seq_off[b] * (int64_t)ROW);
   // always-valid DMA source for "no tile left": this query row's packed queries (H * ROW_BYTES bytes)
@@ -460,7 +542,7 @@ __global__ void __launch_bounds__(256)
   const bool overflowed = (flags[0] | flags[1] | flags[2] | flags[3]) != 0;
   if (overflowed) {
     __syncthreads();
-    exact_chunk(q_packed, kv, rh0, j0, j1, scale_log2, n_chunks, k, part_acc, part_ml, z, lse, smem_raw);
+    exact_chunk(q_packed, kv, rh0, j0, j1, scale_log2, n_chunks, ch.slot, part_acc, part_ml, z, lse, smem_raw);
     return;
   }
   // the accumulator is read by VALU below: 20 wait states after the last MFMA
@@ -474,7 +556,7 @@ __global__ void __launch_bounds__(256)
     if (n_chunks == 1) {
       if (lse != nullptr) lse[rh0 + qhead] = (m_ref + log2f(l_run)) * kLn2;
     } else {
-      float* ml = part_ml + ((rh0 + qhead) * n_chunks + k) * 2;
+      float* ml = part_ml + ((size_t)ch.slot * H + qhead) * 2;
       ml[0] = m_ref;
       ml[1] = l_run;
     }
@@ -483,7 +565,7 @@ __global__ void __launch_bounds__(256)
                             &oc8, &oc9, &oc10, &oc11, &oc12, &oc13, &oc14, &oc15};
   if (n_chunks > 1) {
     // ---- partial: 64 stores of 1 KB per wave, straight from the accumulators (layout above)
-    float* blk = part_acc + ((size_t)bt * n_chunks + k) * PART_FLOATS + (size_t)w * (PART_FLOATS / 4) + 4 * lane;
+    float* blk = part_acc + (size_t)ch.slot * PART_FLOATS + (size_t)w * (PART_FLOATS / 4) + 4 * lane;
 #pragma unroll
     for (int cb = 0; cb < 16; ++cb)
 #pragma unroll
@@ -522,91 +604,88 @@ __global__ void __launch_bounds__(256)
 
 // Log-sum-exp merge of the split-K partials of the fast path (layout above). One workgroup per
 // (query row, head block hb, col block cb): 32 heads x 32 latent columns, each lane owning one
-// head and 16 columns. With M = max_k m_k over live chunks (m in log2 units),
-// z = sum_k 2^(m_k - M) O_k / sum_k 2^(m_k - M) l_k. The (m, l) pairs of the 32 heads are first
-// turned into weights in LDS, so the stream over the partials has no global-memory dependency:
-// the 4 waves take the chunks round-robin, two chunks (8 coalesced 1 KB loads) per step, and
-// meet in LDS. A chunk with l = 0 saw no key (it is empty for every head) and is not read.
+// head and 16 columns. The row's chunks are the slots base .. base + nck - 1 (every one saw at
+// least one key), as published by the row's first chunk. With M = max_k m_k (m in log2 units),
+// z = sum_k 2^(m_k - M) O_k / sum_k 2^(m_k - M) l_k. The 4 waves take the chunks round-robin,
+// two chunks (8 coalesced 1 KB loads) per step, each lane weighting its own head; the wave sums
+// meet in LDS. Rows computed as a single chunk were written directly and are skipped.
 __global__ void __launch_bounds__(256) attn_merge_frag(const float* __restrict__ part_acc,
-                                                       const float* __restrict__ part_ml, int n_chunks,
+                                                       const float* __restrict__ part_ml,
+                                                       const int2* __restrict__ row_chunks,
                                                        float* __restrict__ z, float* __restrict__ lse) {
-  extern __shared__ __attribute__((aligned(16))) float2 wl[];   // [32 heads][n_chunks]: (weight, l)
   __shared__ f32x4 red[3][4][64];
-  __shared__ float mh[32], lh[32];
+  __shared__ float lred[3][64];
   const int bt = blockIdx.y, slab = blockIdx.x;   // slab = hb * 16 + cb
   const int hb = slab >> 4, cb = slab & 15;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int g = lane >> 5, hl = lane & 31;
-  const float2* ml = reinterpret_cast<const float2*>(part_ml) + ((size_t)bt * H + 32 * hb) * n_chunks;
-  for (int e = tid; e < 32 * n_chunks; e += 256) wl[e] = ml[e];
-  __syncthreads();
-  {  // per head: M over live chunks (8 lanes per head), then the weights and their l-weighted sum
-    const int h = tid >> 3, sub = tid & 7;
-    float M = -INFINITY;
-    for (int kk = sub; kk < n_chunks; kk += 8) {
-      const float2 v = wl[h * n_chunks + kk];
-      if (v.y > 0.0f) M = fmaxf(M, v.x);
+  const int2 rc = row_chunks[bt];
+  if (rc.y <= 1) return;
+  const int base = rc.x, nck = rc.y;
+  const size_t head = (size_t)32 * hb + hl;
+  const float2* ml = reinterpret_cast<const float2*>(part_ml) + (size_t)base * H + head;   // stride H
+  const float* src = part_acc + (size_t)base * PART_FLOATS + (size_t)slab * 1024 + 4 * lane;
+  // M: each wave scans every fourth chunk, eight loads in flight per lane, then the waves agree
+  __shared__ float mred[4][64];
+  float M = -INFINITY;
+  for (int k0 = wv; k0 < nck; k0 += 32) {
+    float mv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int kk = k0 + 4 * u;
+      mv[u] = kk < nck ? ml[(size_t)kk * H].x : -INFINITY;
     }
 #pragma unroll
-    for (int o = 1; o < 8; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-    float Lsum = 0.0f;
-    for (int kk = sub; kk < n_chunks; kk += 8) {
-      float2 v = wl[h * n_chunks + kk];
-      v.x = v.y > 0.0f ? exp2f(v.x - M) : 0.0f;
-      Lsum = fmaf(v.x, v.y, Lsum);
-      wl[h * n_chunks + kk] = v;
-    }
-#pragma unroll
-    for (int o = 1; o < 8; o <<= 1) Lsum += __shfl_xor(Lsum, o, 64);
-    if (sub == 0) {
-      mh[h] = M;
-      lh[h] = Lsum;
-    }
+    for (int u = 0; u < 8; ++u) M = fmaxf(M, mv[u]);
   }
+  mred[wv][lane] = M;
   __syncthreads();
-  const float* base = part_acc + (size_t)bt * n_chunks * PART_FLOATS + (size_t)slab * 1024 + 4 * lane;
-  const float2* wrow = wl + hl * n_chunks;
+  M = fmaxf(fmaxf(mred[0][lane], mred[1][lane]), fmaxf(mred[2][lane], mred[3][lane]));
   f32x4 acc[4] = {};
-  for (int k0 = wv; k0 < n_chunks; k0 += 8) {
+  float Lsum = 0.0f;
+  for (int k0 = wv; k0 < nck; k0 += 8) {
     const int k1 = k0 + 4;
-    const bool live0 = wl[k0].y > 0.0f;                      // head 0's l: the same for every head
-    const bool live1 = k1 < n_chunks && wl[k1].y > 0.0f;
+    const bool two = k1 < nck;
     f32x4 x0[4], x1[4];
-    if (live0) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) x0[j] = *reinterpret_cast<const f32x4*>(base + (size_t)k0 * PART_FLOATS + j * 256);
+    for (int j = 0; j < 4; ++j) x0[j] = *reinterpret_cast<const f32x4*>(src + (size_t)k0 * PART_FLOATS + j * 256);
+    if (two) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x1[j] = *reinterpret_cast<const f32x4*>(src + (size_t)k1 * PART_FLOATS + j * 256);
     }
-    if (live1) {
+    const float2 v0 = ml[(size_t)k0 * H];
+    const float w0 = exp2f(v0.x - M);
+    Lsum = fmaf(w0, v0.y, Lsum);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) x1[j] = *reinterpret_cast<const f32x4*>(base + (size_t)k1 * PART_FLOATS + j * 256);
-    }
-    if (live0) {
-      const float wk = wrow[k0].x;
+    for (int j = 0; j < 4; ++j) acc[j] += w0 * x0[j];
+    if (two) {
+      const float2 v1 = ml[(size_t)k1 * H];
+      const float w1 = exp2f(v1.x - M);
+      Lsum = fmaf(w1, v1.y, Lsum);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] += wk * x0[j];
-    }
-    if (live1) {
-      const float wk = wrow[k1].x;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] += wk * x1[j];
+      for (int j = 0; j < 4; ++j) acc[j] += w1 * x1[j];
     }
   }
   if (wv > 0) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) red[wv - 1][j][lane] = acc[j];
+    lred[wv - 1][lane] = Lsum;
   }
   __syncthreads();
   if (wv == 0) {
 #pragma unroll
-    for (int u = 0; u < 3; ++u)
+    for (int u = 0; u < 3; ++u) {
+      Lsum += lred[u][lane];
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[j] += red[u][j][lane];
-    const size_t rh = (size_t)bt * H + 32 * hb + hl;
-    const float inv = 1.0f / lh[hl];
+    }
+    // the two lane halves of a head summed the same chunks: Lsum agrees between them
+    const size_t rh = (size_t)bt * H + head;
+    const float inv = 1.0f / Lsum;
     float* dst = z + rh * DC + 32 * cb + 4 * g;
 #pragma unroll
     for (int j = 0; j < 4; ++j) *reinterpret_cast<f32x4*>(dst + 8 * j) = acc[j] * inv;
-    if (lse != nullptr && cb == 0 && g == 0) lse[rh] = (mh[hl] + log2f(lh[hl])) * kLn2;
+    if (lse != nullptr && cb == 0 && g == 0) lse[rh] = (M + log2f(Lsum)) * kLn2;
   }
 }
 
@@ -616,31 +695,50 @@ bool attn_fast_supported(const LayerDims& L) {
   return L.n_heads == fast::H && L.d_latent == fast::DC && L.d_rope == fast::DR;
 }
 
+// workspace of the MFMA path: partial accumulators, (m, l) pairs, one (first slot, count) per row
+size_t attn_fast_workspace_bytes(const SplitPlan& plan, int rows) {
+  if (plan.fast_slots == 0) return 0;
+  return (size_t)plan.fast_slots * ((size_t)fast::PART_FLOATS + 2 * fast::H) * sizeof(float) + (size_t)rows * sizeof(int2);
+}
+
+void attn_fast_plan(int rows, int n_splits, SplitPlan* plan) {
+  if (n_splits > 0) {
+    plan->fast_mode = fast::FIXED;
+    plan->fast_grid_x = plan->n_chunks;
+    plan->fast_slots = plan->n_chunks > 1 ? rows * plan->n_chunks : 0;
+  } else if (rows <= fast::kBalanceRows) {
+    plan->fast_mode = fast::BALANCED;
+    plan->fast_grid_x = fast::kBalanceGrid;
+    plan->fast_slots = fast::kBalanceGrid;
+  } else {
+    plan->fast_mode = fast::PER_ROW;
+    plan->fast_grid_x = rows;
+    plan->fast_slots = 0;
+  }
+}
+
 hipError_t launch_attn_fast(const LayerDims& L, int batch, int n_q, const void* q_packed, const void* cache,
                             const int64_t* seq_off, const int32_t* seq_len, const SplitPlan& plan, void* workspace,
                             float* z, float* lse, hipStream_t stream) {
+  const int rows = batch * n_q;
   float* part_acc = (float*)workspace;
-  float* part_ml =
-      plan.n_chunks > 1 ? part_acc + (size_t)batch * n_q * plan.n_chunks * fast::PART_FLOATS : nullptr;
+  float* part_ml = plan.fast_slots > 0 ? part_acc + (size_t)plan.fast_slots * fast::PART_FLOATS : nullptr;
+  int2* row_chunks = plan.fast_slots > 0 ? reinterpret_cast<int2*>(part_ml + (size_t)plan.fast_slots * 2 * fast::H) : nullptr;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)fast::decode_attn_fast, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)sizeof(fast::Smem));
     if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute((const void*)fast::attn_merge_frag, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            32 * kMaxSplits * (int)sizeof(float2));
-    if (e != hipSuccess) return e;
     attr_set = true;
   }
-  dim3 grid(plan.n_chunks, batch * n_q);
+  const dim3 grid(plan.fast_grid_x, plan.fast_mode == fast::FIXED ? rows : 1);
   hipLaunchKernelGGL(fast::decode_attn_fast, grid, dim3(256), sizeof(fast::Smem), stream, (const bf16*)q_packed,
-                     (const bf16*)cache, seq_off, seq_len, n_q, L.softmax_scale * kLog2e, plan.chunk_len,
-                     plan.n_chunks, part_acc, part_ml, z, lse);
+                     (const bf16*)cache, seq_off, seq_len, n_q, rows, L.softmax_scale * kLog2e, plan.fast_mode,
+                     plan.n_chunks, plan.chunk_len, part_acc, part_ml, row_chunks, z, lse);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || plan.n_chunks == 1) return e;
-  const size_t merge_lds = (size_t)32 * plan.n_chunks * sizeof(float2);
-  hipLaunchKernelGGL(fast::attn_merge_frag, dim3(64, batch * n_q), dim3(256), merge_lds, stream, part_acc, part_ml,
-                     plan.n_chunks, z, lse);
+  if (e != hipSuccess || plan.fast_slots == 0) return e;
+  hipLaunchKernelGGL(fast::attn_merge_frag, dim3(64, rows), dim3(256), 0, stream, part_acc, part_ml, row_chunks, z,
+                     lse);
   return hipGetLastError();
 }
 

@@ -18,6 +18,11 @@ struct LayerDims {
 struct SplitPlan {
   int n_chunks;
   int chunk_len;
+  // MFMA path only: how its workgroups take chunks (see attn_fast_plan), the grid's x extent and
+  // the number of partial slots in the workspace
+  int fast_mode;
+  int fast_grid_x;
+  int fast_slots;
 };
 
 constexpr int kMaxSplits = 256;
@@ -46,6 +51,8 @@ hipError_t launch_attn_merge(int n_rowheads, int n_chunks, int d_latent, const f
 
 // MFMA path for the DeepSeek-V2/V3 shape (H 128, d_latent 512, d_rope 64, bf16)
 bool attn_fast_supported(const LayerDims& L);
+void attn_fast_plan(int rows, int n_splits, SplitPlan* plan);
+size_t attn_fast_workspace_bytes(const SplitPlan& plan, int rows);
 hipError_t launch_attn_fast(const LayerDims& L, int batch, int n_q, const void* q_packed, const void* cache,
                             const int64_t* seq_off, const int32_t* seq_len, const SplitPlan& plan, void* workspace,
                             float* z, float* lse, hipStream_t stream);

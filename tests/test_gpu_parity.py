@@ -144,6 +144,18 @@ def test_ragged_batch_sampled():
     assert np.array_equal(np32(lse1[0]), np32(run.lse[b]))
 
 
+def test_ragged_batch_balanced_chunks():
+    """The library's own chunking of a ragged batch (every row cut into chunks of one common
+    length, sized so that the whole batch fills one grid): the shortest, the longest and two
+    middle sequences against the oracle."""
+    cfg = CONFIGS[2]
+    hi = host_inputs(cfg)
+    run = run_pipeline(hi)
+    lens = hi.lens
+    for b in sorted({int(np.argmin(lens)), int(np.argmax(lens)), 5, 40}):
+        _check_outputs(run, hi, b, heads=[1, 77])
+
+
 @pytest.mark.slow
 def test_long_context_128k_sampled():
     cfg = CONFIGS[3]
