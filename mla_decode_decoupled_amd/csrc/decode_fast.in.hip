@@ -603,19 +603,25 @@ __global__ void __launch_bounds__(256)
 }
 
 // Log-sum-exp merge of the split-K partials of the fast path (layout above). One workgroup per
-// (query row, head block hb, col block cb): 32 heads x 32 latent columns, each lane owning one
-// head and 16 columns. The row's chunks are the slots base .. base + nck - 1 (every one saw at
-// least one key), as published by the row's first chunk. With M = max_k m_k (m in log2 units),
-// z = sum_k 2^(m_k - M) O_k / sum_k 2^(m_k - M) l_k. The 4 waves take the chunks round-robin,
-// two chunks (8 coalesced 1 KB loads) per step, each lane weighting its own head; the wave sums
-// meet in LDS. Rows computed as a single chunk were written directly and are skipped.
+// (query row, head block hb, col block cb, JN of the 4 row groups j): 32 heads x 8 JN latent
+// columns, each lane owning one head and 4 JN columns (JN = 4 for many rows; JN = 1 spreads a
+// few rows over four times as many workgroups). The row's chunks are the slots
+// base .. base + nck - 1 (every one saw at least one key), as published by the row's first chunk.
+// With M = max_k m_k (m in log2 units), z = sum_k 2^(m_k - M) O_k / sum_k 2^(m_k - M) l_k. The 4
+// waves take the chunks round-robin with 8 coalesced 1 KB loads in flight per step, each lane
+// weighting its own head; the wave sums meet in LDS. Rows computed as a single chunk were written
+// directly and are skipped.
+template <int JN>
 __global__ void __launch_bounds__(256) attn_merge_frag(const float* __restrict__ part_acc,
                                                        const float* __restrict__ part_ml,
                                                        const int2* __restrict__ row_chunks,
                                                        float* __restrict__ z, float* __restrict__ lse) {
-  __shared__ f32x4 red[3][4][64];
+  constexpr int CU = 8 / JN;   // chunks per step and wave
+  __shared__ f32x4 red[3][JN][64];
   __shared__ float lred[3][64];
-  const int bt = blockIdx.y, slab = blockIdx.x;   // slab = hb * 16 + cb
+  __shared__ float mred[4][64];
+  const int bt = blockIdx.y;
+  const int slab = blockIdx.x / (4 / JN), jbase = (blockIdx.x % (4 / JN)) * JN;   // slab = hb * 16 + cb
   const int hb = slab >> 4, cb = slab & 15;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int g = lane >> 5, hl = lane & 31;
@@ -624,9 +630,8 @@ __global__ void __launch_bounds__(256) attn_merge_frag(const float* __restrict__
   const int base = rc.x, nck = rc.y;
   const size_t head = (size_t)32 * hb + hl;
   const float2* ml = reinterpret_cast<const float2*>(part_ml) + (size_t)base * H + head;   // stride H
-  const float* src = part_acc + (size_t)base * PART_FLOATS + (size_t)slab * 1024 + 4 * lane;
+  const float* src = part_acc + (size_t)base * PART_FLOATS + (size_t)slab * 1024 + (size_t)jbase * 256 + 4 * lane;
   // M: each wave scans every fourth chunk, eight loads in flight per lane, then the waves agree
-  __shared__ float mred[4][64];
   float M = -INFINITY;
   for (int k0 = wv; k0 < nck; k0 += 32) {
     float mv[8];
@@ -641,34 +646,33 @@ __global__ void __launch_bounds__(256) attn_merge_frag(const float* __restrict__
   mred[wv][lane] = M;
   __syncthreads();
   M = fmaxf(fmaxf(mred[0][lane], mred[1][lane]), fmaxf(mred[2][lane], mred[3][lane]));
-  f32x4 acc[4] = {};
+  f32x4 acc[JN] = {};
   float Lsum = 0.0f;
-  for (int k0 = wv; k0 < nck; k0 += 8) {
-    const int k1 = k0 + 4;
-    const bool two = k1 < nck;
-    f32x4 x0[4], x1[4];
+  for (int k0 = wv; k0 < nck; k0 += 4 * CU) {
+    f32x4 x[CU][JN];
+    float2 v[CU];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) x0[j] = *reinterpret_cast<const f32x4*>(src + (size_t)k0 * PART_FLOATS + j * 256);
-    if (two) {
+    for (int u = 0; u < CU; ++u) {
+      const int kk = k0 + 4 * u;
+      if (kk < nck) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) x1[j] = *reinterpret_cast<const f32x4*>(src + (size_t)k1 * PART_FLOATS + j * 256);
+        for (int j = 0; j < JN; ++j) x[u][j] = *reinterpret_cast<const f32x4*>(src + (size_t)kk * PART_FLOATS + j * 256);
+        v[u] = ml[(size_t)kk * H];
+      }
     }
-    const float2 v0 = ml[(size_t)k0 * H];
-    const float w0 = exp2f(v0.x - M);
-    Lsum = fmaf(w0, v0.y, Lsum);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[j] += w0 * x0[j];
-    if (two) {
-      const float2 v1 = ml[(size_t)k1 * H];
-      const float w1 = exp2f(v1.x - M);
-      Lsum = fmaf(w1, v1.y, Lsum);
+    for (int u = 0; u < CU; ++u) {
+      if (k0 + 4 * u < nck) {
+        const float wk = exp2f(v[u].x - M);
+        Lsum = fmaf(wk, v[u].y, Lsum);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] += w1 * x1[j];
+        for (int j = 0; j < JN; ++j) acc[j] += wk * x[u][j];
+      }
     }
   }
   if (wv > 0) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) red[wv - 1][j][lane] = acc[j];
+    for (int j = 0; j < JN; ++j) red[wv - 1][j][lane] = acc[j];
     lred[wv - 1][lane] = Lsum;
   }
   __syncthreads();
@@ -677,15 +681,15 @@ __global__ void __launch_bounds__(256) attn_merge_frag(const float* __restrict__
     for (int u = 0; u < 3; ++u) {
       Lsum += lred[u][lane];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] += red[u][j][lane];
+      for (int j = 0; j < JN; ++j) acc[j] += red[u][j][lane];
     }
     // the two lane halves of a head summed the same chunks: Lsum agrees between them
     const size_t rh = (size_t)bt * H + head;
     const float inv = 1.0f / Lsum;
-    float* dst = z + rh * DC + 32 * cb + 4 * g;
+    float* dst = z + rh * DC + 32 * cb + 8 * jbase + 4 * g;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) *reinterpret_cast<f32x4*>(dst + 8 * j) = acc[j] * inv;
-    if (lse != nullptr && cb == 0 && g == 0) lse[rh] = (M + log2f(Lsum)) * kLn2;
+    for (int j = 0; j < JN; ++j) *reinterpret_cast<f32x4*>(dst + 8 * j) = acc[j] * inv;
+    if (lse != nullptr && cb == 0 && jbase == 0 && g == 0) lse[rh] = (M + log2f(Lsum)) * kLn2;
   }
 }
 
@@ -737,8 +741,12 @@ hipError_t launch_attn_fast(const LayerDims& L, int batch, int n_q, const void* 
                      plan.n_chunks, plan.chunk_len, part_acc, part_ml, row_chunks, z, lse);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.fast_slots == 0) return e;
-  hipLaunchKernelGGL(fast::attn_merge_frag, dim3(64, rows), dim3(256), 0, stream, part_acc, part_ml, row_chunks, z,
-                     lse);
+  if (rows <= 16)   // few rows: four workgroups per (row, 32 x 32 block) to keep enough loads in flight
+    hipLaunchKernelGGL(fast::attn_merge_frag<1>, dim3(256, rows), dim3(256), 0, stream, part_acc, part_ml, row_chunks,
+                       z, lse);
+  else
+    hipLaunchKernelGGL(fast::attn_merge_frag<4>, dim3(64, rows), dim3(256), 0, stream, part_acc, part_ml, row_chunks,
+                       z, lse);
   return hipGetLastError();
 }
 
