@@ -78,7 +78,7 @@ mla_status plan_splits(int32_t max_seq_len, int32_t n_splits, int64_t rows, bool
   plan->chunk_len = (int)((max_seq_len + n - 1) / n);
   plan->n_chunks = (max_seq_len + plan->chunk_len - 1) / plan->chunk_len;
   plan->fast_mode = plan->fast_grid_x = plan->fast_slots = 0;
-  if (fast) mla::attn_fast_plan((int)rows, n_splits, plan);
+  if (fast) mla::attn_fast_plan((int)rows, n_splits, max_seq_len, plan);
   return MLA_OK;
 }
 

@@ -124,10 +124,19 @@ __device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_base) {
 
 __device__ __forceinline__ void wait_vmcnt_9() { __builtin_amdgcn_s_waitcnt((9 & 15) | (7 << 4) | (15 << 8)); }
 __device__ __forceinline__ void wait_vmcnt_0() { __builtin_amdgcn_s_waitcnt((0) | (7 << 4) | (15 << 8)); }
+// vmcnt has six bits on gfx9: the low four at [3:0], the high two at [15:14]
+__device__ __forceinline__ void wait_vmcnt_18() {
+  __builtin_amdgcn_s_waitcnt((18 & 15) | ((18 >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_vmcnt_27() {
+  __builtin_amdgcn_s_waitcnt((27 & 15) | ((27 >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 // Split-K partials of the fast path are stored in the accumulator's own register order, so the
 // attention kernel writes them with whole 1 KB stores straight from the accumulators and the merge
-// reads them the same way. Per (query row, chunk) one block of H * DC floats:
+// reads them the same way. Both sides use nontemporal accesses: the partials are streamed through
+// once, and left dirty in L2 they would only lengthen the write-back at the end of the kernel.
+// Per (query row, chunk) one block of H * DC floats:
 //   [head block hb][col block cb (16)][row group j][lane][4]
 // holds O^T[col][head] for col = 32cb + 8j + 4(lane / 32) + e, head = 32hb + lane % 32.
 constexpr int PART_FLOATS = H * DC;   // per (query row, chunk)
@@ -146,20 +155,27 @@ __device__ __forceinline__ int frag_offset(int head, int col) {
 //   one workgroup, whatever the mix of lengths; the chunks of all rows are numbered in row order
 //   and chunk number = workgroup = partial slot.
 // PER_ROW: one chunk per row (many rows already fill the chip).
-enum ChunkMode { FIXED = 0, BALANCED = 1, PER_ROW = 2 };
+// HSPLIT (few rows and few keys, the latency-bound case): the BALANCED cut with kHsplitChunks
+//   chunks of at least kHsplitMinTiles tiles, and four workgroups per chunk, one per head block of
+//   32 heads (decode_attn_hsplit).
+enum ChunkMode { FIXED = 0, BALANCED = 1, PER_ROW = 2, HSPLIT = 3 };
 constexpr int kBalanceGrid = 256;
 constexpr int kBalanceRows = 128;
 constexpr int kMinTiles = 4;
+constexpr int kHsplitChunks = 64;
+constexpr int kHsplitMinTiles = 2;
+constexpr int kHsplitRows = 16;
+constexpr int kHsplitMaxTiles = 1024;   // rows x tiles of the longest row
 
 struct Chunk {
   int bt, k, nck, slot, j0, j1;
 };
 
-// BALANCED plan, computed by every lane of wave 0 for all rows (rows <= 128: two per lane): the
-// chunk of `target` (a workgroup index), or of row `target_row` when target < 0. Returns false
-// when `target` lies past the last chunk.
-__device__ bool balanced_chunk(const int32_t* __restrict__ seq_len, int n_q, int rows, int target, int target_row,
-                               Chunk* out) {
+// BALANCED plan over `grid` chunks of at least `min_tiles` tiles, computed by every lane of wave 0
+// for all rows (rows <= 128: two per lane): the chunk numbered `target`. Returns false when
+// `target` lies past the last chunk.
+__device__ bool balanced_chunk(const int32_t* __restrict__ seq_len, int n_q, int rows, int target, int grid,
+                               int min_tiles, Chunk* out) {
   const int lane = threadIdx.x & 63;
   int nvis[2], tiles[2];
   int64_t tsum = 0;
@@ -172,8 +188,8 @@ __device__ bool balanced_chunk(const int32_t* __restrict__ seq_len, int n_q, int
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) tsum += __shfl_xor(tsum, o, 64);
-  const int64_t share = (tsum + (kBalanceGrid - rows) - 1) / (kBalanceGrid - rows);
-  const int q = (int)max((int64_t)kMinTiles, share);
+  const int64_t share = (tsum + (grid - rows) - 1) / (grid - rows);
+  const int q = (int)max((int64_t)min_tiles, share);
   bool found = false;
   int carry = 0;
 #pragma unroll
@@ -187,13 +203,13 @@ __device__ bool balanced_chunk(const int32_t* __restrict__ seq_len, int n_q, int
     }
     const int first = carry + incl - nck;
     const int r = lane + 64 * u;
-    const bool mine = r < rows && (target >= 0 ? (target >= first && target < first + nck) : r == target_row);
+    const bool mine = r < rows && target >= first && target < first + nck;
     const uint64_t hit = __ballot(mine);
     if (hit) {
       const int src = __ffsll((unsigned long long)hit) - 1;
       const int f = __shfl(first, src, 64), n = __shfl(nck, src, 64), nv = __shfl(nvis[u], src, 64);
-      const int k = target >= 0 ? target - f : 0;
-      *out = Chunk{src + 64 * u, k, n, target >= 0 ? target : f, k * q * TILE, min((k + 1) * q * TILE, nv)};
+      const int k = target - f;
+      *out = Chunk{src + 64 * u, k, n, target, k * q * TILE, min((k + 1) * q * TILE, nv)};
       found = true;
     }
     carry += __shfl(incl, 63, 64);
@@ -201,19 +217,20 @@ __device__ bool balanced_chunk(const int32_t* __restrict__ seq_len, int n_q, int
   return found;
 }
 
-// Exact fallback for one (query row, chunk): per head, a float32 online softmax that rescales
-// its running sum and latent accumulator at every block of 256 keys. Same outputs as the MFMA
+// Exact fallback for one (query row, chunk) and heads h_begin .. h_end - 1: per head, a float32
+// online softmax that rescales its running sum and latent accumulator at every block of 256 keys. Same outputs as the MFMA
 // path (final z/lse with one chunk, otherwise a partial in log2 units). Kept out of line so the
 // MFMA loop's register allocation does not see it.
 __device__ __noinline__ void exact_chunk(const bf16* __restrict__ q_packed, const unsigned char* __restrict__ kv,
                                          size_t rh0, int j0, int j1, float scale_log2, int n_chunks, int slot,
                                          float* __restrict__ part_acc, float* __restrict__ part_ml,
-                                         float* __restrict__ z, float* __restrict__ lse, unsigned char* smem) {
+                                         float* __restrict__ z, float* __restrict__ lse, unsigned char* smem,
+                                         int h_begin, int h_end) {
   float* qs = reinterpret_cast<float*>(smem);   // [ROW]
   float* ps = qs + ROW;                         // [256]
   float* red = ps + 256;                        // [8]
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  for (int h = 0; h < H; ++h) {
+  for (int h = h_begin; h < h_end; ++h) {
     const size_t rh = rh0 + h;
     for (int d = tid; d < ROW; d += 256) qs[d] = (float)q_packed[rh * ROW + d];
     __syncthreads();
@@ -296,7 +313,7 @@ __global__ void __launch_bounds__(256)
     Chunk* shared_ch = reinterpret_cast<Chunk*>(smem_raw + FLAGS_OFF + 64);
     if (w == 0) {
       Chunk c;
-      const bool found = balanced_chunk(seq_len, n_q, rows, (int)blockIdx.x, -1, &c);
+      const bool found = balanced_chunk(seq_len, n_q, rows, (int)blockIdx.x, kBalanceGrid, kMinTiles, &c);
       if (lane == 0) {
         if (!found) c.nck = 0;
         *shared_ch = c;
@@ -542,7 +559,7 @@ __global__ void __launch_bounds__(256)
   const bool overflowed = (flags[0] | flags[1] | flags[2] | flags[3]) != 0;
   if (overflowed) {
     __syncthreads();
-    exact_chunk(q_packed, kv, rh0, j0, j1, scale_log2, n_chunks, ch.slot, part_acc, part_ml, z, lse, smem_raw);
+    exact_chunk(q_packed, kv, rh0, j0, j1, scale_log2, n_chunks, ch.slot, part_acc, part_ml, z, lse, smem_raw, 0, H);
     return;
   }
   // the accumulator is read by VALU below: 20 wait states after the last MFMA
@@ -571,7 +588,8 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const f32x16& o = *oacc[cb];
-        *reinterpret_cast<f32x4*>(blk + (cb * 4 + j) * 256) = f32x4{o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]};
+        __builtin_nontemporal_store(f32x4{o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]},
+                                    reinterpret_cast<f32x4*>(blk + (cb * 4 + j) * 256));
       }
     return;
   }
@@ -599,6 +617,267 @@ __global__ void __launch_bounds__(256)
       *reinterpret_cast<f32x4*>(z + (rh0 + w * 32 + i) * DC + 256 * half + 4 * lane) = v;
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads done before the next half's writes
+  }
+}
+
+// ---- Head-split kernel for few query rows and short histories (latency-bound decode).
+// Four workgroups share each chunk, one per head block hb of 32 heads; inside a workgroup the
+// 4 waves split both contractions instead of the heads: wave w scores the 32 keys of a tile
+// against its 32 heads over dims 144w .. 144w+143 (9 MFMA k-steps), the four partial score tiles
+// meet in LDS, every wave runs the same softmax on their sum (added in wave order, so all waves
+// hold bitwise the same probabilities), and wave w accumulates latent columns 128w .. 128w+127
+// (col blocks 4w .. 4w+3). Per tile a wave issues 17 MFMAs instead of 68, so a chunk of a few
+// tiles finishes in a fraction of the big kernel's time, the queries a workgroup stages are 36 KB
+// instead of 147 KB, and the split-K partials come out 4x fewer for the same number of
+// workgroups. The price is that each cache tile is streamed into four workgroups; they run on
+// the same XCD, so three of the four reads hit its L2. Same tile layout (swizzled DMA), same
+// fixed-reference softmax with the exact fallback, same partial layout as decode_attn_fast.
+typedef __bf16 bf16x8e __attribute__((ext_vector_type(8)));
+typedef short i16x4e __attribute__((ext_vector_type(4)));
+typedef float f32x16e __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2e __attribute__((ext_vector_type(2)));
+typedef float f32x2e __attribute__((ext_vector_type(2)));
+
+// LDS (all 160 KB): tile t being computed on, t+1 .. t+3 in flight (the queries are staged in the
+// buffer of tile 3), and the partial-score exchange
+constexpr int HS_NBUF = 4;
+struct SmemH {
+  unsigned char tile[HS_NBUF][TILE_BYTES];
+  float exch[WAVES][4][64][4];   // partial scores: [wave][register quad][lane][4]
+};
+static_assert(sizeof(SmemH) <= 160 * 1024, "LDS budget");
+
+__device__ __forceinline__ f32x16e mfma_bf16(bf16x8e a, bf16x8e b, f32x16e c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16-byte operand piece of logical chunk c (8 dims) of tile row r
+__device__ __forceinline__ bf16x8e row_piece(const unsigned char* tile, int r, int c) {
+  return *reinterpret_cast<const bf16x8e*>(tile + r * ROW_BYTES + phys_chunk(c, r) * 16);
+}
+
+// A operand V^T (32 latent columns of block cb x 16 keys of step s) by two transpose reads: lane
+// l = 16q + L gets tile[16s + 8g + e][32cb + l % 32], e = 0..7; source lane L of its 16-lane group
+// points at row 16s + 8g + 4h + L/4, columns 32cb + 16(q & 1) + 4(L & 3) .. +3, halves h = 0, 1.
+__device__ __forceinline__ bf16x8e v_fragment(const unsigned char* tile, int s, int cb, int lane) {
+  const int g = lane >> 5, q = lane >> 4, L = lane & 15;
+  const int c = 4 * cb + 2 * (q & 1) + ((L >> 1) & 1);   // logical 16-byte chunk of the 4 columns
+  i16x4e hv[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = 16 * s + 8 * g + 4 * h + (L >> 2);
+    const unsigned char* p = tile + r * ROW_BYTES + phys_chunk(c, r) * 16 + 8 * (L & 1);
+    hv[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4e*)MLA_LDS(unsigned char, p));
+  }
+  return __builtin_bit_cast(bf16x8e, hv);
+}
+
+// The BALANCED cut for the head-split grid (kHsplitChunks chunks of at least kHsplitMinTiles
+// tiles), computed by every lane from uniform loads of seq_len (scalar loads, so they wait on
+// lgkmcnt and never on the tile DMAs in flight): the chunk numbered `target`, or false when the
+// plan has fewer chunks. rows <= kHsplitRows.
+__device__ __forceinline__ bool hsplit_chunk(const int32_t* __restrict__ seq_len, int n_q, int rows, int target,
+                                             Chunk* out) {
+  int total = 0;
+  for (int r = 0; r < rows; ++r) total += (seq_len[r / n_q] - n_q + (r % n_q) + 1 + TILE - 1) / TILE;
+  const int q = max(kHsplitMinTiles, (total + (kHsplitChunks - rows) - 1) / (kHsplitChunks - rows));
+  int first = 0;
+  for (int r = 0; r < rows; ++r) {
+    const int nvis = seq_len[r / n_q] - n_q + (r % n_q) + 1;
+    const int nck = ((nvis + TILE - 1) / TILE + q - 1) / q;
+    if (target < first + nck) {
+      const int k = target - first;
+      *out = Chunk{r, k, nck, target, k * q * TILE, min((k + 1) * q * TILE, nvis)};
+      return true;
+    }
+    first += nck;
+  }
+  return false;
+}
+
+// grid: 4 * kHsplitChunks workgroups, 256 threads, sizeof(SmemH) dynamic LDS
+__global__ void __launch_bounds__(256)
+    decode_attn_hsplit(const bf16* __restrict__ q_packed, const bf16* __restrict__ cache,
+                       const int64_t* __restrict__ seq_off, const int32_t* __restrict__ seq_len, int n_q, int rows,
+                       float scale_log2, float* __restrict__ part_acc, float* __restrict__ part_ml,
+                       int2* __restrict__ row_chunks, float* __restrict__ z, float* __restrict__ lse) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  SmemH& sm = *reinterpret_cast<SmemH*>(smem_raw);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
+  // Workgroups are dealt to the 8 XCDs in turn: the four head blocks of chunk 8a + x are
+  // workgroups 32a + 8hb + x, all on XCD x.
+  const int wg = blockIdx.x;
+  const int hb = (wg >> 3) & 3, cidx = ((wg >> 5) << 3) | (wg & 7);
+  const int head0 = 32 * hb;
+
+  // DMA plan as in decode_attn_fast: slot (row r, physical chunk p) <- logical chunk phys_chunk(p, r)
+  uint32_t dma_off[DMA_PER_WAVE];
+#pragma unroll
+  for (int it = 0; it < DMA_PER_WAVE; ++it) {
+    const int slot = w * SLOTS_PER_WAVE + it * 64 + lane;
+    const int r = slot / ROW_CHUNKS, p = slot % ROW_CHUNKS;
+    dma_off[it] = r * ROW_BYTES + phys_chunk(p, r) * 16;
+  }
+  auto buf_lds = [&](int buf) { return (uint32_t)(uintptr_t)MLA_LDS(unsigned char, sm.tile[buf]); };
+  // 32 rows of 1152 bytes from `src` (rows past `last` re-read row `last`) into buffer `buf`
+  auto dma_rows = [&](const unsigned char* src, int last, int buf) {
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(buf_lds(buf) + (w * SLOTS_PER_WAVE) * 16);
+#pragma unroll
+    for (int it = 0; it < DMA_PER_WAVE; ++it) {
+      const int r = dma_off[it] / ROW_BYTES;
+      const uint32_t o = dma_off[it] - (r > last ? r - last : 0) * ROW_BYTES;
+      dma16(src + o, dst + it * 1024);
+    }
+  };
+  // queries of heads head0 .. head0+31 (32 contiguous rows), staged like a tile in buffer 3. With
+  // one query row the row is known before the plan, and the load overlaps it.
+  auto stage_queries = [&](int bt) {
+    dma_rows(reinterpret_cast<const unsigned char*>(q_packed + ((size_t)bt * H + head0) * ROW), TILE - 1, 3);
+  };
+  if (rows == 1) stage_queries(0);
+  Chunk ch;
+  if (!hsplit_chunk(seq_len, n_q, rows, cidx, &ch)) {   // the plan has fewer chunks than the grid
+    wait_vmcnt_0();   // no LDS load may land after the workgroup has ended
+    return;
+  }
+  const int bt = ch.bt, j0 = ch.j0, j1 = ch.j1, n_chunks = ch.nck;
+  const int b = bt / n_q;
+  const size_t rh0 = (size_t)bt * H;
+  if (row_chunks != nullptr && ch.k == 0 && hb == 0 && threadIdx.x == 0) row_chunks[bt] = make_int2(ch.slot, n_chunks);
+  const int n_tiles = (j1 - j0 + TILE - 1) / TILE;
+  const unsigned char* kv = reinterpret_cast<const unsigned char*>(cache + seq_off[b] * (int64_t)ROW);
+  auto issue_tile = [&](int tile) {
+    const int key0 = j0 + tile * TILE;
+    dma_rows(kv + (int64_t)key0 * ROW_BYTES, min(TILE, j1 - key0) - 1, tile % HS_NBUF);
+  };
+
+  // queries (unless already in flight), then up to three tiles; vmcnt counts in issue order, so
+  // once at most 9 x (tiles issued) loads are outstanding the queries have landed
+  if (rows != 1) stage_queries(bt);
+  issue_tile(0);
+  if (n_tiles > 2) {
+    issue_tile(1);
+    issue_tile(2);
+    wait_vmcnt_27();
+  } else if (n_tiles > 1) {
+    issue_tile(1);
+    wait_vmcnt_18();
+  } else {
+    wait_vmcnt_9();
+  }
+  lds_barrier();
+  // B operand of the scores: head l32, dims 16s + 8g .. +7 for this wave's k-steps s = 9w + u
+  bf16x8e qf[9];
+#pragma unroll
+  for (int u = 0; u < 9; ++u) qf[u] = row_piece(sm.tile[3], l32, 2 * (9 * w + u) + g);
+  const int akey = key_of_row(l32);   // A operand row l32 holds key pi(l32)
+
+  f32x16e oacc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) oacc[i] = f32x16e{};
+  float m_ref = -INFINITY, l_run = 0.0f;
+  bool ovf = false;
+  for (int t = 0; t < n_tiles; ++t) {
+    if (t + 2 < n_tiles)   // tile t landed; tiles t+1 and t+2 may still be in flight
+      wait_vmcnt_18();
+    else if (t + 1 < n_tiles)
+      wait_vmcnt_9();
+    else
+      wait_vmcnt_0();
+    lds_barrier();      // tile t visible; iteration t-1 (and the query reads) finished everywhere
+    if (t + 3 < n_tiles) issue_tile(t + 3);   // into the buffer of tile t-1 (or of the queries)
+    const unsigned char* tb = sm.tile[t % HS_NBUF];
+    f32x16e sp = f32x16e{};
+#pragma unroll
+    for (int u = 0; u < 9; ++u) sp = mfma_bf16(row_piece(tb, akey, 2 * (9 * w + u) + g), qf[u], sp);
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd)
+      *reinterpret_cast<f32x4*>(&sm.exch[w][qd][lane][0]) = f32x4{sp[4 * qd], sp[4 * qd + 1], sp[4 * qd + 2], sp[4 * qd + 3]};
+    lds_barrier();
+    float sv[16];
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) {
+      f32x4 v = *reinterpret_cast<const f32x4*>(&sm.exch[0][qd][lane][0]);
+#pragma unroll
+      for (int u = 1; u < WAVES; ++u) v += *reinterpret_cast<const f32x4*>(&sm.exch[u][qd][lane][0]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sv[4 * qd + e] = v[e] * scale_log2;
+    }
+    // softmax against the chunk's fixed reference (the first tile's maximum), keys past the end
+    // of a tail tile masked
+    const int key0 = j0 + t * TILE;
+    if (key0 + TILE > j1) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (key0 + key_of_reg(r, g) >= j1) sv[r] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sv[r]);
+    if (t == 0) {
+      m_ref = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    } else {
+      ovf |= mx > m_ref + HEADROOM;
+    }
+    int pk[8];
+    float psum = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {   // 2^x of the hardware (results below 2^-126 flush to 0)
+      const float p0 = __builtin_amdgcn_exp2f(sv[r] - m_ref), p1 = __builtin_amdgcn_exp2f(sv[r + 1] - m_ref);
+      psum += p0 + p1;
+      pk[r / 2] = __builtin_bit_cast(int, __builtin_convertvector((f32x2e){p0, p1}, bf16x2e));
+    }
+    l_run += psum;
+    // P^T B fragments: keys 16s + 8g + e of this lane's head are score registers 8s + e
+    const int pk0[4] = {pk[0], pk[1], pk[2], pk[3]}, pk1[4] = {pk[4], pk[5], pk[6], pk[7]};
+    const bf16x8e pb0 = __builtin_bit_cast(bf16x8e, pk0), pb1 = __builtin_bit_cast(bf16x8e, pk1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int cb = 4 * w + i;
+      oacc[i] = mfma_bf16(v_fragment(tb, 0, cb, lane), pb0, oacc[i]);
+      oacc[i] = mfma_bf16(v_fragment(tb, 1, cb, lane), pb1, oacc[i]);
+    }
+  }
+
+  // every wave ran the same softmax, so the flags agree; they still meet in LDS once
+  int* flags = reinterpret_cast<int*>(&sm.exch[0][0][0][0]);
+  const bool wave_ovf = __any(ovf);
+  lds_barrier();   // every wave is done with the exchange area
+  if (lane == 0) flags[w] = wave_ovf ? 1 : 0;
+  __syncthreads();
+  if ((flags[0] | flags[1] | flags[2] | flags[3]) != 0) {
+    __syncthreads();
+    exact_chunk(q_packed, kv, rh0, j0, j1, scale_log2, n_chunks, ch.slot, part_acc, part_ml, z, lse, smem_raw, head0,
+                head0 + 32);
+    return;
+  }
+  l_run += __shfl_xor(l_run, 32, 64);
+  const int head = head0 + l32;
+  if (n_chunks == 1) {
+    // z = O / l: lane (g, head) holds columns 32cb + 8j + 4g .. +3
+    const float inv = 1.0f / l_run;
+    float* zr = z + (rh0 + head) * DC + 4 * g;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<f32x4*>(zr + 32 * (4 * w + i) + 8 * j) =
+            f32x4{oacc[i][4 * j], oacc[i][4 * j + 1], oacc[i][4 * j + 2], oacc[i][4 * j + 3]} * inv;
+    if (lse != nullptr && w == 0 && g == 0) lse[rh0 + head] = (m_ref + log2f(l_run)) * kLn2;
+    return;
+  }
+  float* blk = part_acc + (size_t)ch.slot * PART_FLOATS + (size_t)hb * (PART_FLOATS / 4) + 4 * lane;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      __builtin_nontemporal_store(f32x4{oacc[i][4 * j], oacc[i][4 * j + 1], oacc[i][4 * j + 2], oacc[i][4 * j + 3]},
+                                  reinterpret_cast<f32x4*>(blk + ((4 * w + i) * 4 + j) * 256));
+  if (w == 0 && g == 0) {
+    float* ml = part_ml + ((size_t)ch.slot * H + head) * 2;
+    ml[0] = m_ref;
+    ml[1] = l_run;
   }
 }
 
@@ -656,7 +935,8 @@ __global__ void __launch_bounds__(256) attn_merge_frag(const float* __restrict__
       const int kk = k0 + 4 * u;
       if (kk < nck) {
 #pragma unroll
-        for (int j = 0; j < JN; ++j) x[u][j] = *reinterpret_cast<const f32x4*>(src + (size_t)kk * PART_FLOATS + j * 256);
+        for (int j = 0; j < JN; ++j)
+          x[u][j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + (size_t)kk * PART_FLOATS + j * 256));
         v[u] = ml[(size_t)kk * H];
       }
     }
@@ -705,8 +985,13 @@ size_t attn_fast_workspace_bytes(const SplitPlan& plan, int rows) {
   return (size_t)plan.fast_slots * ((size_t)fast::PART_FLOATS + 2 * fast::H) * sizeof(float) + (size_t)rows * sizeof(int2);
 }
 
-void attn_fast_plan(int rows, int n_splits, SplitPlan* plan) {
-  if (n_splits > 0) {
+void attn_fast_plan(int rows, int n_splits, int max_seq_len, SplitPlan* plan) {
+  const int64_t max_tiles = ((int64_t)max_seq_len + fast::TILE - 1) / fast::TILE;
+  if (n_splits == 0 && rows <= fast::kHsplitRows && rows * max_tiles <= fast::kHsplitMaxTiles) {
+    plan->fast_mode = fast::HSPLIT;
+    plan->fast_grid_x = 4 * fast::kHsplitChunks;
+    plan->fast_slots = fast::kHsplitChunks;
+  } else if (n_splits > 0) {
     plan->fast_mode = fast::FIXED;
     plan->fast_grid_x = plan->n_chunks;
     plan->fast_slots = plan->n_chunks > 1 ? rows * plan->n_chunks : 0;
@@ -732,13 +1017,22 @@ hipError_t launch_attn_fast(const LayerDims& L, int batch, int n_q, const void* 
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)fast::decode_attn_fast, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)sizeof(fast::Smem));
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void*)fast::decode_attn_hsplit, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)sizeof(fast::SmemH));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const dim3 grid(plan.fast_grid_x, plan.fast_mode == fast::FIXED ? rows : 1);
-  hipLaunchKernelGGL(fast::decode_attn_fast, grid, dim3(256), sizeof(fast::Smem), stream, (const bf16*)q_packed,
-                     (const bf16*)cache, seq_off, seq_len, n_q, rows, L.softmax_scale * kLog2e, plan.fast_mode,
-                     plan.n_chunks, plan.chunk_len, part_acc, part_ml, row_chunks, z, lse);
+  if (plan.fast_mode == fast::HSPLIT) {
+    hipLaunchKernelGGL(fast::decode_attn_hsplit, dim3(plan.fast_grid_x), dim3(256), sizeof(fast::SmemH), stream,
+                       (const bf16*)q_packed, (const bf16*)cache, seq_off, seq_len, n_q, rows,
+                       L.softmax_scale * kLog2e, part_acc, part_ml, row_chunks, z, lse);
+  } else {
+    const dim3 grid(plan.fast_grid_x, plan.fast_mode == fast::FIXED ? rows : 1);
+    hipLaunchKernelGGL(fast::decode_attn_fast, grid, dim3(256), sizeof(fast::Smem), stream, (const bf16*)q_packed,
+                       (const bf16*)cache, seq_off, seq_len, n_q, rows, L.softmax_scale * kLog2e, plan.fast_mode,
+                       plan.n_chunks, plan.chunk_len, part_acc, part_ml, row_chunks, z, lse);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.fast_slots == 0) return e;
   if (rows <= 16)   // few rows: four workgroups per (row, 32 x 32 block) to keep enough loads in flight

@@ -51,7 +51,7 @@ hipError_t launch_attn_merge(int n_rowheads, int n_chunks, int d_latent, const f
 
 // MFMA path for the DeepSeek-V2/V3 shape (H 128, d_latent 512, d_rope 64, bf16)
 bool attn_fast_supported(const LayerDims& L);
-void attn_fast_plan(int rows, int n_splits, SplitPlan* plan);
+void attn_fast_plan(int rows, int n_splits, int max_seq_len, SplitPlan* plan);
 size_t attn_fast_workspace_bytes(const SplitPlan& plan, int rows);
 hipError_t launch_attn_fast(const LayerDims& L, int batch, int n_q, const void* q_packed, const void* cache,
                             const int64_t* seq_off, const int32_t* seq_len, const SplitPlan& plan, void* workspace,

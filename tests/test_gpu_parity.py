@@ -88,9 +88,11 @@ def test_v3_decode_4k_all_heads():
     _check_outputs(run, hi, 0)
 
 
-@pytest.mark.parametrize("cid,n_splits", [(0, 1), (0, 7), (1, 1), (1, 3), (1, 64)])
+@pytest.mark.parametrize("cid,n_splits", [(0, 1), (0, 7), (1, 0), (1, 1), (1, 3), (1, 64)])
 def test_split_count_does_not_change_results(cid, n_splits):
-    """fp32: only the float32 summation order changes -> 1e-5.
+    """fp32: only the float32 summation order changes -> 1e-5. n_splits = 0 on the batch-1 4K
+    workload is the library's own choice: the head-split kernel, whose scores are summed from four
+    partial dot products.
 
     bf16: each chunk rounds its probabilities to bf16 relative to its own reference max, so the
     rounding (at most 2^-9 relative per weight, independent across keys) differs between split
@@ -142,6 +144,21 @@ def test_ragged_batch_sampled():
     torch.cuda.synchronize()
     assert np.array_equal(np32(z1[0]), np32(run.z[b]))
     assert np.array_equal(np32(lse1[0]), np32(run.lse[b]))
+
+
+def test_head_split_small_batch_mixed_lengths():
+    """Few query rows over short histories take the head-split kernel (four workgroups per chunk,
+    one per block of 32 heads, the waves splitting the dims and the latent columns). The lengths
+    give a row short enough for a single chunk (written directly), rows cut into several chunks
+    (merged) and tail tiles; two queries per sequence give rows of different visible length.
+    Heads from all four blocks, at both ends of each block."""
+    cfg = MLAConfig(**{**CONFIGS[1].__dict__, "batch": 3, "n_q": 2})
+    hi = host_inputs(cfg, lens=[41, 700, 3001])
+    run = run_pipeline(hi)
+    for b in range(3):
+        _check_cache(run, hi, b)
+        _check_qpacked(run, hi, b)
+        _check_outputs(run, hi, b, heads=[0, 31, 32, 63, 64, 95, 96, 127])
 
 
 def test_ragged_batch_balanced_chunks():
@@ -287,7 +304,7 @@ def test_multi_step_decode_matches_oracle_each_step():
         assert_close(np32(z)[0, 0], ref["z"][0], "f32", f"z step {t}")
 
 
-@pytest.mark.parametrize("n_splits", [1, 3])
+@pytest.mark.parametrize("n_splits", [0, 1, 3])
 def test_later_scores_far_above_the_first_tile(n_splits):
     """A chunk whose later keys score far above its first tile (by more than 64 in log2 units)
     must still match the oracle: the fast kernel's fixed per-chunk reference cannot hold those
@@ -297,7 +314,8 @@ def test_later_scores_far_above_the_first_tile(n_splits):
     (score 0); keys 32.. all carry the same latent c* = sign(q~ of head 0), and every position
     part is zero. Head 0 then scores its later keys at scale * sum|q~| (about 100 in natural
     units), every other head at a moderate value; each head's softmax has two levels, which keeps
-    the comparison well conditioned."""
+    the comparison well conditioned. n_splits = 0 takes the head-split kernel (chunks of two
+    tiles): its first chunk falls back, for each block of 32 heads separately."""
     cfg = CONFIGS[1]
     n = 32 + 200
     hi = host_inputs(cfg, lens=[n])
