@@ -134,8 +134,12 @@ __device__ __forceinline__ void wait_vmcnt_27() {
 
 // Split-K partials of the fast path are stored in the accumulator's own register order, so the
 // attention kernel writes them with whole 1 KB stores straight from the accumulators and the merge
-// reads them the same way. Both sides use nontemporal accesses: the partials are streamed through
-// once, and left dirty in L2 they would only lengthen the write-back at the end of the kernel.
+// reads them the same way. The head-split kernel writes its (few, latency-bound) partials with
+// nontemporal stores, which shortens the write-back at the end of the kernel, and its merge reads
+// them nontemporally too (cached by the merge, the lines would slow the next call's stores); the
+// big kernel's partials go through the caches both ways, where the merge finds part of them
+// (measured: the nontemporal form slows that merge by a fifth and gains nothing in the attention
+// kernel).
 // Per (query row, chunk) one block of H * DC floats:
 //   [head block hb][col block cb (16)][row group j][lane][4]
 // holds O^T[col][head] for col = 32cb + 8j + 4(lane / 32) + e, head = 32hb + lane % 32.
@@ -588,8 +592,7 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const f32x16& o = *oacc[cb];
-        __builtin_nontemporal_store(f32x4{o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]},
-                                    reinterpret_cast<f32x4*>(blk + (cb * 4 + j) * 256));
+        *reinterpret_cast<f32x4*>(blk + (cb * 4 + j) * 256) = f32x4{o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]};
       }
     return;
   }
@@ -886,19 +889,20 @@ __global__ void __launch_bounds__(256)
 // columns, each lane owning one head and 4 JN columns (JN = 4 for many rows; JN = 1 spreads a
 // few rows over four times as many workgroups). The row's chunks are the slots
 // base .. base + nck - 1 (every one saw at least one key), as published by the row's first chunk.
-// With M = max_k m_k (m in log2 units), z = sum_k 2^(m_k - M) O_k / sum_k 2^(m_k - M) l_k. The 4
-// waves take the chunks round-robin with 8 coalesced 1 KB loads in flight per step, each lane
-// weighting its own head; the wave sums meet in LDS. Rows computed as a single chunk were written
-// directly and are skipped.
-template <int JN>
+// With M = max_k m_k (m in log2 units), z = sum_k 2^(m_k - M) O_k / sum_k 2^(m_k - M) l_k.
+// One pass: the 4 waves take the chunks round-robin, CU chunks (coalesced 1 KB loads of the
+// partial and its (m, l)) in flight per step, and each wave keeps its own running maximum,
+// rescaling its sums when it grows; the wave sums then meet in LDS against the common maximum.
+// Rows computed as a single chunk were written directly and are skipped.
+template <int JN, bool NT>
 __global__ void __launch_bounds__(256) attn_merge_frag(const float* __restrict__ part_acc,
                                                        const float* __restrict__ part_ml,
                                                        const int2* __restrict__ row_chunks,
                                                        float* __restrict__ z, float* __restrict__ lse) {
-  constexpr int CU = 8 / JN;   // chunks per step and wave
+  constexpr int CU = JN == 1 ? 16 : 2;   // chunks per step and wave
   __shared__ f32x4 red[3][JN][64];
   __shared__ float lred[3][64];
-  __shared__ float mred[4][64];
+  __shared__ float mred[3][64];
   const int bt = blockIdx.y;
   const int slab = blockIdx.x / (4 / JN), jbase = (blockIdx.x % (4 / JN)) * JN;   // slab = hb * 16 + cb
   const int hb = slab >> 4, cb = slab & 15;
@@ -910,58 +914,63 @@ __global__ void __launch_bounds__(256) attn_merge_frag(const float* __restrict__
   const size_t head = (size_t)32 * hb + hl;
   const float2* ml = reinterpret_cast<const float2*>(part_ml) + (size_t)base * H + head;   // stride H
   const float* src = part_acc + (size_t)base * PART_FLOATS + (size_t)slab * 1024 + (size_t)jbase * 256 + 4 * lane;
-  // M: each wave scans every fourth chunk, eight loads in flight per lane, then the waves agree
-  float M = -INFINITY;
-  for (int k0 = wv; k0 < nck; k0 += 32) {
-    float mv[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int kk = k0 + 4 * u;
-      mv[u] = kk < nck ? ml[(size_t)kk * H].x : -INFINITY;
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) M = fmaxf(M, mv[u]);
-  }
-  mred[wv][lane] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(mred[0][lane], mred[1][lane]), fmaxf(mred[2][lane], mred[3][lane]));
+  float m_w = -INFINITY, Lsum = 0.0f;
   f32x4 acc[JN] = {};
-  float Lsum = 0.0f;
-  for (int k0 = wv; k0 < nck; k0 += 4 * CU) {
+  for (int k0 = wv; k0 < nck; k0 += 4 * CU) {   // chunk k0 exists, so every step sees one
     f32x4 x[CU][JN];
     float2 v[CU];
 #pragma unroll
     for (int u = 0; u < CU; ++u) {
       const int kk = k0 + 4 * u;
+      v[u] = make_float2(-INFINITY, 0.0f);
       if (kk < nck) {
 #pragma unroll
         for (int j = 0; j < JN; ++j)
-          x[u][j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + (size_t)kk * PART_FLOATS + j * 256));
+          x[u][j] = NT ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + (size_t)kk * PART_FLOATS + j * 256))
+                       : *reinterpret_cast<const f32x4*>(src + (size_t)kk * PART_FLOATS + j * 256);
         v[u] = ml[(size_t)kk * H];
       }
     }
+    float mb = m_w;
+#pragma unroll
+    for (int u = 0; u < CU; ++u) mb = fmaxf(mb, v[u].x);
+    const float a = exp2f(m_w - mb);   // 0 on the first step (m_w = -inf, mb finite)
+    Lsum *= a;
+#pragma unroll
+    for (int j = 0; j < JN; ++j) acc[j] *= a;
 #pragma unroll
     for (int u = 0; u < CU; ++u) {
       if (k0 + 4 * u < nck) {
-        const float wk = exp2f(v[u].x - M);
+        const float wk = exp2f(v[u].x - mb);
         Lsum = fmaf(wk, v[u].y, Lsum);
 #pragma unroll
         for (int j = 0; j < JN; ++j) acc[j] += wk * x[u][j];
       }
     }
+    m_w = mb;
   }
   if (wv > 0) {
 #pragma unroll
     for (int j = 0; j < JN; ++j) red[wv - 1][j][lane] = acc[j];
     lred[wv - 1][lane] = Lsum;
+    mred[wv - 1][lane] = m_w;
   }
   __syncthreads();
   if (wv == 0) {
+    // wave 0 always holds chunk 0, so M is finite; a wave without chunks weighs 2^-inf = 0
+    float M = m_w;
+#pragma unroll
+    for (int u = 0; u < 3; ++u) M = fmaxf(M, mred[u][lane]);
+    const float a0 = exp2f(m_w - M);
+    Lsum *= a0;
+#pragma unroll
+    for (int j = 0; j < JN; ++j) acc[j] *= a0;
 #pragma unroll
     for (int u = 0; u < 3; ++u) {
-      Lsum += lred[u][lane];
+      const float au = exp2f(mred[u][lane] - M);
+      Lsum = fmaf(au, lred[u][lane], Lsum);
 #pragma unroll
-      for (int j = 0; j < JN; ++j) acc[j] += red[u][j][lane];
+      for (int j = 0; j < JN; ++j) acc[j] += au * red[u][j][lane];
     }
     // the two lane halves of a head summed the same chunks: Lsum agrees between them
     const size_t rh = (size_t)bt * H + head;
@@ -1035,12 +1044,15 @@ hipError_t launch_attn_fast(const LayerDims& L, int batch, int n_q, const void* 
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.fast_slots == 0) return e;
-  if (rows <= 16)   // few rows: four workgroups per (row, 32 x 32 block) to keep enough loads in flight
-    hipLaunchKernelGGL(fast::attn_merge_frag<1>, dim3(256, rows), dim3(256), 0, stream, part_acc, part_ml, row_chunks,
-                       z, lse);
+  if (plan.fast_mode == fast::HSPLIT)
+    hipLaunchKernelGGL((fast::attn_merge_frag<1, true>), dim3(256, rows), dim3(256), 0, stream, part_acc, part_ml,
+                       row_chunks, z, lse);
+  else if (rows <= 16)   // few rows: four workgroups per (row, 32 x 32 block) to keep enough loads in flight
+    hipLaunchKernelGGL((fast::attn_merge_frag<1, false>), dim3(256, rows), dim3(256), 0, stream, part_acc, part_ml,
+                       row_chunks, z, lse);
   else
-    hipLaunchKernelGGL(fast::attn_merge_frag<4>, dim3(64, rows), dim3(256), 0, stream, part_acc, part_ml, row_chunks,
-                       z, lse);
+    hipLaunchKernelGGL((fast::attn_merge_frag<4, false>), dim3(64, rows), dim3(256), 0, stream, part_acc, part_ml,
+                       row_chunks, z, lse);
   return hipGetLastError();
 }
 

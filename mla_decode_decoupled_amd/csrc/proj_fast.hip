@@ -3,9 +3,9 @@
 //
 // At decode batch sizes both calls are matrix-vector products whose cost is reading the
 // per-head weights once (W_UK and W_UV are 16.8 MB each in bf16), so the kernels are built for
-// HBM streaming: every lane issues 16-byte weight loads, a workgroup owns one 64 KB weight slab,
-// and the 256 workgroups cover the chip once. Query rows are processed kRowBlock at a time
-// against the same weight registers.
+// HBM streaming: every lane issues independent 16-byte weight loads, a workgroup owns one 32 KB
+// weight slab, and 512 workgroups (two per CU) cover the weights once. Query rows are processed
+// kRowBlock at a time against the same weight registers.
 //
 //   absorb: q~[r, i, c] = sum_a W_UK[i, a, c] q_nope[r, i, a]   ("从零理解 MLA", section "矩阵吸收")
 //   out:    o[r, i, v]  = sum_c W_UV[i, v, c] z[r, i, c]        (same section, output side)
@@ -31,25 +31,27 @@ __device__ __forceinline__ void unpack8(const i32x4 v, float* f) {
   }
 }
 
-// grid (H, 2 column halves, row blocks); 256 threads: column group cg = t % 32 (8 columns),
-// row group ag = t / 32 (16 rows a of W_UK[i]). Partial sums over the 8 row groups meet in LDS.
+// grid (H, 4 column quarters, row blocks): 512 workgroups of 256 threads, two per CU, each
+// streaming a 32 KB slab of W_UK[i] (128 rows x 128 columns) with 8 independent 16-byte loads per
+// lane. Column group cg = t % 16 (8 columns), row group ag = t / 16 (8 rows a); the partial sums
+// of the 16 row groups meet in LDS. The first quarter also rotates the rows' position queries
+// while the weights are in flight.
 __global__ void __launch_bounds__(256) absorb_q_gemv(const bf16* __restrict__ q_nope, const bf16* __restrict__ q_rope,
                                                      const int32_t* __restrict__ q_pos, const bf16* __restrict__ w_uk,
                                                      bf16* __restrict__ q_packed, int n_rows, double base) {
   __shared__ float qs[kRowBlock][DN];
-  __shared__ float red[8][kRowBlock][256 + 4];
-  const int i = blockIdx.x, half = blockIdx.y;
+  __shared__ float red[16][kRowBlock][128 + 4];
+  const int i = blockIdx.x, quarter = blockIdx.y;
   const int r0 = blockIdx.z * kRowBlock;
   const int nr = min(kRowBlock, n_rows - r0);
-  const int t = threadIdx.x, cg = t & 31, ag = t >> 5;
-
-  // weights first: 16 independent 16-byte loads per lane
-  const bf16* wp = w_uk + ((size_t)i * DN + ag * 16) * DC + half * 256 + cg * 8;
-  i32x4 wv[16];
+  const int t = threadIdx.x, cg = t & 15, ag = t >> 4;
+  // weights first: 8 independent 16-byte loads per lane
+  const bf16* wp = w_uk + ((size_t)i * DN + ag * 8) * DC + quarter * 128 + cg * 8;
+  i32x4 wv[8];
 #pragma unroll
-  for (int a = 0; a < 16; ++a) wv[a] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(wp + (size_t)a * DC));
-  // while they are in flight: rotate the position part of these rows (blocks of the first half)
-  if (half == 0) {
+  for (int a = 0; a < 8; ++a) wv[a] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(wp + (size_t)a * DC));
+  // while they are in flight: rotate the position part of these rows
+  if (quarter == 0) {
     for (int e = t; e < nr * (DR / 2); e += 256) {
       const int rr = e / (DR / 2), j = e % (DR / 2);
       const size_t r = (size_t)(r0 + rr);
@@ -67,19 +69,18 @@ __global__ void __launch_bounds__(256) absorb_q_gemv(const bf16* __restrict__ q_
     qs[rr][a] = rr < nr ? (float)q_nope[((size_t)(r0 + rr) * H + i) * DN + a] : 0.0f;
   }
   __syncthreads();
-
   float acc[kRowBlock][8];
 #pragma unroll
   for (int rr = 0; rr < kRowBlock; ++rr)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[rr][e] = 0.0f;
 #pragma unroll
-  for (int a = 0; a < 16; ++a) {
+  for (int a = 0; a < 8; ++a) {
     float w[8];
     unpack8(wv[a], w);
 #pragma unroll
     for (int rr = 0; rr < kRowBlock; ++rr) {
-      const float q = qs[rr][ag * 16 + a];
+      const float q = qs[rr][ag * 8 + a];
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[rr][e] = fmaf(w[e], q, acc[rr][e]);
     }
@@ -89,13 +90,14 @@ __global__ void __launch_bounds__(256) absorb_q_gemv(const bf16* __restrict__ q_
 #pragma unroll
     for (int e = 0; e < 8; ++e) red[ag][rr][cg * 8 + e] = acc[rr][e];
   __syncthreads();
-  // thread t sums column t (0..255) over the 8 row groups for each row
-  for (int rr = 0; rr < nr; ++rr) {
-    float s = 0.0f;
+  // thread t < 128 sums column t of the quarter over the 16 row groups for each row
+  if (t < 128)
+    for (int rr = 0; rr < nr; ++rr) {
+      float s = 0.0f;
 #pragma unroll
-    for (int g = 0; g < 8; ++g) s += red[g][rr][t];
-    q_packed[((size_t)(r0 + rr) * H + i) * ROW + half * 256 + t] = (bf16)s;
-  }
+      for (int g = 0; g < 16; ++g) s += red[g][rr][t];
+      q_packed[((size_t)(r0 + rr) * H + i) * ROW + quarter * 128 + t] = (bf16)s;
+    }
 }
 
 // grid (H, 4 quarters of the 128 outputs, row blocks); 4 waves, wave w owns 8 outputs
@@ -179,7 +181,7 @@ bool proj_fast_supported(const LayerDims& L) {
 hipError_t launch_absorb_q_fast(const LayerDims& L, int n_rows, const void* q_nope, const void* q_rope,
                                 const int32_t* q_pos, const void* w_uk, void* q_packed, hipStream_t stream) {
   const int rb = (n_rows + proj::kRowBlock - 1) / proj::kRowBlock;
-  hipLaunchKernelGGL(proj::absorb_q_gemv, dim3(proj::H, 2, rb), dim3(256), 0, stream, (const bf16*)q_nope,
+  hipLaunchKernelGGL(proj::absorb_q_gemv, dim3(proj::H, 4, rb), dim3(256), 0, stream, (const bf16*)q_nope,
                      (const bf16*)q_rope, q_pos, (const bf16*)w_uk, (bf16*)q_packed, n_rows, L.rope_base);
   return hipGetLastError();
 }
