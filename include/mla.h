@@ -145,9 +145,14 @@ mla_status mla_decode_attn(const mla_config* cfg, int32_t batch, int32_t n_q, co
  *  z     float32 [n_rows, H, d_latent] device
  *  w_uv  [H, d_v, d_latent] storage dtype, device (nn.Linear(d_latent, H*d_v).weight)
  *  o     [n_rows, H, d_v] storage dtype, device, written
- *  d_model, w_o, u: the optional W_O projection u = W_O concat_i(o_i) is not provided by this
- *        version; pass d_model = 0, w_o = NULL, u = NULL (anything else returns
- *        MLA_ERR_UNSUPPORTED).
+ *  d_model, w_o, u: optional layer output u = W_O concat_i(o_i) ("Decoupled RoPE · MLA Part 2",
+ *        §5 step 5 and the output line of the §7 forward pass; "从零理解 MLA", section "矩阵吸收").
+ *        d_model = 0 with w_o = u = NULL skips it. With d_model > 0:
+ *          w_o  [d_model, H * d_v] storage dtype, device (nn.Linear(H*d_v, d_model).weight); the
+ *               concatenation is head-major: column i * d_v + v multiplies o[r, i, v]
+ *          u    [n_rows, d_model] storage dtype, device, written (fp32 accumulation over the o
+ *               this call stores, rounded once)
+ *        Any other combination returns MLA_ERR_INVALID_ARG.
  */
 mla_status mla_out_proj(const mla_config* cfg, int32_t n_rows, const float* z, const void* w_uv,
                         void* o, int32_t d_model, const void* w_o, void* u, void* stream);

@@ -207,8 +207,10 @@ mla_status mla_out_proj(const mla_config* cfg, int32_t n_rows, const float* z, c
   mla_status s = check_cfg(cfg, &L);
   if (s != MLA_OK) return s;
   if (n_rows < 0) return fail(MLA_ERR_INVALID_ARG, "n_rows must be >= 0");
-  if (w_o != nullptr || u != nullptr || d_model != 0)
-    return fail(MLA_ERR_UNSUPPORTED, "the W_O projection is not provided; pass d_model = 0, w_o = u = NULL");
+  if (d_model < 0) return fail(MLA_ERR_INVALID_ARG, "d_model must be >= 0, got %d", d_model);
+  const bool with_w_o = d_model > 0;
+  if (with_w_o != (w_o != nullptr) || with_w_o != (u != nullptr))
+    return fail(MLA_ERR_INVALID_ARG, "W_O projection: pass d_model > 0 with w_o and u, or d_model = 0 with both NULL");
   if (n_rows == 0) return ok();
   if (L.n_heads > 65535) return fail(MLA_ERR_UNSUPPORTED, "n_heads %d exceeds 65535", L.n_heads);
   if (!z || !w_uv || !o) return fail(MLA_ERR_INVALID_ARG, "NULL pointer argument");
@@ -224,7 +226,16 @@ mla_status mla_out_proj(const mla_config* cfg, int32_t n_rows, const float* z, c
     e = mla::launch_out_proj_generic<float>(L, n_rows, z, w_uv, o, st);
   else
     e = mla::launch_out_proj_generic<__bf16>(L, n_rows, z, w_uv, o, st);
-  return from_hip(e, "mla_out_proj launch");
+  if (e != hipSuccess || !with_w_o) return from_hip(e, "mla_out_proj launch");
+  // u = W_O concat_i(o_i), from the o just written (same stream)
+  const int K = L.n_heads * L.d_v;
+  if (cfg->dtype == MLA_BF16 && mla::w_o_fast_supported(K) && aligned16(o) && aligned16(w_o))
+    e = mla::launch_w_o_fast(n_rows, d_model, o, w_o, u, st);
+  else if (cfg->dtype == MLA_F32)
+    e = mla::launch_w_o_generic<float>(n_rows, K, d_model, o, w_o, u, st);
+  else
+    e = mla::launch_w_o_generic<__bf16>(n_rows, K, d_model, o, w_o, u, st);
+  return from_hip(e, "mla_out_proj W_O launch");
 }
 
 }  // extern "C"

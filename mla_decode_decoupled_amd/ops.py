@@ -119,8 +119,10 @@ def mla_decode_attn(cfg: MlaConfig, q_packed: torch.Tensor, cache: torch.Tensor,
                               _stream(z)), "mla_decode_attn")
 
 
-def mla_out_proj(cfg: MlaConfig, z: torch.Tensor, w_uv: torch.Tensor, o: torch.Tensor) -> None:
-    """o[r, i] = W_UV,i z[r, i]."""
+def mla_out_proj(cfg: MlaConfig, z: torch.Tensor, w_uv: torch.Tensor, o: torch.Tensor,
+                 w_o: Optional[torch.Tensor] = None, u: Optional[torch.Tensor] = None) -> None:
+    """o[r, i] = W_UV,i z[r, i]; with w_o [d_model, H * d_v] and u [R, d_model] also
+    u[r] = W_O concat_i(o[r, i])."""
     dt = storage_dtype(cfg)
     H = cfg.n_heads
     R = z.shape[0] if z.dim() == 3 else -1
@@ -128,7 +130,17 @@ def mla_out_proj(cfg: MlaConfig, z: torch.Tensor, w_uv: torch.Tensor, o: torch.T
     _need(z, "z", torch.float32, (R, H, cfg.d_latent))
     _need(w_uv, "w_uv", dt, (H, cfg.d_v, cfg.d_latent), dev)
     _need(o, "o", dt, (R, H, cfg.d_v), dev)
-    check(lib.mla_out_proj(cfg, R, _ptr(z), _ptr(w_uv), _ptr(o), 0, None, None, _stream(o)), "mla_out_proj")
+    if (w_o is None) != (u is None):
+        raise ValueError("pass w_o and u together")
+    d_model = 0
+    if w_o is not None:
+        if w_o.dim() != 2:
+            raise ValueError("w_o must be [d_model, n_heads * d_v]")
+        d_model = w_o.shape[0]
+        _need(w_o, "w_o", dt, (d_model, H * cfg.d_v), dev)
+        _need(u, "u", dt, (R, d_model), dev)
+    check(lib.mla_out_proj(cfg, R, _ptr(z), _ptr(w_uv), _ptr(o), d_model, _ptr(w_o), _ptr(u), _stream(o)),
+          "mla_out_proj")
 
 
 def version() -> str:

@@ -99,10 +99,13 @@ def test_workspace_rules():
     assert lib.mla_decode_attn_workspace_size(c, 1, 1, 100, 1) == 0
 
 
-def test_w_o_projection_not_provided():
+def test_w_o_projection_arguments_must_agree():
+    """d_model > 0 needs both w_o and u, d_model = 0 neither; checked before any launch."""
     c = cfg()
-    assert lib.mla_out_proj(c, 1, FAKE, FAKE, FAKE, 7168, FAKE, FAKE, None) == MLA_ERR_UNSUPPORTED
-    assert lib.mla_out_proj(c, 1, FAKE, FAKE, FAKE, 0, None, FAKE, None) == MLA_ERR_UNSUPPORTED
+    for d_model, w_o, u in ((7168, None, FAKE), (7168, FAKE, None), (0, FAKE, None), (0, None, FAKE),
+                            (0, FAKE, FAKE), (-1, None, None), (-5, FAKE, FAKE)):
+        assert lib.mla_out_proj(c, 1, FAKE, FAKE, FAKE, d_model, w_o, u, None) == MLA_ERR_INVALID_ARG, (d_model, w_o, u)
+        assert b"W_O" in lib.mla_last_error() or b"d_model" in lib.mla_last_error()
 
 
 def test_empty_work_returns_ok_without_launch():

@@ -211,6 +211,40 @@ def test_projection_row_counts(n_q):
     assert_close(np32(run.o[0]), o_ref, cfg.dtype, "o from GPU z")
 
 
+@pytest.mark.parametrize("dtype,n_rows,d_model", [("f32", 3, 64), ("bf16", 1, 200), ("bf16", 3, 7168),
+                                                  ("bf16", 40, 300)])
+def test_w_o_projection(dtype, n_rows, d_model):
+    """The optional layer output u = W_O concat_i(o_i) of mla_out_proj, every element against the
+    oracle's output projection of its fp64 o. fp32 (4 heads, d_v 16) takes the generic kernel;
+    the bf16 DeepSeek shape (K = 128 x 128) takes the matrix-vector kernel for 1 and 3 rows (200
+    outputs leave a partial block) and the MFMA GEMM for 40 rows (partial tiles both ways)."""
+    if dtype == "f32":
+        cfg = _small_cfg(220, "f32")
+    else:
+        cfg = MLAConfig(**{**CONFIGS[1].__dict__, "cid": 221})
+    H, dv, dc = cfg.n_heads, cfg.d_v, cfg.d_latent
+    rng = np.random.default_rng(1000 + n_rows)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+
+    def stored(x):   # the values the GPU sees, back on the host in float64
+        t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(tdt)
+        return t, t.to(torch.float64).numpy()
+
+    z = rng.standard_normal((n_rows, H, dc)).astype(np.float32)
+    w_uv_t, w_uv = stored(rng.standard_normal((H, dv, dc)) / np.sqrt(dc))
+    w_o_t, w_o = stored(rng.standard_normal((d_model, H * dv)) / np.sqrt(H * dv))
+    lc = lib_config(cfg)
+    o = torch.empty((n_rows, H, dv), dtype=tdt, device="cuda")
+    u = torch.empty((n_rows, d_model), dtype=tdt, device="cuda")
+    mla.mla_out_proj(lc, torch.from_numpy(z).cuda(), w_uv_t.cuda(), o, w_o_t.cuda(), u)
+    torch.cuda.synchronize()
+    o_ref = O.latent_out_projection(z, w_uv)
+    u_ref = O.output_projection(o_ref, w_o)
+    assert_close(np32(o), o_ref, cfg.dtype, "o")
+    st = assert_close(np32(u), u_ref, cfg.dtype, "u")
+    print(f"u: max {st['max_err']:.2e} relL2 {st['rel_l2']:.2e}", flush=True)
+
+
 # ------------------------------------------------------------------------ edge cases
 def _small_cfg(cid, dtype, n_q=1, batch=1, fixed_len=40, H=4, d_c=32, d_r=8, d=16, rms=False):
     return MLAConfig(cid=cid, name="small", batch=batch, n_heads=H, d_model=64, q_lora=None, d_latent=d_c,

@@ -352,3 +352,23 @@ def test_query_compression_path_uses_library_linear():
     assert np.allclose(p["q_rope_pre"].reshape(10, -1), F.linear(cq, T["w_qr"]).numpy(), atol=1e-12)
     assert np.allclose(p["c"], F.linear(T["h"], T["w_dkv"]).numpy(), atol=1e-12)
     assert np.allclose(p["k_rope_pre"], F.linear(T["h"], T["w_kr"]).numpy(), atol=1e-12)
+
+
+def test_output_projection_concatenates_heads_in_order():
+    """u = W_O concat_i(o_i) with a head-major concatenation ("Decoupled RoPE · MLA Part 2", §5
+    step 5): W_O made of one-hot rows picks single entries o[i, v] (a transposed W_O or a
+    v-major concatenation would pick others), and W_O = [I I ... I], one identity block per head,
+    sums the heads' outputs."""
+    rng = np.random.default_rng(7)
+    R, H, dv = 3, 4, 5
+    o = rng.standard_normal((R, H, dv))
+    picks = [(0, 0), (3, 4), (1, 2), (2, 0), (3, 1), (0, 4)]
+    w_sel = np.zeros((len(picks), H * dv))
+    for n, (i, v) in enumerate(picks):
+        w_sel[n, i * dv + v] = 1.0
+    u = O.output_projection(o, w_sel)
+    assert u.shape == (R, len(picks))
+    for n, (i, v) in enumerate(picks):
+        assert np.array_equal(u[:, n], o[:, i, v])
+    w_sum = np.tile(np.eye(dv), (1, H))
+    assert np.max(np.abs(O.output_projection(o, w_sum) - o.sum(axis=1))) <= 1e-15
