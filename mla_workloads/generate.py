@@ -41,6 +41,7 @@ class TensorId(enum.IntEnum):
     LENGTHS = 13
     W_DQ = 14
     W_UQ = 15
+    KV_NORM = 16
 
 
 def _rng(cfg: MLAConfig, tid: TensorId, *index: int) -> np.random.Generator:
@@ -141,7 +142,9 @@ def full_layer_inputs(cfg: MLAConfig, n_tokens: int) -> Dict[str, np.ndarray]:
     Keys: h [n, d_model]; w_dkv [d_latent, d_model]; w_kr [d_rope, d_model];
     either w_q [H*d_nope, d_model] (no query compression) or w_dq [q_lora, d_model]
     and w_uq [H*d_nope, q_lora]; w_qr [H*d_rope, d_model or q_lora];
-    w_uk, w_uv per head; w_o.
+    w_uk, w_uv per head; w_o; and, when the configuration RMS-normalises the latent,
+    kv_norm_w [d_latent] ~ 1 + 0.25 N(0, 1) (a trained-looking gain rather than the
+    all-ones initial value, so that a dropped gain shows).
     """
     H, dm = cfg.n_heads, cfg.d_model
     out = {
@@ -152,6 +155,8 @@ def full_layer_inputs(cfg: MLAConfig, n_tokens: int) -> Dict[str, np.ndarray]:
         "w_uv": weight_uv(cfg),
         "w_o": weight_o(cfg),
     }
+    if cfg.latent_rms_norm:
+        out["kv_norm_w"] = _store(cfg, 1.0 + _normal(cfg, TensorId.KV_NORM, (cfg.d_latent,), 0.25))
     if cfg.q_lora is None:
         out["w_q"] = _store(cfg, _normal(cfg, TensorId.W_Q, (H * cfg.d_nope, dm), 1.0 / np.sqrt(dm)))
         out["w_qr"] = _store(cfg, _normal(cfg, TensorId.W_QR, (H * cfg.d_rope, dm), 1.0 / np.sqrt(dm)))

@@ -16,6 +16,7 @@ from .mla_oracle import (  # noqa: F401
     packed_query,
     latent_attention,
     latent_out_projection,
+    rms_norm,
     project_inputs,
     full_layer,
 )

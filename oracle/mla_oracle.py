@@ -231,18 +231,42 @@ def latent_out_projection(z, w_uv) -> np.ndarray:
 
 
 # -------------------------------------------------------------- whole layer
-def project_inputs(h, weights: Dict[str, np.ndarray], n_heads: int) -> Dict[str, np.ndarray]:
+def rms_norm(x, weight=None, eps: float = 1e-6) -> np.ndarray:
+    """RMSNorm over the last axis: x / sqrt(mean(x^2) + eps), then times ``weight``.
+
+    The definition is the RMSNorm class of "hands-on DeepSeek MLA" (mean of squares
+    over the hidden axis, reciprocal square root with eps, elementwise weight that
+    starts at ones); "构建DeepSeek-V3：MLA 架构" step 1 applies it to the compressed
+    latent, c_KV = RMSNorm(W_dkv x), and "从零理解 MLA" (engineering notes after the
+    decoupled-RoPE check) says the paper adds it after the compressed latent. Here
+    everything stays in float64 (the page's class casts to float32 first).
+    """
+    x = np.asarray(x, dtype=_F)
+    y = x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + _F(eps))
+    if weight is not None:
+        y = y * np.asarray(weight, dtype=_F)
+    return y
+
+
+def project_inputs(h, weights: Dict[str, np.ndarray], n_heads: int,
+                   kv_norm_eps: float = 1e-6) -> Dict[str, np.ndarray]:
     """Projections from hidden states to the attention's inputs.
 
     c = W_DKV h, k_R(pre-rotation) = W_KR h ("Decoupled RoPE · MLA Part 2", §5 and
-    §4.2: the position key comes from h, not from c). Content query q_C = W_Q h, or
-    W_UQ W_DQ h with query compression; position query from h, or from the
-    compressed query c_Q ("从零理解 MLA", sections "查询压缩" and "解耦 RoPE").
+    §4.2: the position key comes from h, not from c). When ``weights`` holds
+    ``kv_norm_w`` the latent is RMS-normalised with that weight, c = RMSNorm(W_DKV h)
+    ("构建DeepSeek-V3：MLA 架构", step 1 and the kv_norm(kv_proj(x)) line of its
+    forward pass); without it c is the plain projection, as in the first page's code.
+    Content query q_C = W_Q h, or W_UQ W_DQ h with query compression; position query
+    from h, or from the compressed query c_Q ("从零理解 MLA", sections "查询压缩" and
+    "解耦 RoPE"; "构建DeepSeek-V3：MLA 架构", q_rope = RoPE(W_qr c_Q), with no norm on c_Q).
     """
     h = np.asarray(h, dtype=_F)
     W = {k: np.asarray(v, dtype=_F) for k, v in weights.items()}
     n = h.shape[0]
     c = h @ W["w_dkv"].T
+    if "kv_norm_w" in W:
+        c = rms_norm(c, W["kv_norm_w"], kv_norm_eps)
     k_rope_pre = h @ W["w_kr"].T
     if "w_q" in W:
         q_c = h @ W["w_q"].T
@@ -261,13 +285,13 @@ def project_inputs(h, weights: Dict[str, np.ndarray], n_heads: int) -> Dict[str,
 
 def full_layer(h, weights: Dict[str, np.ndarray], *, n_heads: int, scale: float, base: float,
                n_q: Optional[int] = None, layout: str = "interleaved",
-               keep_scores: bool = False) -> Dict[str, np.ndarray]:
+               keep_scores: bool = False, kv_norm_eps: float = 1e-6) -> Dict[str, np.ndarray]:
     """Whole attention layer from hidden states h [n, d_model].
 
     The last ``n_q`` tokens (all of them by default, i.e. the square causal mask of a
     full forward) are the query rows; every token is a key.
     """
-    p = project_inputs(h, weights, n_heads)
+    p = project_inputs(h, weights, n_heads, kv_norm_eps)
     n = p["c"].shape[0]
     n_q = n if n_q is None else n_q
     res = explicit_attention(p["c"], p["k_rope_pre"], p["q_nope"][n - n_q:], p["q_rope_pre"][n - n_q:],

@@ -372,3 +372,53 @@ def test_output_projection_concatenates_heads_in_order():
         assert np.array_equal(u[:, n], o[:, i, v])
     w_sum = np.tile(np.eye(dv), (1, H))
     assert np.max(np.abs(O.output_projection(o, w_sum) - o.sum(axis=1))) <= 1e-15
+
+
+# ------------------------------------------------------------- latent RMSNorm
+def test_rms_norm_matches_library_routine():
+    """RMSNorm as defined by the RMSNorm class of "hands-on DeepSeek MLA" is the routine torch
+    ships as torch.nn.functional.rms_norm (float64 here, no float32 cast)."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((5, 32)) * 3.0
+    w = 1.0 + 0.25 * rng.standard_normal(32)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (32,), torch.from_numpy(w), 1e-6).numpy()
+    assert np.max(np.abs(O.rms_norm(x, w, 1e-6) - ref)) <= 1e-12
+
+
+def test_rms_norm_closed_forms():
+    eps = 1e-6
+    w = np.arange(1.0, 9.0)
+    # a constant vector a*1 has RMS |a|: every entry becomes a / sqrt(a^2 + eps), times the gain
+    for a in (2.5, -0.75):
+        y = O.rms_norm(np.full(8, a), w, eps)
+        assert np.max(np.abs(y - w * a / math.sqrt(a * a + eps))) <= 1e-15
+    # [3, 4]: mean of squares 12.5
+    assert np.max(np.abs(O.rms_norm(np.array([3.0, 4.0]), None, 0.0) - np.array([3.0, 4.0]) / math.sqrt(12.5))) <= 1e-15
+    # eps = 0 and a unit gain: RMS exactly 1 per row, and a positive rescaling of the input changes nothing
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((4, 64))
+    y = O.rms_norm(x, None, 0.0)
+    assert np.max(np.abs(np.sqrt(np.mean(y * y, axis=-1)) - 1.0)) <= 1e-14
+    assert np.max(np.abs(O.rms_norm(7.0 * x, None, 0.0) - y)) <= 1e-14
+
+
+def test_normalised_latent_projection_uses_library_routines():
+    """c = RMSNorm(W_DKV h) ("构建DeepSeek-V3：MLA 架构", step 1) when the weights carry the
+    latent's norm gain; the position key and the queries are not normalised."""
+    torch = pytest.importorskip("torch")
+    F = torch.nn.functional
+    cfg = MLAConfig(cid=78, name="toy", batch=1, n_heads=4, d_model=128, q_lora=48, d_latent=32, d_rope=8,
+                    d_nope=16, d_v=16, n_q=6, dtype="f32", fixed_len=6, latent_rms_norm=True)
+    w = G.full_layer_inputs(cfg, 6)
+    assert "kv_norm_w" in w and np.std(w["kv_norm_w"]) > 0.1
+    p = O.project_inputs(w["h"], w, 4, kv_norm_eps=1e-6)
+    T = {k: torch.from_numpy(np.asarray(v, dtype=np.float64)) for k, v in w.items()}
+    c_ref = F.rms_norm(F.linear(T["h"], T["w_dkv"]), (32,), T["kv_norm_w"], 1e-6).numpy()
+    assert np.max(np.abs(p["c"] - c_ref)) <= 1e-12
+    assert np.allclose(p["k_rope_pre"], F.linear(T["h"], T["w_kr"]).numpy(), atol=1e-12)
+    cq = F.linear(T["h"], T["w_dq"])
+    assert np.allclose(p["q_nope"].reshape(6, -1), F.linear(cq, T["w_uq"]).numpy(), atol=1e-12)
+    # the whole layer uses the normalised latent for keys, values and the cache
+    full = O.full_layer(w["h"], w, n_heads=4, scale=cfg.softmax_scale, base=cfg.rope_base)
+    assert np.max(np.abs(full["c"] - c_ref)) <= 1e-12
