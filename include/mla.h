@@ -157,6 +157,74 @@ mla_status mla_decode_attn(const mla_config* cfg, int32_t batch, int32_t n_q, co
 mla_status mla_out_proj(const mla_config* cfg, int32_t n_rows, const float* z, const void* w_uv,
                         void* o, int32_t d_model, const void* w_o, void* u, void* stream);
 
+/*
+ * ---- Upstream projections: from the hidden state h to the inputs of the calls above.
+ *
+ * Bytes of device workspace mla_project_kv_append (d_q = 0) or mla_project_q (its d_q) needs
+ * for n_rows tokens; take the larger of the two to share one buffer. 0 for invalid arguments.
+ */
+size_t mla_project_workspace_size(const mla_config* cfg, int32_t n_rows, int32_t d_model, int32_t d_q);
+
+/*
+ * mla_project_kv_append — cache side of the layer from h ("Decoupled RoPE · MLA Part 2", §5
+ * steps 2–3: the latent and the position key both come from h, and the key is rotated once when
+ * stored; "构建DeepSeek-V3：MLA 架构", step 1: the compressed latent is RMS-normalised,
+ * c_KV = RMSNorm(W_dkv x), with the RMSNorm of "hands-on DeepSeek MLA").
+ *
+ * For b < batch, i < n_new, with x = h[b, i, :] and p = len_before[b] + i:
+ *   c    = W_DKV x, then, when kv_norm_w != NULL, c = kv_norm_w * c / sqrt(mean(c^2) + kv_norm_eps)
+ *   k_R  = W_KR x
+ *   cache[seq_off[b] + p] = [ c ; RoPE_p(k_R) ]        (as mla_rope_append stores it)
+ *  h          [batch, n_new, d_model]  storage dtype, device
+ *  w_dkv      [d_latent, d_model]      storage dtype, device (nn.Linear(d_model, d_latent).weight)
+ *  w_kr       [d_rope, d_model]        storage dtype, device; may be NULL when d_rope = 0
+ *  kv_norm_w  [d_latent] storage dtype, device, the RMSNorm gain; NULL = no normalisation
+ *  kv_norm_eps  >= 0, finite (1e-6 in the pages' RMSNorm); ignored without kv_norm_w
+ *  cache, seq_off, len_before  as for mla_rope_append
+ *  workspace  device scratch of at least mla_project_workspace_size(cfg, batch * n_new, d_model, 0)
+ *             bytes (float32 projections before the norm and the rotation); no initialisation
+ * Products accumulate in float32, the norm is taken in float32, the rotation in float64, and each
+ * stored value is rounded once.
+ */
+mla_status mla_project_kv_append(const mla_config* cfg, int32_t batch, int32_t n_new, int32_t d_model,
+                                 const void* h, const void* w_dkv, const void* w_kr, const void* kv_norm_w,
+                                 float kv_norm_eps, void* cache, const int64_t* seq_off,
+                                 const int32_t* len_before, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/*
+ * mla_project_q — query side of the layer from h ("从零理解 MLA", sections "查询压缩" and
+ * "解耦 RoPE": the content query comes from the compressed c_Q, and so does the position query;
+ * "构建DeepSeek-V3：MLA 架构", q_rope = RoPE(W_qr c_Q), with no norm on c_Q).
+ *
+ * With query compression (d_q > 0):  c_Q = W_DQ h;  q_nope = W_UQ c_Q;  q_rope = W_QR c_Q.
+ * Without (d_q = 0, w_dq = NULL):     q_nope = W_UQ h;  q_rope = W_QR h (W_UQ is then W_Q).
+ * The outputs are exactly mla_absorb_q's inputs: q_rope is NOT rotated here.
+ *  h        [n_rows, d_model] storage dtype, device
+ *  w_dq     [d_q, d_model] storage dtype, device, or NULL when d_q = 0
+ *  w_uq     [H * d_nope, d_q or d_model] storage dtype, device (rows head-major)
+ *  w_qr     [H * d_rope, d_q or d_model] storage dtype, device; may be NULL when d_rope = 0
+ *  q_nope   [n_rows, H, d_nope] storage dtype, device, written
+ *  q_rope   [n_rows, H, d_rope] storage dtype, device, written; may be NULL when d_rope = 0
+ *  workspace  device scratch of at least mla_project_workspace_size(cfg, n_rows, d_model, d_q)
+ *           bytes when d_q > 0 (c_Q, rounded once to the storage dtype); ignored when d_q = 0
+ */
+mla_status mla_project_q(const mla_config* cfg, int32_t n_rows, int32_t d_model, int32_t d_q,
+                         const void* h, const void* w_dq, const void* w_uq, const void* w_qr,
+                         void* q_nope, void* q_rope, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/*
+ * mla_decode_advance — cache growth between decode steps ("从零理解 MLA", the token-by-token
+ * decode loop of its decoupled-RoPE check: every step appends the new token and the next one
+ * attends to one more key). On the device, enqueued on `stream`:
+ *   len_before[b] += n_new and seq_len[b] += n_new for b < batch;  q_pos[r] += n_new for r < n_rows.
+ * Any of the three arrays may be NULL (left alone). With the other calls enqueued on the same
+ * stream, one recorded step (a captured HIP graph) can be replayed for the next token.
+ */
+mla_status mla_decode_advance(int32_t batch, int32_t n_new, int32_t* len_before, int32_t* seq_len,
+                              int32_t n_rows, int32_t* q_pos, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

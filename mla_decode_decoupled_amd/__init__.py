@@ -12,5 +12,9 @@ from .ops import (  # noqa: F401
     mla_decode_attn_workspace_size,
     mla_decode_attn,
     mla_out_proj,
+    mla_project_workspace_size,
+    mla_project_kv_append,
+    mla_project_q,
+    mla_decode_advance,
     version,
 )

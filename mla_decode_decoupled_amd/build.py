@@ -1,6 +1,7 @@
 """Build libmla.so in-tree with hipcc for gfx950.
 
-Usage: python -m mla_decode_decoupled_amd.build [--debug]
+Usage: python mla_decode_decoupled_amd/build.py [--debug]
+(run by path: importing the package first would load the library being replaced)
 """
 
 from __future__ import annotations
@@ -13,7 +14,7 @@ import sys
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_PATH = os.path.join(PKG_DIR, "libmla.so")
-SOURCES = ["api.hip", "generic.hip", "decode_fast.hip", "proj_fast.hip", "proj_gemm.hip", "proj_wo.hip"]
+SOURCES = ["api.hip", "generic.hip", "decode_fast.hip", "proj_fast.hip", "proj_gemm.hip", "proj_wo.hip", "linear.hip"]
 
 # Packed-FP32 instructions (v_pk_*_f32) are switched off for every device pass: the compiler
 # otherwise forms them from plain float code, and the kernels are validated without them.

@@ -3,6 +3,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdint.h>
 #include <string.h>
 
 #include "../../include/mla.h"
@@ -236,6 +237,87 @@ mla_status mla_out_proj(const mla_config* cfg, int32_t n_rows, const float* z, c
   else
     e = mla::launch_w_o_generic<__bf16>(n_rows, K, d_model, o, w_o, u, st);
   return from_hip(e, "mla_out_proj W_O launch");
+}
+
+size_t mla_project_workspace_size(const mla_config* cfg, int32_t n_rows, int32_t d_model, int32_t d_q) {
+  mla::LayerDims L;
+  if (check_cfg(cfg, &L) != MLA_OK) return 0;
+  if (n_rows <= 0 || d_model <= 0 || d_q < 0) return 0;
+  return mla::project_workspace_bytes(L, n_rows, d_q, cfg->dtype == MLA_F32 ? 4 : 2);
+}
+
+mla_status mla_project_kv_append(const mla_config* cfg, int32_t batch, int32_t n_new, int32_t d_model, const void* h,
+                                 const void* w_dkv, const void* w_kr, const void* kv_norm_w, float kv_norm_eps,
+                                 void* cache, const int64_t* seq_off, const int32_t* len_before, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  mla::LayerDims L;
+  mla_status s = check_cfg(cfg, &L);
+  if (s != MLA_OK) return s;
+  if (batch < 0 || n_new < 0) return fail(MLA_ERR_INVALID_ARG, "batch and n_new must be >= 0");
+  if (d_model < 1) return fail(MLA_ERR_INVALID_ARG, "d_model must be >= 1, got %d", d_model);
+  if (kv_norm_w != nullptr && (!(kv_norm_eps >= 0.0f) || !isfinite(kv_norm_eps)))
+    return fail(MLA_ERR_INVALID_ARG, "kv_norm_eps must be finite and >= 0");
+  if (batch == 0 || n_new == 0) return ok();
+  if (batch > 65535) return fail(MLA_ERR_UNSUPPORTED, "batch %d exceeds 65535", batch);
+  if ((int64_t)batch * n_new > (int64_t)INT32_MAX / 2) return fail(MLA_ERR_UNSUPPORTED, "batch * n_new too large");
+  if (!h || !w_dkv || !cache || !seq_off || !len_before || (L.d_rope > 0 && !w_kr))
+    return fail(MLA_ERR_INVALID_ARG, "NULL pointer argument");
+  const size_t need = mla::project_workspace_bytes(L, batch * n_new, 0, cfg->dtype == MLA_F32 ? 4 : 2);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu%s", need, workspace_bytes,
+                workspace ? "" : " (NULL)");
+  hipStream_t st = (hipStream_t)stream;
+  const int use_norm = kv_norm_w != nullptr;
+  hipError_t e = cfg->dtype == MLA_F32
+                     ? mla::launch_project_kv_append<float>(L, batch, n_new, d_model, h, w_dkv, w_kr, kv_norm_w,
+                                                            kv_norm_eps, use_norm, cache, seq_off, len_before,
+                                                            workspace, st)
+                     : mla::launch_project_kv_append<__bf16>(L, batch, n_new, d_model, h, w_dkv, w_kr, kv_norm_w,
+                                                             kv_norm_eps, use_norm, cache, seq_off, len_before,
+                                                             workspace, st);
+  return from_hip(e, "mla_project_kv_append launch");
+}
+
+mla_status mla_project_q(const mla_config* cfg, int32_t n_rows, int32_t d_model, int32_t d_q, const void* h,
+                         const void* w_dq, const void* w_uq, const void* w_qr, void* q_nope, void* q_rope,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  mla::LayerDims L;
+  mla_status s = check_cfg(cfg, &L);
+  if (s != MLA_OK) return s;
+  if (n_rows < 0) return fail(MLA_ERR_INVALID_ARG, "n_rows must be >= 0");
+  if (d_model < 1 || d_q < 0) return fail(MLA_ERR_INVALID_ARG, "need d_model >= 1 and d_q >= 0, got %d, %d", d_model, d_q);
+  if ((d_q > 0) != (w_dq != nullptr))
+    return fail(MLA_ERR_INVALID_ARG, "pass w_dq exactly when d_q > 0 (query compression)");
+  if (n_rows == 0) return ok();
+  if (n_rows > 65535 * 4) return fail(MLA_ERR_UNSUPPORTED, "n_rows %d exceeds %d", n_rows, 65535 * 4);
+  if ((int64_t)L.n_heads * (L.d_nope + L.d_rope) > (int64_t)INT32_MAX / 8)
+    return fail(MLA_ERR_UNSUPPORTED, "query projection too wide");
+  if (!h || !w_uq || !q_nope || (L.d_rope > 0 && (!w_qr || !q_rope)))
+    return fail(MLA_ERR_INVALID_ARG, "NULL pointer argument");
+  if (d_q > 0) {
+    const size_t need = mla::project_workspace_bytes(L, n_rows, d_q, cfg->dtype == MLA_F32 ? 4 : 2);
+    if (workspace == nullptr || workspace_bytes < need)
+      return fail(MLA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu%s", need, workspace_bytes,
+                  workspace ? "" : " (NULL)");
+  }
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = cfg->dtype == MLA_F32
+                     ? mla::launch_project_q<float>(L, n_rows, d_model, d_q, h, w_dq, w_uq, w_qr, q_nope, q_rope,
+                                                    workspace, st)
+                     : mla::launch_project_q<__bf16>(L, n_rows, d_model, d_q, h, w_dq, w_uq, w_qr, q_nope, q_rope,
+                                                     workspace, st);
+  return from_hip(e, "mla_project_q launch");
+}
+
+mla_status mla_decode_advance(int32_t batch, int32_t n_new, int32_t* len_before, int32_t* seq_len, int32_t n_rows,
+                              int32_t* q_pos, void* stream) {
+  if (batch < 0 || n_rows < 0 || n_new < 0) return fail(MLA_ERR_INVALID_ARG, "batch, n_new and n_rows must be >= 0");
+  const bool any_b = batch > 0 && (len_before != nullptr || seq_len != nullptr);
+  const bool any_q = n_rows > 0 && q_pos != nullptr;
+  if (n_new == 0 || (!any_b && !any_q)) return ok();
+  hipError_t e = mla::launch_decode_advance(any_b ? batch : 0, n_new, len_before, seq_len, any_q ? n_rows : 0, q_pos,
+                                            (hipStream_t)stream);
+  return from_hip(e, "mla_decode_advance launch");
 }
 
 }  // extern "C"

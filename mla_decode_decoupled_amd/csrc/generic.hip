@@ -356,6 +356,29 @@ hipError_t launch_out_proj_generic(const LayerDims& L, int n_rows, const float* 
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------- decode advance
+// After a decode step that appended n_new tokens to every sequence, the next step's append
+// position, key count and query positions each move on by n_new (the cache grows by the tokens
+// just written; "从零理解 MLA", decode loop of the decoupled-RoPE check). One thread per entry.
+__global__ void __launch_bounds__(256) decode_advance(int batch, int n_new, int32_t* __restrict__ len_before,
+                                                      int32_t* __restrict__ seq_len, int n_rows,
+                                                      int32_t* __restrict__ q_pos) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < batch) {
+    if (len_before != nullptr) len_before[i] += n_new;
+    if (seq_len != nullptr) seq_len[i] += n_new;
+  }
+  if (i < n_rows && q_pos != nullptr) q_pos[i] += n_new;
+}
+
+hipError_t launch_decode_advance(int batch, int n_new, int32_t* len_before, int32_t* seq_len, int n_rows,
+                                 int32_t* q_pos, hipStream_t stream) {
+  const int n = batch > n_rows ? batch : n_rows;
+  hipLaunchKernelGGL(decode_advance, dim3((n + 255) / 256), dim3(256), 0, stream, batch, n_new, len_before, seq_len,
+                     n_rows, q_pos);
+  return hipGetLastError();
+}
+
 #define MLA_INSTANTIATE(T)                                                                                        \
   template hipError_t launch_rope_append_generic<T>(const LayerDims&, int, int, const void*, const void*, void*,  \
                                                     const int64_t*, const int32_t*, hipStream_t);                \

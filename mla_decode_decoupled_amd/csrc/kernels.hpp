@@ -79,4 +79,21 @@ hipError_t launch_absorb_q_gemm(const LayerDims& L, int n_rows, const void* q_no
 hipError_t launch_out_proj_gemm(const LayerDims& L, int n_rows, const float* z, const void* w_uv, void* o,
                                 hipStream_t stream);
 
+// Upstream projections from the hidden state (linear.hip): workspace bytes, the kv side
+// (W_DKV / W_KR -> RMSNorm -> RoPE -> cache rows) and the query side (W_DQ -> W_UQ / W_QR)
+size_t project_workspace_bytes(const LayerDims& L, int n_rows, int d_q, int elem_bytes);
+template <typename T>
+hipError_t launch_project_kv_append(const LayerDims& L, int batch, int n_new, int d_model, const void* h,
+                                    const void* w_dkv, const void* w_kr, const void* norm_w, float eps, int use_norm,
+                                    void* cache, const int64_t* seq_off, const int32_t* len_before, void* workspace,
+                                    hipStream_t stream);
+template <typename T>
+hipError_t launch_project_q(const LayerDims& L, int n_rows, int d_model, int d_q, const void* h, const void* w_dq,
+                            const void* w_uq, const void* w_qr, void* q_nope, void* q_rope, void* workspace,
+                            hipStream_t stream);
+
+// Position bookkeeping between decode steps (generic.hip)
+hipError_t launch_decode_advance(int batch, int n_new, int32_t* len_before, int32_t* seq_len, int n_rows,
+                                 int32_t* q_pos, hipStream_t stream);
+
 }  // namespace mla

@@ -1,0 +1,374 @@
+// Upstream projections of one MLA layer: from the hidden state h to the inputs of the cache append
+// and of the query absorption.
+//   kv side ("Decoupled RoPE · MLA Part 2", §5 steps 2–3; "构建DeepSeek-V3：MLA 架构", step 1):
+//     c = RMSNorm(W_DKV h) (the norm is optional), k_R = RoPE_p(W_KR h), stored as the token's
+//     packed cache row [c ; k_R];
+//   query side ("从零理解 MLA", sections "查询压缩" and "解耦 RoPE"; "构建DeepSeek-V3：MLA 架构",
+//     query compression): c_Q = W_DQ h, q_C = W_UQ c_Q, q_R = W_QR c_Q (unrotated; mla_absorb_q
+//     rotates it), or q_C = W_Q h, q_R = W_QR h without query compression.
+//
+// Every product is a linear layer y[r, n] = sum_k x[r, k] W[n, k] with W in nn.Linear's [out, in]
+// layout. Two weights that read the same x (W_DKV and W_KR; W_UQ and W_QR) run as one launch over
+// their concatenated rows ("segments"), each segment writing its own output. Three kernels:
+//   * lin_generic: any shape and dtype, one wave per output column;
+//   * lin_gemv (bf16, few rows): weight-bandwidth bound. A wave owns RW weight rows, its lanes
+//     stream them with nontemporal 16-byte loads (several per lane in flight) next to the matching
+//     pieces of the RB activation rows (read through the caches, where every workgroup finds them);
+//   * lin_gemm (bf16, many rows): MFMA 32x32x16, 128 x 128 outputs per workgroup, both operands
+//     K-contiguous and staged through padded LDS rows, the next K step's loads in flight during the
+//     MFMAs.
+// Accumulation is float32; each output is rounded once to its type.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace mla {
+namespace lin {
+
+// output columns [0, n1) come from weight w1 and go to y1 (row stride ldy1); [n1, n) from w2 / y2
+struct Seg2 {
+  const void* w1;
+  const void* w2;
+  void* y1;
+  void* y2;
+  int n1, n, ldy1, ldy2;
+};
+
+template <typename T>
+__device__ __forceinline__ const T* wrow(const Seg2& s, int n, int K) {
+  return n < s.n1 ? (const T*)s.w1 + (size_t)n * K : (const T*)s.w2 + (size_t)(n - s.n1) * K;
+}
+template <typename Ty>
+__device__ __forceinline__ void ystore(const Seg2& s, int r, int n, float v) {
+  if (n < s.n1)
+    ((Ty*)s.y1)[(size_t)r * s.ldy1 + n] = from_f32<Ty>(v);
+  else
+    ((Ty*)s.y2)[(size_t)r * s.ldy2 + (n - s.n1)] = from_f32<Ty>(v);
+}
+
+// ---------------------------------------------------------------- generic
+// grid (ceil(n / 4), min(M, 65535)), 256 threads: wave w computes column 4 blockIdx.x + w for rows
+// blockIdx.y, blockIdx.y + gridDim.y, ...
+template <typename T, typename Ty>
+__global__ void __launch_bounds__(256) lin_generic(const T* __restrict__ x, int ldx, int M, int K, Seg2 s) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int n = blockIdx.x * 4 + w;
+  if (n >= s.n) return;
+  const T* wr = wrow<T>(s, n, K);
+  for (int r = blockIdx.y; r < M; r += gridDim.y) {
+    const T* xr = x + (size_t)r * ldx;
+    float acc = 0.0f;
+    for (int k = lane; k < K; k += 64) acc = fmaf(to_f32(wr[k]), to_f32(xr[k]), acc);
+    acc = warp_sum(acc);
+    if (lane == 0) ystore<Ty>(s, r, n, acc);
+  }
+}
+
+__device__ __forceinline__ void unpack8(const i32x4 v, float* f) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t u = (uint32_t)v[e];
+    f[2 * e] = __uint_as_float(u << 16);
+    f[2 * e + 1] = __uint_as_float(u & 0xFFFF0000u);
+  }
+}
+
+// ---------------------------------------------------------------- few rows
+// grid (ceil(n / (4 RW)), ceil(M / RB)), 256 threads. Wave w owns weight rows
+// (4 blockIdx.x + w) RW .. +RW-1 and activation rows RB blockIdx.y .. +RB-1; lane l takes the
+// 16-byte pieces l, l + 64, ... of each row (K % 8 == 0, x and W 16-byte aligned, ldx % 8 == 0).
+constexpr int kGemvU = 4;   // pieces per lane per step: RW * kGemvU weight loads in flight
+template <int RW, int RB, typename Ty>
+__global__ void __launch_bounds__(256) lin_gemv(const bf16* __restrict__ x, int ldx, int M, int K, Seg2 s) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r0 = blockIdx.y * RB, nr = min(RB, M - r0);
+  const int nb = (blockIdx.x * 4 + w) * RW;
+  if (nb >= s.n) return;
+  const int KP = K / 8;
+  const bf16* wr[RW];
+  bool ok[RW];
+#pragma unroll
+  for (int q = 0; q < RW; ++q) {
+    ok[q] = nb + q < s.n;
+    wr[q] = wrow<bf16>(s, ok[q] ? nb + q : nb, K);
+  }
+  const bf16* xr[RB];
+#pragma unroll
+  for (int rr = 0; rr < RB; ++rr) xr[rr] = x + (size_t)(r0 + (rr < nr ? rr : 0)) * ldx;
+  float acc[RW][RB];
+#pragma unroll
+  for (int q = 0; q < RW; ++q)
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr) acc[q][rr] = 0.0f;
+#pragma unroll 1
+  for (int p0 = 0; p0 < KP; p0 += 64 * kGemvU) {
+    i32x4 wv[RW][kGemvU], xv[RB][kGemvU];
+#pragma unroll
+    for (int u = 0; u < kGemvU; ++u) {
+      const int p = p0 + 64 * u + lane;
+      const bool in = p < KP;
+#pragma unroll
+      for (int q = 0; q < RW; ++q)
+        wv[q][u] = in && ok[q] ? __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(wr[q] + 8 * p))
+                               : i32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int rr = 0; rr < RB; ++rr)
+        xv[rr][u] = in && rr < nr ? *reinterpret_cast<const i32x4*>(xr[rr] + 8 * p) : i32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < kGemvU; ++u) {
+      float xf[RB][8];
+#pragma unroll
+      for (int rr = 0; rr < RB; ++rr) unpack8(xv[rr][u], xf[rr]);
+#pragma unroll
+      for (int q = 0; q < RW; ++q) {
+        float wf[8];
+        unpack8(wv[q][u], wf);
+#pragma unroll
+        for (int rr = 0; rr < RB; ++rr)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[q][rr] = fmaf(wf[e], xf[rr][e], acc[q][rr]);
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < RW; ++q)
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr) {
+      const float v = warp_sum(acc[q][rr]);
+      if (lane == 0 && ok[q] && rr < nr) ystore<Ty>(s, r0 + rr, nb + q, v);
+    }
+}
+
+// ---------------------------------------------------------------- many rows
+typedef __bf16 bf16x8e __attribute__((ext_vector_type(8)));
+typedef float f32x16e __attribute__((ext_vector_type(16)));
+
+constexpr int TM = 128, TN = 128, TK = 32;
+constexpr int SROW = TK + 8;   // bf16 per staged row (80 bytes: 16 lanes of a 16-byte read hit 16 bank groups)
+constexpr int GEMM_LDS = 2 * 2 * TM * SROW * 2;   // two buffers of the A and B tiles
+
+// grid (ceil(n / 128), ceil(M / 128)), 256 threads, GEMM_LDS dynamic LDS; K % 32 == 0.
+// Wave w computes rows 64 (w / 2) .. +63 and columns 64 (w % 2) .. +63 of the tile: 2 x 2 MFMA
+// blocks of 32 x 32. Per K step of 32, every thread moves 2 x 16 bytes of A (x rows) and of B
+// (weight rows) global -> registers -> LDS; the next step's loads are in flight during the MFMAs.
+template <typename Ty>
+__global__ void __launch_bounds__(256) lin_gemm(const bf16* __restrict__ x, int ldx, int M, int K, Seg2 s) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  bf16* As = reinterpret_cast<bf16*>(smem);   // [2][TM][SROW]
+  bf16* Bs = As + 2 * TM * SROW;              // [2][TN][SROW]
+  const int m0 = blockIdx.y * TM, n0 = blockIdx.x * TN;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
+  // loader: thread t moves rows t / 4 and 64 + t / 4, 16-byte piece t % 4 of each K step
+  const int lr = t >> 2, lc = (t & 3) * 8;
+  const bf16* ga[2];
+  const bf16* gb[2];
+  bool va[2], vb[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int ra = m0 + lr + 64 * h, rb = n0 + lr + 64 * h;
+    va[h] = ra < M;
+    vb[h] = rb < s.n;
+    ga[h] = x + (size_t)(va[h] ? ra : 0) * ldx + lc;
+    gb[h] = wrow<bf16>(s, vb[h] ? rb : 0, K) + lc;
+  }
+  i32x4 ra_[2], rb_[2];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      ra_[h] = va[h] ? *reinterpret_cast<const i32x4*>(ga[h] + k0) : i32x4{0, 0, 0, 0};
+      rb_[h] = vb[h] ? *reinterpret_cast<const i32x4*>(gb[h] + k0) : i32x4{0, 0, 0, 0};
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      *reinterpret_cast<i32x4*>(As + ((size_t)buf * TM + lr + 64 * h) * SROW + lc) = ra_[h];
+      *reinterpret_cast<i32x4*>(Bs + ((size_t)buf * TN + lr + 64 * h) * SROW + lc) = rb_[h];
+    }
+  };
+  f32x16e acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16e{};
+  const int wm = 64 * (w >> 1), wn = 64 * (w & 1);
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  const int NK = K / TK;
+  for (int kt = 0; kt < NK; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < NK) gload((kt + 1) * TK);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8e af[2], bfr[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        af[i] = *reinterpret_cast<const bf16x8e*>(As + ((size_t)buf * TM + wm + 32 * i + l32) * SROW + 16 * ks + 8 * g);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        bfr[j] = *reinterpret_cast<const bf16x8e*>(Bs + ((size_t)buf * TN + wn + 32 * j + l32) * SROW + 16 * ks + 8 * g);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < NK) {
+      lstore(buf ^ 1);   // the other buffer was last read before the previous barrier
+      __syncthreads();
+    }
+  }
+  // D block (i, j): lane holds column n = l32, rows 8 q + 4 g + e (register 4 q + e)
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = n0 + wn + 32 * j + l32;
+      if (n >= s.n) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = m0 + wm + 32 * i + 8 * q + 4 * g + e;
+          if (m < M) ystore<Ty>(s, m, n, acc[i][j][4 * q + e]);
+        }
+    }
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// y = x W^T over the two segments; Ty is float or the storage type T
+template <typename T, typename Ty>
+hipError_t linear(const T* x, int ldx, int M, int K, const Seg2& s, hipStream_t stream) {
+  if (M <= 0 || s.n <= 0) return hipSuccess;
+  if constexpr (sizeof(T) == 2) {
+    const bool vec = K % 8 == 0 && ldx % 8 == 0 && aligned16(x) && aligned16(s.w1) && (s.n == s.n1 || aligned16(s.w2));
+    if (vec && M >= kGemmMinRows && K % TK == 0) {
+      static bool attr_set = false;
+      if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)lin_gemm<Ty>, hipFuncAttributeMaxDynamicSharedMemorySize, GEMM_LDS);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+      }
+      hipLaunchKernelGGL(lin_gemm<Ty>, dim3((s.n + TN - 1) / TN, (M + TM - 1) / TM), dim3(256), GEMM_LDS, stream,
+                         x, ldx, M, K, s);
+      return hipGetLastError();
+    }
+    if (vec && M < kGemmMinRows) {
+      // one weight row per wave while that still leaves fewer than ~2 workgroups per CU
+      const bool rw1 = (s.n + 3) / 4 <= 512;
+      const int rb = M == 1 ? 1 : (M == 2 ? 2 : 4);
+      const int gx = rw1 ? (s.n + 3) / 4 : (s.n + 7) / 8;
+      const dim3 grid(gx, (M + rb - 1) / rb);
+#define MLA_LIN_GEMV(RW, RB) hipLaunchKernelGGL((lin_gemv<RW, RB, Ty>), grid, dim3(256), 0, stream, x, ldx, M, K, s)
+      if (rw1) {
+        if (rb == 1) MLA_LIN_GEMV(1, 1); else if (rb == 2) MLA_LIN_GEMV(1, 2); else MLA_LIN_GEMV(1, 4);
+      } else {
+        if (rb == 1) MLA_LIN_GEMV(2, 1); else if (rb == 2) MLA_LIN_GEMV(2, 2); else MLA_LIN_GEMV(2, 4);
+      }
+#undef MLA_LIN_GEMV
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((lin_generic<T, Ty>), dim3((s.n + 3) / 4, M < 65535 ? M : 65535), dim3(256), 0, stream, x, ldx,
+                     M, K, s);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- kv finish
+// One block per new token: RMS-normalise the latent part of the projected row (float32 sums of
+// squares; gain optional), rotate the position part by the token's position in float64, and store
+// the packed row into the token's cache slot. pre [batch * n_new, d_latent + d_rope] float32.
+template <typename T>
+__global__ void __launch_bounds__(256) kv_finish(const float* __restrict__ pre, const T* __restrict__ norm_w, float eps,
+                                                 int use_norm, T* __restrict__ cache,
+                                                 const int64_t* __restrict__ seq_off,
+                                                 const int32_t* __restrict__ len_before, int n_new, int d_latent,
+                                                 int d_rope, double base) {
+  __shared__ float red[4];
+  const int i = blockIdx.x, b = blockIdx.y;
+  const int row = d_latent + d_rope;
+  const size_t tok = (size_t)b * n_new + i;
+  const float* src = pre + tok * row;
+  const int64_t p = (int64_t)len_before[b] + i;
+  T* dst = cache + (seq_off[b] + p) * (int64_t)row;
+  float inv = 1.0f;
+  if (use_norm) {
+    float ss = 0.0f;
+    for (int c = threadIdx.x; c < d_latent; c += blockDim.x) ss = fmaf(src[c], src[c], ss);
+    ss = warp_sum(ss);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float tot = red[0] + red[1] + red[2] + red[3];
+    inv = 1.0f / sqrtf(tot / (float)d_latent + eps);
+  }
+  for (int c = threadIdx.x; c < d_latent; c += blockDim.x) {
+    float v = src[c] * inv;
+    if (use_norm && norm_w != nullptr) v *= to_f32(norm_w[c]);
+    dst[c] = from_f32<T>(v);
+  }
+  for (int j = threadIdx.x; j < d_rope / 2; j += blockDim.x) {
+    double sn, cs;
+    rope_sincos_f64(rope_theta(base, j, d_rope), p, &sn, &cs);
+    const double x0 = src[d_latent + 2 * j], x1 = src[d_latent + 2 * j + 1];
+    dst[d_latent + 2 * j] = from_f64<T>(x0 * cs - x1 * sn);
+    dst[d_latent + 2 * j + 1] = from_f64<T>(x0 * sn + x1 * cs);
+  }
+}
+
+}  // namespace lin
+
+size_t project_workspace_bytes(const LayerDims& L, int n_rows, int d_q, int elem_bytes) {
+  const size_t kv = (size_t)n_rows * (L.d_latent + L.d_rope) * sizeof(float);
+  const size_t q = (size_t)n_rows * d_q * elem_bytes;
+  size_t b = kv > q ? kv : q;
+  return (b + 255) & ~(size_t)255;
+}
+
+template <typename T>
+hipError_t launch_project_kv_append(const LayerDims& L, int batch, int n_new, int d_model, const void* h,
+                                    const void* w_dkv, const void* w_kr, const void* norm_w, float eps, int use_norm,
+                                    void* cache, const int64_t* seq_off, const int32_t* len_before, void* workspace,
+                                    hipStream_t stream) {
+  const int row = L.d_latent + L.d_rope;
+  float* pre = (float*)workspace;
+  lin::Seg2 s{w_dkv, w_kr, pre, pre + L.d_latent, L.d_latent, row, row, row};
+  hipError_t e = lin::linear<T, float>((const T*)h, d_model, batch * n_new, d_model, s, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(lin::kv_finish<T>, dim3(n_new, batch), dim3(256), 0, stream, (const float*)pre,
+                     (const T*)norm_w, eps, use_norm, (T*)cache, seq_off, len_before, n_new, L.d_latent, L.d_rope,
+                     L.rope_base);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_project_q(const LayerDims& L, int n_rows, int d_model, int d_q, const void* h, const void* w_dq,
+                            const void* w_uq, const void* w_qr, void* q_nope, void* q_rope, void* workspace,
+                            hipStream_t stream) {
+  const T* x = (const T*)h;
+  int K = d_model;
+  if (d_q > 0) {
+    lin::Seg2 s{w_dq, nullptr, workspace, nullptr, d_q, d_q, d_q, 0};
+    hipError_t e = lin::linear<T, T>(x, d_model, n_rows, d_model, s, stream);
+    if (e != hipSuccess) return e;
+    x = (const T*)workspace;
+    K = d_q;
+  }
+  const int n1 = L.n_heads * L.d_nope, n2 = L.n_heads * L.d_rope;
+  lin::Seg2 s{w_uq, w_qr, q_nope, q_rope, n1, n1 + n2, n1, n2};
+  return lin::linear<T, T>(x, K, n_rows, K, s, stream);
+}
+
+template hipError_t launch_project_kv_append<float>(const LayerDims&, int, int, int, const void*, const void*,
+                                                    const void*, const void*, float, int, void*, const int64_t*,
+                                                    const int32_t*, void*, hipStream_t);
+template hipError_t launch_project_kv_append<__bf16>(const LayerDims&, int, int, int, const void*, const void*,
+                                                     const void*, const void*, float, int, void*, const int64_t*,
+                                                     const int32_t*, void*, hipStream_t);
+template hipError_t launch_project_q<float>(const LayerDims&, int, int, int, const void*, const void*, const void*,
+                                            const void*, void*, void*, void*, hipStream_t);
+template hipError_t launch_project_q<__bf16>(const LayerDims&, int, int, int, const void*, const void*, const void*,
+                                             const void*, void*, void*, void*, hipStream_t);
+
+}  // namespace mla

@@ -143,6 +143,99 @@ def mla_out_proj(cfg: MlaConfig, z: torch.Tensor, w_uv: torch.Tensor, o: torch.T
           "mla_out_proj")
 
 
+def _ws(workspace: Optional[torch.Tensor], dev) -> tuple:
+    if workspace is None:
+        return None, 0
+    _need(workspace, "workspace", workspace.dtype, None, dev)
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def mla_project_workspace_size(cfg: MlaConfig, n_rows: int, d_model: int, d_q: int = 0) -> int:
+    return int(lib.mla_project_workspace_size(cfg, n_rows, d_model, d_q))
+
+
+def mla_project_kv_append(cfg: MlaConfig, h: torch.Tensor, w_dkv: torch.Tensor, w_kr: Optional[torch.Tensor],
+                          cache: torch.Tensor, seq_off: torch.Tensor, len_before: torch.Tensor,
+                          kv_norm_w: Optional[torch.Tensor] = None, kv_norm_eps: float = 1e-6,
+                          workspace: Optional[torch.Tensor] = None) -> None:
+    """cache[seq_off[b] + len_before[b] + i] = [RMSNorm(W_DKV h[b, i]) ; RoPE(W_KR h[b, i])]
+    (no norm when kv_norm_w is None)."""
+    dt = storage_dtype(cfg)
+    if h.dim() != 3:
+        raise ValueError("h must be [batch, n_new, d_model]")
+    B, n_new, dm = h.shape
+    dev = h.device
+    _need(h, "h", dt)
+    _need(w_dkv, "w_dkv", dt, (cfg.d_latent, dm), dev)
+    if cfg.d_rope > 0 or w_kr is not None:
+        _need(w_kr, "w_kr", dt, (cfg.d_rope, dm), dev)
+    if kv_norm_w is not None:
+        _need(kv_norm_w, "kv_norm_w", dt, (cfg.d_latent,), dev)
+    _need(cache, "cache", dt, None, dev)
+    if cache.dim() != 2 or cache.shape[1] != cfg.d_latent + cfg.d_rope:
+        raise ValueError("cache must be [rows, d_latent + d_rope]")
+    _need(seq_off, "seq_off", torch.int64, (B,), dev)
+    _need(len_before, "len_before", torch.int32, (B,), dev)
+    wp, wb = _ws(workspace, dev)
+    check(lib.mla_project_kv_append(cfg, B, n_new, dm, _ptr(h), _ptr(w_dkv), _ptr(w_kr), _ptr(kv_norm_w),
+                                    float(kv_norm_eps), _ptr(cache), _ptr(seq_off), _ptr(len_before), wp, wb,
+                                    _stream(cache)), "mla_project_kv_append")
+
+
+def mla_project_q(cfg: MlaConfig, h: torch.Tensor, w_uq: torch.Tensor, w_qr: Optional[torch.Tensor],
+                  q_nope: torch.Tensor, q_rope: Optional[torch.Tensor], w_dq: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None) -> None:
+    """q_nope / q_rope (unrotated) from h [R, d_model]: through c_Q = W_DQ h when w_dq is given,
+    else straight from h."""
+    dt = storage_dtype(cfg)
+    H = cfg.n_heads
+    if h.dim() != 2:
+        raise ValueError("h must be [n_rows, d_model]")
+    R, dm = h.shape
+    dev = h.device
+    _need(h, "h", dt)
+    d_q = 0
+    if w_dq is not None:
+        if w_dq.dim() != 2:
+            raise ValueError("w_dq must be [d_q, d_model]")
+        d_q = w_dq.shape[0]
+        _need(w_dq, "w_dq", dt, (d_q, dm), dev)
+    K = d_q if d_q > 0 else dm
+    _need(w_uq, "w_uq", dt, (H * cfg.d_nope, K), dev)
+    _need(q_nope, "q_nope", dt, (R, H, cfg.d_nope), dev)
+    if cfg.d_rope > 0 or w_qr is not None:
+        _need(w_qr, "w_qr", dt, (H * cfg.d_rope, K), dev)
+    if cfg.d_rope > 0 or q_rope is not None:
+        _need(q_rope, "q_rope", dt, (R, H, cfg.d_rope), dev)
+    wp, wb = _ws(workspace, dev)
+    check(lib.mla_project_q(cfg, R, dm, d_q, _ptr(h), _ptr(w_dq), _ptr(w_uq), _ptr(w_qr), _ptr(q_nope),
+                            _ptr(q_rope), wp, wb, _stream(q_nope)), "mla_project_q")
+
+
+def mla_decode_advance(n_new: int, len_before: Optional[torch.Tensor] = None, seq_len: Optional[torch.Tensor] = None,
+                       q_pos: Optional[torch.Tensor] = None) -> None:
+    """len_before += n_new, seq_len += n_new, q_pos += n_new on the device (any may be None)."""
+    given = [t for t in (len_before, seq_len, q_pos) if t is not None]
+    if not given:
+        return
+    dev = given[0].device
+    B = None
+    for name, t in (("len_before", len_before), ("seq_len", seq_len)):
+        if t is not None:
+            _need(t, name, torch.int32, None, dev)
+            if t.dim() != 1 or (B is not None and t.shape[0] != B):
+                raise ValueError("len_before and seq_len must be [batch]")
+            B = t.shape[0]
+    R = 0
+    if q_pos is not None:
+        _need(q_pos, "q_pos", torch.int32, None, dev)
+        if q_pos.dim() != 1:
+            raise ValueError("q_pos must be [n_rows]")
+        R = q_pos.shape[0]
+    check(lib.mla_decode_advance(B or 0, int(n_new), _ptr(len_before), _ptr(seq_len), R, _ptr(q_pos),
+                                 _stream(given[0])), "mla_decode_advance")
+
+
 def version() -> str:
     return lib.mla_version().decode()
 
@@ -155,6 +248,10 @@ __all__ = [
     "mla_decode_attn_workspace_size",
     "mla_decode_attn",
     "mla_out_proj",
+    "mla_project_workspace_size",
+    "mla_project_kv_append",
+    "mla_project_q",
+    "mla_decode_advance",
     "version",
     "_lib",
 ]

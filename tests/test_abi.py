@@ -130,3 +130,47 @@ def test_python_wrappers_validate_before_calling():
     with pytest.raises(ValueError):
         mla.mla_absorb_q(c, torch.zeros(1, 4, 16), torch.zeros(1, 4, 8), torch.zeros(1, dtype=torch.int32),
                          torch.zeros(4, 16, 32), torch.zeros(1, 4, 40))   # host tensors are refused
+
+
+def test_projection_and_advance_arguments():
+    """The upstream-projection calls and the decode advance validate before launching."""
+    c = cfg()
+    ws = lib.mla_project_workspace_size(c, 4, 7168, 1536)
+    assert ws >= 4 * 576 * 4 and ws >= 4 * 1536 * 2 and ws % 256 == 0
+    assert lib.mla_project_workspace_size(cfg(n_heads=0), 4, 7168, 0) == 0
+    assert lib.mla_project_workspace_size(c, 4, 0, 0) == 0
+    # bad config, NULL pointers, negative sizes, missing or short workspace
+    assert lib.mla_project_kv_append(cfg(d_rope=7), 1, 1, 7168, FAKE, FAKE, FAKE, None, 1e-6, FAKE, FAKE, FAKE,
+                                     FAKE, ws, None) == MLA_ERR_INVALID_ARG
+    assert lib.mla_project_kv_append(c, 1, 1, 7168, None, FAKE, FAKE, None, 1e-6, FAKE, FAKE, FAKE, FAKE, ws,
+                                     None) == MLA_ERR_INVALID_ARG
+    assert lib.mla_project_kv_append(c, 1, 1, 7168, FAKE, FAKE, None, None, 1e-6, FAKE, FAKE, FAKE, FAKE, ws,
+                                     None) == MLA_ERR_INVALID_ARG   # W_KR needed when d_rope > 0
+    assert lib.mla_project_kv_append(c, -1, 1, 7168, FAKE, FAKE, FAKE, None, 1e-6, FAKE, FAKE, FAKE, FAKE, ws,
+                                     None) == MLA_ERR_INVALID_ARG
+    assert lib.mla_project_kv_append(c, 1, 1, 7168, FAKE, FAKE, FAKE, FAKE, -1.0, FAKE, FAKE, FAKE, FAKE, ws,
+                                     None) == MLA_ERR_INVALID_ARG   # negative eps with a norm
+    assert lib.mla_project_kv_append(c, 4, 1, 7168, FAKE, FAKE, FAKE, None, 1e-6, FAKE, FAKE, FAKE, None, ws,
+                                     None) == MLA_ERR_WORKSPACE
+    assert lib.mla_project_kv_append(c, 4, 1, 7168, FAKE, FAKE, FAKE, None, 1e-6, FAKE, FAKE, FAKE, FAKE,
+                                     4 * 576 * 4 - 1, None) == MLA_ERR_WORKSPACE
+    assert lib.mla_project_q(cfg(softmax_scale=0.0), 1, 7168, 0, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, 0,
+                             None) == MLA_ERR_INVALID_ARG
+    assert lib.mla_project_q(c, 1, 7168, 1536, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, ws,
+                             None) == MLA_ERR_INVALID_ARG   # d_q > 0 without W_DQ
+    assert lib.mla_project_q(c, 1, 7168, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws,
+                             None) == MLA_ERR_INVALID_ARG   # W_DQ with d_q = 0
+    assert lib.mla_project_q(c, 1, 7168, 1536, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, ws,
+                             None) == MLA_ERR_INVALID_ARG
+    assert lib.mla_project_q(c, 4, 7168, 1536, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4 * 1536 * 2 - 1,
+                             None) == MLA_ERR_WORKSPACE
+    assert lib.mla_project_q(c, -1, 7168, 0, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, 0, None) == MLA_ERR_INVALID_ARG
+    assert lib.mla_decode_advance(-1, 1, FAKE, FAKE, 0, None, None) == MLA_ERR_INVALID_ARG
+    assert lib.mla_decode_advance(1, -1, FAKE, FAKE, 0, None, None) == MLA_ERR_INVALID_ARG
+    # empty work is a no-op
+    assert lib.mla_project_kv_append(c, 0, 3, 7168, None, None, None, None, 1e-6, None, None, None, None, 0,
+                                     None) == MLA_OK
+    assert lib.mla_project_q(c, 0, 7168, 0, None, None, None, None, None, None, None, 0, None) == MLA_OK
+    assert lib.mla_decode_advance(4, 0, FAKE, FAKE, 4, FAKE, None) == MLA_OK
+    assert lib.mla_decode_advance(4, 1, None, None, 4, None, None) == MLA_OK
+    assert lib.mla_last_error() == b""
