@@ -48,6 +48,12 @@ def parse():
     ap.add_argument("--eager", action="store_true",
                     help="launch the four calls from Python every step instead of replaying a captured HIP graph")
     ap.add_argument("--verbose", action="store_true")
+    ap.add_argument("--decode-loop", action="store_true",
+                    help="instead of the single step: time token-by-token decode through a stack of full MLA "
+                         "layers (h -> projections -> attention -> W_O) replayed as one HIP graph per token")
+    ap.add_argument("--layers", type=int, default=61, help="--decode-loop: layers in the stack")
+    ap.add_argument("--loop-context", type=int, default=4096, help="--decode-loop: tokens prefilled per sequence")
+    ap.add_argument("--loop-batch", type=int, default=1, help="--decode-loop: sequences decoded together")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="instead of the step: time a plain 1 GiB device copy (the reference kernel that scales "
                          "the FETCH_SIZE / WRITE_SIZE counters to bytes)")
@@ -115,6 +121,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args)
+        return
+    if args.decode_loop:
+        decode_loop(args)
         return
 
     import numpy as np
@@ -310,6 +319,69 @@ def main():
     if args.verbose:
         print(f"setup {setup_s:.1f}s, copies {n_copies} x {per_copy / 1e6:.1f} MB", file=sys.stderr)
     print(json.dumps(out), flush=True)
+
+
+def decode_loop(args):
+    """Per-token latency of a stack of DeepSeek-V3-shaped MLA layers at batch B: every layer runs
+    mla_project_kv_append, mla_project_q, mla_absorb_q, mla_decode_attn and mla_out_proj with W_O,
+    the layer's output feeding the next layer; the caches are first filled by a prefill of
+    --loop-context tokens through the same stack, then one captured decode step (all layers and
+    the position advance) is replayed per token. The weights of 61 layers (~23 GB) are far beyond
+    the last-level cache, so every token streams them from HBM."""
+    import torch
+
+    import mla_decode_decoupled_amd as mla
+    from mla_decode_decoupled_amd.decode_loop import DecodeStack, random_layers
+    from mla_workloads import get_config
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = get_config(1)
+    lc = mla.make_config(cfg.n_heads, cfg.d_nope, cfg.d_latent, cfg.d_rope, cfg.d_v, cfg.dtype, cfg.rope_base)
+    B, L, S = args.loop_batch, args.layers, args.loop_context
+    layers = random_layers(lc, L, cfg.d_model, cfg.q_lora, dev, seed=7)
+    stack = DecodeStack(lc, layers, batch=B, capacity=S + args.warmup + args.steps + 2)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(11)
+    h_prefix = torch.randn((B, S, cfg.d_model), generator=gen, device=dev).to(torch.bfloat16)
+    t0 = time.time()
+    stack.forward(h_prefix)
+    torch.cuda.synchronize()
+    prefill_s = time.time() - t0
+    del h_prefix
+    g = stack.capture_decode()
+    g.h_in.copy_(torch.randn((B, 1, cfg.d_model), generator=gen, device=dev).to(torch.bfloat16))
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ctx0 = stack.length
+    start.record(stream)
+    for _ in range(args.steps):
+        g.replay()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_token = start.elapsed_time(stop) / args.steps
+    esz = 2
+    w_bytes = sum(t.numel() * esz for t in layers[0].values()) * L
+    keys = B * (ctx0 + 1 + args.steps / 2.0)               # mean keys per sequence over the timed tokens
+    cache_bytes = keys * cfg.row * esz * L
+    moved = w_bytes + cache_bytes
+    gbs = moved / (ms_token * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "MLA decode loop: per-token latency through a stack of full attention layers",
+        "value": round(B / (ms_token * 1e-3), 2), "unit": "tokens/s", "ms_per_token": round(ms_token, 4),
+        "steps": args.steps, "warmup": args.warmup, "launch": "hip_graph", "dtype": "bf16",
+        "data": "synthetic (seeded device N(0,1/fan_in) weights and N(0,1) hidden states)",
+        "config": {"workload": "v3_decode_loop", "layers": L, "batch": B, "context_tokens": ctx0,
+                   "d_model": cfg.d_model, "q_lora": cfg.q_lora, "heads": cfg.n_heads},
+        "bytes_per_token": {"weights": w_bytes, "cache": int(cache_bytes)},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4)},
+        "prefill_s": round(prefill_s, 3),
+    }), flush=True)
 
 
 def cpu_baseline(cfg, c_host, k_host, qn_host, qr_host, wuk_host, wuv_host, lens, budget_s):
