@@ -230,12 +230,9 @@ mla_status mla_out_proj(const mla_config* cfg, int32_t n_rows, const float* z, c
   if (e != hipSuccess || !with_w_o) return from_hip(e, "mla_out_proj launch");
   // u = W_O concat_i(o_i), from the o just written (same stream)
   const int K = L.n_heads * L.d_v;
-  if (cfg->dtype == MLA_BF16 && mla::w_o_fast_supported(K) && aligned16(o) && aligned16(w_o))
-    e = mla::launch_w_o_fast(n_rows, d_model, o, w_o, u, st);
-  else if (cfg->dtype == MLA_F32)
-    e = mla::launch_w_o_generic<float>(n_rows, K, d_model, o, w_o, u, st);
-  else
-    e = mla::launch_w_o_generic<__bf16>(n_rows, K, d_model, o, w_o, u, st);
+  if ((int64_t)K > INT32_MAX / 8) return fail(MLA_ERR_UNSUPPORTED, "H * d_v too large");
+  e = cfg->dtype == MLA_F32 ? mla::launch_linear<float>(o, K, n_rows, K, w_o, d_model, u, d_model, st)
+                            : mla::launch_linear<__bf16>(o, K, n_rows, K, w_o, d_model, u, d_model, st);
   return from_hip(e, "mla_out_proj W_O launch");
 }
 

@@ -67,13 +67,11 @@ hipError_t launch_out_proj_fast(const LayerDims& L, int n_rows, const float* z, 
 // MFMA GEMM forms of the same two projections (same shape), for many query rows at once
 constexpr int kGemmMinRows = 16;
 
-// Optional W_O projection u[r] = W_O concat_i(o[r, i]) (proj_wo.hip): any shape, and a matrix-vector
-// / MFMA GEMM path for bf16 with K = H * d_v = 16384
+// y[r, n] = sum_k x[r, k] W[n, k] (linear.hip): the generic, matrix-vector or MFMA GEMM kernel by
+// shape, dtype and alignment. Serves the optional W_O projection of mla_out_proj.
 template <typename T>
-hipError_t launch_w_o_generic(int n_rows, int K, int d_model, const void* o, const void* w_o, void* u,
-                              hipStream_t stream);
-bool w_o_fast_supported(int K);
-hipError_t launch_w_o_fast(int n_rows, int d_model, const void* o, const void* w_o, void* u, hipStream_t stream);
+hipError_t launch_linear(const void* x, int ldx, int M, int K, const void* w, int N, void* y, int ldy,
+                         hipStream_t stream);
 hipError_t launch_absorb_q_gemm(const LayerDims& L, int n_rows, const void* q_nope, const void* q_rope,
                                 const int32_t* q_pos, const void* w_uk, void* q_packed, hipStream_t stream);
 hipError_t launch_out_proj_gemm(const LayerDims& L, int n_rows, const float* z, const void* w_uv, void* o,

@@ -73,23 +73,30 @@ __device__ __forceinline__ void unpack8(const i32x4 v, float* f) {
 }
 
 // ---------------------------------------------------------------- few rows
-// grid (ceil(n / (4 RW)), ceil(M / RB)), 256 threads. Wave w owns weight rows
-// (4 blockIdx.x + w) RW .. +RW-1 and activation rows RB blockIdx.y .. +RB-1; lane l takes the
-// 16-byte pieces l, l + 64, ... of each row (K % 8 == 0, x and W 16-byte aligned, ldx % 8 == 0).
-constexpr int kGemvU = 4;   // pieces per lane per step: RW * kGemvU weight loads in flight
-template <int RW, int RB, typename Ty>
+// grid (ceil(n / (RW 4 / KS)), ceil(M / RB)), 256 threads. The 4 waves form 4 / KS groups of KS
+// waves; group g owns weight rows (blockIdx.x (4 / KS) + g) RW .. +RW-1 and the KS waves of a group
+// split K between them (wave part p takes the 16-byte pieces 64 p + lane + 64 KS j), so a short
+// K still gives every lane several independent loads. Each lane keeps RW x U weight loads in
+// flight (nontemporal: the weights are read once) next to the matching pieces of the RB
+// activation rows (through the caches, where every workgroup finds them). K % 8 == 0, x and W
+// 16-byte aligned, ldx % 8 == 0.
+template <int RW, int RB, int KS, typename Ty>
 __global__ void __launch_bounds__(256) lin_gemv(const bf16* __restrict__ x, int ldx, int M, int K, Seg2 s) {
+  constexpr int U = 8 / RW;
+  constexpr int G = 4 / KS;
+  __shared__ float red[4][RW][RB];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int grp = w / KS, part = w % KS;
   const int r0 = blockIdx.y * RB, nr = min(RB, M - r0);
-  const int nb = (blockIdx.x * 4 + w) * RW;
-  if (nb >= s.n) return;
+  const int nb = (blockIdx.x * G + grp) * RW;
+  const bool active = nb < s.n;
   const int KP = K / 8;
   const bf16* wr[RW];
   bool ok[RW];
 #pragma unroll
   for (int q = 0; q < RW; ++q) {
     ok[q] = nb + q < s.n;
-    wr[q] = wrow<bf16>(s, ok[q] ? nb + q : nb, K);
+    wr[q] = wrow<bf16>(s, ok[q] ? nb + q : (active ? nb : 0), K);
   }
   const bf16* xr[RB];
 #pragma unroll
@@ -99,34 +106,36 @@ __global__ void __launch_bounds__(256) lin_gemv(const bf16* __restrict__ x, int 
   for (int q = 0; q < RW; ++q)
 #pragma unroll
     for (int rr = 0; rr < RB; ++rr) acc[q][rr] = 0.0f;
+  if (active) {
 #pragma unroll 1
-  for (int p0 = 0; p0 < KP; p0 += 64 * kGemvU) {
-    i32x4 wv[RW][kGemvU], xv[RB][kGemvU];
+    for (int p0 = 64 * part; p0 < KP; p0 += 64 * KS * U) {
+      i32x4 wv[RW][U], xv[RB][U];
 #pragma unroll
-    for (int u = 0; u < kGemvU; ++u) {
-      const int p = p0 + 64 * u + lane;
-      const bool in = p < KP;
+      for (int u = 0; u < U; ++u) {
+        const int p = p0 + 64 * KS * u + lane;
+        const bool in = p < KP;
 #pragma unroll
-      for (int q = 0; q < RW; ++q)
-        wv[q][u] = in && ok[q] ? __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(wr[q] + 8 * p))
-                               : i32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int rr = 0; rr < RB; ++rr)
-        xv[rr][u] = in && rr < nr ? *reinterpret_cast<const i32x4*>(xr[rr] + 8 * p) : i32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int u = 0; u < kGemvU; ++u) {
-      float xf[RB][8];
-#pragma unroll
-      for (int rr = 0; rr < RB; ++rr) unpack8(xv[rr][u], xf[rr]);
-#pragma unroll
-      for (int q = 0; q < RW; ++q) {
-        float wf[8];
-        unpack8(wv[q][u], wf);
+        for (int q = 0; q < RW; ++q)
+          wv[q][u] = in && ok[q] ? __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(wr[q] + 8 * p))
+                                 : i32x4{0, 0, 0, 0};
 #pragma unroll
         for (int rr = 0; rr < RB; ++rr)
+          xv[rr][u] = in && rr < nr ? *reinterpret_cast<const i32x4*>(xr[rr] + 8 * p) : i32x4{0, 0, 0, 0};
+      }
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[q][rr] = fmaf(wf[e], xf[rr][e], acc[q][rr]);
+      for (int u = 0; u < U; ++u) {
+        float xf[RB][8];
+#pragma unroll
+        for (int rr = 0; rr < RB; ++rr) unpack8(xv[rr][u], xf[rr]);
+#pragma unroll
+        for (int q = 0; q < RW; ++q) {
+          float wf[8];
+          unpack8(wv[q][u], wf);
+#pragma unroll
+          for (int rr = 0; rr < RB; ++rr)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[q][rr] = fmaf(wf[e], xf[rr][e], acc[q][rr]);
+        }
       }
     }
   }
@@ -135,8 +144,26 @@ __global__ void __launch_bounds__(256) lin_gemv(const bf16* __restrict__ x, int 
 #pragma unroll
     for (int rr = 0; rr < RB; ++rr) {
       const float v = warp_sum(acc[q][rr]);
-      if (lane == 0 && ok[q] && rr < nr) ystore<Ty>(s, r0 + rr, nb + q, v);
+      if constexpr (KS == 1) {
+        if (lane == 0 && ok[q] && active && rr < nr) ystore<Ty>(s, r0 + rr, nb + q, v);
+      } else {
+        if (lane == 0) red[w][q][rr] = v;
+      }
     }
+  if constexpr (KS > 1) {
+    __syncthreads();
+    if (part == 0 && lane == 0 && active) {
+#pragma unroll
+      for (int q = 0; q < RW; ++q)
+#pragma unroll
+        for (int rr = 0; rr < RB; ++rr) {
+          float v = red[w][q][rr];
+#pragma unroll
+          for (int k = 1; k < KS; ++k) v += red[w + k][q][rr];
+          if (ok[q] && rr < nr) ystore<Ty>(s, r0 + rr, nb + q, v);
+        }
+    }
+  }
 }
 
 // ---------------------------------------------------------------- many rows
@@ -256,16 +283,28 @@ hipError_t linear(const T* x, int ldx, int M, int K, const Seg2& s, hipStream_t 
       return hipGetLastError();
     }
     if (vec && M < kGemmMinRows) {
-      // one weight row per wave while that still leaves fewer than ~2 workgroups per CU
-      const bool rw1 = (s.n + 3) / 4 <= 512;
+      // two weight rows per wave for wide outputs; split K over 2 or 4 waves until about 16 waves
+      // per CU have work, as long as every lane keeps at least 2 pieces of each row
+      const int rw = s.n >= 8192 ? 2 : 1;
+      const int64_t row_waves = (s.n + rw - 1) / rw;
+      int ks = 1;
+      while (ks < 4 && row_waves * ks < 4096 && K / 8 >= 64 * 2 * (2 * ks)) ks *= 2;
       const int rb = M == 1 ? 1 : (M == 2 ? 2 : 4);
-      const int gx = rw1 ? (s.n + 3) / 4 : (s.n + 7) / 8;
-      const dim3 grid(gx, (M + rb - 1) / rb);
-#define MLA_LIN_GEMV(RW, RB) hipLaunchKernelGGL((lin_gemv<RW, RB, Ty>), grid, dim3(256), 0, stream, x, ldx, M, K, s)
-      if (rw1) {
-        if (rb == 1) MLA_LIN_GEMV(1, 1); else if (rb == 2) MLA_LIN_GEMV(1, 2); else MLA_LIN_GEMV(1, 4);
+      const int rows_per_wg = rw * 4 / ks;
+      const dim3 grid((s.n + rows_per_wg - 1) / rows_per_wg, (M + rb - 1) / rb);
+#define MLA_LIN_GEMV(RW, KS)                                                                                     \
+  do {                                                                                                           \
+    if (rb == 1)                                                                                                 \
+      hipLaunchKernelGGL((lin_gemv<RW, 1, KS, Ty>), grid, dim3(256), 0, stream, x, ldx, M, K, s);                \
+    else if (rb == 2)                                                                                            \
+      hipLaunchKernelGGL((lin_gemv<RW, 2, KS, Ty>), grid, dim3(256), 0, stream, x, ldx, M, K, s);                \
+    else                                                                                                         \
+      hipLaunchKernelGGL((lin_gemv<RW, 4, KS, Ty>), grid, dim3(256), 0, stream, x, ldx, M, K, s);                \
+  } while (0)
+      if (rw == 1) {
+        if (ks == 1) MLA_LIN_GEMV(1, 1); else if (ks == 2) MLA_LIN_GEMV(1, 2); else MLA_LIN_GEMV(1, 4);
       } else {
-        if (rb == 1) MLA_LIN_GEMV(2, 1); else if (rb == 2) MLA_LIN_GEMV(2, 2); else MLA_LIN_GEMV(2, 4);
+        if (ks == 1) MLA_LIN_GEMV(2, 1); else if (ks == 2) MLA_LIN_GEMV(2, 2); else MLA_LIN_GEMV(2, 4);
       }
 #undef MLA_LIN_GEMV
       return hipGetLastError();
@@ -359,6 +398,15 @@ hipError_t launch_project_q(const LayerDims& L, int n_rows, int d_model, int d_q
   lin::Seg2 s{w_uq, w_qr, q_nope, q_rope, n1, n1 + n2, n1, n2};
   return lin::linear<T, T>(x, K, n_rows, K, s, stream);
 }
+
+template <typename T>
+hipError_t launch_linear(const void* x, int ldx, int M, int K, const void* w, int N, void* y, int ldy,
+                         hipStream_t stream) {
+  lin::Seg2 s{w, nullptr, y, nullptr, N, N, ldy, 0};
+  return lin::linear<T, T>((const T*)x, ldx, M, K, s, stream);
+}
+template hipError_t launch_linear<float>(const void*, int, int, int, const void*, int, void*, int, hipStream_t);
+template hipError_t launch_linear<__bf16>(const void*, int, int, int, const void*, int, void*, int, hipStream_t);
 
 template hipError_t launch_project_kv_append<float>(const LayerDims&, int, int, int, const void*, const void*,
                                                     const void*, const void*, float, int, void*, const int64_t*,
