@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--eager", action="store_true",
                     help="launch the four calls from Python every step instead of replaying a captured HIP graph")
     ap.add_argument("--verbose", action="store_true")
+    ap.add_argument("--explicit", action="store_true",
+                    help="many-row workloads: the step is mla_rope_append + mla_prefill_explicit (the non-absorbed "
+                         "form) instead of absorb + latent attention + W_UV")
     ap.add_argument("--decode-loop", action="store_true",
                     help="instead of the single step: time token-by-token decode through a stack of full MLA "
                          "layers (h -> projections -> attention -> W_O) replayed as one HIP graph per token")
@@ -185,7 +188,12 @@ def main():
     z = torch.empty((B, n_q, H, cfg.d_latent), dtype=torch.float32, device=dev)
     lse = torch.empty((B, n_q, H), dtype=torch.float32, device=dev)
     o = torch.empty((R, H, cfg.d_v), dtype=dt, device=dev)
-    ws_bytes = mla.mla_decode_attn_workspace_size(lc, B, n_q, max_len, n_splits)
+    if args.explicit:
+        ws_bytes = mla.mla_prefill_explicit_workspace_size(lc, B, n_q, max_len)
+        if ws_bytes == 0:
+            raise SystemExit("--explicit needs the bf16 DeepSeek head shape and n_q <= keys")
+    else:
+        ws_bytes = mla.mla_decode_attn_workspace_size(lc, B, n_q, max_len, n_splits)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     setup_s = time.time() - t0
@@ -201,6 +209,19 @@ def main():
         mla.mla_rope_append(lc, c_new, k_new, cache, seq_off, len_before)
         if timed:
             marks[1].record(stream)
+        if args.explicit:
+            # the non-absorbed form: keys and values rebuilt from the cache, o written directly
+            if timed:
+                marks[2].record(stream)
+            mla.mla_prefill_explicit(lc, qn.view(B, n_q, H, cfg.d_nope), qr.view(B, n_q, H, cfg.d_rope), cache,
+                                     seq_off, seq_len, max_len, wuk, wuv, o.view(B, n_q, H, cfg.d_v), lse=lse,
+                                     workspace=ws)
+            if timed:
+                marks[3].record(stream)
+                marks[4].record(stream)
+                for j, k in enumerate(("append", "absorb", "attn", "proj")):
+                    ev[k].append((marks[j], marks[j + 1]))
+            return
         mla.mla_absorb_q(lc, qn, qr, q_pos, wuk, q_packed)
         if timed:
             marks[2].record(stream)
@@ -260,6 +281,14 @@ def main():
         vis_pairs = int(sum(n_q * (int(l) - n_q) + n_q * (n_q + 1) // 2 for l in lens))
     attn_bytes = keys * row * esz + R * H * row * esz + R * H * cfg.d_latent * 4 + R * H * 4
     attn_flops = 2 * H * (row + cfg.d_latent) * vis_pairs
+    if args.explicit:
+        # per (row, key, head): 192-wide scores and 128-wide values; plus rebuilding K_C and V per key;
+        # bytes: cache rows, the rebuilt keys and values written and read once, queries in, o out
+        attn_flops = (2 * H * (cfg.d_nope + cfg.d_rope + cfg.d_v) * vis_pairs
+                      + 2 * keys * cfg.d_latent * H * (cfg.d_nope + cfg.d_v))
+        attn_bytes = (keys * row * esz + 2 * keys * H * (cfg.d_nope + cfg.d_v) * esz
+                      + 2 * H * cfg.d_nope * cfg.d_latent * esz
+                      + R * H * (cfg.d_nope + cfg.d_rope) * esz + R * H * cfg.d_v * esz + R * H * 4)
     kernel_bytes = {
         "append": R * (cfg.d_latent + cfg.d_rope) * esz + R * row * esz,
         "absorb": H * cfg.d_nope * cfg.d_latent * esz + R * H * (cfg.d_nope + cfg.d_rope) * esz + R * H * row * esz,
@@ -300,15 +329,17 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
         "data": "synthetic (seeded N(0,1) inputs, N(0,1/fan_in) weights, RMS-normalised latent)",
-        "config": {"workload": cfg.name, "batch": B, "n_q": n_q, "heads": H, "d_latent": cfg.d_latent,
+        "config": {"workload": cfg.name + ("_explicit" if args.explicit else ""), "batch": B, "n_q": n_q, "heads": H, "d_latent": cfg.d_latent,
                    "d_rope": cfg.d_rope, "d_nope": cfg.d_nope, "d_v": cfg.d_v,
                    "seq_len_keys": int(max_len) if len(set(lens.tolist())) == 1 else [int(lens.min()), int(lens.max())],
                    "n_splits": n_splits, "cold_copies": n_copies, "parallelism": "single GPU"},
-        "roofline": {"kernel": {"attn": "mla_decode_attn", "absorb": "mla_absorb_q", "proj": "mla_out_proj",
+        "roofline": {"kernel": {"attn": "mla_prefill_explicit" if args.explicit else "mla_decode_attn",
+                                "absorb": "mla_absorb_q", "proj": "mla_out_proj",
                                 "append": "mla_rope_append"}[dominant],
                      "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4),
-                     "traffic": recorded_traffic(cfg.name, n_splits, not args.hot) if dominant == "attn" else None,
+                     "traffic": (recorded_traffic(cfg.name, n_splits, not args.hot)
+                                 if dominant == "attn" and not args.explicit else None),
                      "algorithmic_bytes_per_launch": kernel_bytes[dominant],
                      "avg_launch_ms": round(per_kernel_ms[dominant], 6)},
         "kernels_ms": {k: round(v, 6) for k, v in per_kernel_ms.items()},

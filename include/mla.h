@@ -215,6 +215,45 @@ mla_status mla_project_q(const mla_config* cfg, int32_t n_rows, int32_t d_model,
                          void* stream);
 
 /*
+ * ---- Explicit (non-absorbed) prefill: the same attention output o for many query rows at once.
+ *
+ * Bytes of device workspace mla_prefill_explicit needs (the rebuilt content keys and values:
+ * 2 * batch * max_seq_len * H * 128 bf16). 0 for invalid arguments or a shape the call does not
+ * cover.
+ */
+size_t mla_prefill_explicit_workspace_size(const mla_config* cfg, int32_t batch, int32_t n_q,
+                                           int32_t max_seq_len);
+
+/*
+ * mla_prefill_explicit — attention of n_q new query rows per sequence in the non-absorbed form
+ * ("Decoupled RoPE · MLA Part 2", §2.1 and §3.2: per head the content key W_UK,i c and the value
+ * W_UV,i c are rebuilt from the cached latent, the shared rotated position key is concatenated to
+ * the content key, q = [q_nope ; RoPE(q_rope)]; "从零理解 MLA", the non-absorbed forward). For long
+ * query chunks this needs 2 H (192 + 128) flops per (row, key) instead of the absorbed 2 H (576 + 512).
+ *
+ * Same mask and positions as mla_decode_attn (query row t of sequence b at position
+ * seq_len[b] - n_q + t sees keys j <= seq_len[b] - n_q + t); the cache must already hold the rows of
+ * all seq_len[b] tokens (mla_rope_append). For each (b, t, head i):
+ *   s_j  = softmax_scale * ( q_nope[b,t,i] . (W_UK,i c_j) + RoPE_pos(q_rope[b,t,i]) . k_R,j )
+ *   o    = sum_j softmax(s)_j (W_UV,i c_j);   lse = ln sum_j exp(s_j)
+ * which equals mla_out_proj(mla_decode_attn(mla_absorb_q(...))) up to rounding.
+ *  q_nope   [batch, n_q, H, 128] bf16, device;  q_rope [batch, n_q, H, 64] bf16, device, unrotated
+ *  cache, seq_off, seq_len, max_seq_len   as for mla_decode_attn
+ *  w_uk     [H, 128, 512] bf16, device;  w_uv [H, 128, 512] bf16, device
+ *  workspace  >= mla_prefill_explicit_workspace_size(...) bytes, device; no initialisation
+ *  o        [batch, n_q, H, 128] bf16, device, written
+ *  lse      float32 [batch, n_q, H], device, written; may be NULL
+ * Covers bf16 with d_nope = d_v = 128, d_rope = 64, d_latent = 512 (any head count); anything
+ * else returns MLA_ERR_UNSUPPORTED. All tensors must be 16-byte aligned. Keys and values are
+ * rounded once to bf16 when rebuilt; scores, softmax and sums accumulate in float32.
+ */
+mla_status mla_prefill_explicit(const mla_config* cfg, int32_t batch, int32_t n_q, const void* q_nope,
+                                const void* q_rope, const void* cache, const int64_t* seq_off,
+                                const int32_t* seq_len, int32_t max_seq_len, const void* w_uk,
+                                const void* w_uv, void* workspace, size_t workspace_bytes, void* o,
+                                float* lse, void* stream);
+
+/*
  * mla_decode_advance — cache growth between decode steps ("从零理解 MLA", the token-by-token
  * decode loop of its decoupled-RoPE check: every step appends the new token and the next one
  * attends to one more key). On the device, enqueued on `stream`:

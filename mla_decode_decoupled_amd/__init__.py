@@ -16,5 +16,7 @@ from .ops import (  # noqa: F401
     mla_project_kv_append,
     mla_project_q,
     mla_decode_advance,
+    mla_prefill_explicit_workspace_size,
+    mla_prefill_explicit,
     version,
 )

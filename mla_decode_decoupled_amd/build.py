@@ -14,7 +14,7 @@ import sys
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_PATH = os.path.join(PKG_DIR, "libmla.so")
-SOURCES = ["api.hip", "generic.hip", "decode_fast.hip", "proj_fast.hip", "proj_gemm.hip", "linear.hip"]
+SOURCES = ["api.hip", "generic.hip", "decode_fast.hip", "proj_fast.hip", "proj_gemm.hip", "linear.hip", "prefill_explicit.hip"]
 
 # Packed-FP32 instructions (v_pk_*_f32) are switched off for every device pass: the compiler
 # otherwise forms them from plain float code, and the kernels are validated without them.

@@ -306,6 +306,44 @@ mla_status mla_project_q(const mla_config* cfg, int32_t n_rows, int32_t d_model,
   return from_hip(e, "mla_project_q launch");
 }
 
+size_t mla_prefill_explicit_workspace_size(const mla_config* cfg, int32_t batch, int32_t n_q, int32_t max_seq_len) {
+  mla::LayerDims L;
+  if (check_cfg(cfg, &L) != MLA_OK) return 0;
+  if (batch <= 0 || n_q <= 0 || max_seq_len < n_q) return 0;
+  if (cfg->dtype != MLA_BF16 || !mla::prefill_explicit_supported(L)) return 0;
+  return mla::prefill_explicit_workspace_bytes(L, batch, max_seq_len);
+}
+
+mla_status mla_prefill_explicit(const mla_config* cfg, int32_t batch, int32_t n_q, const void* q_nope,
+                                const void* q_rope, const void* cache, const int64_t* seq_off, const int32_t* seq_len,
+                                int32_t max_seq_len, const void* w_uk, const void* w_uv, void* workspace,
+                                size_t workspace_bytes, void* o, float* lse, void* stream) {
+  mla::LayerDims L;
+  mla_status s = check_cfg(cfg, &L);
+  if (s != MLA_OK) return s;
+  if (batch < 0 || n_q < 0) return fail(MLA_ERR_INVALID_ARG, "batch and n_q must be >= 0");
+  if (batch == 0 || n_q == 0) return ok();
+  if (max_seq_len < n_q) return fail(MLA_ERR_INVALID_ARG, "max_seq_len (%d) must be >= n_q (%d)", max_seq_len, n_q);
+  if (cfg->dtype != MLA_BF16 || !mla::prefill_explicit_supported(L))
+    return fail(MLA_ERR_UNSUPPORTED, "the explicit prefill covers bf16 with d_nope = d_v = 128, d_rope = 64, d_latent = 512");
+  if ((int64_t)batch * L.n_heads * ((n_q + 127) / 128) > INT32_MAX)
+    return fail(MLA_ERR_UNSUPPORTED, "batch * heads * query blocks too large");
+  if ((int64_t)max_seq_len > 65535 * 128) return fail(MLA_ERR_UNSUPPORTED, "max_seq_len %d too large", max_seq_len);
+  if (batch > 65535) return fail(MLA_ERR_UNSUPPORTED, "batch %d exceeds 65535", batch);
+  if (!q_nope || !q_rope || !cache || !seq_off || !seq_len || !w_uk || !w_uv || !o)
+    return fail(MLA_ERR_INVALID_ARG, "NULL pointer argument");
+  if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(cache) || !aligned16(w_uk) || !aligned16(w_uv) ||
+      !aligned16(o) || !aligned16(workspace))
+    return fail(MLA_ERR_INVALID_ARG, "tensors of the explicit prefill must be 16-byte aligned");
+  const size_t need = mla::prefill_explicit_workspace_bytes(L, batch, max_seq_len);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu%s", need, workspace_bytes,
+                workspace ? "" : " (NULL)");
+  hipError_t e = mla::launch_prefill_explicit(L, batch, n_q, q_nope, q_rope, cache, seq_off, seq_len, max_seq_len, w_uk,
+                                              w_uv, workspace, o, lse, (hipStream_t)stream);
+  return from_hip(e, "mla_prefill_explicit launch");
+}
+
 mla_status mla_decode_advance(int32_t batch, int32_t n_new, int32_t* len_before, int32_t* seq_len, int32_t n_rows,
                               int32_t* q_pos, void* stream) {
   if (batch < 0 || n_rows < 0 || n_new < 0) return fail(MLA_ERR_INVALID_ARG, "batch, n_new and n_rows must be >= 0");

@@ -90,6 +90,19 @@ hipError_t launch_project_q(const LayerDims& L, int n_rows, int d_model, int d_q
                             const void* w_uq, const void* w_qr, void* q_nope, void* q_rope, void* workspace,
                             hipStream_t stream);
 
+// Explicit (non-absorbed) prefill for the DeepSeek head shape (prefill_explicit.hip): K_C and V
+// rebuilt by a GEMM over the cached latents (linear.hip), then multi-head attention with 192-wide
+// keys; writes the heads' outputs o directly
+hipError_t launch_kv_expand(int batch, int max_seq_len, int n_out, int d_latent, int row, const void* cache,
+                            const int64_t* seq_off, const int32_t* seq_len, const void* w_uk, const void* w_uv,
+                            void* kc, void* vv, hipStream_t stream);
+bool prefill_explicit_supported(const LayerDims& L);
+size_t prefill_explicit_workspace_bytes(const LayerDims& L, int batch, int max_seq_len);
+hipError_t launch_prefill_explicit(const LayerDims& L, int batch, int n_q, const void* q_nope, const void* q_rope,
+                                   const void* cache, const int64_t* seq_off, const int32_t* seq_len, int max_seq_len,
+                                   const void* w_uk, const void* w_uv, void* workspace, void* o, float* lse,
+                                   hipStream_t stream);
+
 // Position bookkeeping between decode steps (generic.hip)
 hipError_t launch_decode_advance(int batch, int n_new, int32_t* len_before, int32_t* seq_len, int n_rows,
                                  int32_t* q_pos, hipStream_t stream);

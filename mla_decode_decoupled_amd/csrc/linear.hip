@@ -174,13 +174,30 @@ constexpr int TM = 128, TN = 128, TK = 32;
 constexpr int SROW = TK + 8;   // bf16 per staged row (80 bytes: 16 lanes of a 16-byte read hit 16 bank groups)
 constexpr int GEMM_LDS = 2 * 2 * TM * SROW * 2;   // two buffers of the A and B tiles
 
-// grid (ceil(n / 128), ceil(M / 128)), 256 threads, GEMM_LDS dynamic LDS; K % 32 == 0.
+// Per-sequence rows (SEQ form): blockIdx.z is a sequence b whose M = len[b] rows start at row
+// off[b] of x; its outputs start y_bstride elements further per b.
+struct SeqRows {
+  const int32_t* len;
+  const int64_t* off;
+  int64_t y_bstride;
+};
+
+// grid (ceil(n / 128), ceil(M / 128)[, sequences]), 256 threads, GEMM_LDS dynamic LDS; K % 32 == 0.
 // Wave w computes rows 64 (w / 2) .. +63 and columns 64 (w % 2) .. +63 of the tile: 2 x 2 MFMA
 // blocks of 32 x 32. Per K step of 32, every thread moves 2 x 16 bytes of A (x rows) and of B
 // (weight rows) global -> registers -> LDS; the next step's loads are in flight during the MFMAs.
-template <typename Ty>
-__global__ void __launch_bounds__(256) lin_gemm(const bf16* __restrict__ x, int ldx, int M, int K, Seg2 s) {
+template <typename Ty, bool SEQ>
+__global__ void __launch_bounds__(256) lin_gemm(const bf16* __restrict__ x, int ldx, int M, int K, Seg2 s,
+                                                SeqRows sq) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  if constexpr (SEQ) {
+    const int b = blockIdx.z;
+    M = sq.len[b];
+    if ((int)blockIdx.y * TM >= M) return;   // whole workgroup, before any barrier
+    x += sq.off[b] * (int64_t)ldx;
+    s.y1 = (Ty*)s.y1 + b * sq.y_bstride;
+    s.y2 = (Ty*)s.y2 + b * sq.y_bstride;
+  }
   bf16* As = reinterpret_cast<bf16*>(smem);   // [2][TM][SROW]
   bf16* Bs = As + 2 * TM * SROW;              // [2][TN][SROW]
   const int m0 = blockIdx.y * TM, n0 = blockIdx.x * TN;
@@ -274,12 +291,13 @@ hipError_t linear(const T* x, int ldx, int M, int K, const Seg2& s, hipStream_t 
     if (vec && M >= kGemmMinRows && K % TK == 0) {
       static bool attr_set = false;
       if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)lin_gemm<Ty>, hipFuncAttributeMaxDynamicSharedMemorySize, GEMM_LDS);
+        hipError_t e = hipFuncSetAttribute((const void*)lin_gemm<Ty, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           GEMM_LDS);
         if (e != hipSuccess) return e;
         attr_set = true;
       }
-      hipLaunchKernelGGL(lin_gemm<Ty>, dim3((s.n + TN - 1) / TN, (M + TM - 1) / TM), dim3(256), GEMM_LDS, stream,
-                         x, ldx, M, K, s);
+      hipLaunchKernelGGL((lin_gemm<Ty, false>), dim3((s.n + TN - 1) / TN, (M + TM - 1) / TM), dim3(256), GEMM_LDS,
+                         stream, x, ldx, M, K, s, SeqRows{nullptr, nullptr, 0});
       return hipGetLastError();
     }
     if (vec && M < kGemmMinRows) {
@@ -407,6 +425,27 @@ hipError_t launch_linear(const void* x, int ldx, int M, int K, const void* w, in
 }
 template hipError_t launch_linear<float>(const void*, int, int, int, const void*, int, void*, int, hipStream_t);
 template hipError_t launch_linear<__bf16>(const void*, int, int, int, const void*, int, void*, int, hipStream_t);
+
+// K_C = C W_UK^T and V = C W_UV^T for every key of every sequence (the explicit form's key and
+// value reconstruction): per sequence b the latents are the first d_latent columns of its cache
+// rows seq_off[b] .. seq_off[b] + seq_len[b] - 1; outputs kc / vv [batch][max_seq_len][H * 128].
+hipError_t launch_kv_expand(int batch, int max_seq_len, int n_out, int d_latent, int row, const void* cache,
+                            const int64_t* seq_off, const int32_t* seq_len, const void* w_uk, const void* w_uv,
+                            void* kc, void* vv, hipStream_t stream) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)lin::lin_gemm<bf16, true>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lin::GEMM_LDS);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  lin::Seg2 s{w_uk, w_uv, kc, vv, n_out, 2 * n_out, n_out, n_out};
+  lin::SeqRows sq{seq_len, seq_off, (int64_t)max_seq_len * n_out};
+  const dim3 grid((2 * n_out + lin::TN - 1) / lin::TN, (max_seq_len + lin::TM - 1) / lin::TM, batch);
+  hipLaunchKernelGGL((lin::lin_gemm<bf16, true>), grid, dim3(256), lin::GEMM_LDS, stream, (const bf16*)cache, row,
+                     max_seq_len, d_latent, s, sq);
+  return hipGetLastError();
+}
 
 template hipError_t launch_project_kv_append<float>(const LayerDims&, int, int, int, const void*, const void*,
                                                     const void*, const void*, float, int, void*, const int64_t*,

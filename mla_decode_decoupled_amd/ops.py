@@ -212,6 +212,38 @@ def mla_project_q(cfg: MlaConfig, h: torch.Tensor, w_uq: torch.Tensor, w_qr: Opt
                             _ptr(q_rope), wp, wb, _stream(q_nope)), "mla_project_q")
 
 
+def mla_prefill_explicit_workspace_size(cfg: MlaConfig, batch: int, n_q: int, max_seq_len: int) -> int:
+    return int(lib.mla_prefill_explicit_workspace_size(cfg, batch, n_q, max_seq_len))
+
+
+def mla_prefill_explicit(cfg: MlaConfig, q_nope: torch.Tensor, q_rope: torch.Tensor, cache: torch.Tensor,
+                         seq_off: torch.Tensor, seq_len: torch.Tensor, max_seq_len: int, w_uk: torch.Tensor,
+                         w_uv: torch.Tensor, o: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None) -> None:
+    """Non-absorbed attention of q [batch, n_q, H, .] over the cache; writes the heads' outputs
+    o [batch, n_q, H, d_v] (and lse)."""
+    dt = storage_dtype(cfg)
+    H = cfg.n_heads
+    if q_nope.dim() != 4:
+        raise ValueError("q_nope must be [batch, n_q, H, d_nope]")
+    B, n_q = q_nope.shape[0], q_nope.shape[1]
+    dev = q_nope.device
+    _need(q_nope, "q_nope", dt, (B, n_q, H, cfg.d_nope))
+    _need(q_rope, "q_rope", dt, (B, n_q, H, cfg.d_rope), dev)
+    _need(cache, "cache", dt, None, dev)
+    _need(seq_off, "seq_off", torch.int64, (B,), dev)
+    _need(seq_len, "seq_len", torch.int32, (B,), dev)
+    _need(w_uk, "w_uk", dt, (H, cfg.d_nope, cfg.d_latent), dev)
+    _need(w_uv, "w_uv", dt, (H, cfg.d_v, cfg.d_latent), dev)
+    _need(o, "o", dt, (B, n_q, H, cfg.d_v), dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, n_q, H), dev)
+    wp, wb = _ws(workspace, dev)
+    check(lib.mla_prefill_explicit(cfg, B, n_q, _ptr(q_nope), _ptr(q_rope), _ptr(cache), _ptr(seq_off), _ptr(seq_len),
+                                   int(max_seq_len), _ptr(w_uk), _ptr(w_uv), wp, wb, _ptr(o), _ptr(lse), _stream(o)),
+          "mla_prefill_explicit")
+
+
 def mla_decode_advance(n_new: int, len_before: Optional[torch.Tensor] = None, seq_len: Optional[torch.Tensor] = None,
                        q_pos: Optional[torch.Tensor] = None) -> None:
     """len_before += n_new, seq_len += n_new, q_pos += n_new on the device (any may be None)."""
@@ -252,6 +284,8 @@ __all__ = [
     "mla_project_kv_append",
     "mla_project_q",
     "mla_decode_advance",
+    "mla_prefill_explicit_workspace_size",
+    "mla_prefill_explicit",
     "version",
     "_lib",
 ]

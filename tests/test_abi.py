@@ -174,3 +174,25 @@ def test_projection_and_advance_arguments():
     assert lib.mla_decode_advance(4, 0, FAKE, FAKE, 4, FAKE, None) == MLA_OK
     assert lib.mla_decode_advance(4, 1, None, None, 4, None, None) == MLA_OK
     assert lib.mla_last_error() == b""
+
+
+def test_explicit_prefill_arguments():
+    c = cfg()
+    ws = lib.mla_prefill_explicit_workspace_size(c, 2, 2048, 4096)
+    assert ws == 2 * 2 * 4096 * 128 * 128 * 2
+    assert lib.mla_prefill_explicit_workspace_size(cfg(dtype=MLA_F32), 2, 2048, 4096) == 0   # not covered
+    assert lib.mla_prefill_explicit_workspace_size(c, 2, 2048, 100) == 0                     # max_seq_len < n_q
+    args = lambda c, ws_ptr, ws_bytes, o=FAKE: (c, 2, 2048, FAKE, FAKE, FAKE, FAKE, FAKE, 4096, FAKE, FAKE,   # noqa: E731
+                                                 ws_ptr, ws_bytes, o, None, None)
+    assert lib.mla_prefill_explicit(*args(cfg(dtype=MLA_F32), FAKE, ws)) == MLA_ERR_UNSUPPORTED
+    assert lib.mla_prefill_explicit(*args(cfg(d_rope=32), FAKE, ws)) == MLA_ERR_UNSUPPORTED
+    assert lib.mla_prefill_explicit(*args(c, None, ws)) == MLA_ERR_WORKSPACE
+    assert lib.mla_prefill_explicit(*args(c, FAKE, ws - 1)) == MLA_ERR_WORKSPACE
+    assert lib.mla_prefill_explicit(*args(c, FAKE, ws, o=None)) == MLA_ERR_INVALID_ARG
+    assert lib.mla_prefill_explicit(c, 2, 2048, FAKE, FAKE, FAKE, FAKE, FAKE, 100, FAKE, FAKE, FAKE, ws, FAKE, None,
+                                    None) == MLA_ERR_INVALID_ARG                                  # max_seq_len < n_q
+    odd = ctypes.c_void_p(0x1008)
+    assert lib.mla_prefill_explicit(c, 2, 2048, odd, FAKE, FAKE, FAKE, FAKE, 4096, FAKE, FAKE, FAKE, ws, FAKE, None,
+                                    None) == MLA_ERR_INVALID_ARG                                  # misaligned
+    assert lib.mla_prefill_explicit(c, 0, 2048, None, None, None, None, None, 0, None, None, None, 0, None, None,
+                                    None) == MLA_OK
