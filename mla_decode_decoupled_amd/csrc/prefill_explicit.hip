@@ -105,6 +105,7 @@ __global__ void __launch_bounds__(256, 2) attn_explicit(const bf16* __restrict__
   const int row = t0 + 32 * w + l32;         // this lane's query row (the B / accumulator column)
   const bool row_ok = row < n_q;
   const int pos = S - n_q + (row_ok ? row : n_q - 1);   // its position = last visible key
+  const int wave_pos0 = S - n_q + t0 + 32 * w;           // position of the wave's first row
   // keys the workgroup needs: up to the last row's position
   const int last_row = min(t0 + BM, n_q) - 1;
   const int n_keys = S - n_q + last_row + 1;
@@ -143,15 +144,30 @@ __global__ void __launch_bounds__(256, 2) attn_explicit(const bf16* __restrict__
   const int tk = threadIdx.x >> 4, tc = threadIdx.x & 15;     // content keys / values
   const int rk = threadIdx.x >> 3, rc = threadIdx.x & 7;      // position keys
   i32x4 ld[PIECES_PER_THREAD];
+  // whole tiles advance three base pointers; only the sequence's last, partial tile clamps keys
+  const bf16* kc_p = kc + ((kvrow0 + tk) * H + i) * DN + 8 * tc;
+  const bf16* vv_p = vv + ((kvrow0 + tk) * H + i) * DV + 8 * tc;
+  const bf16* kr_p = cache + (off + rk) * ROW + DC + 8 * rc;
+  const size_t kv_step = (size_t)TK * H * DN;   // one tile of keys in kc / vv
   auto gload = [&](int tile) {
     const int j0 = tile * TK;
+    if (j0 + TK <= S) {
+      const size_t o = (size_t)tile * kv_step;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int key = min(j0 + tk + 16 * h, S - 1);
-      ld[h] = *reinterpret_cast<const i32x4*>(kc + ((kvrow0 + key) * H + i) * DN + 8 * tc);
-      ld[3 + h] = *reinterpret_cast<const i32x4*>(vv + ((kvrow0 + key) * H + i) * DV + 8 * tc);
+      for (int h = 0; h < 2; ++h) {
+        ld[h] = *reinterpret_cast<const i32x4*>(kc_p + o + (size_t)16 * h * H * DN);
+        ld[3 + h] = *reinterpret_cast<const i32x4*>(vv_p + o + (size_t)16 * h * H * DV);
+      }
+      ld[2] = *reinterpret_cast<const i32x4*>(kr_p + (size_t)j0 * ROW);
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int key = min(j0 + tk + 16 * h, S - 1);
+        ld[h] = *reinterpret_cast<const i32x4*>(kc + ((kvrow0 + key) * H + i) * DN + 8 * tc);
+        ld[3 + h] = *reinterpret_cast<const i32x4*>(vv + ((kvrow0 + key) * H + i) * DV + 8 * tc);
+      }
+      ld[2] = *reinterpret_cast<const i32x4*>(cache + (off + min(j0 + rk, S - 1)) * ROW + DC + 8 * rc);
     }
-    ld[2] = *reinterpret_cast<const i32x4*>(cache + (off + min(j0 + rk, S - 1)) * ROW + DC + 8 * rc);
   };
   auto lstore = [&](int buf) {
     bf16* ks = smem + buf * BUF_ELEMS;
@@ -179,21 +195,34 @@ __global__ void __launch_bounds__(256, 2) attn_explicit(const bf16* __restrict__
     const bf16* ks = smem + buf * BUF_ELEMS;
     const bf16* vs = ks + KS_ELEMS;
     // scores of the tile: A = key rows (permuted), B = this wave's query fragments
+    // all 12 key fragments are read before the first MFMA, so the chain waits for one LDS round trip
     f32x16e sacc = f32x16e{};
     const bf16* krow = ks + akey * KS_STRIDE + 8 * g;
+    bf16x8e kf[12];
 #pragma unroll
-    for (int s = 0; s < 12; ++s) sacc = mfma(*reinterpret_cast<const bf16x8e*>(krow + 16 * s), qf[s], sacc);
-    // causal mask and online softmax; register r holds key 16 (r / 8) + 8 g + (r % 8)
+    for (int s = 0; s < 12; ++s) kf[s] = *reinterpret_cast<const bf16x8e*>(krow + 16 * s);
+#pragma unroll
+    for (int s = 0; s < 12; ++s) sacc = mfma(kf[s], qf[s], sacc);
+    // keep the scheduler from interleaving the reads back between the MFMAs: 12 LDS reads, then
+    // the 12 MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
+    // causal mask and online softmax on the raw scores (the scale is positive, so it is applied in
+    // the exponent); register r holds key 16 (r / 8) + 8 g + (r % 8). Only tiles reaching past the
+    // first position of the wave's rows need the mask.
     const int j0 = t * TK;
     float sv[16];
-    float mx = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = j0 + 16 * (r >> 3) + 8 * g + (r & 7);
-      sv[r] = key <= pos ? sacc[r] * scale_log2 : -INFINITY;
-      mx = fmaxf(mx, sv[r]);
+    for (int r = 0; r < 16; ++r) sv[r] = sacc[r];
+    if (j0 + TK - 1 > wave_pos0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (j0 + 16 * (r >> 3) + 8 * g + (r & 7) > pos) sv[r] = -INFINITY;
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    float mx = sv[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sv[r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
     // Lazy rescaling: the running reference m_run only moves when a score exceeds it by more than
     // RESCALE (log2 units), so probabilities stay below 2^RESCALE and the accumulator is rescaled
     // only on those (rare, mostly early) tiles. Softmax is exact for any reference. Key 0 is
@@ -210,7 +239,8 @@ __global__ void __launch_bounds__(256, 2) attn_explicit(const bf16* __restrict__
     float psum = 0.0f;
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(sv[r] - m_run), p1 = __builtin_amdgcn_exp2f(sv[r + 1] - m_run);
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(sv[r], scale_log2, -m_run));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(sv[r + 1], scale_log2, -m_run));
       psum += p0 + p1;
       pk[r / 2] = __builtin_bit_cast(int, __builtin_convertvector((f32x2e){p0, p1}, bf16x2e));
     }
@@ -221,6 +251,7 @@ __global__ void __launch_bounds__(256, 2) attn_explicit(const bf16* __restrict__
     // 32 c + l32, gathered by two transpose reads (lane L of a 16-lane group points at row
     // 16 s + 8 g + 4 h + L / 4, columns 32 c + 16 (q & 1) + 4 (L & 3) .. +3, q = lane / 16)
     const int q = lane >> 4, L = lane & 15;
+    bf16x8e vf[2][4];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
@@ -231,8 +262,14 @@ __global__ void __launch_bounds__(256, 2) attn_explicit(const bf16* __restrict__
           const bf16* p = vs + (16 * s + 8 * g + 4 * h + (L >> 2)) * VS_STRIDE + 32 * c + 16 * (q & 1) + 4 * (L & 3);
           hv[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4e*)MLA_LDS(bf16, p));
         }
-        oacc[c] = mfma(__builtin_bit_cast(bf16x8e, hv), pb[s], oacc[c]);
+        vf[s][c] = __builtin_bit_cast(bf16x8e, hv);
       }
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) oacc[c] = mfma(vf[s][c], pb[s], oacc[c]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     if (t + 1 < n_tiles) {
       // the other buffer was last read in iteration t - 1, which every wave finished before the
       // previous barrier
