@@ -739,6 +739,9 @@ __global__ void __launch_bounds__(256)
     dma_rows(reinterpret_cast<const unsigned char*>(q_packed + ((size_t)bt * H + head0) * ROW), TILE - 1, 3);
   };
   if (rows == 1) stage_queries(0);
+  // sequence 0's slab offset is loaded next to the plan's lengths rather than after it: with one
+  // sequence (the latency-bound case) the tile addresses then wait for one memory round trip
+  const int64_t off0 = seq_off[0];
   Chunk ch;
   if (!hsplit_chunk(seq_len, n_q, rows, cidx, &ch)) {   // the plan has fewer chunks than the grid
     wait_vmcnt_0();   // no LDS load may land after the workgroup has ended
@@ -749,7 +752,7 @@ __global__ void __launch_bounds__(256)
   const size_t rh0 = (size_t)bt * H;
   if (row_chunks != nullptr && ch.k == 0 && hb == 0 && threadIdx.x == 0) row_chunks[bt] = make_int2(ch.slot, n_chunks);
   const int n_tiles = (j1 - j0 + TILE - 1) / TILE;
-  const unsigned char* kv = reinterpret_cast<const unsigned char*>(cache + seq_off[b] * (int64_t)ROW);
+  const unsigned char* kv = reinterpret_cast<const unsigned char*>(cache + (b == 0 ? off0 : seq_off[b]) * (int64_t)ROW);
   auto issue_tile = [&](int tile) {
     const int key0 = j0 + tile * TILE;
     dma_rows(kv + (int64_t)key0 * ROW_BYTES, min(TILE, j1 - key0) - 1, tile % HS_NBUF);
