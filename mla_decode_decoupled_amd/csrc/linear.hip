@@ -186,7 +186,13 @@ struct SeqRows {
 // Wave w computes rows 64 (w / 2) .. +63 and columns 64 (w % 2) .. +63 of the tile: 2 x 2 MFMA
 // blocks of 32 x 32. Per K step of 32, every thread moves 2 x 16 bytes of A (x rows) and of B
 // (weight rows) global -> registers -> LDS; the next step's loads are in flight during the MFMAs.
-template <typename Ty, bool SEQ>
+// STAGED (bf16 outputs whose rows and segments allow 16-byte stores): the MFMAs compute the tile
+// transposed, D[n][m], so each lane holds 4 consecutive outputs of one row; the tile is staged in
+// LDS and written back with 16-byte stores, 16 lanes per 256-byte row.
+constexpr int CS_STRIDE = TN + 8;   // bf16 per staged output row (272 bytes)
+static_assert(TM * CS_STRIDE * 2 <= GEMM_LDS, "output staging fits the operand buffers");
+
+template <typename Ty, bool SEQ, bool STAGED>
 __global__ void __launch_bounds__(256) lin_gemm(const bf16* __restrict__ x, int ldx, int M, int K, Seg2 s,
                                                 SeqRows sq) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -256,12 +262,43 @@ __global__ void __launch_bounds__(256) lin_gemm(const bf16* __restrict__ x, int 
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = STAGED ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0)
+                             : __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
     if (kt + 1 < NK) {
       lstore(buf ^ 1);   // the other buffer was last read before the previous barrier
       __syncthreads();
     }
+  }
+  if constexpr (STAGED) {
+    // D^T block (i, j): lane holds row m = l32 of block i, columns 8 q + 4 g + e of block j
+    __syncthreads();   // every wave is done with the operand buffers
+    bf16* Cs = As;     // [TM][CS_STRIDE]
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          bf16x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (bf16)acc[i][j][4 * q + e];
+          *reinterpret_cast<bf16x4*>(Cs + (wm + 32 * i + l32) * CS_STRIDE + wn + 32 * j + 8 * q + 4 * g) = v;
+        }
+    __syncthreads();
+    const int c = t & 15;
+#pragma unroll
+    for (int k = 0; k < TM / 16; ++k) {
+      const int r = (t >> 4) + 16 * k;
+      const int m = m0 + r, n = n0 + 8 * c;
+      if (m < M && n < s.n) {
+        const i32x4 v = *reinterpret_cast<const i32x4*>(Cs + r * CS_STRIDE + 8 * c);
+        bf16* dst = n < s.n1 ? (bf16*)s.y1 + (size_t)m * s.ldy1 + n : (bf16*)s.y2 + (size_t)m * s.ldy2 + (n - s.n1);
+        *reinterpret_cast<i32x4*>(dst) = v;
+      }
+    }
+    return;
   }
   // D block (i, j): lane holds column n = l32, rows 8 q + 4 g + e (register 4 q + e)
 #pragma unroll
@@ -282,6 +319,13 @@ __global__ void __launch_bounds__(256) lin_gemm(const bf16* __restrict__ x, int 
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// the staged GEMM epilogue writes 8 consecutive bf16 outputs per 16-byte store
+bool staged_ok(const Seg2& s) {
+  const bool two = s.n != s.n1;
+  return s.n % 8 == 0 && s.n1 % 8 == 0 && s.ldy1 % 8 == 0 && aligned16(s.y1) &&
+         (!two || (s.ldy2 % 8 == 0 && aligned16(s.y2)));
+}
+
 // y = x W^T over the two segments; Ty is float or the storage type T
 template <typename T, typename Ty>
 hipError_t linear(const T* x, int ldx, int M, int K, const Seg2& s, hipStream_t stream) {
@@ -291,13 +335,21 @@ hipError_t linear(const T* x, int ldx, int M, int K, const Seg2& s, hipStream_t 
     if (vec && M >= kGemmMinRows && K % TK == 0) {
       static bool attr_set = false;
       if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)lin_gemm<Ty, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           GEMM_LDS);
+        hipError_t e = hipFuncSetAttribute((const void*)lin_gemm<Ty, false, false>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, GEMM_LDS);
+        if (e == hipSuccess)
+          e = hipFuncSetAttribute((const void*)lin_gemm<Ty, false, sizeof(Ty) == 2>,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, GEMM_LDS);
         if (e != hipSuccess) return e;
         attr_set = true;
       }
-      hipLaunchKernelGGL((lin_gemm<Ty, false>), dim3((s.n + TN - 1) / TN, (M + TM - 1) / TM), dim3(256), GEMM_LDS,
-                         stream, x, ldx, M, K, s, SeqRows{nullptr, nullptr, 0});
+      const dim3 grid((s.n + TN - 1) / TN, (M + TM - 1) / TM);
+      if (sizeof(Ty) == 2 && staged_ok(s))
+        hipLaunchKernelGGL((lin_gemm<Ty, false, sizeof(Ty) == 2>), grid, dim3(256), GEMM_LDS, stream, x, ldx, M, K, s,
+                           SeqRows{nullptr, nullptr, 0});
+      else
+        hipLaunchKernelGGL((lin_gemm<Ty, false, false>), grid, dim3(256), GEMM_LDS, stream, x, ldx, M, K, s,
+                           SeqRows{nullptr, nullptr, 0});
       return hipGetLastError();
     }
     if (vec && M < kGemmMinRows) {
@@ -434,7 +486,7 @@ hipError_t launch_kv_expand(int batch, int max_seq_len, int n_out, int d_latent,
                             void* kc, void* vv, hipStream_t stream) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)lin::lin_gemm<bf16, true>,
+    hipError_t e = hipFuncSetAttribute((const void*)lin::lin_gemm<bf16, true, true>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lin::GEMM_LDS);
     if (e != hipSuccess) return e;
     attr_set = true;
@@ -442,8 +494,9 @@ hipError_t launch_kv_expand(int batch, int max_seq_len, int n_out, int d_latent,
   lin::Seg2 s{w_uk, w_uv, kc, vv, n_out, 2 * n_out, n_out, n_out};
   lin::SeqRows sq{seq_len, seq_off, (int64_t)max_seq_len * n_out};
   const dim3 grid((2 * n_out + lin::TN - 1) / lin::TN, (max_seq_len + lin::TM - 1) / lin::TM, batch);
-  hipLaunchKernelGGL((lin::lin_gemm<bf16, true>), grid, dim3(256), lin::GEMM_LDS, stream, (const bf16*)cache, row,
-                     max_seq_len, d_latent, s, sq);
+  // n_out = H * 128 and the workspace rows keep every staged 16-byte store aligned
+  hipLaunchKernelGGL((lin::lin_gemm<bf16, true, true>), grid, dim3(256), lin::GEMM_LDS, stream, (const bf16*)cache,
+                     row, max_seq_len, d_latent, s, sq);
   return hipGetLastError();
 }
 

@@ -143,13 +143,13 @@ __global__ void __launch_bounds__(256, 2) attn_explicit(const bf16* __restrict__
   const size_t kvrow0 = (size_t)b * max_seq_len;
   const int tk = threadIdx.x >> 4, tc = threadIdx.x & 15;     // content keys / values
   const int rk = threadIdx.x >> 3, rc = threadIdx.x & 7;      // position keys
-  i32x4 ld[PIECES_PER_THREAD];
+  i32x4 ldA[PIECES_PER_THREAD], ldB[PIECES_PER_THREAD];   // two register sets: tiles t+1 and t+2 in flight
   // whole tiles advance three base pointers; only the sequence's last, partial tile clamps keys
   const bf16* kc_p = kc + ((kvrow0 + tk) * H + i) * DN + 8 * tc;
   const bf16* vv_p = vv + ((kvrow0 + tk) * H + i) * DV + 8 * tc;
   const bf16* kr_p = cache + (off + rk) * ROW + DC + 8 * rc;
   const size_t kv_step = (size_t)TK * H * DN;   // one tile of keys in kc / vv
-  auto gload = [&](int tile) {
+  auto gload = [&](i32x4 (&ld)[PIECES_PER_THREAD], int tile) {
     const int j0 = tile * TK;
     if (j0 + TK <= S) {
       const size_t o = (size_t)tile * kv_step;
@@ -169,7 +169,7 @@ __global__ void __launch_bounds__(256, 2) attn_explicit(const bf16* __restrict__
       ld[2] = *reinterpret_cast<const i32x4*>(cache + (off + min(j0 + rk, S - 1)) * ROW + DC + 8 * rc);
     }
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](const i32x4 (&ld)[PIECES_PER_THREAD], int buf) {
     bf16* ks = smem + buf * BUF_ELEMS;
     bf16* vs = ks + KS_ELEMS;
 #pragma unroll
@@ -186,12 +186,11 @@ __global__ void __launch_bounds__(256, 2) attn_explicit(const bf16* __restrict__
   float m_run = -INFINITY, l_run = 0.0f;
   const int akey = key_of_row(l32);
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int t = 0; t < n_tiles; ++t) {
+  // Tile t is in LDS buffer t % 2 while the registers hold tiles t + 1 and t + 2 in flight (two
+  // sets, alternating), so a tile's global loads have two iterations to land before they are
+  // stored to LDS at the end of the iteration before its own.
+  auto compute = [&](int t) {
     const int buf = t & 1;
-    if (t + 1 < n_tiles) gload(t + 1);
     const bf16* ks = smem + buf * BUF_ELEMS;
     const bf16* vs = ks + KS_ELEMS;
     // scores of the tile: A = key rows (permuted), B = this wave's query fragments
@@ -200,13 +199,21 @@ __global__ void __launch_bounds__(256, 2) attn_explicit(const bf16* __restrict__
     const bf16* krow = ks + akey * KS_STRIDE + 8 * g;
     bf16x8e kf[12];
 #pragma unroll
-    for (int s = 0; s < 12; ++s) kf[s] = *reinterpret_cast<const bf16x8e*>(krow + 16 * s);
+    for (int s = 0; s < 6; ++s) kf[s] = *reinterpret_cast<const bf16x8e*>(krow + 16 * s);
 #pragma unroll
-    for (int s = 0; s < 12; ++s) sacc = mfma(kf[s], qf[s], sacc);
-    // keep the scheduler from interleaving the reads back between the MFMAs: 12 LDS reads, then
-    // the 12 MFMAs
-    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
+    for (int s = 0; s < 12; ++s) {
+      sacc = mfma(kf[s], qf[s], sacc);
+      if (s + 6 < 12) kf[s + 6] = *reinterpret_cast<const bf16x8e*>(krow + 16 * (s + 6));
+    }
+    // six reads ahead of the chain, then one read behind each MFMA (it reuses the registers the
+    // MFMA has just consumed), then the last six MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int s = 0; s < 6; ++s) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
     // causal mask and online softmax on the raw scores (the scale is positive, so it is applied in
     // the exponent); register r holds key 16 (r / 8) + 8 g + (r % 8). Only tiles reaching past the
     // first position of the wave's rows need the mask.
@@ -270,12 +277,24 @@ __global__ void __launch_bounds__(256, 2) attn_explicit(const bf16* __restrict__
       for (int c = 0; c < 4; ++c) oacc[c] = mfma(vf[s][c], pb[s], oacc[c]);
     __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-    if (t + 1 < n_tiles) {
-      // the other buffer was last read in iteration t - 1, which every wave finished before the
-      // previous barrier
-      lstore(buf ^ 1);
-      __syncthreads();
-    }
+  };
+  gload(ldA, 0);
+  if (n_tiles > 1) gload(ldB, 1);
+  lstore(ldA, 0);
+  __syncthreads();
+  for (int t = 0; t < n_tiles; t += 2) {
+    // even tile: set A is free (tile t was stored), set B holds tile t + 1
+    if (t + 2 < n_tiles) gload(ldA, t + 2);
+    compute(t);
+    if (t + 1 >= n_tiles) break;
+    lstore(ldB, (t + 1) & 1);   // buffer (t + 1) % 2 was last read in iteration t - 1
+    __syncthreads();
+    // odd tile: set B is free, set A holds tile t + 2
+    if (t + 3 < n_tiles) gload(ldB, t + 3);
+    compute(t + 1);
+    if (t + 2 >= n_tiles) break;
+    lstore(ldA, t & 1);
+    __syncthreads();
   }
   // ---- output: o[row][32 c + 8 r4 + 4 g + e] = O^T / l, four consecutive values per store
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);

@@ -79,9 +79,12 @@ def test_decode_loop_tiny_two_layers():
         assert torch.equal(got, want), f"replay at token {t} differs from the eager step"
         check(got, t, t + 1, "replayed step")
     assert eager.length == graphed.length == T
-    # the caches the two stacks built agree bit for bit, and hold the oracle's rows for layer 0
+    # the rows the two stacks wrote (T per sequence; the rest of each slab is never written) agree
+    # bit for bit, and hold the oracle's rows for layer 0
     for l in range(2):
-        assert torch.equal(eager.caches[l], graphed.caches[l])
+        written_e = eager.caches[l].view(B, T + 3, -1)[:, :T]
+        written_g = graphed.caches[l].view(B, T + 3, -1)[:, :T]
+        assert torch.equal(written_e, written_g)
     for b in range(B):
         p = O.project_inputs(h[b], {k: host[0][k] for k in LAYER_KEYS if k in host[0]}, cfg.n_heads)
         rows = O.cache_rows(p["c"], p["k_rope_pre"], np.arange(T), cfg.rope_base)
