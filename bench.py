@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--explicit", action="store_true",
                     help="many-row workloads: the step is mla_rope_append + mla_prefill_explicit (the non-absorbed "
                          "form) instead of absorb + latent attention + W_UV")
+    ap.add_argument("--merged-wo-check", action="store_true",
+                    help="time the output side at batch 1 both ways: W_UV per head then W_O (the library's "
+                         "path) against one pre-merged [d_model x H*d_latent] matrix W_O W_UV applied to z")
     ap.add_argument("--decode-loop", action="store_true",
                     help="instead of the single step: time token-by-token decode through a stack of full MLA "
                          "layers (h -> projections -> attention -> W_O) replayed as one HIP graph per token")
@@ -127,6 +130,9 @@ def main():
         return
     if args.decode_loop:
         decode_loop(args)
+        return
+    if args.merged_wo_check:
+        merged_wo_check(args)
         return
 
     import numpy as np
@@ -435,6 +441,56 @@ def decode_loop(args):
                      "frac": round(gbs / HBM_PEAK_GBS, 4)},
         "prefill_s": round(prefill_s, 3),
     }), flush=True)
+
+
+def merged_wo_check(args):
+    """The output side of one decode token (batch 1, DeepSeek-V3 shape), two ways:
+    separate — mla_out_proj with W_O: o_i = W_UV,i z_i, then u = W_O concat(o) (16.8 + 235 MB of weights);
+    merged  — u = (W_O W_UV) z with the pre-multiplied [7168 x 65536] matrix (940 MB), run through the
+              library's linear kernel (mla_project_q on a 56-head layer description whose W_UQ is that
+              matrix: one output row of 7168 values from 65536 inputs).
+    Each weight set is replicated so every timed call reads its weights from HBM."""
+    import torch
+
+    import mla_decode_decoupled_amd as mla
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    bf = torch.bfloat16
+    H, dv, dc, dm = 128, 128, 512, 7168
+    lc = mla.make_config(H, 128, dc, 64, dv, "bf16", 10000.0)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    reps = 4
+    z = torch.randn((1, H, dc), generator=gen, device=dev)
+    zb = z.to(bf).view(1, H * dc)
+    sep = [((torch.randn((H, dv, dc), generator=gen, device=dev) / dc ** 0.5).to(bf),
+            (torch.randn((dm, H * dv), generator=gen, device=dev) / (H * dv) ** 0.5).to(bf)) for _ in range(reps)]
+    merged = [(torch.randn((dm, H * dc), generator=gen, device=dev) / (H * dc) ** 0.5).to(bf) for _ in range(reps)]
+    o = torch.empty((1, H, dv), dtype=bf, device=dev)
+    u = torch.empty((1, dm), dtype=bf, device=dev)
+    lm = mla.make_config(dm // 128, 128, dc, 0, 128, "bf16", 10000.0)   # W_UQ rows = 56 * 128 = 7168
+    qn = torch.empty((1, dm // 128, 128), dtype=bf, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn, n):
+        for i in range(reps):
+            fn(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(n):
+            fn(i % reps)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n * 1e3
+
+    t_sep = timed(lambda i: mla.mla_out_proj(lc, z, sep[i][0], o, w_o=sep[i][1], u=u), args.steps)
+    t_mer = timed(lambda i: mla.mla_project_q(lm, zb, merged[i], None, qn, None), args.steps)
+    print(json.dumps({"metric": "output side of one batch-1 decode token", "unit": "us",
+                      "separate_us": round(t_sep, 2), "separate_weight_bytes": (H * dv * dc + dm * H * dv) * 2,
+                      "merged_us": round(t_mer, 2), "merged_weight_bytes": dm * H * dc * 2,
+                      "steps": args.steps}), flush=True)
 
 
 def cpu_baseline(cfg, c_host, k_host, qn_host, qr_host, wuk_host, wuv_host, lens, budget_s):

@@ -45,7 +45,8 @@ def _small_cfg(cid, H, n_q, lens):
     (4, 40, [100, 57]),          # one ragged query block, two sequences of different lengths
     (8, 300, [300, 333]),        # three query blocks; the first sequence has no cached prefix
     (6, 129, [129 + 31, 1000]),   # 12 (sequence, head) pairs; a query block of one row; a key tail
-], ids=["h4_q40", "h8_q300_empty_prefix", "h6_q129_tail"])
+    (4, 1, [1, 70]),              # one query row (a decode step): a sequence whose only key is itself
+], ids=["h4_q40", "h8_q300_empty_prefix", "h6_q129_tail", "h4_q1_single_key"])
 def test_explicit_prefill_all_outputs(H, n_q, lens):
     cfg = _small_cfg(200 + H, H, n_q, lens)
     hi = host_inputs(cfg, lens=lens)

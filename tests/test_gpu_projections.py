@@ -94,14 +94,14 @@ def test_project_q_tiny_fp32(q_lora):
 @pytest.fixture(scope="module")
 def v3_weights():
     cfg = get_config(1)
-    w = G.full_layer_inputs(cfg, 160)
+    w = G.full_layer_inputs(cfg, 520)
     w.pop("w_o")
     return cfg, w
 
 
 # 1-5 rows: the matrix-vector kernel (row blocks of 1, 2 and 4, with a ragged tail);
-# 16 and 160 rows: the MFMA GEMM (one partial row tile, and a ragged second tile)
-@pytest.mark.parametrize("rows", [1, 2, 3, 5, 16, 160])
+# 16, 160 and 520 rows: the MFMA GEMM (one partial row tile, a ragged second tile, five tiles)
+@pytest.mark.parametrize("rows", [1, 2, 3, 5, 16, 160, 520])
 def test_project_v3_shape_bf16(v3_weights, rows):
     cfg, w = v3_weights
     h = w["h"][:rows]
@@ -112,9 +112,10 @@ def test_project_v3_shape_bf16(v3_weights, rows):
     # sequences of one token each at scattered positions
     got, ref = _run_kv(cfg, w, h[None], np.array([100]))
     s3 = assert_close(got, ref, "bf16", f"cache rows rows={rows} (one sequence)")
-    lb = np.random.default_rng(rows).integers(0, 5000, size=rows)
-    got, ref = _run_kv(cfg, w, h[:, None], lb)
-    assert_close(got, ref, "bf16", f"cache rows rows={rows} (one token per sequence)")
+    if rows <= 160:
+        lb = np.random.default_rng(rows).integers(0, 5000, size=rows)
+        got, ref = _run_kv(cfg, w, h[:, None], lb)
+        assert_close(got, ref, "bf16", f"cache rows rows={rows} (one token per sequence)")
     print(f"rows={rows} q_nope {s1} q_rope {s2} cache {s3}")
 
 
