@@ -31,20 +31,21 @@ __device__ __forceinline__ void unpack8(const i32x4 v, float* f) {
   }
 }
 
-// grid (H, 4 column quarters, row blocks): 512 workgroups of 256 threads, two per CU, each
+// grid (H, 4 column quarters, row blocks of RB): 512 workgroups of 256 threads, two per CU, each
 // streaming a 32 KB slab of W_UK[i] (128 rows x 128 columns) with 8 independent 16-byte loads per
-// lane. Column group cg = t % 16 (8 columns), row group ag = t / 16 (8 rows a); the partial sums
-// of the 16 row groups meet in LDS. The first quarter also rotates the rows' position queries
-// while the weights are in flight.
+// lane. Column group cg = t % 16 (8 columns), row group ag = t / 16 (8 rows a). The partial sums
+// of the 4 row groups of a wave meet by lane exchanges, those of the 4 waves in LDS. The first
+// quarter also rotates the rows' position queries while the weights are in flight.
+template <int RB>
 __global__ void __launch_bounds__(256) absorb_q_gemv(const bf16* __restrict__ q_nope, const bf16* __restrict__ q_rope,
                                                      const int32_t* __restrict__ q_pos, const bf16* __restrict__ w_uk,
                                                      bf16* __restrict__ q_packed, int n_rows, double base) {
-  __shared__ float qs[kRowBlock][DN];
-  __shared__ float red[16][kRowBlock][128 + 4];
+  __shared__ float qs[RB][DN];
+  __shared__ f32x4 red[4][RB][32];   // [wave][row][column quad]
   const int i = blockIdx.x, quarter = blockIdx.y;
-  const int r0 = blockIdx.z * kRowBlock;
-  const int nr = min(kRowBlock, n_rows - r0);
-  const int t = threadIdx.x, cg = t & 15, ag = t >> 4;
+  const int r0 = blockIdx.z * RB;
+  const int nr = min(RB, n_rows - r0);
+  const int t = threadIdx.x, cg = t & 15, ag = t >> 4, w = t >> 6;
   // weights first: 8 independent 16-byte loads per lane
   const bf16* wp = w_uk + ((size_t)i * DN + ag * 8) * DC + quarter * 128 + cg * 8;
   i32x4 wv[8];
@@ -64,39 +65,48 @@ __global__ void __launch_bounds__(256) absorb_q_gemv(const bf16* __restrict__ q_
       dst[2 * j + 1] = (bf16)(x0 * sn + x1 * co);
     }
   }
-  for (int e = t; e < kRowBlock * DN; e += 256) {
+  for (int e = t; e < RB * DN; e += 256) {
     const int rr = e / DN, a = e % DN;
     qs[rr][a] = rr < nr ? (float)q_nope[((size_t)(r0 + rr) * H + i) * DN + a] : 0.0f;
   }
   __syncthreads();
-  float acc[kRowBlock][8];
+  float acc[RB][8];
 #pragma unroll
-  for (int rr = 0; rr < kRowBlock; ++rr)
+  for (int rr = 0; rr < RB; ++rr)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[rr][e] = 0.0f;
 #pragma unroll
   for (int a = 0; a < 8; ++a) {
-    float w[8];
-    unpack8(wv[a], w);
+    float wf[8];
+    unpack8(wv[a], wf);
 #pragma unroll
-    for (int rr = 0; rr < kRowBlock; ++rr) {
+    for (int rr = 0; rr < RB; ++rr) {
       const float q = qs[rr][ag * 8 + a];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[rr][e] = fmaf(w[e], q, acc[rr][e]);
+      for (int e = 0; e < 8; ++e) acc[rr][e] = fmaf(wf[e], q, acc[rr][e]);
     }
   }
+  // lanes l, l ^ 16, l ^ 32, l ^ 48 hold the same 8 columns for the wave's 4 row groups
 #pragma unroll
-  for (int rr = 0; rr < kRowBlock; ++rr)
+  for (int rr = 0; rr < RB; ++rr)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) red[ag][rr][cg * 8 + e] = acc[rr][e];
+    for (int e = 0; e < 8; ++e) {
+      acc[rr][e] += __shfl_xor(acc[rr][e], 16, 64);
+      acc[rr][e] += __shfl_xor(acc[rr][e], 32, 64);
+    }
+  if ((t & 63) < 16)
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr) {
+      red[w][rr][2 * cg] = f32x4{acc[rr][0], acc[rr][1], acc[rr][2], acc[rr][3]};
+      red[w][rr][2 * cg + 1] = f32x4{acc[rr][4], acc[rr][5], acc[rr][6], acc[rr][7]};
+    }
   __syncthreads();
-  // thread t < 128 sums column t of the quarter over the 16 row groups for each row
+  // thread t < 128 sums column t of the quarter over the 4 waves for each row
   if (t < 128)
     for (int rr = 0; rr < nr; ++rr) {
-      float s = 0.0f;
-#pragma unroll
-      for (int g = 0; g < 16; ++g) s += red[g][rr][t];
-      q_packed[((size_t)(r0 + rr) * H + i) * ROW + quarter * 128 + t] = (bf16)s;
+      const float* rp = reinterpret_cast<const float*>(&red[0][rr][0]) + t;
+      const float sum = rp[0] + rp[RB * 128] + rp[2 * RB * 128] + rp[3 * RB * 128];
+      q_packed[((size_t)(r0 + rr) * H + i) * ROW + quarter * 128 + t] = (bf16)sum;
     }
 }
 
@@ -180,9 +190,15 @@ bool proj_fast_supported(const LayerDims& L) {
 
 hipError_t launch_absorb_q_fast(const LayerDims& L, int n_rows, const void* q_nope, const void* q_rope,
                                 const int32_t* q_pos, const void* w_uk, void* q_packed, hipStream_t stream) {
-  const int rb = (n_rows + proj::kRowBlock - 1) / proj::kRowBlock;
-  hipLaunchKernelGGL(proj::absorb_q_gemv, dim3(proj::H, 4, rb), dim3(256), 0, stream, (const bf16*)q_nope,
-                     (const bf16*)q_rope, q_pos, (const bf16*)w_uk, (bf16*)q_packed, n_rows, L.rope_base);
+  if (n_rows == 1) {
+    hipLaunchKernelGGL(proj::absorb_q_gemv<1>, dim3(proj::H, 4, 1), dim3(256), 0, stream, (const bf16*)q_nope,
+                       (const bf16*)q_rope, q_pos, (const bf16*)w_uk, (bf16*)q_packed, n_rows, L.rope_base);
+  } else {
+    const int rb = (n_rows + proj::kRowBlock - 1) / proj::kRowBlock;
+    hipLaunchKernelGGL(proj::absorb_q_gemv<proj::kRowBlock>, dim3(proj::H, 4, rb), dim3(256), 0, stream,
+                       (const bf16*)q_nope, (const bf16*)q_rope, q_pos, (const bf16*)w_uk, (bf16*)q_packed, n_rows,
+                       L.rope_base);
+  }
   return hipGetLastError();
 }
 
