@@ -47,50 +47,59 @@ __device__ __forceinline__ f32x16e mfma(bf16x8e a, bf16x8e b, f32x16e c) {
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)MLA_LDS(const char, p); }
 
-// B operand (16 k x 32 n) of a row-major bf16 tile T[k][n] in LDS (row stride `stride` bytes),
-// k-step s, column block nb, via two transpose reads. Lane l = 16q + L (g = l / 32) gets
-// T[16s + 8g + e][32nb + l % 32] for e = 0..7: source lane L of each 16-lane group points at
-// row 16s + 8g + 4h + L/4, columns 32nb + 16(q & 1) + 4(L & 3) .. +3, for the halves h = 0, 1.
-__device__ __forceinline__ bf16x8e tr_fragment(const unsigned char* tile, int stride, int s, int nb, int lane) {
+// ---------------------------------------------------------------- absorb
+// grid (4 column quarters, ceil(R / 64), H), 256 threads: one workgroup per (head i, 64 rows,
+// quarter of the 512 latent columns), so the 4 quarters of a row tile run side by side and share
+// its q_nope rows through L2. LDS: W_UK[i][:, quarter] (128 rows a x 256 B; 16-byte piece c of
+// row a sits at slot c ^ 4 (a & 3), so the 4 rows x 4 pieces of a transpose read hit distinct
+// banks), the 64 q_nope rows (256 B each, pieces XOR-swizzled by row & 15), the RoPE frequencies;
+// the output tile reuses the weight area. Quarter q also rotates a quarter of each row's position
+// query.
+constexpr int WQ_ROW = 128 * 2;                 // 256 B: one quarter of a W_UK row
+constexpr int A_OFF = DN * WQ_ROW;              // 32768
+constexpr int THETA_OFF = A_OFF + BM * DN * 2;  // 49152
+constexpr int ABSORB_LDS = THETA_OFF + (DR / 2) * 8;
+constexpr int OUT_STRIDE = 128 * 2 + 16;        // staged output rows (bf16, one quarter)
+static_assert(BM * OUT_STRIDE <= A_OFF, "output tile must fit the weight area");
+
+// B operand (16 k x 32 n) of the swizzled quarter slab W[k][n] (rows of 256 B), k-step s, column
+// block nb, via two transpose reads: lane l = 16q + L (g = l / 32) gets W[16s + 8g + e][32nb + l % 32]
+// for e = 0..7; source lane L of each 16-lane group points at row 16s + 8g + 4h + L/4, columns
+// 32nb + 16(q & 1) + 4(L & 3) .. +3 (in 16-byte piece (that column) / 8, swizzled), halves h = 0, 1.
+__device__ __forceinline__ bf16x8e wq_fragment(const unsigned char* slab, int s, int nb, int lane) {
   const int g = lane >> 5, q = lane >> 4, L = lane & 15;
   const int col = 32 * nb + 16 * (q & 1) + 4 * (L & 3);
-  i16x4e h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) i16x4e*)MLA_LDS(unsigned char, tile + (16 * s + 8 * g + (L >> 2)) * stride + 2 * col));
-  i16x4e h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) i16x4e*)MLA_LDS(unsigned char, tile + (16 * s + 8 * g + 4 + (L >> 2)) * stride + 2 * col));
-  const i16x4e h[2] = {h0, h1};
-  return __builtin_bit_cast(bf16x8e, h);
+  i16x4e hv[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int row = 16 * s + 8 * g + 4 * h + (L >> 2);
+    const int piece = (col >> 3) ^ (4 * (row & 3));
+    hv[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4e*)MLA_LDS(
+        unsigned char, slab + row * WQ_ROW + 16 * piece + 2 * (col & 7)));
+  }
+  return __builtin_bit_cast(bf16x8e, hv);
 }
-
-// ---------------------------------------------------------------- absorb
-// grid (ceil(R / 64), H), 256 threads. LDS: W_UK[i] (128 x 512 bf16, rows padded to 1088 B: four
-// consecutive rows then start 16 banks apart, so the 32 lanes of a transpose read hit distinct
-// banks), the 64 q_nope rows (256 B each, 16-byte pieces XOR-swizzled by row), the RoPE
-// frequencies; the output tile reuses the weight area.
-constexpr int WK_STRIDE = DC * 2 + 64;        // 1088
-constexpr int A_OFF = DN * WK_STRIDE;         // 139264
-constexpr int THETA_OFF = A_OFF + BM * DN * 2;  // 155648
-constexpr int ABSORB_LDS = THETA_OFF + (DR / 2) * 8;
-constexpr int OUT_STRIDE = DC * 2 + 16;       // staged output rows (bf16)
-static_assert(BM * OUT_STRIDE <= A_OFF, "output tile must fit the weight area");
 
 __global__ void __launch_bounds__(256) absorb_q_gemm(const bf16* __restrict__ q_nope, const bf16* __restrict__ q_rope,
                                                      const int32_t* __restrict__ q_pos, const bf16* __restrict__ w_uk,
                                                      bf16* __restrict__ q_packed, int n_rows, double base) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const int i = blockIdx.y, r0 = blockIdx.x * BM;
+  const int quarter = blockIdx.x, r0 = blockIdx.y * BM, i = blockIdx.z;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int g = lane >> 5, l32 = lane & 31;
   const int nr = min(BM, n_rows - r0);
   double* theta = reinterpret_cast<double*>(smem + THETA_OFF);
 
-  // W_UK[i]: one 1 KB row per instruction (wave w: rows w, w+4, ..)
+  // W_UK[i][:, quarter]: four 256 B rows per instruction (wave w: instructions w, w + 4, ..);
+  // lane l fills row 4k + l/16, slot l%16 with piece (l%16) ^ 4 (row & 3)
   {
-    const unsigned char* wsrc = reinterpret_cast<const unsigned char*>(w_uk + (size_t)i * DN * DC) + 16 * lane;
     const uint32_t lds0 = lds_addr(smem);
-#pragma unroll 8
-    for (int row = w; row < DN; row += 4)
-      dma16(wsrc + (size_t)row * DC * 2, __builtin_amdgcn_readfirstlane(lds0 + row * WK_STRIDE));
+#pragma unroll
+    for (int k = w; k < DN / 4; k += 4) {
+      const int row = 4 * k + (lane >> 4), slot = lane & 15;
+      const bf16* src = w_uk + ((size_t)i * DN + row) * DC + 128 * quarter + 8 * (slot ^ (4 * (row & 3)));
+      dma16(src, __builtin_amdgcn_readfirstlane(lds0 + k * 1024));
+    }
   }
   // q_nope rows: four 256 B rows per instruction; lane l fills row 4q + l/16, slot l%16 with
   // piece (l%16) ^ (row & 15). Rows past the end repeat the last row (never stored).
@@ -108,22 +117,22 @@ __global__ void __launch_bounds__(256) absorb_q_gemm(const bf16* __restrict__ q_
   __builtin_amdgcn_s_waitcnt(0);   // vmcnt 0: this wave's rows have landed
   __syncthreads();
 
-  // position part of these rows, one thread per (row, 16 pairs): float64-reduced angle, float32
-  // rotation; the 64 bytes of a row half are loaded and stored as four 16-byte pieces
-  if (t < 2 * nr) {
-    const int rr = t >> 1, hj = t & 1;
+  // position part of these rows: quarter q rotates pairs 8q .. 8q + 7 (dims 16q .. 16q + 15), one
+  // thread per row; float64-reduced angle, float32 rotation, two 16-byte pieces in and out
+  if (t < nr) {
+    const int rr = t;
     const size_t r = (size_t)(r0 + rr);
     const int64_t pos = q_pos[r];
-    const i32x4* src = reinterpret_cast<const i32x4*>(q_rope + (r * H + i) * DR + 32 * hj);
-    i32x4 x[4];
+    const i32x4* src = reinterpret_cast<const i32x4*>(q_rope + (r * H + i) * DR + 16 * quarter);
+    i32x4 x[2];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) x[u] = src[u];
-    i32x4 y[4];
+    for (int u = 0; u < 2; ++u) x[u] = src[u];
+    i32x4 y[2];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {   // one pair (2j, 2j+1) per 32-bit word
-        const int j = 16 * hj + 4 * u + e;
+        const int j = 8 * quarter + 4 * u + e;
         float sn, co;
         rope_sincos(theta[j], pos, &sn, &co);
         const uint32_t wd = (uint32_t)x[u][e];
@@ -132,18 +141,14 @@ __global__ void __launch_bounds__(256) absorb_q_gemm(const bf16* __restrict__ q_
         y[u][e] = (int)((uint32_t)__builtin_bit_cast(unsigned short, y0) |
                         ((uint32_t)__builtin_bit_cast(unsigned short, y1) << 16));
       }
-    i32x4* dst = reinterpret_cast<i32x4*>(q_packed + (r * H + i) * ROW + DC + 32 * hj);
+    i32x4* dst = reinterpret_cast<i32x4*>(q_packed + (r * H + i) * ROW + DC + 16 * quarter);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) dst[u] = y[u];
+    for (int u = 0; u < 2; ++u) dst[u] = y[u];
   }
 
-  // wave w: output columns 128w .. 128w + 127 (4 blocks of 32) x both row blocks
-  f32x16e acc[2][4];
+  // wave w: quarter columns 32w .. 32w + 31 x both row blocks
+  f32x16e acc[2] = {f32x16e{}, f32x16e{}};
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) acc[rb][nb] = f32x16e{};
-#pragma unroll 2
   for (int s = 0; s < DN / 16; ++s) {
     bf16x8e a[2];
 #pragma unroll
@@ -151,32 +156,27 @@ __global__ void __launch_bounds__(256) absorb_q_gemm(const bf16* __restrict__ q_
       const int m = 32 * rb + l32;
       a[rb] = *reinterpret_cast<const bf16x8e*>(smem + A_OFF + m * (DN * 2) + 16 * ((2 * s + g) ^ (m & 15)));
     }
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const bf16x8e b = tr_fragment(smem, WK_STRIDE, s, 4 * w + nb, lane);
-      acc[0][nb] = mfma(a[0], b, acc[0][nb]);
-      acc[1][nb] = mfma(a[1], b, acc[1][nb]);
-    }
+    const bf16x8e b = wq_fragment(smem, s, w, lane);
+    acc[0] = mfma(a[0], b, acc[0]);
+    acc[1] = mfma(a[1], b, acc[1]);
   }
   __syncthreads();   // every wave is done with W: the area takes the output tile
 
-  // D layout: lane holds column 32nb' + l32 (nb' = 4w + nb) of rows 32rb + 8j + 4g + e
+  // D layout: lane holds quarter column 32w + l32 of rows 32rb + 8j + 4g + e
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = 32 * rb + 8 * j + 4 * g + e, col = 128 * w + 32 * nb + l32;
-          *reinterpret_cast<bf16*>(smem + row * OUT_STRIDE + 2 * col) = (bf16)acc[rb][nb][4 * j + e];
-        }
+      for (int e = 0; e < 4; ++e) {
+        const int row = 32 * rb + 8 * j + 4 * g + e, col = 32 * w + l32;
+        *reinterpret_cast<bf16*>(smem + row * OUT_STRIDE + 2 * col) = (bf16)acc[rb][4 * j + e];
+      }
   __syncthreads();
-  // whole 1 KB rows out: 64 rows x 64 pieces of 16 bytes
-  for (int p = t; p < nr * (DC / 8); p += 256) {
-    const int row = p / (DC / 8), ch = p % (DC / 8);
-    *reinterpret_cast<i32x4*>(q_packed + ((size_t)(r0 + row) * H + i) * ROW + ch * 8) =
+  // the quarter's 256 B of each row out: 64 rows x 16 pieces of 16 bytes
+  for (int p = t; p < nr * 16; p += 256) {
+    const int row = p >> 4, ch = p & 15;
+    *reinterpret_cast<i32x4*>(q_packed + ((size_t)(r0 + row) * H + i) * ROW + 128 * quarter + ch * 8) =
         *reinterpret_cast<const i32x4*>(smem + row * OUT_STRIDE + ch * 16);
   }
 }
@@ -283,7 +283,8 @@ hipError_t launch_absorb_q_gemm(const LayerDims& L, int n_rows, const void* q_no
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const dim3 grid((n_rows + gemm::BM - 1) / gemm::BM, gemm::H);   // row tiles of one head run together
+  // the quarters of a row tile, then the row tiles of one head, run together
+  const dim3 grid(4, (n_rows + gemm::BM - 1) / gemm::BM, gemm::H);
   hipLaunchKernelGGL(gemm::absorb_q_gemm, grid, dim3(256), gemm::ABSORB_LDS, stream, (const bf16*)q_nope,
                      (const bf16*)q_rope, q_pos, (const bf16*)w_uk, (bf16*)q_packed, n_rows, L.rope_base);
   return hipGetLastError();
