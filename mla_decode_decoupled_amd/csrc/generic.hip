@@ -9,18 +9,26 @@ namespace mla {
 // ------------------------------------------------------------------------------ append
 // One block per new token: copy the latent, rotate the position key in float64, store both
 // into the token's cache row ("Decoupled RoPE · MLA Part 2", §3.4 and §4.3).
+// With vec set (16-byte aligned rows whose latent part is a whole number of 16-byte pieces) the
+// latent is copied 16 bytes per thread.
 template <typename T>
 __global__ void __launch_bounds__(128) rope_append_kernel(const T* __restrict__ c_new, const T* __restrict__ k_new,
                                                           T* __restrict__ cache, const int64_t* __restrict__ seq_off,
                                                           const int32_t* __restrict__ len_before, int n_new,
-                                                          int d_latent, int d_rope, double base) {
+                                                          int d_latent, int d_rope, double base, int vec) {
   const int i = blockIdx.x, b = blockIdx.y;
   const int row = d_latent + d_rope;
   const int64_t p = (int64_t)len_before[b] + i;
   T* dst = cache + (seq_off[b] + p) * (int64_t)row;
   const size_t tok = (size_t)b * n_new + i;
   const T* sc = c_new + tok * d_latent;
-  for (int c = threadIdx.x; c < d_latent; c += blockDim.x) dst[c] = sc[c];
+  if (vec) {
+    const int n16 = d_latent * (int)sizeof(T) / 16;
+    for (int c = threadIdx.x; c < n16; c += blockDim.x)
+      reinterpret_cast<i32x4*>(dst)[c] = reinterpret_cast<const i32x4*>(sc)[c];
+  } else {
+    for (int c = threadIdx.x; c < d_latent; c += blockDim.x) dst[c] = sc[c];
+  }
   const T* sk = k_new + tok * d_rope;
   // cached keys are rotated in float64 and rounded once, so a stored row is exactly the rounding
   // of the true rotated value
@@ -306,8 +314,10 @@ hipError_t launch_rope_append_generic(const LayerDims& L, int batch, int n_new, 
                                       const void* k_new, void* cache, const int64_t* seq_off,
                                       const int32_t* len_before, hipStream_t stream) {
   dim3 grid(n_new, batch);
+  const bool vec = ((size_t)L.d_latent * sizeof(T)) % 16 == 0 && ((size_t)(L.d_latent + L.d_rope) * sizeof(T)) % 16 == 0 &&
+                   ((uintptr_t)c_new & 15u) == 0 && ((uintptr_t)cache & 15u) == 0;
   hipLaunchKernelGGL(rope_append_kernel<T>, grid, dim3(128), 0, stream, (const T*)c_new, (const T*)k_new, (T*)cache,
-                     seq_off, len_before, n_new, L.d_latent, L.d_rope, L.rope_base);
+                     seq_off, len_before, n_new, L.d_latent, L.d_rope, L.rope_base, vec ? 1 : 0);
   return hipGetLastError();
 }
 
