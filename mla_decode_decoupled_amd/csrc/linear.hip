@@ -175,14 +175,16 @@ constexpr int SROW = TK + 8;   // bf16 per staged row (80 bytes: 16 lanes of a 1
 constexpr int GEMM_LDS = 2 * 2 * TM * SROW * 2;   // two buffers of the A and B tiles
 
 // Per-sequence rows (SEQ form): blockIdx.z is a sequence b whose M = len[b] rows start at row
-// off[b] of x; its outputs start y_bstride elements further per b.
+// off[b] of x; its outputs start y_bstride elements further per b. The row tile is blockIdx.x
+// and the column tile blockIdx.y in this form.
 struct SeqRows {
   const int32_t* len;
   const int64_t* off;
   int64_t y_bstride;
 };
 
-// grid (ceil(n / 128), ceil(M / 128)[, sequences]), 256 threads, GEMM_LDS dynamic LDS; K % 32 == 0.
+// grid (ceil(n / 128), ceil(M / 128)), or (ceil(M / 128), ceil(n / 128), sequences) in the SEQ form;
+// 256 threads, GEMM_LDS dynamic LDS; K % 32 == 0.
 // Wave w computes rows 64 (w / 2) .. +63 and columns 64 (w % 2) .. +63 of the tile: 2 x 2 MFMA
 // blocks of 32 x 32. Per K step of 32, every thread moves 2 x 16 bytes of A (x rows) and of B
 // (weight rows) global -> registers -> LDS; the next step's loads are in flight during the MFMAs.
@@ -199,14 +201,16 @@ __global__ void __launch_bounds__(256) lin_gemm(const bf16* __restrict__ x, int 
   if constexpr (SEQ) {
     const int b = blockIdx.z;
     M = sq.len[b];
-    if ((int)blockIdx.y * TM >= M) return;   // whole workgroup, before any barrier
+    if ((int)blockIdx.x * TM >= M) return;   // whole workgroup, before any barrier
     x += sq.off[b] * (int64_t)ldx;
     s.y1 = (Ty*)s.y1 + b * sq.y_bstride;
     s.y2 = (Ty*)s.y2 + b * sq.y_bstride;
   }
   bf16* As = reinterpret_cast<bf16*>(smem);   // [2][TM][SROW]
   bf16* Bs = As + 2 * TM * SROW;              // [2][TN][SROW]
-  const int m0 = blockIdx.y * TM, n0 = blockIdx.x * TN;
+  // SEQ grids run the row tiles fastest: the workgroups dealt to one XCD then share a weight tile
+  // and a few row tiles through its L2 (the per-sequence products have a short K)
+  const int m0 = (SEQ ? blockIdx.x : blockIdx.y) * TM, n0 = (SEQ ? blockIdx.y : blockIdx.x) * TN;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int g = lane >> 5, l32 = lane & 31;
   // loader: thread t moves rows t / 4 and 64 + t / 4, 16-byte piece t % 4 of each K step
@@ -493,7 +497,7 @@ hipError_t launch_kv_expand(int batch, int max_seq_len, int n_out, int d_latent,
   }
   lin::Seg2 s{w_uk, w_uv, kc, vv, n_out, 2 * n_out, n_out, n_out};
   lin::SeqRows sq{seq_len, seq_off, (int64_t)max_seq_len * n_out};
-  const dim3 grid((2 * n_out + lin::TN - 1) / lin::TN, (max_seq_len + lin::TM - 1) / lin::TM, batch);
+  const dim3 grid((max_seq_len + lin::TM - 1) / lin::TM, (2 * n_out + lin::TN - 1) / lin::TN, batch);
   // n_out = H * 128 and the workspace rows keep every staged 16-byte store aligned
   hipLaunchKernelGGL((lin::lin_gemm<bf16, true, true>), grid, dim3(256), lin::GEMM_LDS, stream, (const bf16*)cache,
                      row, max_seq_len, d_latent, s, sq);
