@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--eager", action="store_true",
                     help="launch the four calls from Python every step instead of replaying a captured HIP graph")
     ap.add_argument("--verbose", action="store_true")
+    ap.add_argument("--single-calls", action="store_true",
+                    help="time the step as the four single calls instead of one mla_decode_step")
     ap.add_argument("--explicit", action="store_true",
                     help="many-row workloads: the step is mla_rope_append + mla_prefill_explicit (the non-absorbed "
                          "form) instead of absorb + latent attention + W_UV")
@@ -201,6 +203,11 @@ def main():
     else:
         ws_bytes = mla.mla_decode_attn_workspace_size(lc, B, n_q, max_len, n_splits)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    ws_step = None
+    if not args.explicit:
+        ws_step = torch.empty(mla.mla_decode_step_workspace_size(lc, B, n_q, max_len, n_splits), dtype=torch.uint8,
+                              device=dev)
+    fused = not args.explicit and not args.single_calls
     torch.cuda.synchronize()
     setup_s = time.time() - t0
 
@@ -209,6 +216,12 @@ def main():
 
     def step(i, timed):
         cache, wuk, wuv, qn, qr = copies[i % n_copies]
+        if fused and not timed:
+            # the four calls as one (two launches fewer for few rows); the per-call timing pass
+            # below runs them one by one to time each
+            mla.mla_decode_step(lc, c_new, k_new, qn, qr, wuk, wuv, cache, seq_off, seq_len, max_len, q_packed,
+                                z, o, lse=lse, n_splits=n_splits, workspace=ws_step)
+            return
         marks = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if timed else None
         if timed:
             marks[0].record(stream)
@@ -352,6 +365,8 @@ def main():
         "ms_per_step_eager": round(ms_step_eager, 6),
         "ms_per_step_graph1": None if ms_step_graph1 is None else round(ms_step_graph1, 6),
         "launch": "eager" if args.eager else "hip_graph",
+        "step_call": ("mla_prefill_explicit" if args.explicit
+                      else "mla_decode_step" if fused else "four single calls"),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

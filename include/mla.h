@@ -158,6 +158,47 @@ mla_status mla_out_proj(const mla_config* cfg, int32_t n_rows, const float* z, c
                         void* o, int32_t d_model, const void* w_o, void* u, void* stream);
 
 /*
+ * ---- The four calls as one decode step.
+ *
+ * Bytes of device workspace mla_decode_step needs (the attention's split-K partials plus
+ * 4 (batch + batch * n_q) bytes of positions). 0 for invalid arguments.
+ */
+size_t mla_decode_step_workspace_size(const mla_config* cfg, int32_t batch, int32_t n_q,
+                                      int32_t max_seq_len, int32_t n_splits);
+
+/*
+ * mla_decode_step — one step of the inference flow of "Decoupled RoPE · MLA Part 2", §5 (steps
+ * 2–5): append the n_q new tokens of every sequence, absorb their queries, attend, project
+ * through W_UV. The positions come from seq_len, which already counts the new tokens: token t of
+ * sequence b (row r = b * n_q + t) sits at position p = seq_len[b] - n_q + t. The results are
+ * those of the four single calls in order:
+ *   mla_rope_append(cfg, batch, n_q, c_new, k_rope_new, cache, seq_off, len_before = seq_len - n_q)
+ *   mla_absorb_q(cfg, batch * n_q, q_nope, q_rope, q_pos = p of each row, w_uk, q_packed)
+ *   mla_decode_attn(cfg, batch, n_q, q_packed, cache, seq_off, seq_len, max_seq_len, n_splits, ..., z, lse)
+ *   mla_out_proj(cfg, batch * n_q, z, w_uv, o, 0, NULL, NULL)
+ * the cache rows and q_packed bit for bit, z, lse and o bit for bit except where the step fuses
+ * the split-K merge: for few rows of the DeepSeek shape in bf16 (batch * n_q < 16) it needs two
+ * launches fewer, as the append rides on the absorption's launch and the head-split attention's
+ * merge on the projection's; z and lse then differ from mla_decode_attn's only by float32
+ * summation order, and o by the one bf16 rounding that follows.
+ *  c_new [batch, n_q, d_latent], k_rope_new [batch, n_q, d_rope] (unrotated), q_nope
+ *        [batch * n_q, H, d_nope], q_rope [batch * n_q, H, d_rope] (unrotated), w_uk, w_uv: as for
+ *        the single calls (storage dtype, device)
+ *  cache, seq_off, seq_len, max_seq_len, n_splits: as for mla_decode_attn; cache is written
+ *  workspace  >= mla_decode_step_workspace_size(...) bytes, device; no initialisation
+ *  q_packed [batch * n_q, H, d_latent + d_rope], z float32 [batch, n_q, H, d_latent], o
+ *        [batch * n_q, H, d_v]: written (q_packed and z are the intermediate results of the
+ *        single calls); lse float32 [batch, n_q, H] written, may be NULL
+ * Errors and limits: those of the four single calls.
+ */
+mla_status mla_decode_step(const mla_config* cfg, int32_t batch, int32_t n_q, const void* c_new,
+                           const void* k_rope_new, const void* q_nope, const void* q_rope,
+                           const void* w_uk, const void* w_uv, void* cache, const int64_t* seq_off,
+                           const int32_t* seq_len, int32_t max_seq_len, int32_t n_splits,
+                           void* workspace, size_t workspace_bytes, void* q_packed, float* z,
+                           float* lse, void* o, void* stream);
+
+/*
  * ---- Upstream projections: from the hidden state h to the inputs of the calls above.
  *
  * Bytes of device workspace mla_project_kv_append (d_q = 0) or mla_project_q (its d_q) needs

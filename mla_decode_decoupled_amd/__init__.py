@@ -12,6 +12,8 @@ from .ops import (  # noqa: F401
     mla_decode_attn_workspace_size,
     mla_decode_attn,
     mla_out_proj,
+    mla_decode_step_workspace_size,
+    mla_decode_step,
     mla_project_workspace_size,
     mla_project_kv_append,
     mla_project_q,

@@ -53,6 +53,9 @@ SIGNATURES = {
     "mla_decode_attn": (ctypes.c_int, [ctypes.POINTER(MlaConfig), _I32, _I32, _VP, _VP, _VP, _VP, _I32, _I32,
                                        _VP, ctypes.c_size_t, _VP, _VP, _VP]),
     "mla_out_proj": (ctypes.c_int, [ctypes.POINTER(MlaConfig), _I32, _VP, _VP, _VP, _I32, _VP, _VP, _VP]),
+    "mla_decode_step_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(MlaConfig), _I32, _I32, _I32, _I32]),
+    "mla_decode_step": (ctypes.c_int, [ctypes.POINTER(MlaConfig), _I32, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                       _VP, _VP, _I32, _I32, _VP, ctypes.c_size_t, _VP, _VP, _VP, _VP, _VP]),
     "mla_project_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(MlaConfig), _I32, _I32, _I32]),
     "mla_project_kv_append": (ctypes.c_int, [ctypes.POINTER(MlaConfig), _I32, _I32, _I32, _VP, _VP, _VP, _VP,
                                              ctypes.c_float, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),

@@ -99,6 +99,47 @@ size_t attn_workspace_bytes(const mla::LayerDims& L, int batch, int n_q, const m
   return generic > fastb ? generic : fastb;
 }
 
+// Launch choices shared by the single calls and mla_decode_step: the MFMA GEMM for many rows,
+// the matrix-vector kernels for few, the generic kernels for other shapes, dtypes or alignments.
+hipError_t absorb_dispatch(const mla_config* cfg, const mla::LayerDims& L, int n_rows, const void* q_nope,
+                           const void* q_rope, const int32_t* q_pos, const void* w_uk, void* q_packed,
+                           hipStream_t st) {
+  const bool fast = cfg->dtype == MLA_BF16 && mla::proj_fast_supported(L) && aligned16(w_uk);
+  if (fast && n_rows >= mla::kGemmMinRows && aligned16(q_nope) && aligned16(q_rope) && aligned16(q_packed))
+    return mla::launch_absorb_q_gemm(L, n_rows, q_nope, q_rope, q_pos, w_uk, q_packed, st);
+  if (fast) return mla::launch_absorb_q_fast(L, n_rows, q_nope, q_rope, q_pos, w_uk, q_packed, st);
+  if (cfg->dtype == MLA_F32)
+    return mla::launch_absorb_q_generic<float>(L, n_rows, q_nope, q_rope, q_pos, w_uk, q_packed, st);
+  return mla::launch_absorb_q_generic<__bf16>(L, n_rows, q_nope, q_rope, q_pos, w_uk, q_packed, st);
+}
+
+// `defer` asks to leave a head-split plan's merge to launch_merge_out_proj; *deferred says whether
+// it was (only on the MFMA path).
+hipError_t attn_dispatch(const mla_config* cfg, const mla::LayerDims& L, int batch, int n_q, const void* q_packed,
+                         const void* cache, const int64_t* seq_off, const int32_t* seq_len, const mla::SplitPlan& plan,
+                         bool fast, void* workspace, float* z, float* lse, hipStream_t st, bool defer, bool* deferred) {
+  if (deferred != nullptr) *deferred = false;
+  if (fast && aligned16(q_packed) && aligned16(cache) && aligned16(z) && aligned16(workspace)) {
+    const bool d = defer && mla::attn_fast_is_hsplit(plan);
+    if (deferred != nullptr) *deferred = d;
+    return mla::launch_attn_fast(L, batch, n_q, q_packed, cache, seq_off, seq_len, plan, workspace, z, lse, st, d);
+  }
+  if (cfg->dtype == MLA_F32)
+    return mla::launch_attn_generic<float>(L, batch, n_q, q_packed, cache, seq_off, seq_len, plan, workspace, z, lse, st);
+  return mla::launch_attn_generic<__bf16>(L, batch, n_q, q_packed, cache, seq_off, seq_len, plan, workspace, z, lse, st);
+}
+
+hipError_t out_proj_dispatch(const mla_config* cfg, const mla::LayerDims& L, int n_rows, const float* z,
+                             const void* w_uv, void* o, hipStream_t st) {
+  const bool fast = cfg->dtype == MLA_BF16 && mla::proj_fast_supported(L) && aligned16(w_uv) && aligned16(z);
+  if (fast && n_rows >= mla::kGemmMinRows) return mla::launch_out_proj_gemm(L, n_rows, z, w_uv, o, st);
+  if (fast) return mla::launch_out_proj_fast(L, n_rows, z, w_uv, o, st);
+  if (cfg->dtype == MLA_F32) return mla::launch_out_proj_generic<float>(L, n_rows, z, w_uv, o, st);
+  return mla::launch_out_proj_generic<__bf16>(L, n_rows, z, w_uv, o, st);
+}
+
+size_t round_up256(size_t n) { return (n + 255) & ~(size_t)255; }
+
 }  // namespace
 
 extern "C" {
@@ -146,19 +187,9 @@ mla_status mla_absorb_q(const mla_config* cfg, int32_t n_rows, const void* q_nop
   if (L.n_heads > 65535) return fail(MLA_ERR_UNSUPPORTED, "n_heads %d exceeds 65535", L.n_heads);
   if (!q_nope || !q_pos || !w_uk || !q_packed || (L.d_rope > 0 && !q_rope))
     return fail(MLA_ERR_INVALID_ARG, "NULL pointer argument");
-  hipStream_t st = (hipStream_t)stream;
-  hipError_t e;
   if (n_rows > 65535 * 4) return fail(MLA_ERR_UNSUPPORTED, "n_rows %d exceeds %d", n_rows, 65535 * 4);
-  const bool fast = cfg->dtype == MLA_BF16 && mla::proj_fast_supported(L) && aligned16(w_uk);
-  if (fast && n_rows >= mla::kGemmMinRows && aligned16(q_nope) && aligned16(q_rope) && aligned16(q_packed))
-    e = mla::launch_absorb_q_gemm(L, n_rows, q_nope, q_rope, q_pos, w_uk, q_packed, st);
-  else if (fast)
-    e = mla::launch_absorb_q_fast(L, n_rows, q_nope, q_rope, q_pos, w_uk, q_packed, st);
-  else if (cfg->dtype == MLA_F32)
-    e = mla::launch_absorb_q_generic<float>(L, n_rows, q_nope, q_rope, q_pos, w_uk, q_packed, st);
-  else
-    e = mla::launch_absorb_q_generic<__bf16>(L, n_rows, q_nope, q_rope, q_pos, w_uk, q_packed, st);
-  return from_hip(e, "mla_absorb_q launch");
+  return from_hip(absorb_dispatch(cfg, L, n_rows, q_nope, q_rope, q_pos, w_uk, q_packed, (hipStream_t)stream),
+                  "mla_absorb_q launch");
 }
 
 size_t mla_decode_attn_workspace_size(const mla_config* cfg, int32_t batch, int32_t n_q, int32_t max_seq_len,
@@ -191,15 +222,9 @@ mla_status mla_decode_attn(const mla_config* cfg, int32_t batch, int32_t n_q, co
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))
     return fail(MLA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu%s", need, workspace_bytes,
                 workspace ? "" : " (NULL)");
-  hipStream_t st = (hipStream_t)stream;
-  hipError_t e;
-  if (fast && aligned16(q_packed) && aligned16(cache) && aligned16(z) && aligned16(workspace))
-    e = mla::launch_attn_fast(L, batch, n_q, q_packed, cache, seq_off, seq_len, plan, workspace, z, lse, st);
-  else if (cfg->dtype == MLA_F32)
-    e = mla::launch_attn_generic<float>(L, batch, n_q, q_packed, cache, seq_off, seq_len, plan, workspace, z, lse, st);
-  else
-    e = mla::launch_attn_generic<__bf16>(L, batch, n_q, q_packed, cache, seq_off, seq_len, plan, workspace, z, lse, st);
-  return from_hip(e, "mla_decode_attn launch");
+  return from_hip(attn_dispatch(cfg, L, batch, n_q, q_packed, cache, seq_off, seq_len, plan, fast, workspace, z, lse,
+                                (hipStream_t)stream, false, nullptr),
+                  "mla_decode_attn launch");
 }
 
 mla_status mla_out_proj(const mla_config* cfg, int32_t n_rows, const float* z, const void* w_uv, void* o,
@@ -216,17 +241,8 @@ mla_status mla_out_proj(const mla_config* cfg, int32_t n_rows, const float* z, c
   if (L.n_heads > 65535) return fail(MLA_ERR_UNSUPPORTED, "n_heads %d exceeds 65535", L.n_heads);
   if (!z || !w_uv || !o) return fail(MLA_ERR_INVALID_ARG, "NULL pointer argument");
   hipStream_t st = (hipStream_t)stream;
-  hipError_t e;
   if (n_rows > 65535 * 4) return fail(MLA_ERR_UNSUPPORTED, "n_rows %d exceeds %d", n_rows, 65535 * 4);
-  const bool fast = cfg->dtype == MLA_BF16 && mla::proj_fast_supported(L) && aligned16(w_uv) && aligned16(z);
-  if (fast && n_rows >= mla::kGemmMinRows)
-    e = mla::launch_out_proj_gemm(L, n_rows, z, w_uv, o, st);
-  else if (fast)
-    e = mla::launch_out_proj_fast(L, n_rows, z, w_uv, o, st);
-  else if (cfg->dtype == MLA_F32)
-    e = mla::launch_out_proj_generic<float>(L, n_rows, z, w_uv, o, st);
-  else
-    e = mla::launch_out_proj_generic<__bf16>(L, n_rows, z, w_uv, o, st);
+  hipError_t e = out_proj_dispatch(cfg, L, n_rows, z, w_uv, o, st);
   if (e != hipSuccess || !with_w_o) return from_hip(e, "mla_out_proj launch");
   // u = W_O concat_i(o_i), from the o just written (same stream)
   const int K = L.n_heads * L.d_v;
@@ -234,6 +250,75 @@ mla_status mla_out_proj(const mla_config* cfg, int32_t n_rows, const float* z, c
   e = cfg->dtype == MLA_F32 ? mla::launch_linear<float>(o, K, n_rows, K, w_o, d_model, u, d_model, st)
                             : mla::launch_linear<__bf16>(o, K, n_rows, K, w_o, d_model, u, d_model, st);
   return from_hip(e, "mla_out_proj W_O launch");
+}
+
+size_t mla_decode_step_workspace_size(const mla_config* cfg, int32_t batch, int32_t n_q, int32_t max_seq_len,
+                                      int32_t n_splits) {
+  mla::LayerDims L;
+  if (check_cfg(cfg, &L) != MLA_OK) return 0;
+  if (batch <= 0 || n_q <= 0 || max_seq_len < n_q || (int64_t)batch * n_q > 65535) return 0;
+  mla::SplitPlan plan;
+  if (plan_splits(max_seq_len, n_splits, (int64_t)batch * n_q, use_fast_attn(cfg, L), &plan) != MLA_OK) return 0;
+  // the attention's partials, then int32 append and query positions for the unfused launches
+  return round_up256(attn_workspace_bytes(L, batch, n_q, plan, use_fast_attn(cfg, L))) +
+         ((size_t)batch + (size_t)batch * n_q) * sizeof(int32_t);
+}
+
+mla_status mla_decode_step(const mla_config* cfg, int32_t batch, int32_t n_q, const void* c_new, const void* k_rope_new,
+                           const void* q_nope, const void* q_rope, const void* w_uk, const void* w_uv, void* cache,
+                           const int64_t* seq_off, const int32_t* seq_len, int32_t max_seq_len, int32_t n_splits,
+                           void* workspace, size_t workspace_bytes, void* q_packed, float* z, float* lse, void* o,
+                           void* stream) {
+  mla::LayerDims L;
+  mla_status s = check_cfg(cfg, &L);
+  if (s != MLA_OK) return s;
+  if (batch < 0 || n_q < 0) return fail(MLA_ERR_INVALID_ARG, "batch and n_q must be >= 0");
+  if (batch == 0 || n_q == 0) return ok();
+  if (max_seq_len < n_q) return fail(MLA_ERR_INVALID_ARG, "max_seq_len (%d) must be >= n_q (%d)", max_seq_len, n_q);
+  if ((int64_t)batch * n_q > 65535) return fail(MLA_ERR_UNSUPPORTED, "batch * n_q exceeds 65535");
+  if (L.n_heads > 65535) return fail(MLA_ERR_UNSUPPORTED, "n_heads %d exceeds 65535", L.n_heads);
+  if (!c_new || !q_nope || !w_uk || !w_uv || !cache || !seq_off || !seq_len || !q_packed || !z || !o ||
+      (L.d_rope > 0 && (!k_rope_new || !q_rope)))
+    return fail(MLA_ERR_INVALID_ARG, "NULL pointer argument");
+  const int rows = batch * n_q;
+  const bool fast = use_fast_attn(cfg, L);
+  mla::SplitPlan plan;
+  s = plan_splits(max_seq_len, n_splits, rows, fast, &plan);
+  if (s != MLA_OK) return s;
+  const size_t attn_bytes = round_up256(attn_workspace_bytes(L, batch, n_q, plan, fast));
+  const size_t need = attn_bytes + ((size_t)batch + rows) * sizeof(int32_t);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu%s", need, workspace_bytes,
+                workspace ? "" : " (NULL)");
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
+  // few rows of the DeepSeek shape: the append rides on the absorption launch, and the
+  // head-split attention's merge on the W_UV launch (the same kernels and arithmetic as the
+  // single calls, two launches fewer)
+  const bool few = cfg->dtype == MLA_BF16 && mla::proj_fast_supported(L) && rows < mla::kGemmMinRows;
+  if (few && aligned16(w_uk)) {
+    const mla::StepAppend ap{c_new, k_rope_new, cache, seq_off, seq_len, n_q,
+                             mla::append_vec_ok(L, sizeof(__bf16), c_new, cache) ? 1 : 0};
+    e = mla::launch_absorb_q_fast(L, rows, q_nope, q_rope, nullptr, w_uk, q_packed, st, &ap);
+    if (e != hipSuccess) return from_hip(e, "mla_decode_step append/absorb launch");
+  } else {
+    int32_t* len_before = (int32_t*)((char*)workspace + attn_bytes);
+    int32_t* q_pos = len_before + batch;
+    e = mla::launch_step_positions(seq_len, batch, n_q, len_before, q_pos, st);
+    if (e == hipSuccess)
+      e = cfg->dtype == MLA_F32
+              ? mla::launch_rope_append_generic<float>(L, batch, n_q, c_new, k_rope_new, cache, seq_off, len_before, st)
+              : mla::launch_rope_append_generic<__bf16>(L, batch, n_q, c_new, k_rope_new, cache, seq_off, len_before, st);
+    if (e == hipSuccess) e = absorb_dispatch(cfg, L, rows, q_nope, q_rope, q_pos, w_uk, q_packed, st);
+    if (e != hipSuccess) return from_hip(e, "mla_decode_step append/absorb launch");
+  }
+  bool deferred = false;
+  e = attn_dispatch(cfg, L, batch, n_q, q_packed, cache, seq_off, seq_len, plan, fast, workspace, z, lse, st,
+                    few && aligned16(w_uv), &deferred);
+  if (e != hipSuccess) return from_hip(e, "mla_decode_step attention launch");
+  e = deferred ? mla::launch_merge_out_proj(L, rows, plan, workspace, w_uv, z, lse, o, st)
+               : out_proj_dispatch(cfg, L, rows, z, w_uv, o, st);
+  return from_hip(e, "mla_decode_step output projection launch");
 }
 
 size_t mla_project_workspace_size(const mla_config* cfg, int32_t n_rows, int32_t d_model, int32_t d_q) {

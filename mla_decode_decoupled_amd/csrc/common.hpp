@@ -62,6 +62,30 @@ __device__ __forceinline__ void rope_sincos(double theta, int64_t pos, float* s,
   sincosf((float)r, s, c);
 }
 
+// Cache row of one new token at position p ("Decoupled RoPE · MLA Part 2", §3.4 and §4.3): the
+// latent copied, the position key rotated in float64 and rounded once, so a stored row is exactly
+// the rounding of the true rotated value. Threads tid, tid + nthr, ... share the row; with vec
+// (16-byte aligned rows whose latent part is whole 16-byte pieces) the latent moves 16 bytes per
+// thread. Every kernel that appends goes through here, so they all store the same bits.
+template <typename T>
+__device__ __forceinline__ void append_token(const T* __restrict__ c_src, const T* __restrict__ k_src,
+                                             T* __restrict__ dst, int64_t p, int d_latent, int d_rope, double base,
+                                             bool vec, int tid, int nthr) {
+  if (vec) {
+    const int n16 = d_latent * (int)sizeof(T) / 16;
+    for (int c = tid; c < n16; c += nthr) reinterpret_cast<i32x4*>(dst)[c] = reinterpret_cast<const i32x4*>(c_src)[c];
+  } else {
+    for (int c = tid; c < d_latent; c += nthr) dst[c] = c_src[c];
+  }
+  for (int j = tid; j < d_rope / 2; j += nthr) {
+    double s, co;
+    rope_sincos_f64(rope_theta(base, j, d_rope), p, &s, &co);
+    const double x0 = to_f32(k_src[2 * j]), x1 = to_f32(k_src[2 * j + 1]);
+    dst[d_latent + 2 * j] = from_f64<T>(x0 * co - x1 * s);
+    dst[d_latent + 2 * j + 1] = from_f64<T>(x0 * s + x1 * co);
+  }
+}
+
 __device__ __forceinline__ float warp_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);

@@ -132,17 +132,19 @@ __device__ __forceinline__ void wait_vmcnt_27() {
   __builtin_amdgcn_s_waitcnt((27 & 15) | ((27 >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Split-K partials of the fast path are stored in the accumulator's own register order, so the
-// attention kernel writes them with whole 1 KB stores straight from the accumulators and the merge
-// reads them the same way. The head-split kernel writes its (few, latency-bound) partials with
-// nontemporal stores, which shortens the write-back at the end of the kernel, and its merge reads
-// them nontemporally too (cached by the merge, the lines would slow the next call's stores); the
-// big kernel's partials go through the caches both ways, where the merge finds part of them
-// (measured: the nontemporal form slows that merge by a fifth and gains nothing in the attention
-// kernel).
-// Per (query row, chunk) one block of H * DC floats:
+// Split-K partials: per (query row, chunk) one block of H * DC floats and H (m, l) pairs.
+// The attention kernels store them in the accumulator's own register order, so they write them
+// with whole 1 KB stores straight from the accumulators and attn_merge_frag reads them the same way:
 //   [head block hb][col block cb (16)][row group j][lane][4]
 // holds O^T[col][head] for col = 32cb + 8j + 4(lane / 32) + e, head = 32hb + lane % 32.
+// For mla_decode_step, decode_attn_hsplit stores them head-major instead, [head][col], so that one
+// head's 2 KB row per chunk is contiguous for merge_heads_out_proj, which merges and projects one
+// head per workgroup. The head-split kernel writes its (few, latency-bound) partials with
+// nontemporal stores, which shortens the write-back at the end of the kernel, and attn_merge_frag
+// reads them nontemporally too (cached by the merge, the lines would slow the next call's
+// stores); the big kernel's partials go through the caches both ways, where the merge finds part
+// of them (measured: the nontemporal form slows that merge by a fifth and gains nothing in the
+// attention kernel).
 constexpr int PART_FLOATS = H * DC;   // per (query row, chunk)
 __device__ __forceinline__ int frag_offset(int head, int col) {
   const int cb = col >> 5, j = (col >> 3) & 3, g = (col >> 2) & 1, e = col & 3;
@@ -229,7 +231,7 @@ __device__ __noinline__ void exact_chunk(const bf16* __restrict__ q_packed, cons
                                          size_t rh0, int j0, int j1, float scale_log2, int n_chunks, int slot,
                                          float* __restrict__ part_acc, float* __restrict__ part_ml,
                                          float* __restrict__ z, float* __restrict__ lse, unsigned char* smem,
-                                         int h_begin, int h_end) {
+                                         int h_begin, int h_end, bool head_major) {
   float* qs = reinterpret_cast<float*>(smem);   // [ROW]
   float* ps = qs + ROW;                         // [256]
   float* red = ps + 256;                        // [8]
@@ -278,8 +280,8 @@ __device__ __noinline__ void exact_chunk(const bf16* __restrict__ q_packed, cons
       if (lse != nullptr && tid == 0) lse[rh] = (m + log2f(l)) * kLn2;
     } else {
       float* blk = part_acc + (size_t)slot * PART_FLOATS;
-      blk[frag_offset(h, tid)] = acc0;
-      blk[frag_offset(h, tid + 256)] = acc1;
+      blk[head_major ? h * DC + tid : frag_offset(h, tid)] = acc0;
+      blk[head_major ? h * DC + tid + 256 : frag_offset(h, tid + 256)] = acc1;
       if (tid == 0) {
         part_ml[((size_t)slot * H + h) * 2 + 0] = m;
         part_ml[((size_t)slot * H + h) * 2 + 1] = l;
@@ -563,7 +565,8 @@ __global__ void __launch_bounds__(256)
   const bool overflowed = (flags[0] | flags[1] | flags[2] | flags[3]) != 0;
   if (overflowed) {
     __syncthreads();
-    exact_chunk(q_packed, kv, rh0, j0, j1, scale_log2, n_chunks, ch.slot, part_acc, part_ml, z, lse, smem_raw, 0, H);
+    exact_chunk(q_packed, kv, rh0, j0, j1, scale_log2, n_chunks, ch.slot, part_acc, part_ml, z, lse, smem_raw, 0, H,
+                false);
     return;
   }
   // the accumulator is read by VALU below: 20 wait states after the last MFMA
@@ -633,8 +636,9 @@ __global__ void __launch_bounds__(256)
 // tiles finishes in a fraction of the big kernel's time, the queries a workgroup stages are 36 KB
 // instead of 147 KB, and the split-K partials come out 4x fewer for the same number of
 // workgroups. The price is that each cache tile is streamed into four workgroups; they run on
-// the same XCD, so three of the four reads hit its L2. Same tile layout (swizzled DMA), same
-// fixed-reference softmax with the exact fallback, same partial layout as decode_attn_fast.
+// the same XCD, so three of the four reads hit its L2. Same tile layout (swizzled DMA),
+// fixed-reference softmax with the exact fallback and partial layout as decode_attn_fast, or, with
+// head_major, the head-major partials that merge_heads_out_proj reads.
 typedef __bf16 bf16x8e __attribute__((ext_vector_type(8)));
 typedef short i16x4e __attribute__((ext_vector_type(4)));
 typedef float f32x16e __attribute__((ext_vector_type(16)));
@@ -649,6 +653,8 @@ struct SmemH {
   float exch[WAVES][4][64][4];   // partial scores: [wave][register quad][lane][4]
 };
 static_assert(sizeof(SmemH) <= 160 * 1024, "LDS budget");
+constexpr int HS_STAGE = DC + 4;   // floats per staged partial row (the pad spreads 16 heads over the banks)
+static_assert(32 * HS_STAGE * 4 <= HS_NBUF * TILE_BYTES, "partial staging fits the tile buffers");
 
 __device__ __forceinline__ f32x16e mfma_bf16(bf16x8e a, bf16x8e b, f32x16e c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -703,7 +709,8 @@ __global__ void __launch_bounds__(256)
     decode_attn_hsplit(const bf16* __restrict__ q_packed, const bf16* __restrict__ cache,
                        const int64_t* __restrict__ seq_off, const int32_t* __restrict__ seq_len, int n_q, int rows,
                        float scale_log2, float* __restrict__ part_acc, float* __restrict__ part_ml,
-                       int2* __restrict__ row_chunks, float* __restrict__ z, float* __restrict__ lse) {
+                       int2* __restrict__ row_chunks, float* __restrict__ z, float* __restrict__ lse,
+                       int head_major) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   SmemH& sm = *reinterpret_cast<SmemH*>(smem_raw);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -855,7 +862,7 @@ __global__ void __launch_bounds__(256)
   if ((flags[0] | flags[1] | flags[2] | flags[3]) != 0) {
     __syncthreads();
     exact_chunk(q_packed, kv, rh0, j0, j1, scale_log2, n_chunks, ch.slot, part_acc, part_ml, z, lse, smem_raw, head0,
-                head0 + 32);
+                head0 + 32, head_major != 0);
     return;
   }
   l_run += __shfl_xor(l_run, 32, 64);
@@ -873,13 +880,37 @@ __global__ void __launch_bounds__(256)
     if (lse != nullptr && w == 0 && g == 0) lse[rh0 + head] = (m_ref + log2f(l_run)) * kLn2;
     return;
   }
-  float* blk = part_acc + (size_t)ch.slot * PART_FLOATS + (size_t)hb * (PART_FLOATS / 4) + 4 * lane;
+  if (head_major) {
+    // head-major partial, staged through the (now idle) tile buffers: each lane holds 32-byte
+    // pieces of 16 head rows, so the rows are assembled in LDS first and then leave as whole 1 KB
+    // stores
+    float* stage = reinterpret_cast<float*>(&sm.tile[0][0]);   // [32 heads][HS_STAGE]
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      __builtin_nontemporal_store(f32x4{oacc[i][4 * j], oacc[i][4 * j + 1], oacc[i][4 * j + 2], oacc[i][4 * j + 3]},
-                                  reinterpret_cast<f32x4*>(blk + ((4 * w + i) * 4 + j) * 256));
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<f32x4*>(stage + l32 * HS_STAGE + 32 * (4 * w + i) + 8 * j + 4 * g) =
+            f32x4{oacc[i][4 * j], oacc[i][4 * j + 1], oacc[i][4 * j + 2], oacc[i][4 * j + 3]};
+    __syncthreads();
+    float* prow = part_acc + (size_t)ch.slot * PART_FLOATS + (size_t)head0 * DC + 4 * lane;
+#pragma unroll
+    for (int hh = 0; hh < 8; ++hh) {
+      const int hl = 8 * w + hh;
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(stage + hl * HS_STAGE + 256 * c + 4 * lane),
+                                    reinterpret_cast<f32x4*>(prow + (size_t)hl * DC + 256 * c));
+    }
+  } else {
+    // register-order partial: 1 KB stores straight from the accumulators
+    float* blk = part_acc + (size_t)ch.slot * PART_FLOATS + (size_t)hb * (PART_FLOATS / 4) + 4 * lane;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        __builtin_nontemporal_store(f32x4{oacc[i][4 * j], oacc[i][4 * j + 1], oacc[i][4 * j + 2], oacc[i][4 * j + 3]},
+                                    reinterpret_cast<f32x4*>(blk + ((4 * w + i) * 4 + j) * 256));
+  }
   if (w == 0 && g == 0) {
     float* ml = part_ml + ((size_t)ch.slot * H + head) * 2;
     ml[0] = m_ref;
@@ -887,7 +918,7 @@ __global__ void __launch_bounds__(256)
   }
 }
 
-// Log-sum-exp merge of the split-K partials of the fast path (layout above). One workgroup per
+// Log-sum-exp merge of decode_attn_fast's split-K partials (register order). One workgroup per
 // (query row, head block hb, col block cb, JN of the 4 row groups j): 32 heads x 8 JN latent
 // columns, each lane owning one head and 4 JN columns (JN = 4 for many rows; JN = 1 spreads a
 // few rows over four times as many workgroups). The row's chunks are the slots
@@ -985,6 +1016,158 @@ __global__ void __launch_bounds__(256) attn_merge_frag(const float* __restrict__
   }
 }
 
+// Log-sum-exp merge of decode_attn_hsplit's head-major partials fused with the output
+// projection o = W_UV,i z ("从零理解 MLA", section "矩阵吸收", output side), for mla_decode_step:
+// the merge costs no launch of its own, and the weights stream in while the partials are read.
+// One (query row, head, half of the 128 outputs) per workgroup of 8 waves.
+//   merge: the waves take the row's chunks round-robin (every chunk in one step); lane l reads
+//   latent columns 4l .. 4l+3 and 256 + 4l .. +3 (two 1 KB loads per wave and chunk) and keeps a
+//   running maximum; the wave sums meet in LDS against the common maximum,
+//   z = sum_k 2^(m_k - M) O_k / sum_k 2^(m_k - M) l_k. A row computed as one chunk already has its
+//   final z, written by the attention kernel, and is read back.
+//   projection: wave w owns the 8 outputs 64 y + 8 w + j of half y; its lanes load
+//   W_UV,i[v, 8l .. 8l+7] first, then dot them with z[8l .. 8l+7] and reduce across the wave exactly
+//   as out_proj_gemv does, so o is bitwise what out_proj_gemv makes of this z. Half 0 writes z
+//   and lse.
+// grid (H, 2, rows), 64 MERGE_WAVES threads.
+constexpr int MERGE_WAVES = 8;
+__global__ void __launch_bounds__(64 * MERGE_WAVES)
+    merge_heads_out_proj(const float* __restrict__ part_acc, const float* __restrict__ part_ml,
+                         const int2* __restrict__ row_chunks, const bf16* __restrict__ w_uv, float* __restrict__ z,
+                         float* __restrict__ lse, bf16* __restrict__ o) {
+  constexpr int MW = MERGE_WAVES;
+  constexpr int CU = kHsplitChunks / MW;   // chunks per step and wave: every chunk in one step
+  constexpr int DV = 128;                  // d_v
+  __shared__ f32x4 wacc[MW][2][64];
+  __shared__ float wm[MW], wl[MW];
+  __shared__ __attribute__((aligned(16))) float zs[DC];
+  const int i = blockIdx.x, half = blockIdx.y, bt = blockIdx.z;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const size_t rh = (size_t)bt * H + i;
+  i32x4 wv[8];
+  {
+    const bf16* wp = w_uv + ((size_t)i * DV + 64 * half + 8 * w) * DC + 8 * lane;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) wv[j] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(wp + (size_t)j * DC));
+  }
+  const int2 rc = row_chunks[bt];
+  if (rc.y <= 1) {
+    for (int c = t; c < DC; c += MW * 64) zs[c] = z[rh * DC + c];
+  } else {
+    const int base = rc.x, nck = rc.y;
+    const float* src = part_acc + (size_t)base * PART_FLOATS + (size_t)i * DC + 4 * lane;
+    const float2* ml = reinterpret_cast<const float2*>(part_ml) + (size_t)base * H + i;   // stride H per chunk
+    float m_w = -INFINITY, Lsum = 0.0f;
+    f32x4 a0 = {}, a1 = {};
+    for (int k0 = w; k0 < nck; k0 += MW * CU) {
+      f32x4 x0[CU], x1[CU];
+      float2 v[CU];
+#pragma unroll
+      for (int u = 0; u < CU; ++u) {
+        const int kk = k0 + MW * u;
+        v[u] = make_float2(-INFINITY, 0.0f);
+        if (kk < nck) {
+          x0[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + (size_t)kk * PART_FLOATS));
+          x1[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + (size_t)kk * PART_FLOATS + 256));
+          v[u] = ml[(size_t)kk * H];
+        }
+      }
+      float mb = m_w;
+#pragma unroll
+      for (int u = 0; u < CU; ++u) mb = fmaxf(mb, v[u].x);
+      const float a = exp2f(m_w - mb);   // 0 on the first step (m_w = -inf, mb finite)
+      Lsum *= a;
+      a0 *= a;
+      a1 *= a;
+#pragma unroll
+      for (int u = 0; u < CU; ++u) {
+        if (k0 + MW * u < nck) {
+          const float wk = exp2f(v[u].x - mb);
+          Lsum = fmaf(wk, v[u].y, Lsum);
+          a0 += wk * x0[u];
+          a1 += wk * x1[u];
+        }
+      }
+      m_w = mb;
+    }
+    wacc[w][0][lane] = a0;
+    wacc[w][1][lane] = a1;
+    if (lane == 0) {
+      wm[w] = m_w;
+      wl[w] = Lsum;
+    }
+    __syncthreads();
+    if (t < 128) {
+      // wave 0 holds chunk 0, so M is finite; a wave without chunks weighs 2^-inf = 0
+      float M = wm[0];
+#pragma unroll
+      for (int u = 1; u < MW; ++u) M = fmaxf(M, wm[u]);
+      float e[MW];
+      float L = 0.0f;
+#pragma unroll
+      for (int u = 0; u < MW; ++u) {
+        e[u] = exp2f(wm[u] - M);
+        L = fmaf(e[u], wl[u], L);
+      }
+      const int hq = t >> 6, l = t & 63;
+      f32x4 acc = e[0] * wacc[0][hq][l];
+#pragma unroll
+      for (int u = 1; u < MW; ++u) acc += e[u] * wacc[u][hq][l];
+      const float inv = 1.0f / L;
+      const f32x4 zq = acc * inv;
+      const int c = 256 * hq + 4 * l;
+      *reinterpret_cast<f32x4*>(&zs[c]) = zq;
+      if (half == 0) {
+        *reinterpret_cast<f32x4*>(z + rh * DC + c) = zq;
+        if (lse != nullptr && t == 0) lse[rh] = (M + log2f(L)) * kLn2;
+      }
+    }
+  }
+  {
+    __syncthreads();   // zs complete
+    const f32x4 za = *reinterpret_cast<const f32x4*>(&zs[8 * lane]);
+    const f32x4 zb = *reinterpret_cast<const f32x4*>(&zs[8 * lane + 4]);
+    float d[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float wf[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t u = (uint32_t)wv[j][e];
+        wf[2 * e] = __uint_as_float(u << 16);
+        wf[2 * e + 1] = __uint_as_float(u & 0xFFFF0000u);
+      }
+      float s = wf[0] * za[0];
+      s = fmaf(wf[1], za[1], s);
+      s = fmaf(wf[2], za[2], s);
+      s = fmaf(wf[3], za[3], s);
+      s = fmaf(wf[4], zb[0], s);
+      s = fmaf(wf[5], zb[1], s);
+      s = fmaf(wf[6], zb[2], s);
+      s = fmaf(wf[7], zb[3], s);
+      d[j] = s;
+    }
+    // reduce-scatter (xor 32: 8 -> 4 outputs per lane, 16: 4 -> 2, 8: 2 -> 1), then xor 4, 2, 1
+#pragma unroll
+    for (int m = 32, n = 4; m >= 8; m >>= 1, n >>= 1) {
+      const bool hi = lane & m;
+#pragma unroll
+      for (int j = 0; j < n; ++j) {
+        const float send = hi ? d[j] : d[j + n];
+        const float recv = __shfl_xor(send, m, 64);
+        d[j] = (hi ? d[j + n] : d[j]) + recv;
+      }
+    }
+    float s = d[0];
+    s += __shfl_xor(s, 4, 64);
+    s += __shfl_xor(s, 2, 64);
+    s += __shfl_xor(s, 1, 64);
+    // lane bits 5, 4, 3 -> output bits 2, 1, 0
+    const int j = ((lane >> 5) & 1) * 4 + ((lane >> 4) & 1) * 2 + ((lane >> 3) & 1);
+    if ((lane & 7) == 0) o[rh * DV + 64 * half + 8 * w + j] = (bf16)s;
+  }
+}
+
 }  // namespace fast
 
 bool attn_fast_supported(const LayerDims& L) {
@@ -1018,13 +1201,40 @@ void attn_fast_plan(int rows, int n_splits, int max_seq_len, SplitPlan* plan) {
   }
 }
 
+bool attn_fast_is_hsplit(const SplitPlan& plan) { return plan.fast_mode == fast::HSPLIT; }
+
+namespace {
+// workspace of the MFMA path: partial accumulators, then (m, l) pairs, then (first slot, count) per row
+struct FastParts {
+  float* acc;
+  float* ml;
+  int2* row_chunks;
+};
+FastParts fast_parts(const SplitPlan& plan, void* workspace) {
+  float* acc = (float*)workspace;
+  float* ml = plan.fast_slots > 0 ? acc + (size_t)plan.fast_slots * fast::PART_FLOATS : nullptr;
+  int2* rc = plan.fast_slots > 0 ? reinterpret_cast<int2*>(ml + (size_t)plan.fast_slots * 2 * fast::H) : nullptr;
+  return FastParts{acc, ml, rc};
+}
+}  // namespace
+
+hipError_t launch_merge_out_proj(const LayerDims& L, int rows, const SplitPlan& plan, const void* workspace,
+                                 const void* w_uv, float* z, float* lse, void* o, hipStream_t stream) {
+  (void)L;
+  const FastParts P = fast_parts(plan, const_cast<void*>(workspace));
+  hipLaunchKernelGGL(fast::merge_heads_out_proj, dim3(fast::H, 2, rows), dim3(64 * fast::MERGE_WAVES), 0, stream,
+                     P.acc, P.ml, P.row_chunks, (const bf16*)w_uv, z, lse, (bf16*)o);
+  return hipGetLastError();
+}
+
 hipError_t launch_attn_fast(const LayerDims& L, int batch, int n_q, const void* q_packed, const void* cache,
                             const int64_t* seq_off, const int32_t* seq_len, const SplitPlan& plan, void* workspace,
-                            float* z, float* lse, hipStream_t stream) {
+                            float* z, float* lse, hipStream_t stream, bool defer_merge) {
   const int rows = batch * n_q;
-  float* part_acc = (float*)workspace;
-  float* part_ml = plan.fast_slots > 0 ? part_acc + (size_t)plan.fast_slots * fast::PART_FLOATS : nullptr;
-  int2* row_chunks = plan.fast_slots > 0 ? reinterpret_cast<int2*>(part_ml + (size_t)plan.fast_slots * 2 * fast::H) : nullptr;
+  const FastParts P = fast_parts(plan, workspace);
+  float* part_acc = P.acc;
+  float* part_ml = P.ml;
+  int2* row_chunks = P.row_chunks;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)fast::decode_attn_fast, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1038,7 +1248,7 @@ hipError_t launch_attn_fast(const LayerDims& L, int batch, int n_q, const void* 
   if (plan.fast_mode == fast::HSPLIT) {
     hipLaunchKernelGGL(fast::decode_attn_hsplit, dim3(plan.fast_grid_x), dim3(256), sizeof(fast::SmemH), stream,
                        (const bf16*)q_packed, (const bf16*)cache, seq_off, seq_len, n_q, rows,
-                       L.softmax_scale * kLog2e, part_acc, part_ml, row_chunks, z, lse);
+                       L.softmax_scale * kLog2e, part_acc, part_ml, row_chunks, z, lse, defer_merge ? 1 : 0);
   } else {
     const dim3 grid(plan.fast_grid_x, plan.fast_mode == fast::FIXED ? rows : 1);
     hipLaunchKernelGGL(fast::decode_attn_fast, grid, dim3(256), sizeof(fast::Smem), stream, (const bf16*)q_packed,
@@ -1047,15 +1257,17 @@ hipError_t launch_attn_fast(const LayerDims& L, int batch, int n_q, const void* 
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.fast_slots == 0) return e;
-  if (plan.fast_mode == fast::HSPLIT)
+  if (plan.fast_mode == fast::HSPLIT) {
+    if (defer_merge) return hipSuccess;
     hipLaunchKernelGGL((fast::attn_merge_frag<1, true>), dim3(256, rows), dim3(256), 0, stream, part_acc, part_ml,
                        row_chunks, z, lse);
-  else if (rows <= 16)   // few rows: four workgroups per (row, 32 x 32 block) to keep enough loads in flight
+  } else if (rows <= 16) {   // few rows: four workgroups per (row, 32 x 32 block) to keep enough loads in flight
     hipLaunchKernelGGL((fast::attn_merge_frag<1, false>), dim3(256, rows), dim3(256), 0, stream, part_acc, part_ml,
                        row_chunks, z, lse);
-  else
+  } else {
     hipLaunchKernelGGL((fast::attn_merge_frag<4, false>), dim3(64, rows), dim3(256), 0, stream, part_acc, part_ml,
                        row_chunks, z, lse);
+  }
   return hipGetLastError();
 }
 

@@ -7,39 +7,18 @@
 namespace mla {
 
 // ------------------------------------------------------------------------------ append
-// One block per new token: copy the latent, rotate the position key in float64, store both
-// into the token's cache row ("Decoupled RoPE · MLA Part 2", §3.4 and §4.3).
-// With vec set (16-byte aligned rows whose latent part is a whole number of 16-byte pieces) the
-// latent is copied 16 bytes per thread.
+// One block per new token, which stores the token's cache row with append_token ("Decoupled
+// RoPE · MLA Part 2", §3.4 and §4.3).
 template <typename T>
 __global__ void __launch_bounds__(128) rope_append_kernel(const T* __restrict__ c_new, const T* __restrict__ k_new,
                                                           T* __restrict__ cache, const int64_t* __restrict__ seq_off,
                                                           const int32_t* __restrict__ len_before, int n_new,
                                                           int d_latent, int d_rope, double base, int vec) {
   const int i = blockIdx.x, b = blockIdx.y;
-  const int row = d_latent + d_rope;
   const int64_t p = (int64_t)len_before[b] + i;
-  T* dst = cache + (seq_off[b] + p) * (int64_t)row;
   const size_t tok = (size_t)b * n_new + i;
-  const T* sc = c_new + tok * d_latent;
-  if (vec) {
-    const int n16 = d_latent * (int)sizeof(T) / 16;
-    for (int c = threadIdx.x; c < n16; c += blockDim.x)
-      reinterpret_cast<i32x4*>(dst)[c] = reinterpret_cast<const i32x4*>(sc)[c];
-  } else {
-    for (int c = threadIdx.x; c < d_latent; c += blockDim.x) dst[c] = sc[c];
-  }
-  const T* sk = k_new + tok * d_rope;
-  // cached keys are rotated in float64 and rounded once, so a stored row is exactly the rounding
-  // of the true rotated value
-  for (int j = threadIdx.x; j < d_rope / 2; j += blockDim.x) {
-    double s, co;
-    rope_sincos_f64(rope_theta(base, j, d_rope), p, &s, &co);
-    const double x0 = to_f32(sk[2 * j]), x1 = to_f32(sk[2 * j + 1]);
-    dst[d_latent + 2 * j] = from_f64<T>(x0 * co - x1 * s);
-    dst[d_latent + 2 * j + 1] = from_f64<T>(x0 * s + x1 * co);
-  }
-
+  append_token<T>(c_new + tok * d_latent, k_new + tok * d_rope, cache + (seq_off[b] + p) * (int64_t)(d_latent + d_rope),
+                  p, d_latent, d_rope, base, vec != 0, threadIdx.x, blockDim.x);
 }
 
 // ----------------------------------------------------------------------------- absorb
@@ -309,13 +288,17 @@ __global__ void __launch_bounds__(256) out_proj_generic(const float* __restrict_
 }
 
 // -------------------------------------------------------------------------- launchers
+bool append_vec_ok(const LayerDims& L, size_t elem_bytes, const void* c_new, const void* cache) {
+  return ((size_t)L.d_latent * elem_bytes) % 16 == 0 && ((size_t)(L.d_latent + L.d_rope) * elem_bytes) % 16 == 0 &&
+         ((uintptr_t)c_new & 15u) == 0 && ((uintptr_t)cache & 15u) == 0;
+}
+
 template <typename T>
 hipError_t launch_rope_append_generic(const LayerDims& L, int batch, int n_new, const void* c_new,
                                       const void* k_new, void* cache, const int64_t* seq_off,
                                       const int32_t* len_before, hipStream_t stream) {
   dim3 grid(n_new, batch);
-  const bool vec = ((size_t)L.d_latent * sizeof(T)) % 16 == 0 && ((size_t)(L.d_latent + L.d_rope) * sizeof(T)) % 16 == 0 &&
-                   ((uintptr_t)c_new & 15u) == 0 && ((uintptr_t)cache & 15u) == 0;
+  const bool vec = append_vec_ok(L, sizeof(T), c_new, cache);
   hipLaunchKernelGGL(rope_append_kernel<T>, grid, dim3(128), 0, stream, (const T*)c_new, (const T*)k_new, (T*)cache,
                      seq_off, len_before, n_new, L.d_latent, L.d_rope, L.rope_base, vec ? 1 : 0);
   return hipGetLastError();
@@ -386,6 +369,27 @@ hipError_t launch_decode_advance(int batch, int n_new, int32_t* len_before, int3
   const int n = batch > n_rows ? batch : n_rows;
   hipLaunchKernelGGL(decode_advance, dim3((n + 255) / 256), dim3(256), 0, stream, batch, n_new, len_before, seq_len,
                      n_rows, q_pos);
+  return hipGetLastError();
+}
+
+// Positions of a decode step's new tokens from the key counts (mla_decode_step): row r = b n_q + t
+// of sequence b is the token at position seq_len[b] - n_q + t, and sequence b's first new token
+// goes after its seq_len[b] - n_q cached ones. One thread per row.
+__global__ void __launch_bounds__(256) step_positions(const int32_t* __restrict__ seq_len, int n_q, int n_rows,
+                                                      int32_t* __restrict__ len_before, int32_t* __restrict__ q_pos) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= n_rows) return;
+  const int b = r / n_q, t = r % n_q;
+  const int32_t first = seq_len[b] - n_q;
+  q_pos[r] = first + t;
+  if (t == 0) len_before[b] = first;
+}
+
+hipError_t launch_step_positions(const int32_t* seq_len, int batch, int n_q, int32_t* len_before, int32_t* q_pos,
+                                 hipStream_t stream) {
+  const int rows = batch * n_q;
+  hipLaunchKernelGGL(step_positions, dim3((rows + 255) / 256), dim3(256), 0, stream, seq_len, n_q, rows, len_before,
+                     q_pos);
   return hipGetLastError();
 }
 

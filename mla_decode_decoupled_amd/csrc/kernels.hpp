@@ -53,15 +53,38 @@ hipError_t launch_attn_merge(int n_rowheads, int n_chunks, int d_latent, const f
 bool attn_fast_supported(const LayerDims& L);
 void attn_fast_plan(int rows, int n_splits, int max_seq_len, SplitPlan* plan);
 size_t attn_fast_workspace_bytes(const SplitPlan& plan, int rows);
+// With defer_merge, a head-split plan's partials are left for launch_merge_out_proj.
 hipError_t launch_attn_fast(const LayerDims& L, int batch, int n_q, const void* q_packed, const void* cache,
                             const int64_t* seq_off, const int32_t* seq_len, const SplitPlan& plan, void* workspace,
-                            float* z, float* lse, hipStream_t stream);
+                            float* z, float* lse, hipStream_t stream, bool defer_merge = false);
+bool attn_fast_is_hsplit(const SplitPlan& plan);
+// The head-split plan's merge fused with the W_UV projection (rows < kGemmMinRows, bf16, the
+// shape of proj_fast_supported): z, lse and o = W_UV z of every row, as the merge followed by
+// launch_out_proj_fast would write them.
+hipError_t launch_merge_out_proj(const LayerDims& L, int rows, const SplitPlan& plan, const void* workspace,
+                                 const void* w_uv, float* z, float* lse, void* o, hipStream_t stream);
+
+// The cache append of a decode step carried by the absorption launch (mla_decode_step): row
+// r = b n_q + t is the new token t of sequence b, at position seq_len[b] - n_q + t; its latent is
+// c_new[r] and its unrotated position key k_new[r]. vec as for the append kernel.
+struct StepAppend {
+  const void* c_new;
+  const void* k_new;
+  void* cache;
+  const int64_t* seq_off;
+  const int32_t* seq_len;
+  int n_q;
+  int vec;
+};
+bool append_vec_ok(const LayerDims& L, size_t elem_bytes, const void* c_new, const void* cache);
 
 // GEMV-style projections for the DeepSeek-V2/V3 shape (H 128, d_nope = d_v 128, d_latent 512,
-// d_rope 64, bf16)
+// d_rope 64, bf16). With `ap` the absorption launch also appends the step's new tokens (one
+// extra workgroup column) and takes the query positions from ap->seq_len (q_pos NULL).
 bool proj_fast_supported(const LayerDims& L);
 hipError_t launch_absorb_q_fast(const LayerDims& L, int n_rows, const void* q_nope, const void* q_rope,
-                                const int32_t* q_pos, const void* w_uk, void* q_packed, hipStream_t stream);
+                                const int32_t* q_pos, const void* w_uk, void* q_packed, hipStream_t stream,
+                                const StepAppend* ap = nullptr);
 hipError_t launch_out_proj_fast(const LayerDims& L, int n_rows, const float* z, const void* w_uv, void* o,
                                 hipStream_t stream);
 // MFMA GEMM forms of the same two projections (same shape), for many query rows at once
@@ -106,5 +129,8 @@ hipError_t launch_prefill_explicit(const LayerDims& L, int batch, int n_q, const
 // Position bookkeeping between decode steps (generic.hip)
 hipError_t launch_decode_advance(int batch, int n_new, int32_t* len_before, int32_t* seq_len, int n_rows,
                                  int32_t* q_pos, hipStream_t stream);
+// Append positions and query positions of a decode step from its key counts (generic.hip)
+hipError_t launch_step_positions(const int32_t* seq_len, int batch, int n_q, int32_t* len_before, int32_t* q_pos,
+                                 hipStream_t stream);
 
 }  // namespace mla

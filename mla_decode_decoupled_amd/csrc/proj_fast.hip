@@ -36,16 +36,29 @@ __device__ __forceinline__ void unpack8(const i32x4 v, float* f) {
 // lane. Column group cg = t % 16 (8 columns), row group ag = t / 16 (8 rows a). The partial sums
 // of the 4 row groups of a wave meet by lane exchanges, those of the 4 waves in LDS. The first
 // quarter also rotates the rows' position queries while the weights are in flight.
+// In a decode step (ap.cache set) the grid has one more column of workgroups, x = H: workgroup
+// (H, y, z) appends the new token of row z RB + y (y < RB), and the query positions come from
+// ap.seq_len; the append costs no launch of its own.
 template <int RB>
 __global__ void __launch_bounds__(256) absorb_q_gemv(const bf16* __restrict__ q_nope, const bf16* __restrict__ q_rope,
                                                      const int32_t* __restrict__ q_pos, const bf16* __restrict__ w_uk,
-                                                     bf16* __restrict__ q_packed, int n_rows, double base) {
+                                                     bf16* __restrict__ q_packed, int n_rows, double base,
+                                                     StepAppend ap) {
   __shared__ float qs[RB][DN];
   __shared__ f32x4 red[4][RB][32];   // [wave][row][column quad]
   const int i = blockIdx.x, quarter = blockIdx.y;
   const int r0 = blockIdx.z * RB;
   const int nr = min(RB, n_rows - r0);
   const int t = threadIdx.x, cg = t & 15, ag = t >> 4, w = t >> 6;
+  if (i == H) {   // the step's cache append (the whole workgroup takes this branch)
+    const int r = r0 + quarter;
+    if (quarter >= RB || r >= n_rows) return;
+    const int b = r / ap.n_q;
+    const int64_t p = (int64_t)ap.seq_len[b] - ap.n_q + r % ap.n_q;
+    append_token<bf16>((const bf16*)ap.c_new + (size_t)r * DC, (const bf16*)ap.k_new + (size_t)r * DR,
+                       (bf16*)ap.cache + (ap.seq_off[b] + p) * (int64_t)ROW, p, DC, DR, base, ap.vec != 0, t, 256);
+    return;
+  }
   // weights first: 8 independent 16-byte loads per lane
   const bf16* wp = w_uk + ((size_t)i * DN + ag * 8) * DC + quarter * 128 + cg * 8;
   i32x4 wv[8];
@@ -58,7 +71,8 @@ __global__ void __launch_bounds__(256) absorb_q_gemv(const bf16* __restrict__ q_
       const size_t r = (size_t)(r0 + rr);
       const bf16* src = q_rope + (r * H + i) * DR;
       float sn, co;
-      rope_sincos(rope_theta(base, j, DR), q_pos[r], &sn, &co);
+      const int pos = q_pos != nullptr ? q_pos[r] : ap.seq_len[r / ap.n_q] - ap.n_q + (int)(r % ap.n_q);
+      rope_sincos(rope_theta(base, j, DR), pos, &sn, &co);
       const float x0 = (float)src[2 * j], x1 = (float)src[2 * j + 1];
       bf16* dst = q_packed + (r * H + i) * ROW + DC;
       dst[2 * j] = (bf16)(x0 * co - x1 * sn);
@@ -189,15 +203,19 @@ bool proj_fast_supported(const LayerDims& L) {
 }
 
 hipError_t launch_absorb_q_fast(const LayerDims& L, int n_rows, const void* q_nope, const void* q_rope,
-                                const int32_t* q_pos, const void* w_uk, void* q_packed, hipStream_t stream) {
+                                const int32_t* q_pos, const void* w_uk, void* q_packed, hipStream_t stream,
+                                const StepAppend* ap) {
+  const StepAppend none{nullptr, nullptr, nullptr, nullptr, nullptr, 1, 0};
+  const int gx = proj::H + (ap != nullptr ? 1 : 0);
   if (n_rows == 1) {
-    hipLaunchKernelGGL(proj::absorb_q_gemv<1>, dim3(proj::H, 4, 1), dim3(256), 0, stream, (const bf16*)q_nope,
-                       (const bf16*)q_rope, q_pos, (const bf16*)w_uk, (bf16*)q_packed, n_rows, L.rope_base);
+    hipLaunchKernelGGL(proj::absorb_q_gemv<1>, dim3(gx, 4, 1), dim3(256), 0, stream, (const bf16*)q_nope,
+                       (const bf16*)q_rope, q_pos, (const bf16*)w_uk, (bf16*)q_packed, n_rows, L.rope_base,
+                       ap != nullptr ? *ap : none);
   } else {
     const int rb = (n_rows + proj::kRowBlock - 1) / proj::kRowBlock;
-    hipLaunchKernelGGL(proj::absorb_q_gemv<proj::kRowBlock>, dim3(proj::H, 4, rb), dim3(256), 0, stream,
+    hipLaunchKernelGGL(proj::absorb_q_gemv<proj::kRowBlock>, dim3(gx, 4, rb), dim3(256), 0, stream,
                        (const bf16*)q_nope, (const bf16*)q_rope, q_pos, (const bf16*)w_uk, (bf16*)q_packed, n_rows,
-                       L.rope_base);
+                       L.rope_base, ap != nullptr ? *ap : none);
   }
   return hipGetLastError();
 }

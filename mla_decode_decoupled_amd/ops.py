@@ -143,6 +143,46 @@ def mla_out_proj(cfg: MlaConfig, z: torch.Tensor, w_uv: torch.Tensor, o: torch.T
           "mla_out_proj")
 
 
+def mla_decode_step_workspace_size(cfg: MlaConfig, batch: int, n_q: int, max_seq_len: int, n_splits: int = 0) -> int:
+    return int(lib.mla_decode_step_workspace_size(cfg, batch, n_q, max_seq_len, n_splits))
+
+
+def mla_decode_step(cfg: MlaConfig, c_new: torch.Tensor, k_rope_new: torch.Tensor, q_nope: torch.Tensor,
+                    q_rope: torch.Tensor, w_uk: torch.Tensor, w_uv: torch.Tensor, cache: torch.Tensor,
+                    seq_off: torch.Tensor, seq_len: torch.Tensor, max_seq_len: int, q_packed: torch.Tensor,
+                    z: torch.Tensor, o: torch.Tensor, lse: Optional[torch.Tensor] = None, n_splits: int = 0,
+                    workspace: Optional[torch.Tensor] = None) -> None:
+    """One decode step: append c_new / k_rope_new [batch, n_q, .] at positions seq_len - n_q + t,
+    absorb q_nope / q_rope [batch * n_q, H, .], attend, project; writes q_packed, z, o (and lse)."""
+    dt = storage_dtype(cfg)
+    H, row = cfg.n_heads, cfg.d_latent + cfg.d_rope
+    if c_new.dim() != 3:
+        raise ValueError("c_new must be [batch, n_q, d_latent]")
+    B, n_q = c_new.shape[0], c_new.shape[1]
+    R = B * n_q
+    dev = c_new.device
+    _need(c_new, "c_new", dt, (B, n_q, cfg.d_latent))
+    _need(k_rope_new, "k_rope_new", dt, (B, n_q, cfg.d_rope), dev)
+    _need(q_nope, "q_nope", dt, (R, H, cfg.d_nope), dev)
+    _need(q_rope, "q_rope", dt, (R, H, cfg.d_rope), dev)
+    _need(w_uk, "w_uk", dt, (H, cfg.d_nope, cfg.d_latent), dev)
+    _need(w_uv, "w_uv", dt, (H, cfg.d_v, cfg.d_latent), dev)
+    _need(cache, "cache", dt, None, dev)
+    if cache.dim() != 2 or cache.shape[1] != row:
+        raise ValueError("cache must be [rows, d_latent + d_rope]")
+    _need(seq_off, "seq_off", torch.int64, (B,), dev)
+    _need(seq_len, "seq_len", torch.int32, (B,), dev)
+    _need(q_packed, "q_packed", dt, (R, H, row), dev)
+    _need(z, "z", torch.float32, (B, n_q, H, cfg.d_latent), dev)
+    _need(o, "o", dt, (R, H, cfg.d_v), dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, n_q, H), dev)
+    wp, wb = _ws(workspace, dev)
+    check(lib.mla_decode_step(cfg, B, n_q, _ptr(c_new), _ptr(k_rope_new), _ptr(q_nope), _ptr(q_rope), _ptr(w_uk),
+                              _ptr(w_uv), _ptr(cache), _ptr(seq_off), _ptr(seq_len), int(max_seq_len), int(n_splits),
+                              wp, wb, _ptr(q_packed), _ptr(z), _ptr(lse), _ptr(o), _stream(o)), "mla_decode_step")
+
+
 def _ws(workspace: Optional[torch.Tensor], dev) -> tuple:
     if workspace is None:
         return None, 0
@@ -278,6 +318,8 @@ __all__ = [
     "mla_rope_append",
     "mla_absorb_q",
     "mla_decode_attn_workspace_size",
+    "mla_decode_step_workspace_size",
+    "mla_decode_step",
     "mla_decode_attn",
     "mla_out_proj",
     "mla_project_workspace_size",

@@ -103,6 +103,41 @@ def run_pipeline(hi: HostInputs, n_splits: int = 0, scale: Optional[float] = Non
     return DeviceRun(cache, seq_off, seq_len, q_packed.view(B, n_q, H, cfg.row), z, lse, o.view(B, n_q, H, cfg.d_v))
 
 
+def run_step(hi: HostInputs, n_splits: int = 0, scale: Optional[float] = None, lib_cfg=None,
+             max_len: Optional[int] = None) -> DeviceRun:
+    """The same history and step as run_pipeline, the step as one mla_decode_step call."""
+    cfg = hi.cfg
+    lc = lib_config(cfg, scale) if lib_cfg is None else lib_cfg
+    dt = mla.storage_dtype(lc)
+    B, n_q, H = len(hi.lens), cfg.n_q, cfg.n_heads
+    lens = hi.lens
+    offs = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    cache = torch.empty((int(lens.sum()), cfg.row), dtype=dt, device="cuda")
+    cache.fill_(float("nan"))
+    seq_off = torch.from_numpy(offs).cuda()
+    seq_len = torch.from_numpy(lens.astype(np.int32)).cuda()
+    for b in range(B):
+        h = int(lens[b]) - n_q
+        if h > 0:
+            mla.mla_rope_append(lc, tdev(hi.c[b][None, :h], dt), tdev(hi.k_pre[b][None, :h], dt), cache,
+                                seq_off[b:b + 1], torch.zeros(1, dtype=torch.int32, device="cuda"))
+    c_new = tdev(np.stack([hi.c[b][int(lens[b]) - n_q:] for b in range(B)]), dt)
+    k_new = tdev(np.stack([hi.k_pre[b][int(lens[b]) - n_q:] for b in range(B)]), dt)
+    R = B * n_q
+    q_packed = torch.empty((R, H, cfg.row), dtype=dt, device="cuda")
+    z = torch.empty((B, n_q, H, cfg.d_latent), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, n_q, H), dtype=torch.float32, device="cuda")
+    o = torch.empty((R, H, cfg.d_v), dtype=dt, device="cuda")
+    max_len = int(lens.max()) if max_len is None else int(max_len)
+    ws = torch.empty(mla.mla_decode_step_workspace_size(lc, B, n_q, max_len, n_splits), dtype=torch.uint8,
+                     device="cuda")
+    mla.mla_decode_step(lc, c_new, k_new, tdev(hi.q_nope.reshape(R, H, cfg.d_nope), dt),
+                        tdev(hi.q_rope.reshape(R, H, cfg.d_rope), dt), tdev(hi.w_uk, dt), tdev(hi.w_uv, dt), cache,
+                        seq_off, seq_len, max_len, q_packed, z, o, lse=lse, n_splits=n_splits, workspace=ws)
+    torch.cuda.synchronize()
+    return DeviceRun(cache, seq_off, seq_len, q_packed.view(B, n_q, H, cfg.row), z, lse, o.view(B, n_q, H, cfg.d_v))
+
+
 def np32(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 

@@ -196,3 +196,32 @@ def test_explicit_prefill_arguments():
                                     None) == MLA_ERR_INVALID_ARG                                  # misaligned
     assert lib.mla_prefill_explicit(c, 0, 2048, None, None, None, None, None, 0, None, None, None, 0, None, None,
                                     None) == MLA_OK
+
+
+def test_decode_step_arguments():
+    """mla_decode_step validates like the four calls it stands for, before any launch."""
+    c = cfg()
+    need = lib.mla_decode_step_workspace_size(c, 1, 1, 4097, 0)
+    attn = lib.mla_decode_attn_workspace_size(c, 1, 1, 4097, 0)
+    assert need >= attn + 8 and need == lib.mla_decode_step_workspace_size(c, 1, 1, 4097, 0)
+    assert lib.mla_decode_step_workspace_size(c, 1, 8, 4, 0) == 0          # max_seq_len < n_q
+    assert lib.mla_decode_step_workspace_size(cfg(reserved=1), 1, 1, 10, 0) == 0
+    # a single chunk still needs the position scratch
+    assert lib.mla_decode_step_workspace_size(c, 2, 1, 100, 1) >= 16
+
+    def call(c, ws_ptr, ws_bytes, batch=1, n_q=1, max_len=4097, n_splits=0, c_new=FAKE, o=FAKE, z=FAKE):
+        return lib.mla_decode_step(c, batch, n_q, c_new, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, max_len,
+                                   n_splits, ws_ptr, ws_bytes, FAKE, z, None, o, None)
+
+    assert call(cfg(reserved=1), FAKE, need) == MLA_ERR_INVALID_ARG
+    assert call(c, None, need) == MLA_ERR_WORKSPACE
+    assert call(c, FAKE, need - 1) == MLA_ERR_WORKSPACE
+    assert call(c, FAKE, need, c_new=None) == MLA_ERR_INVALID_ARG
+    assert call(c, FAKE, need, o=None) == MLA_ERR_INVALID_ARG
+    assert call(c, FAKE, need, z=None) == MLA_ERR_INVALID_ARG
+    assert call(c, FAKE, need, n_q=8, max_len=4) == MLA_ERR_INVALID_ARG
+    assert call(c, FAKE, need, n_splits=999) == MLA_ERR_INVALID_ARG
+    assert call(c, FAKE, need, batch=-1) == MLA_ERR_INVALID_ARG
+    assert call(c, FAKE, need, batch=300, n_q=300) == MLA_ERR_UNSUPPORTED
+    assert lib.mla_decode_step(c, 0, 1, None, None, None, None, None, None, None, None, None, 0, 0, None, 0, None,
+                               None, None, None, None) == MLA_OK
