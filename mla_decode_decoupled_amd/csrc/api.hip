@@ -415,6 +415,8 @@ mla_status mla_prefill_explicit(const mla_config* cfg, int32_t batch, int32_t n_
     return fail(MLA_ERR_UNSUPPORTED, "batch * heads * query blocks too large");
   if ((int64_t)max_seq_len > 65535 * 128) return fail(MLA_ERR_UNSUPPORTED, "max_seq_len %d too large", max_seq_len);
   if (batch > 65535) return fail(MLA_ERR_UNSUPPORTED, "batch %d exceeds 65535", batch);
+  // the key/value rebuild runs 2 H column tiles of 128 in its grid's second dimension
+  if (L.n_heads > 32767) return fail(MLA_ERR_UNSUPPORTED, "n_heads %d exceeds 32767", L.n_heads);
   if (!q_nope || !q_rope || !cache || !seq_off || !seq_len || !w_uk || !w_uv || !o)
     return fail(MLA_ERR_INVALID_ARG, "NULL pointer argument");
   if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(cache) || !aligned16(w_uk) || !aligned16(w_uv) ||

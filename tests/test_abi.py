@@ -191,6 +191,9 @@ def test_explicit_prefill_arguments():
     assert lib.mla_prefill_explicit(*args(c, FAKE, ws, o=None)) == MLA_ERR_INVALID_ARG
     assert lib.mla_prefill_explicit(c, 2, 2048, FAKE, FAKE, FAKE, FAKE, FAKE, 100, FAKE, FAKE, FAKE, ws, FAKE, None,
                                     None) == MLA_ERR_INVALID_ARG                                  # max_seq_len < n_q
+    # 2 H column tiles in the rebuild grid's second dimension
+    assert lib.mla_prefill_explicit(*args(cfg(n_heads=40000), FAKE, ws)) == MLA_ERR_UNSUPPORTED
+    assert b"32767" in lib.mla_last_error()
     odd = ctypes.c_void_p(0x1008)
     assert lib.mla_prefill_explicit(c, 2, 2048, odd, FAKE, FAKE, FAKE, FAKE, 4096, FAKE, FAKE, FAKE, ws, FAKE, None,
                                     None) == MLA_ERR_INVALID_ARG                                  # misaligned
