@@ -16,7 +16,10 @@
 //     pieces of the RB activation rows (read through the caches, where every workgroup finds them);
 //   * lin_gemm (bf16, many rows): MFMA 32x32x16, 128 x 128 outputs per workgroup, both operands
 //     K-contiguous and staged through padded LDS rows, the next K step's loads in flight during the
-//     MFMAs.
+//     MFMAs;
+//   * lin_gemm_wide (bf16 in and out, 256 rows or more): 256 x 128 outputs per workgroup, operands
+//     loaded straight into LDS, two workgroups per CU (also the key/value rebuild of the explicit
+//     prefill).
 // Accumulation is float32; each output is rounded once to its type.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -321,6 +324,143 @@ __global__ void __launch_bounds__(256) lin_gemm(const bf16* __restrict__ x, int 
     }
 }
 
+// ---------------------------------------------------------------- many rows, wide tiles
+// 256 x 128 outputs per workgroup for large GEMMs (the key/value rebuild of the explicit prefill),
+// two workgroups per CU so that one's loads, barriers and output stores overlap the other's
+// MFMAs: each of the 4 waves owns 128 x 64 outputs (4 x 2 MFMA blocks, 128 accumulators). K steps
+// of 32: both operand tiles (rows x 64 B) reach LDS by direct 1 KB global->LDS loads (no staging
+// registers) into a ring of three stages, two steps' loads in flight during a step's MFMAs;
+// 16-byte piece c of LDS row r sits at slot c ^ ((r >> 2) & 3), so the 16 rows read together by
+// a fragment load fall on distinct bank groups. Outputs are computed transposed, D[n][m], staged
+// in LDS and written with 16-byte stores (bf16 outputs whose rows and segments allow them).
+// grid (ceil(n / 128), ceil(M / 256)), or (ceil(M / 256), ceil(n / 128), sequences) in the SEQ
+// form; 256 threads, WIDE_LDS dynamic LDS; K % 32 == 0, x and weights 16-byte aligned, ldx % 8 == 0.
+constexpr int WM = 256, WN = 128, WK = 32, WSTAGES = 3;
+constexpr int WROW = WK * 2;                         // 64 bytes per staged operand row
+constexpr int WBUF = (WM + WN) * WROW;               // A and B of one K step (24 KB)
+constexpr int WLOADS = (WM + WN) / 64;               // 1 KB loads per wave and K step
+constexpr int WCS = WN + 8;                          // bf16 per staged output row (272 bytes)
+constexpr int WIDE_LDS = WM * WCS * 2 > WSTAGES * WBUF ? WM * WCS * 2 : WSTAGES * WBUF;
+static_assert(2 * WIDE_LDS <= 160 * 1024, "two workgroups per CU");
+
+__device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gaddr), "s"(lds_base)
+               : "memory", "m0");
+}
+__device__ __forceinline__ int wslot(int c, int r) { return c ^ ((r >> 2) & 3); }
+// Barrier for LDS traffic only: __syncthreads() would also wait for the loads in flight (its
+// fence covers the global->LDS loads), which would empty the ring at every step.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// wait until at most N of this wave's loads are in flight; vmcnt: bits 3:0 and 15:14
+template <int N>
+__device__ __forceinline__ void wait_loads() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <bool SEQ>
+__global__ void __launch_bounds__(256, 2) lin_gemm_wide(const bf16* __restrict__ x, int ldx, int M, int K, Seg2 s,
+                                                        SeqRows sq) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int rt = SEQ ? blockIdx.x : blockIdx.y, nt = SEQ ? blockIdx.y : blockIdx.x;
+  if constexpr (SEQ) {
+    const int b = blockIdx.z;
+    M = sq.len[b];
+    if (rt * WM >= M) return;   // whole workgroup, before any barrier
+    x += sq.off[b] * (int64_t)ldx;
+    s.y1 = (bf16*)s.y1 + b * sq.y_bstride;
+    s.y2 = (bf16*)s.y2 + b * sq.y_bstride;
+  }
+  const int m0 = rt * WM, n0 = nt * WN;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)MLA_LDS(unsigned char, smem);
+  // loader: the stage holds WM rows of x then WN weight rows; wave w fills rows
+  // (WM + WN) / 4 * w .. +95, 16 rows (1 KB) per load; lane l writes slot l % 4 of its row and so
+  // loads logical piece wslot(l % 4, row)
+  const bf16* gp[WLOADS];
+#pragma unroll
+  for (int k = 0; k < WLOADS; ++k) {
+    const int r = (WM + WN) / 4 * w + 16 * k + (lane >> 2);
+    const int piece = wslot(lane & 3, r);
+    gp[k] = r < WM ? x + (size_t)min(m0 + r, M - 1) * ldx + 8 * piece
+                   : wrow<bf16>(s, min(n0 + r - WM, s.n - 1), K) + 8 * piece;
+  }
+  auto issue = [&](int kt) {
+    const uint32_t base = lds0 + (kt % WSTAGES) * WBUF + ((WM + WN) / 4 * w) * WROW;
+#pragma unroll
+    for (int k = 0; k < WLOADS; ++k) dma16(gp[k] + kt * WK, __builtin_amdgcn_readfirstlane(base + k * 1024));
+  };
+  f32x16e acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16e{};
+  const int wm = 128 * (w >> 1), wn = 64 * (w & 1);
+  const int NK = K / WK;
+  issue(0);
+  if (NK > 1) issue(1);
+  for (int kt = 0; kt < NK; ++kt) {
+    if (kt + 1 < NK)   // step kt landed; step kt + 1 may still be in flight
+      wait_loads<WLOADS>();
+    else
+      wait_loads<0>();
+    lds_barrier();   // everyone's loads of step kt are in; step kt - 1's stage is no longer read
+    if (kt + 2 < NK) issue(kt + 2);   // into the stage of step kt - 1
+    const unsigned char* A = smem + (kt % WSTAGES) * WBUF;
+    const unsigned char* B = A + WM * WROW;
+    // all 12 fragments of the step are read first, then the 16 MFMAs
+    bf16x8e af[WK / 16][4], bfr[WK / 16][2];
+#pragma unroll
+    for (int ks = 0; ks < WK / 16; ++ks) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = wm + 32 * i + l32;
+        af[ks][i] = *reinterpret_cast<const bf16x8e*>(A + r * WROW + 16 * wslot(2 * ks + g, r));
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int r = wn + 32 * j + l32;
+        bfr[ks][j] = *reinterpret_cast<const bf16x8e*>(B + r * WROW + 16 * wslot(2 * ks + g, r));
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < WK / 16; ++ks)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ks][j], af[ks][i], acc[i][j], 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);   // the 12 LDS reads
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);   // then the 16 MFMAs
+  }
+  // D^T block (i, j): lane holds output row m = wm + 32 i + l32, columns wn + 32 j + 8 q + 4 g + e
+  __syncthreads();   // every wave is done with the operand stages (no load is in flight)
+  bf16* Cs = reinterpret_cast<bf16*>(smem);   // [WM][WCS]
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (bf16)acc[i][j][4 * q + e];
+        *reinterpret_cast<bf16x4*>(Cs + (wm + 32 * i + l32) * WCS + wn + 32 * j + 8 * q + 4 * g) = v;
+      }
+  __syncthreads();
+  const int c = t & 15;
+#pragma unroll 4
+  for (int k = 0; k < WM / 16; ++k) {
+    const int r = (t >> 4) + 16 * k;
+    const int m = m0 + r, n = n0 + 8 * c;
+    if (m < M && n < s.n) {
+      const i32x4 v = *reinterpret_cast<const i32x4*>(Cs + r * WCS + 8 * c);
+      bf16* dst = n < s.n1 ? (bf16*)s.y1 + (size_t)m * s.ldy1 + n : (bf16*)s.y2 + (size_t)m * s.ldy2 + (n - s.n1);
+      *reinterpret_cast<i32x4*>(dst) = v;
+    }
+  }
+}
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // the staged GEMM epilogue writes 8 consecutive bf16 outputs per 16-byte store
@@ -336,6 +476,20 @@ hipError_t linear(const T* x, int ldx, int M, int K, const Seg2& s, hipStream_t 
   if (M <= 0 || s.n <= 0) return hipSuccess;
   if constexpr (sizeof(T) == 2) {
     const bool vec = K % 8 == 0 && ldx % 8 == 0 && aligned16(x) && aligned16(s.w1) && (s.n == s.n1 || aligned16(s.w2));
+    if constexpr (sizeof(Ty) == 2) {
+      if (vec && M >= WM && K % WK == 0 && staged_ok(s)) {
+        static bool wide_attr_set = false;
+        if (!wide_attr_set) {
+          const hipError_t e = hipFuncSetAttribute((const void*)lin_gemm_wide<false>,
+                                                   hipFuncAttributeMaxDynamicSharedMemorySize, WIDE_LDS);
+          if (e != hipSuccess) return e;
+          wide_attr_set = true;
+        }
+        hipLaunchKernelGGL((lin_gemm_wide<false>), dim3((s.n + WN - 1) / WN, (M + WM - 1) / WM), dim3(256), WIDE_LDS,
+                           stream, x, ldx, M, K, s, SeqRows{nullptr, nullptr, 0});
+        return hipGetLastError();
+      }
+    }
     if (vec && M >= kGemmMinRows && K % TK == 0) {
       static bool attr_set = false;
       if (!attr_set) {
@@ -490,16 +644,17 @@ hipError_t launch_kv_expand(int batch, int max_seq_len, int n_out, int d_latent,
                             void* kc, void* vv, hipStream_t stream) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)lin::lin_gemm<bf16, true, true>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, lin::GEMM_LDS);
+    hipError_t e = hipFuncSetAttribute((const void*)lin::lin_gemm_wide<true>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lin::WIDE_LDS);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   lin::Seg2 s{w_uk, w_uv, kc, vv, n_out, 2 * n_out, n_out, n_out};
   lin::SeqRows sq{seq_len, seq_off, (int64_t)max_seq_len * n_out};
-  const dim3 grid((max_seq_len + lin::TM - 1) / lin::TM, (2 * n_out + lin::TN - 1) / lin::TN, batch);
-  // n_out = H * 128 and the workspace rows keep every staged 16-byte store aligned
-  hipLaunchKernelGGL((lin::lin_gemm<bf16, true, true>), grid, dim3(256), lin::GEMM_LDS, stream, (const bf16*)cache,
+  // n_out = H * 128 and the workspace rows keep every staged 16-byte store aligned; d_latent = 512
+  // is a whole number of K steps
+  const dim3 grid((max_seq_len + lin::WM - 1) / lin::WM, (2 * n_out + lin::WN - 1) / lin::WN, batch);
+  hipLaunchKernelGGL((lin::lin_gemm_wide<true>), grid, dim3(256), lin::WIDE_LDS, stream, (const bf16*)cache,
                      row, max_seq_len, d_latent, s, sq);
   return hipGetLastError();
 }
