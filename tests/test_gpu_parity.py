@@ -88,7 +88,7 @@ def test_v3_decode_4k_all_heads():
     _check_outputs(run, hi, 0)
 
 
-@pytest.mark.parametrize("cid,n_splits", [(0, 1), (0, 7), (1, 0), (1, 1), (1, 3), (1, 64)])
+@pytest.mark.parametrize("cid,n_splits", [(0, 1), (0, 7), (0, 256), (1, 0), (1, 1), (1, 3), (1, 64), (1, 256)])
 def test_split_count_does_not_change_results(cid, n_splits):
     """fp32: only the float32 summation order changes -> 1e-5. n_splits = 0 on the batch-1 4K
     workload is the library's own choice: the head-split kernel, whose scores are summed from four
