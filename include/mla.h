@@ -256,6 +256,32 @@ mla_status mla_project_q(const mla_config* cfg, int32_t n_rows, int32_t d_model,
                          void* stream);
 
 /*
+ * Bytes of device workspace mla_project_inputs needs for n_rows tokens: the kv side's float32
+ * projection and c_Q side by side. 0 for invalid arguments.
+ */
+size_t mla_project_inputs_workspace_size(const mla_config* cfg, int32_t n_rows, int32_t d_model, int32_t d_q);
+
+/*
+ * mla_project_inputs — both projections of a layer's input h in one call: exactly
+ *   mla_project_kv_append(cfg, batch, n_new, d_model, h, w_dkv, w_kr, kv_norm_w, kv_norm_eps, cache,
+ *                         seq_off, len_before, ...)
+ *   mla_project_q(cfg, batch * n_new, d_model, d_q, h, w_dq, w_uq, w_qr, q_nope, q_rope, ...)
+ * with the same arguments, layouts and limits (the passages cited there), h read as
+ * [batch * n_new, d_model] for the query side. For fewer than 16 rows of bf16 (16-byte aligned
+ * tensors, d_model and d_q multiples of 8) it takes two launches instead of four: h is read once
+ * for W_DKV, W_KR and W_DQ, and the latent's RMSNorm and the key's rotation ride on the W_UQ / W_QR
+ * launch. The products are the same up to float32 summation order.
+ *  workspace  >= mla_project_inputs_workspace_size(cfg, batch * n_new, d_model, d_q) bytes, device;
+ *             no initialisation
+ */
+mla_status mla_project_inputs(const mla_config* cfg, int32_t batch, int32_t n_new, int32_t d_model, int32_t d_q,
+                              const void* h, const void* w_dkv, const void* w_kr, const void* kv_norm_w,
+                              float kv_norm_eps, void* cache, const int64_t* seq_off,
+                              const int32_t* len_before, const void* w_dq, const void* w_uq,
+                              const void* w_qr, void* q_nope, void* q_rope, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/*
  * ---- Explicit (non-absorbed) prefill: the same attention output o for many query rows at once.
  *
  * Bytes of device workspace mla_prefill_explicit needs (the rebuilt content keys and values:

@@ -17,6 +17,8 @@ from .ops import (  # noqa: F401
     mla_project_workspace_size,
     mla_project_kv_append,
     mla_project_q,
+    mla_project_inputs_workspace_size,
+    mla_project_inputs,
     mla_decode_advance,
     mla_prefill_explicit_workspace_size,
     mla_prefill_explicit,

@@ -61,6 +61,10 @@ SIGNATURES = {
                                              ctypes.c_float, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
     "mla_project_q": (ctypes.c_int, [ctypes.POINTER(MlaConfig), _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _VP,
                                      _VP, ctypes.c_size_t, _VP]),
+    "mla_project_inputs_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(MlaConfig), _I32, _I32, _I32]),
+    "mla_project_inputs": (ctypes.c_int, [ctypes.POINTER(MlaConfig), _I32, _I32, _I32, _I32, _VP, _VP, _VP, _VP,
+                                          ctypes.c_float, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                          ctypes.c_size_t, _VP]),
     "mla_decode_advance": (ctypes.c_int, [_I32, _I32, _VP, _VP, _I32, _VP, _VP]),
     "mla_prefill_explicit_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(MlaConfig), _I32, _I32, _I32]),
     "mla_prefill_explicit": (ctypes.c_int, [ctypes.POINTER(MlaConfig), _I32, _I32, _VP, _VP, _VP, _VP, _VP, _I32,

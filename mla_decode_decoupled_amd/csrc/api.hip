@@ -391,6 +391,52 @@ mla_status mla_project_q(const mla_config* cfg, int32_t n_rows, int32_t d_model,
   return from_hip(e, "mla_project_q launch");
 }
 
+size_t mla_project_inputs_workspace_size(const mla_config* cfg, int32_t n_rows, int32_t d_model, int32_t d_q) {
+  mla::LayerDims L;
+  if (check_cfg(cfg, &L) != MLA_OK) return 0;
+  if (n_rows <= 0 || d_model <= 0 || d_q < 0) return 0;
+  return mla::project_inputs_workspace_bytes(L, n_rows, d_q, cfg->dtype == MLA_F32 ? 4 : 2);
+}
+
+mla_status mla_project_inputs(const mla_config* cfg, int32_t batch, int32_t n_new, int32_t d_model, int32_t d_q,
+                              const void* h, const void* w_dkv, const void* w_kr, const void* kv_norm_w,
+                              float kv_norm_eps, void* cache, const int64_t* seq_off, const int32_t* len_before,
+                              const void* w_dq, const void* w_uq, const void* w_qr, void* q_nope, void* q_rope,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  mla::LayerDims L;
+  mla_status s = check_cfg(cfg, &L);
+  if (s != MLA_OK) return s;
+  if (batch < 0 || n_new < 0) return fail(MLA_ERR_INVALID_ARG, "batch and n_new must be >= 0");
+  if (d_model < 1 || d_q < 0) return fail(MLA_ERR_INVALID_ARG, "need d_model >= 1 and d_q >= 0, got %d, %d", d_model, d_q);
+  if ((d_q > 0) != (w_dq != nullptr))
+    return fail(MLA_ERR_INVALID_ARG, "pass w_dq exactly when d_q > 0 (query compression)");
+  if (kv_norm_w != nullptr && (!(kv_norm_eps >= 0.0f) || !isfinite(kv_norm_eps)))
+    return fail(MLA_ERR_INVALID_ARG, "kv_norm_eps must be finite and >= 0");
+  if (batch == 0 || n_new == 0) return ok();
+  if (batch > 65535) return fail(MLA_ERR_UNSUPPORTED, "batch %d exceeds 65535", batch);
+  const int64_t rows = (int64_t)batch * n_new;
+  if (rows > 65535 * 4) return fail(MLA_ERR_UNSUPPORTED, "batch * n_new = %lld exceeds %d", (long long)rows, 65535 * 4);
+  if ((int64_t)L.n_heads * (L.d_nope + L.d_rope) > (int64_t)INT32_MAX / 8)
+    return fail(MLA_ERR_UNSUPPORTED, "query projection too wide");
+  if (!h || !w_dkv || !cache || !seq_off || !len_before || !w_uq || !q_nope ||
+      (L.d_rope > 0 && (!w_kr || !w_qr || !q_rope)))
+    return fail(MLA_ERR_INVALID_ARG, "NULL pointer argument");
+  const size_t need = mla::project_inputs_workspace_bytes(L, (int)rows, d_q, cfg->dtype == MLA_F32 ? 4 : 2);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu%s", need, workspace_bytes,
+                workspace ? "" : " (NULL)");
+  const int use_norm = kv_norm_w != nullptr;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = cfg->dtype == MLA_F32
+                     ? mla::launch_project_inputs<float>(L, batch, n_new, d_model, d_q, h, w_dkv, w_kr, kv_norm_w,
+                                                         kv_norm_eps, use_norm, cache, seq_off, len_before, w_dq, w_uq,
+                                                         w_qr, q_nope, q_rope, workspace, st)
+                     : mla::launch_project_inputs<__bf16>(L, batch, n_new, d_model, d_q, h, w_dkv, w_kr, kv_norm_w,
+                                                          kv_norm_eps, use_norm, cache, seq_off, len_before, w_dq, w_uq,
+                                                          w_qr, q_nope, q_rope, workspace, st);
+  return from_hip(e, "mla_project_inputs launch");
+}
+
 size_t mla_prefill_explicit_workspace_size(const mla_config* cfg, int32_t batch, int32_t n_q, int32_t max_seq_len) {
   mla::LayerDims L;
   if (check_cfg(cfg, &L) != MLA_OK) return 0;

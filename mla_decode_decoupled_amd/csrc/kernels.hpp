@@ -112,6 +112,15 @@ template <typename T>
 hipError_t launch_project_q(const LayerDims& L, int n_rows, int d_model, int d_q, const void* h, const void* w_dq,
                             const void* w_uq, const void* w_qr, void* q_nope, void* q_rope, void* workspace,
                             hipStream_t stream);
+// both projections at once (mla_project_inputs): the kv side's float32 projection, then c_Q, in
+// one workspace of project_inputs_workspace_bytes
+size_t project_inputs_workspace_bytes(const LayerDims& L, int n_rows, int d_q, int elem_bytes);
+template <typename T>
+hipError_t launch_project_inputs(const LayerDims& L, int batch, int n_new, int d_model, int d_q, const void* h,
+                                 const void* w_dkv, const void* w_kr, const void* norm_w, float eps, int use_norm,
+                                 void* cache, const int64_t* seq_off, const int32_t* len_before, const void* w_dq,
+                                 const void* w_uq, const void* w_qr, void* q_nope, void* q_rope, void* workspace,
+                                 hipStream_t stream);
 
 // Explicit (non-absorbed) prefill for the DeepSeek head shape (prefill_explicit.hip): K_C and V
 // rebuilt by a GEMM over the cached latents (linear.hip), then multi-head attention with 192-wide

@@ -48,6 +48,68 @@ __device__ __forceinline__ void ystore(const Seg2& s, int r, int n, float v) {
     ((Ty*)s.y2)[(size_t)r * s.ldy2 + (n - s.n1)] = from_f32<Ty>(v);
 }
 
+// Up to three segments for the matrix-vector kernel, each with its own output type: output
+// columns [end[k-1], end[k]) come from weight w[k] and go to y[k] (row stride ldy[k]), stored as
+// float32 when f32[k] is set, else as bf16.
+struct Seg3 {
+  const void* w[3];
+  void* y[3];
+  int end[3];
+  int ldy[3];
+  int f32[3];
+};
+
+__device__ __forceinline__ int seg_of(const Seg3& s, int n) { return n < s.end[0] ? 0 : (n < s.end[1] ? 1 : 2); }
+__device__ __forceinline__ int seg_base(const Seg3& s, int k) { return k == 0 ? 0 : s.end[k - 1]; }
+
+// The kv side's finish, carried by a projection launch: RMS-normalise the latent part of a token's
+// float32 projection (gain optional), rotate its position part by the token's position in float64,
+// and store the packed row into the token's cache slot. pre [rows, d_latent + d_rope] float32; row
+// r = b n_new + i is token i of sequence b, at position len_before[b] + i.
+struct KvFinish {
+  const float* pre;
+  const void* norm_w;
+  void* cache;
+  const int64_t* seq_off;
+  const int32_t* len_before;
+  float eps;
+  int use_norm, n_new, d_latent, d_rope;
+  double base;
+};
+
+// one token, the whole block (blockDim.x = 256) taking part; red: 4 floats of shared memory
+template <typename T>
+__device__ void finish_token(const KvFinish& f, int r, float* red) {
+  const int row = f.d_latent + f.d_rope;
+  const int b = r / f.n_new, i = r % f.n_new;
+  const float* src = f.pre + (size_t)r * row;
+  const int64_t p = (int64_t)f.len_before[b] + i;
+  T* dst = (T*)f.cache + (f.seq_off[b] + p) * (int64_t)row;
+  float inv = 1.0f;
+  if (f.use_norm) {
+    float ss = 0.0f;
+    for (int c = threadIdx.x; c < f.d_latent; c += blockDim.x) ss = fmaf(src[c], src[c], ss);
+    ss = warp_sum(ss);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float tot = red[0] + red[1] + red[2] + red[3];
+    __syncthreads();   // red is free for the next token
+    inv = 1.0f / sqrtf(tot / (float)f.d_latent + f.eps);
+  }
+  for (int c = threadIdx.x; c < f.d_latent; c += blockDim.x) {
+    float v = src[c] * inv;
+    if (f.use_norm && f.norm_w != nullptr) v *= to_f32(((const T*)f.norm_w)[c]);
+    dst[c] = from_f32<T>(v);
+  }
+  for (int j = threadIdx.x; j < f.d_rope / 2; j += blockDim.x) {
+    double sn, cs;
+    rope_sincos_f64(rope_theta(f.base, j, f.d_rope), p, &sn, &cs);
+    const double x0 = src[f.d_latent + 2 * j], x1 = src[f.d_latent + 2 * j + 1];
+    dst[f.d_latent + 2 * j] = from_f64<T>(x0 * cs - x1 * sn);
+    dst[f.d_latent + 2 * j + 1] = from_f64<T>(x0 * sn + x1 * cs);
+  }
+}
+
 // ---------------------------------------------------------------- generic
 // grid (ceil(n / 4), min(M, 65535)), 256 threads: wave w computes column 4 blockIdx.x + w for rows
 // blockIdx.y, blockIdx.y + gridDim.y, ...
@@ -76,30 +138,38 @@ __device__ __forceinline__ void unpack8(const i32x4 v, float* f) {
 }
 
 // ---------------------------------------------------------------- few rows
-// grid (ceil(n / (RW 4 / KS)), ceil(M / RB)), 256 threads. The 4 waves form 4 / KS groups of KS
-// waves; group g owns weight rows (blockIdx.x (4 / KS) + g) RW .. +RW-1 and the KS waves of a group
-// split K between them (wave part p takes the 16-byte pieces 64 p + lane + 64 KS j), so a short
-// K still gives every lane several independent loads. Each lane keeps RW x U weight loads in
-// flight (nontemporal: the weights are read once) next to the matching pieces of the RB
-// activation rows (through the caches, where every workgroup finds them). K % 8 == 0, x and W
-// 16-byte aligned, ldx % 8 == 0.
-template <int RW, int RB, int KS, typename Ty>
-__global__ void __launch_bounds__(256) lin_gemv(const bf16* __restrict__ x, int ldx, int M, int K, Seg2 s) {
+// grid (ceil(n / (RW 4 / KS)) [+ 1 finish column], ceil(M / RB)), 256 threads. The 4 waves form
+// 4 / KS groups of KS waves; group g owns weight rows (blockIdx.x (4 / KS) + g) RW .. +RW-1 and the
+// KS waves of a group split K between them (wave part p takes the 16-byte pieces
+// 64 p + lane + 64 KS j), so a short K still gives every lane several independent loads. Each lane
+// keeps RW x U weight loads in flight (nontemporal: the weights are read once) next to the
+// matching pieces of the RB activation rows (through the caches, where every workgroup finds
+// them). With a finish (f.cache set) the last column of workgroups runs finish_token for the rows
+// of its row block instead. K % 8 == 0, x and W 16-byte aligned, ldx % 8 == 0.
+template <int RW, int RB, int KS>
+__global__ void __launch_bounds__(256) lin_gemv(const bf16* __restrict__ x, int ldx, int M, int K, Seg3 s, KvFinish f) {
   constexpr int U = 8 / RW;
   constexpr int G = 4 / KS;
   __shared__ float red[4][RW][RB];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int grp = w / KS, part = w % KS;
   const int r0 = blockIdx.y * RB, nr = min(RB, M - r0);
+  if (f.cache != nullptr && (int)blockIdx.x == (int)gridDim.x - 1) {   // the whole workgroup
+    for (int rr = 0; rr < nr; ++rr) finish_token<bf16>(f, r0 + rr, &red[0][0][0]);
+    return;
+  }
+  const int n = s.end[2];
   const int nb = (blockIdx.x * G + grp) * RW;
-  const bool active = nb < s.n;
+  const bool active = nb < n;
   const int KP = K / 8;
   const bf16* wr[RW];
   bool ok[RW];
 #pragma unroll
   for (int q = 0; q < RW; ++q) {
-    ok[q] = nb + q < s.n;
-    wr[q] = wrow<bf16>(s, ok[q] ? nb + q : (active ? nb : 0), K);
+    ok[q] = nb + q < n;
+    const int row = ok[q] ? nb + q : (active ? nb : 0);
+    const int k = seg_of(s, row);
+    wr[q] = (const bf16*)s.w[k] + (size_t)(row - seg_base(s, k)) * K;
   }
   const bf16* xr[RB];
 #pragma unroll
@@ -142,13 +212,21 @@ __global__ void __launch_bounds__(256) lin_gemv(const bf16* __restrict__ x, int 
       }
     }
   }
+  auto store = [&](int r, int col, float v) {
+    const int k = seg_of(s, col);
+    const size_t o = (size_t)r * s.ldy[k] + (col - seg_base(s, k));
+    if (s.f32[k])
+      ((float*)s.y[k])[o] = v;
+    else
+      ((bf16*)s.y[k])[o] = (bf16)v;
+  };
 #pragma unroll
   for (int q = 0; q < RW; ++q)
 #pragma unroll
     for (int rr = 0; rr < RB; ++rr) {
       const float v = warp_sum(acc[q][rr]);
       if constexpr (KS == 1) {
-        if (lane == 0 && ok[q] && active && rr < nr) ystore<Ty>(s, r0 + rr, nb + q, v);
+        if (lane == 0 && ok[q] && active && rr < nr) store(r0 + rr, nb + q, v);
       } else {
         if (lane == 0) red[w][q][rr] = v;
       }
@@ -163,7 +241,7 @@ __global__ void __launch_bounds__(256) lin_gemv(const bf16* __restrict__ x, int 
           float v = red[w][q][rr];
 #pragma unroll
           for (int k = 1; k < KS; ++k) v += red[w + k][q][rr];
-          if (ok[q] && rr < nr) ystore<Ty>(s, r0 + rr, nb + q, v);
+          if (ok[q] && rr < nr) store(r0 + rr, nb + q, v);
         }
     }
   }
@@ -470,6 +548,39 @@ bool staged_ok(const Seg2& s) {
          (!two || (s.ldy2 % 8 == 0 && aligned16(s.y2)));
 }
 
+// The matrix-vector kernel for M < kGemmMinRows rows of bf16 x over up to three segments, and
+// with `fin` the kv finish in one extra column of workgroups. Two weight rows per wave for wide
+// outputs; K split over 2 or 4 waves until about 16 waves per CU have work, as long as every lane
+// keeps at least 2 pieces of each row.
+hipError_t gemv(const bf16* x, int ldx, int M, int K, const Seg3& s, const KvFinish* fin, hipStream_t stream) {
+  const int n = s.end[2];
+  const int rw = n >= 8192 ? 2 : 1;
+  const int64_t row_waves = (n + rw - 1) / rw;
+  int ks = 1;
+  while (ks < 4 && row_waves * ks < 4096 && K / 8 >= 64 * 2 * (2 * ks)) ks *= 2;
+  const int rb = M == 1 ? 1 : (M == 2 ? 2 : 4);
+  const int rows_per_wg = rw * 4 / ks;
+  const dim3 grid((n + rows_per_wg - 1) / rows_per_wg + (fin != nullptr ? 1 : 0), (M + rb - 1) / rb);
+  const KvFinish none{nullptr, nullptr, nullptr, nullptr, nullptr, 0.0f, 0, 1, 0, 0, 0.0};
+  const KvFinish& fk = fin != nullptr ? *fin : none;
+#define MLA_LIN_GEMV(RW, KS)                                                                                     \
+  do {                                                                                                           \
+    if (rb == 1)                                                                                                 \
+      hipLaunchKernelGGL((lin_gemv<RW, 1, KS>), grid, dim3(256), 0, stream, x, ldx, M, K, s, fk);                \
+    else if (rb == 2)                                                                                            \
+      hipLaunchKernelGGL((lin_gemv<RW, 2, KS>), grid, dim3(256), 0, stream, x, ldx, M, K, s, fk);                \
+    else                                                                                                         \
+      hipLaunchKernelGGL((lin_gemv<RW, 4, KS>), grid, dim3(256), 0, stream, x, ldx, M, K, s, fk);                \
+  } while (0)
+  if (rw == 1) {
+    if (ks == 1) MLA_LIN_GEMV(1, 1); else if (ks == 2) MLA_LIN_GEMV(1, 2); else MLA_LIN_GEMV(1, 4);
+  } else {
+    if (ks == 1) MLA_LIN_GEMV(2, 1); else if (ks == 2) MLA_LIN_GEMV(2, 2); else MLA_LIN_GEMV(2, 4);
+  }
+#undef MLA_LIN_GEMV
+  return hipGetLastError();
+}
+
 // y = x W^T over the two segments; Ty is float or the storage type T
 template <typename T, typename Ty>
 hipError_t linear(const T* x, int ldx, int M, int K, const Seg2& s, hipStream_t stream) {
@@ -511,31 +622,9 @@ hipError_t linear(const T* x, int ldx, int M, int K, const Seg2& s, hipStream_t 
       return hipGetLastError();
     }
     if (vec && M < kGemmMinRows) {
-      // two weight rows per wave for wide outputs; split K over 2 or 4 waves until about 16 waves
-      // per CU have work, as long as every lane keeps at least 2 pieces of each row
-      const int rw = s.n >= 8192 ? 2 : 1;
-      const int64_t row_waves = (s.n + rw - 1) / rw;
-      int ks = 1;
-      while (ks < 4 && row_waves * ks < 4096 && K / 8 >= 64 * 2 * (2 * ks)) ks *= 2;
-      const int rb = M == 1 ? 1 : (M == 2 ? 2 : 4);
-      const int rows_per_wg = rw * 4 / ks;
-      const dim3 grid((s.n + rows_per_wg - 1) / rows_per_wg, (M + rb - 1) / rb);
-#define MLA_LIN_GEMV(RW, KS)                                                                                     \
-  do {                                                                                                           \
-    if (rb == 1)                                                                                                 \
-      hipLaunchKernelGGL((lin_gemv<RW, 1, KS, Ty>), grid, dim3(256), 0, stream, x, ldx, M, K, s);                \
-    else if (rb == 2)                                                                                            \
-      hipLaunchKernelGGL((lin_gemv<RW, 2, KS, Ty>), grid, dim3(256), 0, stream, x, ldx, M, K, s);                \
-    else                                                                                                         \
-      hipLaunchKernelGGL((lin_gemv<RW, 4, KS, Ty>), grid, dim3(256), 0, stream, x, ldx, M, K, s);                \
-  } while (0)
-      if (rw == 1) {
-        if (ks == 1) MLA_LIN_GEMV(1, 1); else if (ks == 2) MLA_LIN_GEMV(1, 2); else MLA_LIN_GEMV(1, 4);
-      } else {
-        if (ks == 1) MLA_LIN_GEMV(2, 1); else if (ks == 2) MLA_LIN_GEMV(2, 2); else MLA_LIN_GEMV(2, 4);
-      }
-#undef MLA_LIN_GEMV
-      return hipGetLastError();
+      const int f = sizeof(Ty) == 4 ? 1 : 0;
+      const Seg3 s3{{s.w1, s.w2, s.w2}, {s.y1, s.y2, s.y2}, {s.n1, s.n, s.n}, {s.ldy1, s.ldy2, s.ldy2}, {f, f, f}};
+      return gemv(x, ldx, M, K, s3, nullptr, stream);
     }
   }
   hipLaunchKernelGGL((lin_generic<T, Ty>), dim3((s.n + 3) / 4, M < 65535 ? M : 65535), dim3(256), 0, stream, x, ldx,
@@ -544,44 +633,11 @@ hipError_t linear(const T* x, int ldx, int M, int K, const Seg2& s, hipStream_t 
 }
 
 // ---------------------------------------------------------------- kv finish
-// One block per new token: RMS-normalise the latent part of the projected row (float32 sums of
-// squares; gain optional), rotate the position part by the token's position in float64, and store
-// the packed row into the token's cache slot. pre [batch * n_new, d_latent + d_rope] float32.
+// One block per new token (grid (n_new, batch)): finish_token on the token's float32 projection.
 template <typename T>
-__global__ void __launch_bounds__(256) kv_finish(const float* __restrict__ pre, const T* __restrict__ norm_w, float eps,
-                                                 int use_norm, T* __restrict__ cache,
-                                                 const int64_t* __restrict__ seq_off,
-                                                 const int32_t* __restrict__ len_before, int n_new, int d_latent,
-                                                 int d_rope, double base) {
+__global__ void __launch_bounds__(256) kv_finish(KvFinish f) {
   __shared__ float red[4];
-  const int i = blockIdx.x, b = blockIdx.y;
-  const int row = d_latent + d_rope;
-  const size_t tok = (size_t)b * n_new + i;
-  const float* src = pre + tok * row;
-  const int64_t p = (int64_t)len_before[b] + i;
-  T* dst = cache + (seq_off[b] + p) * (int64_t)row;
-  float inv = 1.0f;
-  if (use_norm) {
-    float ss = 0.0f;
-    for (int c = threadIdx.x; c < d_latent; c += blockDim.x) ss = fmaf(src[c], src[c], ss);
-    ss = warp_sum(ss);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
-    __syncthreads();
-    const float tot = red[0] + red[1] + red[2] + red[3];
-    inv = 1.0f / sqrtf(tot / (float)d_latent + eps);
-  }
-  for (int c = threadIdx.x; c < d_latent; c += blockDim.x) {
-    float v = src[c] * inv;
-    if (use_norm && norm_w != nullptr) v *= to_f32(norm_w[c]);
-    dst[c] = from_f32<T>(v);
-  }
-  for (int j = threadIdx.x; j < d_rope / 2; j += blockDim.x) {
-    double sn, cs;
-    rope_sincos_f64(rope_theta(base, j, d_rope), p, &sn, &cs);
-    const double x0 = src[d_latent + 2 * j], x1 = src[d_latent + 2 * j + 1];
-    dst[d_latent + 2 * j] = from_f64<T>(x0 * cs - x1 * sn);
-    dst[d_latent + 2 * j + 1] = from_f64<T>(x0 * sn + x1 * cs);
-  }
+  finish_token<T>(f, blockIdx.y * f.n_new + blockIdx.x, red);
 }
 
 }  // namespace lin
@@ -603,9 +659,9 @@ hipError_t launch_project_kv_append(const LayerDims& L, int batch, int n_new, in
   lin::Seg2 s{w_dkv, w_kr, pre, pre + L.d_latent, L.d_latent, row, row, row};
   hipError_t e = lin::linear<T, float>((const T*)h, d_model, batch * n_new, d_model, s, stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(lin::kv_finish<T>, dim3(n_new, batch), dim3(256), 0, stream, (const float*)pre,
-                     (const T*)norm_w, eps, use_norm, (T*)cache, seq_off, len_before, n_new, L.d_latent, L.d_rope,
-                     L.rope_base);
+  const lin::KvFinish f{pre, norm_w, cache, seq_off, len_before, eps, use_norm, n_new, L.d_latent, L.d_rope,
+                        L.rope_base};
+  hipLaunchKernelGGL(lin::kv_finish<T>, dim3(n_new, batch), dim3(256), 0, stream, f);
   return hipGetLastError();
 }
 
@@ -625,6 +681,48 @@ hipError_t launch_project_q(const LayerDims& L, int n_rows, int d_model, int d_q
   const int n1 = L.n_heads * L.d_nope, n2 = L.n_heads * L.d_rope;
   lin::Seg2 s{w_uq, w_qr, q_nope, q_rope, n1, n1 + n2, n1, n2};
   return lin::linear<T, T>(x, K, n_rows, K, s, stream);
+}
+
+size_t project_inputs_workspace_bytes(const LayerDims& L, int n_rows, int d_q, int elem_bytes) {
+  const size_t kv = ((size_t)n_rows * (L.d_latent + L.d_rope) * sizeof(float) + 255) & ~(size_t)255;
+  return kv + (((size_t)n_rows * d_q * elem_bytes + 255) & ~(size_t)255);
+}
+
+// Both projections of the layer input: with few rows of bf16 in the layouts the matrix-vector
+// kernel takes, two launches instead of four. The first reads h once for W_DKV, W_KR and W_DQ
+// (three segments: the kv projection in float32, c_Q rounded to bf16); the second runs W_UQ and
+// W_QR over c_Q (or over h without query compression) with the kv finish in one extra column of
+// workgroups. Otherwise the two calls' own launches, on the two halves of the workspace.
+template <typename T>
+hipError_t launch_project_inputs(const LayerDims& L, int batch, int n_new, int d_model, int d_q, const void* h,
+                                 const void* w_dkv, const void* w_kr, const void* norm_w, float eps, int use_norm,
+                                 void* cache, const int64_t* seq_off, const int32_t* len_before, const void* w_dq,
+                                 const void* w_uq, const void* w_qr, void* q_nope, void* q_rope, void* workspace,
+                                 hipStream_t stream) {
+  const int rows = batch * n_new;
+  const int row = L.d_latent + L.d_rope;
+  float* pre = (float*)workspace;
+  void* cq = (char*)workspace + (((size_t)rows * row * sizeof(float) + 255) & ~(size_t)255);
+  const auto al = [](const void* p) { return p == nullptr || lin::aligned16(p); };
+  const bool fused = sizeof(T) == 2 && rows < kGemmMinRows && lin::aligned16(h) && d_model % 8 == 0 && d_q % 8 == 0 &&
+                     al(w_dkv) && al(w_kr) && al(w_dq) && al(w_uq) && al(w_qr);
+  if (!fused) {
+    hipError_t e = launch_project_kv_append<T>(L, batch, n_new, d_model, h, w_dkv, w_kr, norm_w, eps, use_norm, cache,
+                                               seq_off, len_before, pre, stream);
+    if (e != hipSuccess) return e;
+    return launch_project_q<T>(L, rows, d_model, d_q, h, w_dq, w_uq, w_qr, q_nope, q_rope, cq, stream);
+  }
+  const lin::Seg3 s1{{w_dkv, w_kr, w_dq}, {pre, pre + L.d_latent, cq}, {L.d_latent, row, row + d_q}, {row, row, d_q},
+                     {1, 1, 0}};
+  hipError_t e = lin::gemv((const bf16*)h, d_model, rows, d_model, s1, nullptr, stream);
+  if (e != hipSuccess) return e;
+  const int n1 = L.n_heads * L.d_nope, n2 = L.n_heads * L.d_rope;
+  const lin::Seg3 s2{{w_uq, w_qr, w_qr}, {q_nope, q_rope, q_rope}, {n1, n1 + n2, n1 + n2}, {n1, n2, n2}, {0, 0, 0}};
+  const lin::KvFinish f{pre, norm_w, cache, seq_off, len_before, eps, use_norm, n_new, L.d_latent, L.d_rope,
+                        L.rope_base};
+  const bf16* x2 = d_q > 0 ? (const bf16*)cq : (const bf16*)h;
+  const int k2 = d_q > 0 ? d_q : d_model;
+  return lin::gemv(x2, k2, rows, k2, s2, &f, stream);
 }
 
 template <typename T>
@@ -665,6 +763,14 @@ template hipError_t launch_project_kv_append<float>(const LayerDims&, int, int, 
 template hipError_t launch_project_kv_append<__bf16>(const LayerDims&, int, int, int, const void*, const void*,
                                                      const void*, const void*, float, int, void*, const int64_t*,
                                                      const int32_t*, void*, hipStream_t);
+template hipError_t launch_project_inputs<float>(const LayerDims&, int, int, int, int, const void*, const void*,
+                                                 const void*, const void*, float, int, void*, const int64_t*,
+                                                 const int32_t*, const void*, const void*, const void*, void*, void*,
+                                                 void*, hipStream_t);
+template hipError_t launch_project_inputs<__bf16>(const LayerDims&, int, int, int, int, const void*, const void*,
+                                                  const void*, const void*, float, int, void*, const int64_t*,
+                                                  const int32_t*, const void*, const void*, const void*, void*, void*,
+                                                  void*, hipStream_t);
 template hipError_t launch_project_q<float>(const LayerDims&, int, int, int, const void*, const void*, const void*,
                                             const void*, void*, void*, void*, hipStream_t);
 template hipError_t launch_project_q<__bf16>(const LayerDims&, int, int, int, const void*, const void*, const void*,

@@ -3,8 +3,9 @@
 A stack of MLA attention layers is run token by token the way the pages run their check of the
 absorbed form ("从零理解 MLA", the decode loop after the decoupled-RoPE code: every step appends
 the new token's latent and rotated position key to the cache, then attends over the grown
-cache): per layer, mla_project_kv_append -> mla_project_q -> mla_absorb_q -> mla_decode_attn ->
-mla_out_proj (with W_O), and the layer's output u is the next layer's input (the residual
+cache): per layer, mla_project_inputs (mla_project_kv_append and mla_project_q in one call) ->
+mla_absorb_q -> mla_decode_attn -> mla_out_proj (with W_O), and the layer's output u is the next
+layer's input (the residual
 stream and the feed-forward blocks of a full model are not part of this stack). After the last
 layer, mla_decode_advance moves every position on by the tokens just appended, so one recorded
 decode step — a HIP graph captured through torch — can be replayed for every following token.
@@ -43,8 +44,7 @@ class _StepBuffers:
         # layer outputs ping-pong: layer l writes u[l % 2], layer l + 1 reads it
         self.u = [torch.empty((B, n_new, stack.d_model), dtype=dt, device=dev) for _ in range(2)]
         self.h_in = torch.empty((B, n_new, stack.d_model), dtype=dt, device=dev)
-        pw = max(ops.mla_project_workspace_size(cfg, R, stack.d_model, 0),
-                 ops.mla_project_workspace_size(cfg, R, stack.d_model, stack.d_q))
+        pw = ops.mla_project_inputs_workspace_size(cfg, R, stack.d_model, stack.d_q)
         self.ws_proj = torch.empty(max(pw, 256), dtype=torch.uint8, device=dev)
         aw = ops.mla_decode_attn_workspace_size(cfg, B, n_new, stack.capacity, stack.n_splits)
         self.ws_attn = torch.empty(max(aw, 256), dtype=torch.uint8, device=dev)
@@ -101,11 +101,9 @@ class DecodeStack:
         R = B * n
         x = b.h_in
         for l, w in enumerate(self.layers):
-            ops.mla_project_kv_append(cfg, x, w["w_dkv"], w["w_kr"], self.caches[l], self.seq_off, b.len_before,
-                                      kv_norm_w=w.get("kv_norm_w"), kv_norm_eps=self.kv_norm_eps,
-                                      workspace=b.ws_proj)
-            ops.mla_project_q(cfg, x.view(R, self.d_model), w["w_uq"], w["w_qr"], b.q_nope, b.q_rope,
-                              w_dq=w.get("w_dq"), workspace=b.ws_proj)
+            ops.mla_project_inputs(cfg, x, w["w_dkv"], w["w_kr"], self.caches[l], self.seq_off, b.len_before,
+                                   w["w_uq"], w["w_qr"], b.q_nope, b.q_rope, w_dq=w.get("w_dq"),
+                                   kv_norm_w=w.get("kv_norm_w"), kv_norm_eps=self.kv_norm_eps, workspace=b.ws_proj)
             ops.mla_absorb_q(cfg, b.q_nope, b.q_rope, b.q_pos, w["w_uk"], b.q_packed.view(R, cfg.n_heads, -1))
             ops.mla_decode_attn(cfg, b.q_packed, self.caches[l], self.seq_off, b.seq_len, self.capacity, b.z, b.lse,
                                 n_splits=self.n_splits, workspace=b.ws_attn)

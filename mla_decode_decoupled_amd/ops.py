@@ -252,6 +252,55 @@ def mla_project_q(cfg: MlaConfig, h: torch.Tensor, w_uq: torch.Tensor, w_qr: Opt
                             _ptr(q_rope), wp, wb, _stream(q_nope)), "mla_project_q")
 
 
+def mla_project_inputs_workspace_size(cfg: MlaConfig, n_rows: int, d_model: int, d_q: int = 0) -> int:
+    return int(lib.mla_project_inputs_workspace_size(cfg, n_rows, d_model, d_q))
+
+
+def mla_project_inputs(cfg: MlaConfig, h: torch.Tensor, w_dkv: torch.Tensor, w_kr: Optional[torch.Tensor],
+                       cache: torch.Tensor, seq_off: torch.Tensor, len_before: torch.Tensor, w_uq: torch.Tensor,
+                       w_qr: Optional[torch.Tensor], q_nope: torch.Tensor, q_rope: Optional[torch.Tensor],
+                       w_dq: Optional[torch.Tensor] = None, kv_norm_w: Optional[torch.Tensor] = None,
+                       kv_norm_eps: float = 1e-6, workspace: Optional[torch.Tensor] = None) -> None:
+    """mla_project_kv_append and mla_project_q on the same h [batch, n_new, d_model] in one call
+    (the query rows are h viewed as [batch * n_new, d_model])."""
+    dt = storage_dtype(cfg)
+    H = cfg.n_heads
+    if h.dim() != 3:
+        raise ValueError("h must be [batch, n_new, d_model]")
+    B, n_new, dm = h.shape
+    R = B * n_new
+    dev = h.device
+    _need(h, "h", dt)
+    _need(w_dkv, "w_dkv", dt, (cfg.d_latent, dm), dev)
+    if cfg.d_rope > 0 or w_kr is not None:
+        _need(w_kr, "w_kr", dt, (cfg.d_rope, dm), dev)
+    if kv_norm_w is not None:
+        _need(kv_norm_w, "kv_norm_w", dt, (cfg.d_latent,), dev)
+    _need(cache, "cache", dt, None, dev)
+    if cache.dim() != 2 or cache.shape[1] != cfg.d_latent + cfg.d_rope:
+        raise ValueError("cache must be [rows, d_latent + d_rope]")
+    _need(seq_off, "seq_off", torch.int64, (B,), dev)
+    _need(len_before, "len_before", torch.int32, (B,), dev)
+    d_q = 0
+    if w_dq is not None:
+        if w_dq.dim() != 2:
+            raise ValueError("w_dq must be [d_q, d_model]")
+        d_q = w_dq.shape[0]
+        _need(w_dq, "w_dq", dt, (d_q, dm), dev)
+    K = d_q if d_q > 0 else dm
+    _need(w_uq, "w_uq", dt, (H * cfg.d_nope, K), dev)
+    _need(q_nope, "q_nope", dt, (R, H, cfg.d_nope), dev)
+    if cfg.d_rope > 0 or w_qr is not None:
+        _need(w_qr, "w_qr", dt, (H * cfg.d_rope, K), dev)
+    if cfg.d_rope > 0 or q_rope is not None:
+        _need(q_rope, "q_rope", dt, (R, H, cfg.d_rope), dev)
+    wp, wb = _ws(workspace, dev)
+    check(lib.mla_project_inputs(cfg, B, n_new, dm, d_q, _ptr(h), _ptr(w_dkv), _ptr(w_kr), _ptr(kv_norm_w),
+                                 float(kv_norm_eps), _ptr(cache), _ptr(seq_off), _ptr(len_before), _ptr(w_dq),
+                                 _ptr(w_uq), _ptr(w_qr), _ptr(q_nope), _ptr(q_rope), wp, wb, _stream(q_nope)),
+          "mla_project_inputs")
+
+
 def mla_prefill_explicit_workspace_size(cfg: MlaConfig, batch: int, n_q: int, max_seq_len: int) -> int:
     return int(lib.mla_prefill_explicit_workspace_size(cfg, batch, n_q, max_seq_len))
 
@@ -325,6 +374,8 @@ __all__ = [
     "mla_project_workspace_size",
     "mla_project_kv_append",
     "mla_project_q",
+    "mla_project_inputs_workspace_size",
+    "mla_project_inputs",
     "mla_decode_advance",
     "mla_prefill_explicit_workspace_size",
     "mla_prefill_explicit",

@@ -228,3 +228,24 @@ def test_decode_step_arguments():
     assert call(c, FAKE, need, batch=300, n_q=300) == MLA_ERR_UNSUPPORTED
     assert lib.mla_decode_step(c, 0, 1, None, None, None, None, None, None, None, None, None, 0, 0, None, 0, None,
                                None, None, None, None) == MLA_OK
+
+
+def test_project_inputs_arguments():
+    """mla_project_inputs validates like mla_project_kv_append and mla_project_q together."""
+    c = cfg()
+    need = lib.mla_project_inputs_workspace_size(c, 4, 7168, 1536)
+    assert need >= 4 * 576 * 4 + 4 * 1536 * 2
+    assert lib.mla_project_inputs_workspace_size(c, 0, 7168, 1536) == 0
+
+    def call(ws_bytes=need, d_q=1536, w_dq=FAKE, h=FAKE, q_nope=FAKE, eps=1e-6, norm=None, batch=2, n_new=2):
+        return lib.mla_project_inputs(c, batch, n_new, 7168, d_q, h, FAKE, FAKE, norm, eps, FAKE, FAKE, FAKE, w_dq,
+                                      FAKE, FAKE, q_nope, FAKE, FAKE, ws_bytes, None)
+
+    assert call(d_q=1536, w_dq=None) == MLA_ERR_INVALID_ARG      # w_dq exactly when d_q > 0
+    assert call(d_q=0, w_dq=FAKE) == MLA_ERR_INVALID_ARG
+    assert call(h=None) == MLA_ERR_INVALID_ARG
+    assert call(q_nope=None) == MLA_ERR_INVALID_ARG
+    assert call(norm=FAKE, eps=float("nan")) == MLA_ERR_INVALID_ARG
+    assert call(ws_bytes=need - 1) == MLA_ERR_WORKSPACE
+    assert call(batch=-1) == MLA_ERR_INVALID_ARG
+    assert call(batch=0) == MLA_OK

@@ -129,3 +129,59 @@ def test_decode_advance_moves_positions():
     assert lb.tolist() == [2, 9, 102]
     assert sl.tolist() == [4, 11, 104]
     assert qp.tolist() == [2, 9, 102, 5, 11]
+
+
+def _run_inputs(cfg, w, h, len_before, eps=1e-6):
+    """mla_project_inputs on h [B, n_new, d_model]: the cache rows per token and the query outputs."""
+    lc = lib_config(cfg)
+    dt = mla.storage_dtype(lc)
+    B, n_new, dm = h.shape
+    R, H = B * n_new, cfg.n_heads
+    d_q = cfg.q_lora or 0
+    cap = int(len_before.max()) + n_new + 3
+    cache = torch.full((B * cap, cfg.row), float("nan"), dtype=dt, device="cuda")
+    seq_off = torch.arange(B, dtype=torch.int64, device="cuda") * cap
+    lb = torch.from_numpy(len_before.astype(np.int32)).cuda()
+    qn = torch.full((R, H, cfg.d_nope), float("nan"), dtype=dt, device="cuda")
+    qr = torch.full((R, H, cfg.d_rope), float("nan"), dtype=dt, device="cuda")
+    ws = torch.empty(mla.mla_project_inputs_workspace_size(lc, R, dm, d_q), dtype=torch.uint8, device="cuda")
+    norm = tdev(w["kv_norm_w"], dt) if "kv_norm_w" in w else None
+    w_uq = w["w_uq"] if d_q else w["w_q"]
+    mla.mla_project_inputs(lc, tdev(h, dt), tdev(w["w_dkv"], dt), tdev(w["w_kr"], dt), cache, seq_off, lb,
+                           tdev(w_uq, dt), tdev(w["w_qr"], dt), qn, qr,
+                           w_dq=tdev(w["w_dq"], dt) if d_q else None, kv_norm_w=norm, kv_norm_eps=eps, workspace=ws)
+    torch.cuda.synchronize()
+    weights = {k: w[k] for k in PROJ_KEYS if k in w}
+    got, ref = [], []
+    for b in range(B):
+        p = O.project_inputs(h[b], weights, H, kv_norm_eps=eps)
+        pos = int(len_before[b]) + np.arange(n_new)
+        ref.append(O.cache_rows(p["c"], p["k_rope_pre"], pos, cfg.rope_base))
+        got.append(np32(cache[b * cap + pos[0]: b * cap + pos[-1] + 1]))
+        assert np.all(np.isnan(np32(cache[b * cap: b * cap + pos[0]])))
+    pq = O.project_inputs(h.reshape(R, dm), weights, H)
+    return np.concatenate(got), np.concatenate(ref), np32(qn), np32(qr), pq["q_nope"], pq["q_rope_pre"]
+
+
+# 1-15 rows: the two-launch form (h read once for W_DKV, W_KR and W_DQ; the kv finish on the
+# W_UQ / W_QR launch), 16 rows: the four launches of the separate calls
+@pytest.mark.parametrize("batch,n_new", [(1, 1), (3, 1), (5, 3), (16, 1)])
+def test_project_inputs_v3_shape_bf16(v3_weights, batch, n_new):
+    cfg, w = v3_weights
+    h = w["h"][:batch * n_new].reshape(batch, n_new, cfg.d_model)
+    lb = np.random.default_rng(batch * 7 + n_new).integers(0, 3000, size=batch)
+    got, ref, qn, qr, qn_ref, qr_ref = _run_inputs(cfg, w, h, lb)
+    s1 = assert_close(got, ref, "bf16", f"cache rows B={batch} n_new={n_new}")
+    s2 = assert_close(qn, qn_ref, "bf16", "q_nope")
+    s3 = assert_close(qr, qr_ref, "bf16", "q_rope (unrotated)")
+    print(f"B={batch} n_new={n_new}: cache {s1} q_nope {s2} q_rope {s3}")
+
+
+@pytest.mark.parametrize("q_lora,norm", [(None, True), (48, False)], ids=["direct_rmsnorm", "compressed_plain"])
+def test_project_inputs_tiny_fp32(q_lora, norm):
+    cfg = _tiny(q_lora, norm, 94 + (q_lora or 0) + int(norm))
+    w = G.full_layer_inputs(cfg, 6)
+    got, ref, qn, qr, qn_ref, qr_ref = _run_inputs(cfg, w, w["h"].reshape(2, 3, cfg.d_model), np.array([4, 11]))
+    assert_close(got, ref, "f32", "cache rows")
+    assert_close(qn, qn_ref, "f32", "q_nope")
+    assert_close(qr, qr_ref, "f32", "q_rope (unrotated)")
