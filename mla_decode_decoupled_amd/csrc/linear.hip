@@ -144,9 +144,12 @@ __device__ __forceinline__ void unpack8(const i32x4 v, float* f) {
 // 64 p + lane + 64 KS j), so a short K still gives every lane several independent loads. Each lane
 // keeps RW x U weight loads in flight (nontemporal: the weights are read once) next to the
 // matching pieces of the RB activation rows (through the caches, where every workgroup finds
-// them). With a finish (f.cache set) the last column of workgroups runs finish_token for the rows
-// of its row block instead. K % 8 == 0, x and W 16-byte aligned, ldx % 8 == 0.
-template <int RW, int RB, int KS>
+// them). With FIN the first column of workgroups runs finish_token for the rows of its row block
+// instead (first, so that it is dispatched at once: the grid can hold more workgroups than the
+// chip, and a last column would wait for the others); FIN is a template flag because the float64
+// rotation costs registers, and with them occupancy, wherever it is compiled in. K % 8 == 0, x and
+// W 16-byte aligned, ldx % 8 == 0.
+template <int RW, int RB, int KS, bool FIN>
 __global__ void __launch_bounds__(256) lin_gemv(const bf16* __restrict__ x, int ldx, int M, int K, Seg3 s, KvFinish f) {
   constexpr int U = 8 / RW;
   constexpr int G = 4 / KS;
@@ -154,12 +157,16 @@ __global__ void __launch_bounds__(256) lin_gemv(const bf16* __restrict__ x, int 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int grp = w / KS, part = w % KS;
   const int r0 = blockIdx.y * RB, nr = min(RB, M - r0);
-  if (f.cache != nullptr && (int)blockIdx.x == (int)gridDim.x - 1) {   // the whole workgroup
-    for (int rr = 0; rr < nr; ++rr) finish_token<bf16>(f, r0 + rr, &red[0][0][0]);
-    return;
+  int bx = blockIdx.x;
+  if constexpr (FIN) {
+    if (bx == 0) {   // the whole workgroup
+      for (int rr = 0; rr < nr; ++rr) finish_token<bf16>(f, r0 + rr, &red[0][0][0]);
+      return;
+    }
+    --bx;
   }
   const int n = s.end[2];
-  const int nb = (blockIdx.x * G + grp) * RW;
+  const int nb = (bx * G + grp) * RW;
   const bool active = nb < n;
   const int KP = K / 8;
   const bf16* wr[RW];
@@ -563,14 +570,21 @@ hipError_t gemv(const bf16* x, int ldx, int M, int K, const Seg3& s, const KvFin
   const dim3 grid((n + rows_per_wg - 1) / rows_per_wg + (fin != nullptr ? 1 : 0), (M + rb - 1) / rb);
   const KvFinish none{nullptr, nullptr, nullptr, nullptr, nullptr, 0.0f, 0, 1, 0, 0, 0.0};
   const KvFinish& fk = fin != nullptr ? *fin : none;
-#define MLA_LIN_GEMV(RW, KS)                                                                                     \
+#define MLA_LIN_GEMV_F(RW, KS, F)                                                                                \
   do {                                                                                                           \
     if (rb == 1)                                                                                                 \
-      hipLaunchKernelGGL((lin_gemv<RW, 1, KS>), grid, dim3(256), 0, stream, x, ldx, M, K, s, fk);                \
+      hipLaunchKernelGGL((lin_gemv<RW, 1, KS, F>), grid, dim3(256), 0, stream, x, ldx, M, K, s, fk);             \
     else if (rb == 2)                                                                                            \
-      hipLaunchKernelGGL((lin_gemv<RW, 2, KS>), grid, dim3(256), 0, stream, x, ldx, M, K, s, fk);                \
+      hipLaunchKernelGGL((lin_gemv<RW, 2, KS, F>), grid, dim3(256), 0, stream, x, ldx, M, K, s, fk);             \
     else                                                                                                         \
-      hipLaunchKernelGGL((lin_gemv<RW, 4, KS>), grid, dim3(256), 0, stream, x, ldx, M, K, s, fk);                \
+      hipLaunchKernelGGL((lin_gemv<RW, 4, KS, F>), grid, dim3(256), 0, stream, x, ldx, M, K, s, fk);             \
+  } while (0)
+#define MLA_LIN_GEMV(RW, KS)          \
+  do {                                \
+    if (fin != nullptr)               \
+      MLA_LIN_GEMV_F(RW, KS, true);   \
+    else                              \
+      MLA_LIN_GEMV_F(RW, KS, false);  \
   } while (0)
   if (rw == 1) {
     if (ks == 1) MLA_LIN_GEMV(1, 1); else if (ks == 2) MLA_LIN_GEMV(1, 2); else MLA_LIN_GEMV(1, 4);
@@ -578,6 +592,7 @@ hipError_t gemv(const bf16* x, int ldx, int M, int K, const Seg3& s, const KvFin
     if (ks == 1) MLA_LIN_GEMV(2, 1); else if (ks == 2) MLA_LIN_GEMV(2, 2); else MLA_LIN_GEMV(2, 4);
   }
 #undef MLA_LIN_GEMV
+#undef MLA_LIN_GEMV_F
   return hipGetLastError();
 }
 
