@@ -1,20 +1,23 @@
 #!/usr/bin/env python3
 """Benchmark of one absorbed-MLA decode step on one MI355X.
 
-A step is one pass of the whole hot path over one batch: mla_rope_append (the
-new tokens), mla_absorb_q, mla_decode_attn (+ split-K merge) and mla_out_proj,
-all through the C ABI. The default workload is the DeepSeek-V3-shaped decode
+A step is one pass of the whole hot path over one batch: the append of the new
+tokens, the query absorption, the latent attention (+ split-K merge) and the
+W_UV projection, through the C ABI as one mla_decode_step call (three launches
+at batch 1), or with --single-calls as mla_rope_append, mla_absorb_q,
+mla_decode_attn and mla_out_proj. The default workload is the DeepSeek-V3-shaped decode
 step (batch 1, 128 heads, 512-dim latent, 64-dim position part, 4096 cached
 tokens + 1 new, bf16). Inputs are seeded synthetic data of that shape and live
 in HBM before timing starts. Unless --hot is given, every step reads its own
 copy of the cache, weights and queries (copies rotated so the working set is
 at least 1 GiB, four times the 256 MB last-level cache), so the bytes really
 come from HBM. The timed steps replay one captured HIP graph per input copy
-(the same four calls; --eager launches them from Python instead, which is
-bound by the launch overhead at batch 1); the eager time is reported too.
+(--eager launches them from Python instead, which is bound by the launch
+overhead at batch 1); the eager time is reported too. A second pass runs the
+four single calls with HIP events between them for the per-call times.
 
 Prints one JSON line (rank 0) with throughput, a roofline object for the
-dominant kernel (HIP events around its launches inside the timed region) and
+dominant call (mla_decode_attn: HIP events around it in the per-call pass) and
 the fp64 CPU oracle timed on a bounded sample of the same workload.
 """
 
