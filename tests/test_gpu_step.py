@@ -97,6 +97,18 @@ def test_step_without_head_split(n_splits, lens):
     _compare(host_inputs(_v3(len(lens)), lens=lens), n_splits=n_splits)
 
 
+@pytest.mark.parametrize("batch,length", [(1, 32768), (1, 32769), (16, 2048), (16, 2049)],
+                         ids=["b1_1024_tiles_hsplit", "b1_1025_tiles_balanced", "b16_64_tiles_hsplit",
+                              "b16_65_tiles_balanced"])
+def test_step_head_split_boundary(batch, length):
+    """Both sides of the head-split kernel's limit (rows x tiles of the longest row <= 1024, at most
+    16 rows). One key past it the balanced MFMA kernel and the single calls' merge take over. With
+    fewer than 16 rows the step fuses the head-split merge into the W_UV launch; at 16 rows it runs
+    the single calls' kernels either way. Equal lengths, so every row is at the bound."""
+    hsplit = batch * ((length + 31) // 32) <= 1024
+    _compare(host_inputs(_v3(batch), lens=[length] * batch), fused_merge=hsplit and batch < 16)
+
+
 def test_step_chunked_rows():
     """Many query rows per sequence (chunked prefill): GEMM projections, MFMA attention."""
     _compare(host_inputs(_v3(2, 40), lens=[100, 300]))
