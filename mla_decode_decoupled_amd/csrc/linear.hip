@@ -146,11 +146,15 @@ __device__ __forceinline__ void unpack8(const i32x4 v, float* f) {
 // matching pieces of the RB activation rows (through the caches, where every workgroup finds
 // them). With FIN the first column of workgroups runs finish_token for the rows of its row block
 // instead (first, so that it is dispatched at once: the grid can hold more workgroups than the
-// chip, and a last column would wait for the others); FIN is a template flag because the float64
-// rotation costs registers, and with them occupancy, wherever it is compiled in. K % 8 == 0, x and
-// W 16-byte aligned, ldx % 8 == 0.
+// chip, and a last column would wait for the others). FIN is a template flag because the float64
+// rotation costs registers, and with them occupancy, wherever it is compiled in; with one
+// activation row the FIN kernel is held to 7 waves per SIMD (72 VGPRs, the matrix-vector loop's
+// own need), so the finish path spills a few registers to scratch in its one workgroup column
+// instead of the whole launch running at 4 waves per SIMD (W_UQ + W_QR of the DeepSeek-V3 shape:
+// 15.6 us at 7 waves, 16.0 at 6, 17.6 at 4). K % 8 == 0, x and W 16-byte aligned, ldx % 8 == 0.
 template <int RW, int RB, int KS, bool FIN>
-__global__ void __launch_bounds__(256) lin_gemv(const bf16* __restrict__ x, int ldx, int M, int K, Seg3 s, KvFinish f) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FIN && RB == 1 ? 7 : 1)))
+lin_gemv(const bf16* __restrict__ x, int ldx, int M, int K, Seg3 s, KvFinish f) {
   constexpr int U = 8 / RW;
   constexpr int G = 4 / KS;
   __shared__ float red[4][RW][RB];
