@@ -182,34 +182,47 @@ __global__ void __launch_bounds__(256) absorb_q_gemm(const bf16* __restrict__ q_
 }
 
 // ---------------------------------------------------------------- output projection
-// grid (ceil(R / 64), H), 256 threads. The latent dimension is taken in two halves of 256; per
-// half LDS holds W_UV[i][:, half] (128 rows of 512 B) and the 64 z rows' half (64 rows of 1 KB
-// float32, then split in place into bf16 hi / lo parts), both XOR-swizzled by 16-byte piece. Wave w computes outputs v = 32w .. 32w + 31 for
-// all 64 rows.
+// grid (ceil(R / 64), H, DN / NO), 256 threads: one row tile, one head and NO of its 128 outputs
+// per workgroup. NO = 128 normally; NO = 64 when there is a single row tile, so that 64 rows still
+// give 256 workgroups (with more tiles the halves would each load and split the z rows again). The
+// latent dimension is taken in two halves of 256; per half LDS holds W_UV[i][the NO outputs, half
+// of the latent] (NO rows of 512 B) and the 64 z rows' half (64 rows of 1 KB float32, then split in
+// place into bf16 hi / lo parts), both XOR-swizzled by 16-byte piece. The NO / 32 output blocks of
+// 32 are dealt to the waves first, then the two row blocks of 32: wave w computes outputs
+// 32 (w % (NO / 32)) .. +31 for RBW = NO / 64 row blocks from (w / (NO / 32)) RBW on. Every output
+// sums the same products in the same order whatever NO.
 constexpr int KH = DC / 2;                    // latent columns per half
 constexpr int WV_ROW = KH * 2;                // 512 B
 constexpr int Z_ROW = KH * 4;                 // 1024 B
-constexpr int Z_OFF = DN * WV_ROW;            // 65536
-constexpr int OUTP_LDS = Z_OFF + BM * Z_ROW;  // 131072
+template <int NO> constexpr int outp_z_off() { return NO * WV_ROW; }
+template <int NO> constexpr int outp_lds() { return outp_z_off<NO>() + BM * Z_ROW; }   // 128 KB or 96 KB
 
+template <int NO>
 __global__ void __launch_bounds__(256) out_proj_gemm(const float* __restrict__ z, const bf16* __restrict__ w_uv,
                                                      bf16* __restrict__ o, int n_rows) {
+  static_assert(NO == 64 || NO == 128, "half or all of the outputs");
+  constexpr int Z_OFF = outp_z_off<NO>();
+  constexpr int WO = NO / 32;    // waves across the outputs
+  constexpr int RBW = NO / 64;   // row blocks of 32 per wave
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const int i = blockIdx.y, r0 = blockIdx.x * BM;
+  const int i = blockIdx.y, r0 = blockIdx.x * BM, v0 = blockIdx.z * NO;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int g = lane >> 5, l32 = lane & 31;
   const int nr = min(BM, n_rows - r0);
   const uint32_t lds_w = lds_addr(smem), lds_z = lds_addr(smem + Z_OFF);
 
-  f32x16e acc[2] = {f32x16e{}, f32x16e{}};
+  f32x16e acc[RBW];
+#pragma unroll
+  for (int k = 0; k < RBW; ++k) acc[k] = f32x16e{};
+  const int ob = w % WO, rb0 = (w / WO) * RBW;
   for (int kh = 0; kh < 2; ++kh) {
     if (kh > 0) __syncthreads();   // the previous half is no longer read
     // W_UV rows: two 512 B rows per instruction, lane l -> row 2q + l/32, slot (l%32) holds
     // piece (l%32) ^ (row & 15)
 #pragma unroll 4
-    for (int q = w; q < DN / 2; q += 4) {
+    for (int q = w; q < NO / 2; q += 4) {
       const int row = 2 * q + (lane >> 5), slot = lane & 31;
-      const bf16* src = w_uv + ((size_t)i * DN + row) * DC + kh * KH + 8 * (slot ^ (row & 15));
+      const bf16* src = w_uv + ((size_t)i * DN + v0 + row) * DC + kh * KH + 8 * (slot ^ (row & 15));
       dma16(src, __builtin_amdgcn_readfirstlane(lds_w + q * 1024));
     }
     // z rows: one 1 KB row half per instruction, slot l holds piece l ^ (row & 15); rows past
@@ -239,15 +252,15 @@ __global__ void __launch_bounds__(256) out_proj_gemm(const float* __restrict__ z
     }
     __syncthreads();
 
-    const int v = 32 * w + l32;
+    const int v = 32 * ob + l32;   // local W_UV row (output v0 + v)
 #pragma unroll 2
     for (int s = 0; s < KH / 16; ++s) {
-      // B: W_UV[i][v][16s + 8g .. +7] = logical piece 2s + g of row v
+      // B: W_UV[i][v0 + v][16s + 8g .. +7] = logical piece 2s + g of local row v
       const bf16x8e b = *reinterpret_cast<const bf16x8e*>(smem + v * WV_ROW + 16 * ((2 * s + g) ^ (v & 15)));
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
+      for (int k = 0; k < RBW; ++k) {
         // A: z[m][16s + 8g .. +7] = logical float pieces 2(2s + g) and 2(2s + g) + 1 of row m
-        const int m = 32 * rb + l32;
+        const int m = 32 * (rb0 + k) + l32;
         const int p0 = 2 * (2 * s + g);
         const unsigned char* q0 = smem + Z_OFF + m * Z_ROW + 16 * (p0 ^ (m & 15));
         const unsigned char* q1 = smem + Z_OFF + m * Z_ROW + 16 * ((p0 + 1) ^ (m & 15));
@@ -255,20 +268,20 @@ __global__ void __launch_bounds__(256) out_proj_gemm(const float* __restrict__ z
         const i32x2 h0 = *reinterpret_cast<const i32x2*>(q0), h1 = *reinterpret_cast<const i32x2*>(q1);
         const i32x2 l0 = *reinterpret_cast<const i32x2*>(q0 + 8), l1 = *reinterpret_cast<const i32x2*>(q1 + 8);
         const i32x2 hh[2] = {h0, h1}, ll[2] = {l0, l1};
-        acc[rb] = mfma(__builtin_bit_cast(bf16x8e, hh), b, acc[rb]);
-        acc[rb] = mfma(__builtin_bit_cast(bf16x8e, ll), b, acc[rb]);
+        acc[k] = mfma(__builtin_bit_cast(bf16x8e, hh), b, acc[k]);
+        acc[k] = mfma(__builtin_bit_cast(bf16x8e, ll), b, acc[k]);
       }
     }
   }
-  // D layout: lane holds output v = 32w + l32 of rows 32rb + 8j + 4g + e
+  // D layout: lane holds output v0 + 32 ob + l32 of rows 32 (rb0 + k) + 8j + 4g + e
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+  for (int k = 0; k < RBW; ++k)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int row = 32 * rb + 8 * j + 4 * g + e;
-        if (row < nr) o[((size_t)(r0 + row) * H + i) * DN + 32 * w + l32] = (bf16)acc[rb][4 * j + e];
+        const int row = 32 * (rb0 + k) + 8 * j + 4 * g + e;
+        if (row < nr) o[((size_t)(r0 + row) * H + i) * DN + v0 + 32 * ob + l32] = (bf16)acc[k][4 * j + e];
       }
 }
 
@@ -295,14 +308,22 @@ hipError_t launch_out_proj_gemm(const LayerDims& L, int n_rows, const float* z, 
   (void)L;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm::out_proj_gemm, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       gemm::OUTP_LDS);
+    hipError_t e = hipFuncSetAttribute((const void*)gemm::out_proj_gemm<128>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       gemm::outp_lds<128>());
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void*)gemm::out_proj_gemm<64>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              gemm::outp_lds<64>());
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const dim3 grid((n_rows + gemm::BM - 1) / gemm::BM, gemm::H);   // row tiles of one head run together
-  hipLaunchKernelGGL(gemm::out_proj_gemm, grid, dim3(256), gemm::OUTP_LDS, stream, z, (const bf16*)w_uv, (bf16*)o,
-                     n_rows);
+  // row tiles (and output halves) of one head run together
+  const int tiles = (n_rows + gemm::BM - 1) / gemm::BM;
+  if (tiles == 1)
+    hipLaunchKernelGGL(gemm::out_proj_gemm<64>, dim3(1, gemm::H, 2), dim3(256), gemm::outp_lds<64>(), stream, z,
+                       (const bf16*)w_uv, (bf16*)o, n_rows);
+  else
+    hipLaunchKernelGGL(gemm::out_proj_gemm<128>, dim3(tiles, gemm::H), dim3(256), gemm::outp_lds<128>(), stream, z,
+                       (const bf16*)w_uv, (bf16*)o, n_rows);
   return hipGetLastError();
 }
 
