@@ -310,6 +310,9 @@ size_t mla_prefill_explicit_workspace_size(const mla_config* cfg, int32_t batch,
  *  workspace  >= mla_prefill_explicit_workspace_size(...) bytes, device; no initialisation
  *  o        [batch, n_q, H, 128] bf16, device, written
  *  lse      float32 [batch, n_q, H], device, written; may be NULL
+ *  d_model, w_o, u: optional layer output u = W_O concat_i(o_i), exactly as for mla_out_proj
+ *           (d_model = 0 with w_o = u = NULL skips it; w_o [d_model, H * 128], u [batch * n_q, d_model]
+ *           bf16, 16-byte aligned)
  * Covers bf16 with d_nope = d_v = 128, d_rope = 64, d_latent = 512 (any head count); anything
  * else returns MLA_ERR_UNSUPPORTED. All tensors must be 16-byte aligned. Keys and values are
  * rounded once to bf16 when rebuilt; scores, softmax and sums accumulate in float32.
@@ -318,7 +321,18 @@ mla_status mla_prefill_explicit(const mla_config* cfg, int32_t batch, int32_t n_
                                 const void* q_rope, const void* cache, const int64_t* seq_off,
                                 const int32_t* seq_len, int32_t max_seq_len, const void* w_uk,
                                 const void* w_uv, void* workspace, size_t workspace_bytes, void* o,
-                                float* lse, void* stream);
+                                float* lse, int32_t d_model, const void* w_o, void* u, void* stream);
+
+/*
+ * mla_prefill_prefers_explicit — which of the two equivalent forms to run for n_q new query rows
+ * per sequence ("Decoupled RoPE · MLA Part 2", §5 closing remark: the absorbed form is the decode
+ * form, the explicit one pays off when many query rows share each rebuilt key and value; "从零理解
+ * MLA", section "实际配置"). Returns 1 when mla_prefill_explicit covers the shape and n_q is at
+ * least the row count from which it measured faster than mla_absorb_q + mla_decode_attn +
+ * mla_out_proj on this library's kernels (128 new rows per sequence); 0 otherwise, including for
+ * invalid arguments. Host-only: launches nothing.
+ */
+int32_t mla_prefill_prefers_explicit(const mla_config* cfg, int32_t batch, int32_t n_q, int32_t max_seq_len);
 
 /*
  * mla_decode_advance — cache growth between decode steps ("从零理解 MLA", the token-by-token

@@ -22,5 +22,6 @@ from .ops import (  # noqa: F401
     mla_decode_advance,
     mla_prefill_explicit_workspace_size,
     mla_prefill_explicit,
+    mla_prefill_prefers_explicit,
     version,
 )

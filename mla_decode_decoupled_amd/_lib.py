@@ -68,7 +68,8 @@ SIGNATURES = {
     "mla_decode_advance": (ctypes.c_int, [_I32, _I32, _VP, _VP, _I32, _VP, _VP]),
     "mla_prefill_explicit_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(MlaConfig), _I32, _I32, _I32]),
     "mla_prefill_explicit": (ctypes.c_int, [ctypes.POINTER(MlaConfig), _I32, _I32, _VP, _VP, _VP, _VP, _VP, _I32,
-                                            _VP, _VP, _VP, ctypes.c_size_t, _VP, _VP, _VP]),
+                                            _VP, _VP, _VP, ctypes.c_size_t, _VP, _VP, _I32, _VP, _VP, _VP]),
+    "mla_prefill_prefers_explicit": (_I32, [ctypes.POINTER(MlaConfig), _I32, _I32, _I32]),
 }
 
 

@@ -15,6 +15,9 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_PATH = os.path.join(PKG_DIR, "libmla.so")
 SOURCES = ["api.hip", "generic.hip", "decode_fast.hip", "proj_fast.hip", "proj_gemm.hip", "linear.hip", "prefill_explicit.hip"]
+# the ceiling microbenchmarks (MFMA issue, HBM streaming) are a library of their own
+CEIL_LIB_PATH = os.path.join(PKG_DIR, "libmla_ceilings.so")
+CEIL_SOURCES = ["ceilings.hip"]
 
 # Packed-FP32 instructions (v_pk_*_f32) are switched off for every device pass: the compiler
 # otherwise forms them from plain float code, and the kernels are validated without them.
@@ -38,8 +41,14 @@ def hipcc() -> str:
 
 
 def build(debug: bool = False, verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
-    tmp = LIB_PATH + ".tmp"
+    _build_one(SOURCES, LIB_PATH, debug, verbose)
+    _build_one(CEIL_SOURCES, CEIL_LIB_PATH, debug, verbose)
+    return LIB_PATH
+
+
+def _build_one(sources, lib_path: str, debug: bool, verbose: bool) -> str:
+    srcs = [os.path.join(CSRC, s) for s in sources]
+    tmp = lib_path + ".tmp"
     cmd = [hipcc(), *HIP_FLAGS, "-I", os.path.join(PKG_DIR, os.pardir, "include"), "-o", tmp, *srcs]
     if debug:
         cmd = [c for c in cmd if c != "-O3"] + ["-O1", "-g"]
@@ -53,8 +62,8 @@ def build(debug: bool = False, verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if err.strip() and verbose:
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":

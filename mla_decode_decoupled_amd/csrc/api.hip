@@ -448,11 +448,16 @@ size_t mla_prefill_explicit_workspace_size(const mla_config* cfg, int32_t batch,
 mla_status mla_prefill_explicit(const mla_config* cfg, int32_t batch, int32_t n_q, const void* q_nope,
                                 const void* q_rope, const void* cache, const int64_t* seq_off, const int32_t* seq_len,
                                 int32_t max_seq_len, const void* w_uk, const void* w_uv, void* workspace,
-                                size_t workspace_bytes, void* o, float* lse, void* stream) {
+                                size_t workspace_bytes, void* o, float* lse, int32_t d_model, const void* w_o, void* u,
+                                void* stream) {
   mla::LayerDims L;
   mla_status s = check_cfg(cfg, &L);
   if (s != MLA_OK) return s;
   if (batch < 0 || n_q < 0) return fail(MLA_ERR_INVALID_ARG, "batch and n_q must be >= 0");
+  if (d_model < 0) return fail(MLA_ERR_INVALID_ARG, "d_model must be >= 0, got %d", d_model);
+  const bool with_w_o = d_model > 0;
+  if (with_w_o != (w_o != nullptr) || with_w_o != (u != nullptr))
+    return fail(MLA_ERR_INVALID_ARG, "W_O projection: pass d_model > 0 with w_o and u, or d_model = 0 with both NULL");
   if (batch == 0 || n_q == 0) return ok();
   if (max_seq_len < n_q) return fail(MLA_ERR_INVALID_ARG, "max_seq_len (%d) must be >= n_q (%d)", max_seq_len, n_q);
   if (cfg->dtype != MLA_BF16 || !mla::prefill_explicit_supported(L))
@@ -466,15 +471,29 @@ mla_status mla_prefill_explicit(const mla_config* cfg, int32_t batch, int32_t n_
   if (!q_nope || !q_rope || !cache || !seq_off || !seq_len || !w_uk || !w_uv || !o)
     return fail(MLA_ERR_INVALID_ARG, "NULL pointer argument");
   if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(cache) || !aligned16(w_uk) || !aligned16(w_uv) ||
-      !aligned16(o) || !aligned16(workspace))
+      !aligned16(o) || !aligned16(workspace) || (with_w_o && (!aligned16(w_o) || !aligned16(u))))
     return fail(MLA_ERR_INVALID_ARG, "tensors of the explicit prefill must be 16-byte aligned");
+  if (with_w_o && (int64_t)L.n_heads * L.d_v > INT32_MAX / 8) return fail(MLA_ERR_UNSUPPORTED, "H * d_v too large");
   const size_t need = mla::prefill_explicit_workspace_bytes(L, batch, max_seq_len);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(MLA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu%s", need, workspace_bytes,
                 workspace ? "" : " (NULL)");
+  hipStream_t st = (hipStream_t)stream;
   hipError_t e = mla::launch_prefill_explicit(L, batch, n_q, q_nope, q_rope, cache, seq_off, seq_len, max_seq_len, w_uk,
-                                              w_uv, workspace, o, lse, (hipStream_t)stream);
-  return from_hip(e, "mla_prefill_explicit launch");
+                                              w_uv, workspace, o, lse, st);
+  if (e != hipSuccess || !with_w_o) return from_hip(e, "mla_prefill_explicit launch");
+  // u = W_O concat_i(o_i), from the o just written (same stream), as mla_out_proj does
+  const int K = L.n_heads * L.d_v;
+  e = mla::launch_linear<__bf16>(o, K, batch * n_q, K, w_o, d_model, u, d_model, st);
+  return from_hip(e, "mla_prefill_explicit W_O launch");
+}
+
+int32_t mla_prefill_prefers_explicit(const mla_config* cfg, int32_t batch, int32_t n_q, int32_t max_seq_len) {
+  mla::LayerDims L;
+  if (cfg == nullptr || check_cfg(cfg, &L) != MLA_OK) return 0;
+  if (batch <= 0 || n_q <= 0 || max_seq_len < n_q) return 0;
+  if (cfg->dtype != MLA_BF16 || !mla::prefill_explicit_supported(L)) return 0;
+  return n_q >= mla::kExplicitMinRows ? 1 : 0;
 }
 
 mla_status mla_decode_advance(int32_t batch, int32_t n_new, int32_t* len_before, int32_t* seq_len, int32_t n_rows,

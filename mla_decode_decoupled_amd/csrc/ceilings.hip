@@ -1,0 +1,220 @@
+// Ceiling microbenchmarks for MI355X (gfx950): what the chip sustains for the two resources the
+// latent attention is bound by, measured with the same instructions the attention kernels use.
+//   * mfma:   chip-wide v_mfma_f32_32x32x16_bf16 issue with 1 or 2 waves per SIMD, NACC independent
+//             accumulators per wave, operands from registers (random bf16 values: the operand data
+//             changes the power draw and with it the clock). Every wave records the shader clock
+//             counter (s_memtime) and the constant 100 MHz counter (s_memrealtime) around its loop,
+//             so the host can tell the issue interval in cycles from the clock the chip ran at.
+//   * stream: read-only HBM streaming, (a) 16-byte vector loads into registers with U loads in
+//             flight per lane, (b) the attention kernel's tile ring: 32-key tiles of 1152-byte rows
+//             (36 KB) moved by 16-byte global->LDS loads into four LDS buffers, `lookahead` tiles in
+//             flight, one workgroup barrier per tile, one workgroup per CU.
+// Built into libmla_ceilings.so, separate from the attention library.
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/mla_ceilings.h"
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void stamp(unsigned long long* stamps, int slot, unsigned long long t,
+                                      unsigned long long r) {
+  stamps[2 * slot] = t;
+  stamps[2 * slot + 1] = r;
+}
+
+// One workgroup per CU (the host reserves enough LDS to keep a second one out); 64 * WAVES threads.
+template <int WAVES, int NACC>
+__global__ void __launch_bounds__(64 * WAVES) mfma_peak(int iters, const uint32_t* __restrict__ operands,
+                                                         unsigned long long* __restrict__ stamps,
+                                                         float* __restrict__ sink) {
+  extern __shared__ unsigned char reserve[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int gw = blockIdx.x * WAVES + wave;
+  uint32_t ua[4], ub[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ua[i] = operands[(gw * 64 + lane) * 8 + i];
+    ub[i] = operands[(gw * 64 + lane) * 8 + 4 + i];
+  }
+  const bf16x8 a = __builtin_bit_cast(bf16x8, ua), b = __builtin_bit_cast(bf16x8, ub);
+  f32x16 acc[NACC];
+#pragma unroll
+  for (int k = 0; k < NACC; ++k) acc[k] = f32x16{};
+  if (threadIdx.x == 0) reserve[0] = 0;
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int k = 0; k < NACC; ++k) acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[k], 0, 0, 0);
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int k = 0; k < NACC; ++k)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s += acc[k][e];
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+  if (lane == 0) {
+    stamp(stamps, 2 * gw, t0, r0);
+    stamp(stamps, 2 * gw + 1, t1, r1);
+  }
+  sink[gw * 64 + lane] = s;
+}
+
+// (a) vector-load streaming: workgroup g reads the contiguous span [g * per_wg, (g + 1) * per_wg)
+// of 16-byte words, U loads in flight per lane, non-temporal.
+template <int U>
+__global__ void __launch_bounds__(256) stream_vec(const u32x4* __restrict__ src, size_t per_wg,
+                                                  unsigned int* __restrict__ sink) {
+  const u32x4* p = src + (size_t)blockIdx.x * per_wg;
+  u32x4 x = {0, 0, 0, 0};
+  for (size_t i = threadIdx.x; i < per_wg; i += 256 * U) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t j = i + (size_t)u * 256;
+      v[u] = j < per_wg ? __builtin_nontemporal_load(p + j) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) x ^= v[u];
+  }
+  const unsigned int r = x[0] ^ x[1] ^ x[2] ^ x[3];
+  if (r == 0x9e3779b9u) sink[blockIdx.x] = r;   // practically never: keeps the loads alive
+}
+
+// (b) the attention kernel's tile ring: workgroup g streams tiles g * tiles .. (g + 1) * tiles - 1
+// (36 KB each) into four LDS buffers with nine 1 KB global->LDS loads per wave and tile, keeping
+// LA tiles in flight; per tile it waits for the oldest, passes one barrier and reads one dword
+// back, as the attention loop's barrier-per-tile does. The loads are issued from inline asm and the
+// barrier waits only for LDS traffic, as in the attention kernels: the compiler would otherwise
+// wait for every global->LDS load in flight at each barrier.
+constexpr int TILE_BYTES = 32 * 1152;
+constexpr int NBUF = 4;
+
+__device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gaddr), "s"(lds_base)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <int LA>
+__global__ void __launch_bounds__(256) stream_lds(const unsigned char* __restrict__ src, int tiles,
+                                                  unsigned int* __restrict__ sink,
+                                                  unsigned long long* __restrict__ stamps) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const unsigned char* base = src + (size_t)blockIdx.x * tiles * TILE_BYTES + (w * 9 * 64 + lane) * 16;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+  auto issue = [&](int t) {
+    const unsigned char* g = base + (size_t)t * TILE_BYTES;
+    const uint32_t d = __builtin_amdgcn_readfirstlane(lds0 + (t % NBUF) * TILE_BYTES + w * 9 * 1024);
+#pragma unroll
+    for (int it = 0; it < 9; ++it) dma16(g + it * 1024, d + it * 1024);
+  };
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+  for (int t = 0; t < LA && t < tiles; ++t) issue(t);
+  unsigned int x = 0;
+  for (int t = 0; t < tiles; ++t) {
+    // the tile t landed: at most (tiles issued after it) x 9 loads of this wave outstanding
+    const int after = (t + LA - 1 < tiles ? LA - 1 : tiles - 1 - t);
+    if (after >= 2)
+      __builtin_amdgcn_s_waitcnt((18 & 15) | ((18 >> 4) << 14) | (7 << 4) | (15 << 8));
+    else if (after == 1)
+      __builtin_amdgcn_s_waitcnt(9 | (7 << 4) | (15 << 8));
+    else
+      __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+    lds_barrier();   // every wave's share of tile t is in
+    x ^= *reinterpret_cast<const unsigned int*>(lds + (t % NBUF) * TILE_BYTES + threadIdx.x * 16);
+    lds_barrier();   // every wave read buffer t % NBUF before it is refilled
+    if (t + LA < tiles) issue(t + LA);
+  }
+  __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+  if (threadIdx.x == 0) {
+    stamp(stamps, 2 * blockIdx.x, t0, r0);
+    stamp(stamps, 2 * blockIdx.x + 1, t1, r1);
+  }
+  if (x == 0x9e3779b9u) sink[blockIdx.x] = x;
+}
+
+template <int WAVES, int NACC>
+hipError_t launch_mfma(int n_wg, int iters, const uint32_t* ops, unsigned long long* stamps, float* sink,
+                       hipStream_t st) {
+  constexpr int kReserve = 96 * 1024;   // more than half of the 160 KB: one workgroup per CU
+  hipError_t e = hipFuncSetAttribute((const void*)mfma_peak<WAVES, NACC>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, kReserve);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((mfma_peak<WAVES, NACC>), dim3(n_wg), dim3(64 * WAVES), kReserve, st, iters, ops, stamps, sink);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_ceiling_mfma(int waves_per_simd, int n_acc, int n_workgroups, int iters, const void* operands,
+                     unsigned long long* stamps, float* sink, void* stream) {
+  if (n_workgroups < 1 || iters < 1 || !operands || !stamps || !sink) return 1;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
+  const uint32_t* ops = (const uint32_t*)operands;
+  if (waves_per_simd == 1 && n_acc == 4) e = launch_mfma<4, 4>(n_workgroups, iters, ops, stamps, sink, st);
+  else if (waves_per_simd == 1 && n_acc == 8) e = launch_mfma<4, 8>(n_workgroups, iters, ops, stamps, sink, st);
+  else if (waves_per_simd == 1 && n_acc == 1) e = launch_mfma<4, 1>(n_workgroups, iters, ops, stamps, sink, st);
+  else if (waves_per_simd == 2 && n_acc == 4) e = launch_mfma<8, 4>(n_workgroups, iters, ops, stamps, sink, st);
+  else if (waves_per_simd == 2 && n_acc == 8) e = launch_mfma<8, 8>(n_workgroups, iters, ops, stamps, sink, st);
+  else return 2;
+  return e == hipSuccess ? 0 : 4;
+}
+
+int mla_ceiling_stream(int mode, int depth, int n_workgroups, const void* src, size_t bytes_per_workgroup,
+                       unsigned int* sink, unsigned long long* stamps, void* stream) {
+  if (n_workgroups < 1 || !src || !sink || bytes_per_workgroup == 0) return 1;
+  hipStream_t st = (hipStream_t)stream;
+  if (mode == 0) {
+    if (bytes_per_workgroup % 16 != 0) return 1;
+    const size_t per = bytes_per_workgroup / 16;
+    switch (depth) {
+      case 4: hipLaunchKernelGGL(stream_vec<4>, dim3(n_workgroups), dim3(256), 0, st, (const u32x4*)src, per, sink); break;
+      case 8: hipLaunchKernelGGL(stream_vec<8>, dim3(n_workgroups), dim3(256), 0, st, (const u32x4*)src, per, sink); break;
+      case 16: hipLaunchKernelGGL(stream_vec<16>, dim3(n_workgroups), dim3(256), 0, st, (const u32x4*)src, per, sink); break;
+      default: return 2;
+    }
+    return hipGetLastError() == hipSuccess ? 0 : 4;
+  }
+  if (mode == 1) {
+    if (!stamps || bytes_per_workgroup % TILE_BYTES != 0) return 1;
+    const int tiles = (int)(bytes_per_workgroup / TILE_BYTES);
+    const int lds = NBUF * TILE_BYTES;
+    hipError_t e = hipSuccess;
+    switch (depth) {
+      case 1:
+        e = hipFuncSetAttribute((const void*)stream_lds<1>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e == hipSuccess)
+          hipLaunchKernelGGL(stream_lds<1>, dim3(n_workgroups), dim3(256), lds, st, (const unsigned char*)src, tiles, sink, stamps);
+        break;
+      case 2:
+        e = hipFuncSetAttribute((const void*)stream_lds<2>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e == hipSuccess)
+          hipLaunchKernelGGL(stream_lds<2>, dim3(n_workgroups), dim3(256), lds, st, (const unsigned char*)src, tiles, sink, stamps);
+        break;
+      case 3:
+        e = hipFuncSetAttribute((const void*)stream_lds<3>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e == hipSuccess)
+          hipLaunchKernelGGL(stream_lds<3>, dim3(n_workgroups), dim3(256), lds, st, (const unsigned char*)src, tiles, sink, stamps);
+        break;
+      default: return 2;
+    }
+    if (e != hipSuccess) return 4;
+    return hipGetLastError() == hipSuccess ? 0 : 4;
+  }
+  return 2;
+}
+
+}  // extern "C"

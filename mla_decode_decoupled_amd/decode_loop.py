@@ -5,10 +5,15 @@ absorbed form ("从零理解 MLA", the decode loop after the decoupled-RoPE code
 the new token's latent and rotated position key to the cache, then attends over the grown
 cache): per layer, mla_project_inputs (mla_project_kv_append and mla_project_q in one call) ->
 mla_absorb_q -> mla_decode_attn -> mla_out_proj (with W_O), and the layer's output u is the next
-layer's input (the residual
-stream and the feed-forward blocks of a full model are not part of this stack). After the last
-layer, mla_decode_advance moves every position on by the tokens just appended, so one recorded
-decode step — a HIP graph captured through torch — can be replayed for every following token.
+layer's input (the residual stream and the feed-forward blocks of a full model are not part of
+this stack). A step of many new tokens per sequence (a prefill chunk) takes the explicit form
+instead, mla_project_inputs -> mla_prefill_explicit (with W_O), whenever the library reports it as
+the faster one for that row count (mla_prefill_prefers_explicit; "Decoupled RoPE · MLA Part 2", §5
+closing remark: absorption is the decode form). After the last layer, mla_decode_advance moves
+every position on by the tokens just appended, so one recorded decode step — a HIP graph captured
+through torch — can be replayed for every following token. The attention's split plan is chosen
+from the cache capacity (the grid bound every step shares), not from the current length, so one
+captured step serves every following token.
 
 This module only allocates buffers, sets positions and enqueues library calls; every step of the
 computation runs in libmla's kernels.
@@ -46,8 +51,14 @@ class _StepBuffers:
         self.h_in = torch.empty((B, n_new, stack.d_model), dtype=dt, device=dev)
         pw = ops.mla_project_inputs_workspace_size(cfg, R, stack.d_model, stack.d_q)
         self.ws_proj = torch.empty(max(pw, 256), dtype=torch.uint8, device=dev)
-        aw = ops.mla_decode_attn_workspace_size(cfg, B, n_new, stack.capacity, stack.n_splits)
-        self.ws_attn = torch.empty(max(aw, 256), dtype=torch.uint8, device=dev)
+        # the explicit form for long chunks when the library prefers it, else the absorbed calls
+        self.explicit = ops.mla_prefill_prefers_explicit(cfg, B, n_new, stack.capacity)
+        if self.explicit:
+            xw = ops.mla_prefill_explicit_workspace_size(cfg, B, n_new, stack.capacity)
+            self.ws_attn = torch.empty(max(xw, 256), dtype=torch.uint8, device=dev)
+        else:
+            aw = ops.mla_decode_attn_workspace_size(cfg, B, n_new, stack.capacity, stack.n_splits)
+            self.ws_attn = torch.empty(max(aw, 256), dtype=torch.uint8, device=dev)
 
     def set_positions(self, length: int) -> None:
         """Positions of a step that appends n_new tokens after `length` cached ones."""
@@ -88,6 +99,7 @@ class DecodeStack:
         self.seq_off = torch.arange(self.batch, dtype=torch.int64, device=self.device) * self.capacity
         self.length = 0          # tokens cached per sequence
         self._bufs: Dict[int, _StepBuffers] = {}
+        self.last_prefill_path: Optional[str] = None   # "explicit" or "absorbed": the form of the last forward()
 
     def buffers(self, n_new: int) -> _StepBuffers:
         if n_new not in self._bufs:
@@ -100,14 +112,22 @@ class DecodeStack:
         cfg, B, n = self.cfg, self.batch, b.n_new
         R = B * n
         x = b.h_in
+        H = cfg.n_heads
         for l, w in enumerate(self.layers):
             ops.mla_project_inputs(cfg, x, w["w_dkv"], w["w_kr"], self.caches[l], self.seq_off, b.len_before,
                                    w["w_uq"], w["w_qr"], b.q_nope, b.q_rope, w_dq=w.get("w_dq"),
                                    kv_norm_w=w.get("kv_norm_w"), kv_norm_eps=self.kv_norm_eps, workspace=b.ws_proj)
+            u = b.u[l % 2]
+            if b.explicit:
+                ops.mla_prefill_explicit(cfg, b.q_nope.view(B, n, H, cfg.d_nope), b.q_rope.view(B, n, H, cfg.d_rope),
+                                         self.caches[l], self.seq_off, b.seq_len, self.capacity, w["w_uk"], w["w_uv"],
+                                         b.o.view(B, n, H, cfg.d_v), b.lse, workspace=b.ws_attn, w_o=w["w_o"],
+                                         u=u.view(R, self.d_model))
+                x = u
+                continue
             ops.mla_absorb_q(cfg, b.q_nope, b.q_rope, b.q_pos, w["w_uk"], b.q_packed.view(R, cfg.n_heads, -1))
             ops.mla_decode_attn(cfg, b.q_packed, self.caches[l], self.seq_off, b.seq_len, self.capacity, b.z, b.lse,
                                 n_splits=self.n_splits, workspace=b.ws_attn)
-            u = b.u[l % 2]
             ops.mla_out_proj(cfg, b.z.view(R, cfg.n_heads, cfg.d_latent), w["w_uv"], b.o, w_o=w["w_o"],
                              u=u.view(R, self.d_model))
             x = u
@@ -127,6 +147,7 @@ class DecodeStack:
         b.set_positions(self.length)
         b.h_in.copy_(h)
         out = self._enqueue(b)
+        self.last_prefill_path = "explicit" if b.explicit else "absorbed"
         self.length += n
         return out
 

@@ -308,9 +308,11 @@ def mla_prefill_explicit_workspace_size(cfg: MlaConfig, batch: int, n_q: int, ma
 def mla_prefill_explicit(cfg: MlaConfig, q_nope: torch.Tensor, q_rope: torch.Tensor, cache: torch.Tensor,
                          seq_off: torch.Tensor, seq_len: torch.Tensor, max_seq_len: int, w_uk: torch.Tensor,
                          w_uv: torch.Tensor, o: torch.Tensor, lse: Optional[torch.Tensor] = None,
-                         workspace: Optional[torch.Tensor] = None) -> None:
+                         workspace: Optional[torch.Tensor] = None, w_o: Optional[torch.Tensor] = None,
+                         u: Optional[torch.Tensor] = None) -> None:
     """Non-absorbed attention of q [batch, n_q, H, .] over the cache; writes the heads' outputs
-    o [batch, n_q, H, d_v] (and lse)."""
+    o [batch, n_q, H, d_v] (and lse); with w_o [d_model, H * d_v] and u [batch * n_q, d_model] also
+    u = W_O concat_i(o_i)."""
     dt = storage_dtype(cfg)
     H = cfg.n_heads
     if q_nope.dim() != 4:
@@ -327,10 +329,25 @@ def mla_prefill_explicit(cfg: MlaConfig, q_nope: torch.Tensor, q_rope: torch.Ten
     _need(o, "o", dt, (B, n_q, H, cfg.d_v), dev)
     if lse is not None:
         _need(lse, "lse", torch.float32, (B, n_q, H), dev)
+    if (w_o is None) != (u is None):
+        raise ValueError("pass w_o and u together")
+    d_model = 0
+    if w_o is not None:
+        if w_o.dim() != 2:
+            raise ValueError("w_o must be [d_model, n_heads * d_v]")
+        d_model = w_o.shape[0]
+        _need(w_o, "w_o", dt, (d_model, H * cfg.d_v), dev)
+        _need(u, "u", dt, (B * n_q, d_model), dev)
     wp, wb = _ws(workspace, dev)
     check(lib.mla_prefill_explicit(cfg, B, n_q, _ptr(q_nope), _ptr(q_rope), _ptr(cache), _ptr(seq_off), _ptr(seq_len),
-                                   int(max_seq_len), _ptr(w_uk), _ptr(w_uv), wp, wb, _ptr(o), _ptr(lse), _stream(o)),
+                                   int(max_seq_len), _ptr(w_uk), _ptr(w_uv), wp, wb, _ptr(o), _ptr(lse), d_model,
+                                   _ptr(w_o), _ptr(u), _stream(o)),
           "mla_prefill_explicit")
+
+
+def mla_prefill_prefers_explicit(cfg: MlaConfig, batch: int, n_q: int, max_seq_len: int) -> bool:
+    """True when the library would run n_q new query rows per sequence faster in the explicit form."""
+    return bool(lib.mla_prefill_prefers_explicit(cfg, int(batch), int(n_q), int(max_seq_len)))
 
 
 def mla_decode_advance(n_new: int, len_before: Optional[torch.Tensor] = None, seq_len: Optional[torch.Tensor] = None,

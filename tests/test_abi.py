@@ -17,7 +17,7 @@ FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails va
 
 def _declared():
     text = open(HEADER).read()
-    return set(re.findall(r"^\s*(?:const char\*|mla_status|size_t)\s+(mla_\w+)\s*\(", text, re.M))
+    return set(re.findall(r"^\s*(?:const char\*|mla_status|size_t|int32_t)\s+(mla_\w+)\s*\(", text, re.M))
 
 
 def test_header_symbols_exported():
@@ -182,23 +182,43 @@ def test_explicit_prefill_arguments():
     assert ws == 2 * 2 * 4096 * 128 * 128 * 2
     assert lib.mla_prefill_explicit_workspace_size(cfg(dtype=MLA_F32), 2, 2048, 4096) == 0   # not covered
     assert lib.mla_prefill_explicit_workspace_size(c, 2, 2048, 100) == 0                     # max_seq_len < n_q
-    args = lambda c, ws_ptr, ws_bytes, o=FAKE: (c, 2, 2048, FAKE, FAKE, FAKE, FAKE, FAKE, 4096, FAKE, FAKE,   # noqa: E731
-                                                 ws_ptr, ws_bytes, o, None, None)
+    args = lambda c, ws_ptr, ws_bytes, o=FAKE, d_model=0, w_o=None, u=None: (  # noqa: E731
+        c, 2, 2048, FAKE, FAKE, FAKE, FAKE, FAKE, 4096, FAKE, FAKE, ws_ptr, ws_bytes, o, None, d_model, w_o, u, None)
     assert lib.mla_prefill_explicit(*args(cfg(dtype=MLA_F32), FAKE, ws)) == MLA_ERR_UNSUPPORTED
     assert lib.mla_prefill_explicit(*args(cfg(d_rope=32), FAKE, ws)) == MLA_ERR_UNSUPPORTED
     assert lib.mla_prefill_explicit(*args(c, None, ws)) == MLA_ERR_WORKSPACE
     assert lib.mla_prefill_explicit(*args(c, FAKE, ws - 1)) == MLA_ERR_WORKSPACE
     assert lib.mla_prefill_explicit(*args(c, FAKE, ws, o=None)) == MLA_ERR_INVALID_ARG
     assert lib.mla_prefill_explicit(c, 2, 2048, FAKE, FAKE, FAKE, FAKE, FAKE, 100, FAKE, FAKE, FAKE, ws, FAKE, None,
-                                    None) == MLA_ERR_INVALID_ARG                                  # max_seq_len < n_q
+                                    0, None, None, None) == MLA_ERR_INVALID_ARG                   # max_seq_len < n_q
+    # the optional W_O output: all three or none
+    assert lib.mla_prefill_explicit(*args(c, FAKE, ws, d_model=7168)) == MLA_ERR_INVALID_ARG
+    assert lib.mla_prefill_explicit(*args(c, FAKE, ws, w_o=FAKE, u=FAKE)) == MLA_ERR_INVALID_ARG
+    assert lib.mla_prefill_explicit(*args(c, FAKE, ws, d_model=-1)) == MLA_ERR_INVALID_ARG
+    assert lib.mla_prefill_explicit(*args(c, FAKE, ws, d_model=7168, w_o=FAKE, u=ctypes.c_void_p(0x1004))) \
+        == MLA_ERR_INVALID_ARG                                                                    # misaligned u
     # 2 H column tiles in the rebuild grid's second dimension
     assert lib.mla_prefill_explicit(*args(cfg(n_heads=40000), FAKE, ws)) == MLA_ERR_UNSUPPORTED
     assert b"32767" in lib.mla_last_error()
     odd = ctypes.c_void_p(0x1008)
     assert lib.mla_prefill_explicit(c, 2, 2048, odd, FAKE, FAKE, FAKE, FAKE, 4096, FAKE, FAKE, FAKE, ws, FAKE, None,
-                                    None) == MLA_ERR_INVALID_ARG                                  # misaligned
+                                    0, None, None, None) == MLA_ERR_INVALID_ARG                   # misaligned
     assert lib.mla_prefill_explicit(c, 0, 2048, None, None, None, None, None, 0, None, None, None, 0, None, None,
-                                    None) == MLA_OK
+                                    0, None, None, None) == MLA_OK
+
+
+def test_prefill_route():
+    """The explicit form is preferred from the measured row count on, only where it is compiled."""
+    c = cfg()
+    assert lib.mla_prefill_prefers_explicit(c, 2, 2048, 4096) == 1
+    assert lib.mla_prefill_prefers_explicit(c, 64, 1, 8192) == 0            # decode: absorbed
+    assert lib.mla_prefill_prefers_explicit(c, 2, 16, 4096) == 0
+    assert lib.mla_prefill_prefers_explicit(cfg(dtype=MLA_F32), 2, 2048, 4096) == 0
+    assert lib.mla_prefill_prefers_explicit(cfg(d_rope=32), 2, 2048, 4096) == 0
+    assert lib.mla_prefill_prefers_explicit(c, 2, 2048, 100) == 0           # max_seq_len < n_q
+    assert lib.mla_prefill_prefers_explicit(None, 2, 2048, 4096) == 0
+    switch = next(n for n in range(1, 4097) if lib.mla_prefill_prefers_explicit(c, 1, n, 4096))
+    assert all(lib.mla_prefill_prefers_explicit(c, 1, n, 4096) for n in (switch, switch + 1, 4096))
 
 
 def test_decode_step_arguments():
@@ -249,3 +269,26 @@ def test_project_inputs_arguments():
     assert call(ws_bytes=need - 1) == MLA_ERR_WORKSPACE
     assert call(batch=-1) == MLA_ERR_INVALID_ARG
     assert call(batch=0) == MLA_OK
+
+
+CEIL_HEADER = os.path.join(os.path.dirname(HEADER), "mla_ceilings.h")
+
+
+def test_ceilings_library_exports_and_validation():
+    """The ceiling microbenchmark library exports what its header declares and rejects bad
+    arguments before launching."""
+    from mla_decode_decoupled_amd import _ceilings as C
+    names = set(re.findall(r"^\s*int\s+(mla_\w+)\s*\(", open(CEIL_HEADER).read(), re.M))
+    assert names == {"mla_ceiling_mfma", "mla_ceiling_stream"}
+    for n in names:
+        assert hasattr(C.lib, n) and n in C.SIGNATURES
+    assert C.lib.mla_ceiling_mfma(1, 4, 0, 10, FAKE, FAKE, FAKE, None) == 1        # no workgroups
+    assert C.lib.mla_ceiling_mfma(1, 4, 256, 10, None, FAKE, FAKE, None) == 1
+    assert C.lib.mla_ceiling_mfma(3, 4, 256, 10, FAKE, FAKE, FAKE, None) == 2      # 3 waves per SIMD
+    assert C.lib.mla_ceiling_mfma(2, 1, 256, 10, FAKE, FAKE, FAKE, None) == 2
+    assert C.lib.mla_ceiling_stream(0, 8, 256, FAKE, 100, FAKE, None, None) == 1   # not a multiple of 16
+    assert C.lib.mla_ceiling_stream(0, 5, 256, FAKE, 1024, FAKE, None, None) == 2
+    assert C.lib.mla_ceiling_stream(1, 2, 256, FAKE, 36864, FAKE, None, None) == 1  # stamps needed
+    assert C.lib.mla_ceiling_stream(1, 2, 256, FAKE, 1000, FAKE, FAKE, None) == 1   # not whole tiles
+    assert C.lib.mla_ceiling_stream(1, 4, 256, FAKE, 36864, FAKE, FAKE, None) == 2
+    assert C.lib.mla_ceiling_stream(7, 2, 256, FAKE, 36864, FAKE, FAKE, None) == 2

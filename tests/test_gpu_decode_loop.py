@@ -111,3 +111,26 @@ def test_decode_loop_v3_shape_bf16():
         torch.cuda.synchronize()
         s = assert_close(got, ref[t:t + 1], "bf16", f"decode u token {t}")
     print("last step", s)
+
+
+def test_prefill_route_switch_point():
+    """The stack's multi-token step takes the explicit form from the library's switch row count on
+    and the absorbed calls just below it; both prefills, and one decode step after each, match the
+    oracle's full forward (DeepSeek-V3 shape, one layer, batch 1)."""
+    cfg = get_config(1)
+    lc = lib_config(cfg)
+    dt = mla.storage_dtype(lc)
+    switch = next(n for n in range(1, 4097) if mla.mla_prefill_prefers_explicit(lc, 1, n, 4096))
+    T = switch + 1
+    w = G.full_layer_inputs(cfg, T)
+    ref = O.full_layer(w["h"], w, n_heads=cfg.n_heads, scale=cfg.softmax_scale, base=cfg.rope_base)["u"]
+    hd = tdev(w["h"], dt)[None]
+    for P, path in ((switch, "explicit"), (switch - 1, "absorbed")):
+        print(f"prefill of {P} tokens, expecting the {path} form", flush=True)
+        stack = DecodeStack(lc, [_device_layer(w, dt)], batch=1, capacity=4096)
+        got = np32(stack.forward(hd[:, :P])[0])
+        assert stack.last_prefill_path == path
+        assert_close(got, ref[:P], "bf16", f"{path} prefill u ({P} tokens)")
+        got = np32(stack.forward(hd[:, P:P + 1])[0])
+        assert stack.last_prefill_path == "absorbed"
+        assert_close(got, ref[P:P + 1], "bf16", f"decode u token {P} after the {path} prefill")
