@@ -94,6 +94,8 @@ def parse():
                          "the FETCH_SIZE / WRITE_SIZE counters to bytes)")
     ap.add_argument("--mfma-peak", action="store_true",
                     help="measure chip-wide bf16 MFMA issue (1 and 2 waves per SIMD) and the clock it ran at")
+    ap.add_argument("--lds-ceiling", action="store_true",
+                    help="measure LDS read throughput per CU for ds_read_b128 and ds_read_b64_tr_b16")
     ap.add_argument("--stream-ceiling", action="store_true",
                     help="measure read-only HBM streaming: vector loads, and the attention kernel's LDS tile ring")
     return ap.parse_args()
@@ -426,6 +428,7 @@ def main():
         sys.exit(2)
     modes = {"copy_calibration": copy_calibration, "decode_loop": decode_loop, "merged_wo_check": merged_wo_check,
              "a16_check": a16_check, "mfma_peak": mfma_peak, "stream_ceiling": stream_ceiling,
+             "lds_ceiling": lds_ceiling,
              "attn_only": attn_only, "prefill_crossover": prefill_crossover}
     for name, fn in modes.items():
         if getattr(args, name):
@@ -517,7 +520,11 @@ def main():
         reps_ms = _graph_reps(stream, step, K, args.reps)
     ms_step = float(np.median(reps_ms))
 
-    # per-call pass: each call between events, GPU time only
+    # per-call pass: each call between events, GPU time only (the single calls' kernels are
+    # launched a few times first: a kernel's first launch also loads its code)
+    for i in range(max(2, args.warmup)):
+        single_calls(i)
+    torch.cuda.synchronize()
     ev = {k: [] for k in ("append", "absorb", "attn", "proj")}
     for i in range(K):
         torch.cuda._sleep(200_000)
@@ -702,7 +709,7 @@ def _clock_ghz(stamps):
     cyc = s[:, 1, 0] - s[:, 0, 0]
     rt = s[:, 1, 1] - s[:, 0, 1]
     ok = rt > 0
-    return float(np.median(cyc[ok] / rt[ok]) * 0.1), float(np.median(cyc[ok])), float(np.median(rt[ok]) * 10.0)
+    return float(np.median(cyc[ok] / rt[ok]) * 0.1), float(np.median(cyc[ok])), float(np.median(rt[ok]) * 0.01)
 
 
 def mfma_peak(args):
@@ -740,10 +747,45 @@ def mfma_peak(args):
         per_simd = iters * 4 * nacc * wps   # MFMAs issued by one SIMD
         res.append({"waves_per_simd": wps, "accumulators": nacc, "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
                     "frac_of_2500": round(flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-                    "clock_ghz": round(ghz, 3), "cycles_per_mfma_per_simd": round(cyc / per_simd, 2),
-                    "ms": round(ms, 3), "wave_loop_us": round(us, 1)})
+                    "clock_ghz": round(ghz, 3),
+                    # the kernel's wall time at the measured clock, per MFMA issued by one SIMD
+                    "cycles_per_mfma_per_simd": round(ms * 1e-3 * ghz * 1e9 / per_simd, 2),
+                    "ms": round(ms, 3), "median_wave_loop_us": round(us, 1)})
     print(json.dumps({"mfma_peak": res, "instruction": "v_mfma_f32_32x32x16_bf16", "workgroups": n_wg,
                       "note": "32 cycles per MFMA per SIMD is the dense peak (1024 flops/cycle/SIMD)"}), flush=True)
+
+
+def lds_ceiling(args):
+    """LDS read throughput: per CU and clock cycle, for the two read forms of the attention kernels,
+    with one, two and four workgroups of 4 waves per CU."""
+    import numpy as np
+    import torch
+
+    from mla_decode_decoupled_amd import _ceilings as C
+
+    dev = _device()
+    stream = torch.cuda.current_stream(dev)
+    res = []
+    iters = 20000
+    for mode, name, bytes_per_read in ((0, "ds_read_b128", 16), (1, "ds_read_b64_tr_b16", 8)):
+        for n_wg in (256, 512, 1024):
+            stamps = torch.zeros((n_wg * 4 * 4,), dtype=torch.int64, device=dev)
+            sink = torch.zeros((n_wg,), dtype=torch.int32, device=dev)
+            C.lds(mode, n_wg, 10, sink, stamps, stream.cuda_stream)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            C.lds(mode, n_wg, iters, sink, stamps, stream.cuda_stream)
+            b.record(stream)
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b)
+            ghz, cyc, _ = _clock_ghz(stamps)
+            total = n_wg * 4 * iters * 8 * 64 * bytes_per_read
+            cycles = ms * 1e-3 * ghz * 1e9
+            res.append({"read": name, "workgroups_per_cu": n_wg // 256, "bytes_per_clk_per_cu": round(total / 256 / cycles, 1),
+                        "tbs": round(total / (ms * 1e-3) / 1e12, 2), "clock_ghz": round(ghz, 3), "ms": round(ms, 3)})
+    print(json.dumps({"lds_ceiling": res, "note": "bytes per clock per CU from the wall time at the measured clock"}),
+          flush=True)
 
 
 def stream_ceiling(args):

@@ -329,7 +329,7 @@ mla_status mla_prefill_explicit(const mla_config* cfg, int32_t batch, int32_t n_
  * form, the explicit one pays off when many query rows share each rebuilt key and value; "从零理解
  * MLA", section "实际配置"). Returns 1 when mla_prefill_explicit covers the shape and n_q is at
  * least the row count from which it measured faster than mla_absorb_q + mla_decode_attn +
- * mla_out_proj on this library's kernels (128 new rows per sequence); 0 otherwise, including for
+ * mla_out_proj on this library's kernels (256 new rows per sequence); 0 otherwise, including for
  * invalid arguments. Host-only: launches nothing.
  */
 int32_t mla_prefill_prefers_explicit(const mla_config* cfg, int32_t batch, int32_t n_q, int32_t max_seq_len);

@@ -50,6 +50,17 @@ int mla_ceiling_mfma(int waves_per_simd, int n_acc, int n_workgroups, int iters,
 int mla_ceiling_stream(int mode, int depth, int n_workgroups, const void* src, size_t bytes_per_workgroup,
                        unsigned int* sink, unsigned long long* stamps, void* stream);
 
+/*
+ * mla_ceiling_lds — LDS read throughput per CU, workgroups of 4 waves (256 workgroups: one per CU;
+ * 512 or 1024: two or four per CU).
+ *  mode 0  ds_read_b128 (16 bytes per lane), 1: ds_read_b64_tr_b16 (8 bytes per lane, transposed);
+ *          each wave issues 8 conflict-free reads per block and waits for them, `iters` blocks
+ *  stamps  uint64 [n_workgroups * 4 * 4] written (per wave: clock and 100 MHz counters, start and end)
+ *  sink    uint32 [n_workgroups], written only if the folded data equals a fixed constant
+ */
+int mla_ceiling_lds(int mode, int n_workgroups, int iters, unsigned int* sink, unsigned long long* stamps,
+                    void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -15,6 +15,7 @@ _I = ctypes.c_int
 SIGNATURES = {
     "mla_ceiling_mfma": (ctypes.c_int, [_I, _I, _I, _I, _VP, _VP, _VP, _VP]),
     "mla_ceiling_stream": (ctypes.c_int, [_I, _I, _I, _VP, ctypes.c_size_t, _VP, _VP, _VP]),
+    "mla_ceiling_lds": (ctypes.c_int, [_I, _I, _I, _VP, _VP, _VP]),
 }
 
 
@@ -48,3 +49,9 @@ def stream(mode: int, depth: int, n_workgroups: int, src, bytes_per_workgroup: i
     """Enqueue one streaming-read kernel (mode 0: vector loads, 1: the LDS tile ring)."""
     _check(lib.mla_ceiling_stream(mode, depth, n_workgroups, src.data_ptr(), bytes_per_workgroup, sink.data_ptr(),
                                   None if stamps is None else stamps.data_ptr(), stream_), "mla_ceiling_stream")
+
+
+def lds(mode: int, n_workgroups: int, iters: int, sink, stamps, stream_) -> None:
+    """Enqueue the LDS read-throughput kernel (mode 0: ds_read_b128, 1: ds_read_b64_tr_b16)."""
+    _check(lib.mla_ceiling_lds(mode, n_workgroups, iters, sink.data_ptr(), stamps.data_ptr(), stream_),
+           "mla_ceiling_lds")

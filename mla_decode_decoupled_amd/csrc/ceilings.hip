@@ -143,6 +143,61 @@ __global__ void __launch_bounds__(256) stream_lds(const unsigned char* __restric
   if (x == 0x9e3779b9u) sink[blockIdx.x] = x;
 }
 
+// (c) LDS read throughput of the two read forms the attention kernels use, workgroups of 4 waves
+// (one to four per CU, by the grid size): ds_read_b128 (16 bytes per lane, the score operands) and ds_read_b64_tr_b16 (8 bytes
+// per lane, transposed, the value operands). Each wave issues 8 reads per block (every lane a
+// distinct 16-byte slot of a 1 KB row, rows 1 KB apart: no bank conflicts), waits for them, folds
+// the data into one register, and repeats; `iters` blocks per wave.
+template <int MODE>
+__global__ void __launch_bounds__(256) lds_read(int iters, unsigned int* __restrict__ sink,
+                                                unsigned long long* __restrict__ stamps) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  // fill this wave's 8 KB so that the reads see defined data
+  for (int i = lane; i < 8 * 1024 / 4; i += 64)
+    reinterpret_cast<unsigned int*>(lds + w * 8192)[i] = (unsigned int)(i * 2654435761u);
+  __syncthreads();
+  const uint32_t a = (uint32_t)(uintptr_t)(lds + w * 8192 + lane * 16);
+  unsigned int x = 0;
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+  for (int i = 0; i < iters; ++i) {
+    u32x4 v0, v1, v2, v3, v4, v5, v6, v7;
+    if (MODE == 0) {
+      asm volatile(
+          "ds_read_b128 %0, %8 offset:0\n\tds_read_b128 %1, %8 offset:1024\n\t"
+          "ds_read_b128 %2, %8 offset:2048\n\tds_read_b128 %3, %8 offset:3072\n\t"
+          "ds_read_b128 %4, %8 offset:4096\n\tds_read_b128 %5, %8 offset:5120\n\t"
+          "ds_read_b128 %6, %8 offset:6144\n\tds_read_b128 %7, %8 offset:7168\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3), "=&v"(v4), "=&v"(v5), "=&v"(v6), "=&v"(v7)
+          : "v"(a)
+          : "memory");
+      x ^= v0[0] ^ v1[1] ^ v2[2] ^ v3[3] ^ v4[0] ^ v5[1] ^ v6[2] ^ v7[3];
+    } else {
+      typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+      u32x2 h0, h1, h2, h3, h4, h5, h6, h7;
+      asm volatile(
+          "ds_read_b64_tr_b16 %0, %8 offset:0\n\tds_read_b64_tr_b16 %1, %8 offset:1024\n\t"
+          "ds_read_b64_tr_b16 %2, %8 offset:2048\n\tds_read_b64_tr_b16 %3, %8 offset:3072\n\t"
+          "ds_read_b64_tr_b16 %4, %8 offset:4096\n\tds_read_b64_tr_b16 %5, %8 offset:5120\n\t"
+          "ds_read_b64_tr_b16 %6, %8 offset:6144\n\tds_read_b64_tr_b16 %7, %8 offset:7168\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(h0), "=&v"(h1), "=&v"(h2), "=&v"(h3), "=&v"(h4), "=&v"(h5), "=&v"(h6), "=&v"(h7)
+          : "v"(a - (uint32_t)(lane * 8))   // 8 bytes per lane: lanes cover a 512-byte span of the row
+          : "memory");
+      x ^= h0[0] ^ h1[1] ^ h2[0] ^ h3[1] ^ h4[0] ^ h5[1] ^ h6[0] ^ h7[1];
+      (void)v0; (void)v1; (void)v2; (void)v3; (void)v4; (void)v5; (void)v6; (void)v7;
+    }
+  }
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+  if (lane == 0) {
+    const int gw = blockIdx.x * 4 + w;
+    stamp(stamps, 2 * gw, t0, r0);
+    stamp(stamps, 2 * gw + 1, t1, r1);
+  }
+  if (x == 0x9e3779b9u) sink[blockIdx.x] = x;
+}
+
 template <int WAVES, int NACC>
 hipError_t launch_mfma(int n_wg, int iters, const uint32_t* ops, unsigned long long* stamps, float* sink,
                        hipStream_t st) {
@@ -171,6 +226,21 @@ int mla_ceiling_mfma(int waves_per_simd, int n_acc, int n_workgroups, int iters,
   else if (waves_per_simd == 2 && n_acc == 8) e = launch_mfma<8, 8>(n_workgroups, iters, ops, stamps, sink, st);
   else return 2;
   return e == hipSuccess ? 0 : 4;
+}
+
+int mla_ceiling_lds(int mode, int n_workgroups, int iters, unsigned int* sink, unsigned long long* stamps,
+                    void* stream) {
+  if (n_workgroups < 1 || iters < 1 || !sink || !stamps) return 1;
+  if (mode != 0 && mode != 1) return 2;
+  hipStream_t st = (hipStream_t)stream;
+  constexpr int kReserve = 40 * 1024;   // 32 KB used; up to four workgroups per CU
+  const void* fn = mode == 0 ? (const void*)lds_read<0> : (const void*)lds_read<1>;
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kReserve) != hipSuccess) return 4;
+  if (mode == 0)
+    hipLaunchKernelGGL(lds_read<0>, dim3(n_workgroups), dim3(256), kReserve, st, iters, sink, stamps);
+  else
+    hipLaunchKernelGGL(lds_read<1>, dim3(n_workgroups), dim3(256), kReserve, st, iters, sink, stamps);
+  return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 
 int mla_ceiling_stream(int mode, int depth, int n_workgroups, const void* src, size_t bytes_per_workgroup,

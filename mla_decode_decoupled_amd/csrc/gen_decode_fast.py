@@ -172,8 +172,22 @@ def dma():
 def emit(lines):
     return "\n".join(f'        "{l}\\n\\t"' for l in lines)
 
-src = open(os.path.join(HERE, 'decode_fast.in.hip')).read()
-src = src.replace('@GENERATED_NOTE@', '// GENERATED by gen_decode_fast.py from decode_fast.in.hip: edit the template, then rerun it.')
-src = src.replace('@QK_ASM@', emit(qk())).replace('@PVSM_ASM@', emit(pv())).replace('@DMA_ASM@', emit(dma())).replace('@QLOAD_ASM@', emit(qload()))
-open(os.path.join(HERE, 'decode_fast.hip'), 'w').write(src)
-print(len(qk()), len(pv()), len(dma()))
+
+def generate(template_path: str) -> str:
+    """The expanded kernel source for the template at template_path."""
+    src = open(template_path).read()
+    src = src.replace('@GENERATED_NOTE@',
+                      '// GENERATED by gen_decode_fast.py from decode_fast.in.hip: edit the template, then rerun it.')
+    return (src.replace('@QK_ASM@', emit(qk())).replace('@PVSM_ASM@', emit(pv())).replace('@DMA_ASM@', emit(dma()))
+            .replace('@QLOAD_ASM@', emit(qload())))
+
+
+if __name__ == "__main__":
+    import argparse
+    ap = argparse.ArgumentParser(description="expand decode_fast.in.hip into decode_fast.hip")
+    ap.add_argument("--template", default=os.path.join(HERE, 'decode_fast.in.hip'))
+    ap.add_argument("-o", "--output", default=os.path.join(HERE, 'decode_fast.hip'))
+    a = ap.parse_args()
+    with open(a.output, 'w') as fh:
+        fh.write(generate(a.template))
+    print(len(qk()), len(pv()), len(dma()))

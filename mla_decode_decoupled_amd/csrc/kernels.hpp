@@ -131,7 +131,7 @@ hipError_t launch_kv_expand(int batch, int max_seq_len, int n_out, int d_latent,
 bool prefill_explicit_supported(const LayerDims& L);
 // From this many new query rows per sequence on, the explicit form measured faster than the
 // absorbed one (absorb + latent attention + W_UV) on the DeepSeek head shape.
-constexpr int kExplicitMinRows = 128;
+constexpr int kExplicitMinRows = 256;
 size_t prefill_explicit_workspace_bytes(const LayerDims& L, int batch, int max_seq_len);
 hipError_t launch_prefill_explicit(const LayerDims& L, int batch, int n_q, const void* q_nope, const void* q_rope,
                                    const void* cache, const int64_t* seq_off, const int32_t* seq_len, int max_seq_len,

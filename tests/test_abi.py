@@ -279,7 +279,7 @@ def test_ceilings_library_exports_and_validation():
     arguments before launching."""
     from mla_decode_decoupled_amd import _ceilings as C
     names = set(re.findall(r"^\s*int\s+(mla_\w+)\s*\(", open(CEIL_HEADER).read(), re.M))
-    assert names == {"mla_ceiling_mfma", "mla_ceiling_stream"}
+    assert names == {"mla_ceiling_mfma", "mla_ceiling_stream", "mla_ceiling_lds"}
     for n in names:
         assert hasattr(C.lib, n) and n in C.SIGNATURES
     assert C.lib.mla_ceiling_mfma(1, 4, 0, 10, FAKE, FAKE, FAKE, None) == 1        # no workgroups
@@ -292,3 +292,7 @@ def test_ceilings_library_exports_and_validation():
     assert C.lib.mla_ceiling_stream(1, 2, 256, FAKE, 1000, FAKE, FAKE, None) == 1   # not whole tiles
     assert C.lib.mla_ceiling_stream(1, 4, 256, FAKE, 36864, FAKE, FAKE, None) == 2
     assert C.lib.mla_ceiling_stream(7, 2, 256, FAKE, 36864, FAKE, FAKE, None) == 2
+    assert C.lib.mla_ceiling_lds(0, 0, 10, FAKE, FAKE, None) == 1
+    assert C.lib.mla_ceiling_lds(0, 256, 10, None, FAKE, None) == 1
+    assert C.lib.mla_ceiling_lds(2, 256, 10, FAKE, FAKE, None) == 2
+
