@@ -132,24 +132,44 @@ __device__ __forceinline__ void wait_vmcnt_27() {
   __builtin_amdgcn_s_waitcnt((27 & 15) | ((27 >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Split-K partials: per (query row, chunk) one block of H * DC floats and H (m, l) pairs.
+// Split-K partials: per (query row, chunk) one block of H * DC accumulator values, stored as bf16
+// (rounded once, to nearest even), and H (m, l) pairs in float32. The latent sums are accumulated in
+// float32 in the registers; only their hand-over to the merge is rounded (at most 2^-9 relative per
+// value, independent across chunks), which halves the partial traffic of every split row.
 // The attention kernels store them in the accumulator's own register order, so they write them
 // with whole 1 KB stores straight from the accumulators and attn_merge_frag reads them the same way:
-//   [head block hb][col block cb (16)][row group j][lane][4]
-// holds O^T[col][head] for col = 32cb + 8j + 4(lane / 32) + e, head = 32hb + lane % 32.
+//   [head block hb][col block cb (16)][row-group pair jp (2)][lane][8]
+// holds O^T[col][head] for col = 32cb + 8j + 4(lane / 32) + e with j = 2jp + (i / 4), e = i % 4
+// (i = 0..7 the position in the lane's 8 values), head = 32hb + lane % 32: a lane's 8 values are
+// 8 consecutive accumulator registers.
 // For mla_decode_step, decode_attn_hsplit stores them head-major instead, [head][col], so that one
-// head's 2 KB row per chunk is contiguous for merge_heads_out_proj, which merges and projects one
+// head's 1 KB row per chunk is contiguous for merge_heads_out_proj, which merges and projects one
 // head per workgroup. The head-split kernel writes its (few, latency-bound) partials with
 // nontemporal stores, which shortens the write-back at the end of the kernel, and attn_merge_frag
 // reads them nontemporally too (cached by the merge, the lines would slow the next call's
 // stores); the big kernel's partials go through the caches both ways, where the merge finds part
-// of them (measured: the nontemporal form slows that merge by a fifth and gains nothing in the
-// attention kernel).
-constexpr int PART_FLOATS = H * DC;   // per (query row, chunk)
+// of them.
+constexpr int PART_ELEMS = H * DC;   // bf16 values per (query row, chunk)
 __device__ __forceinline__ int frag_offset(int head, int col) {
   const int cb = col >> 5, j = (col >> 3) & 3, g = (col >> 2) & 1, e = col & 3;
   const int hb = head >> 5, lane = 32 * g + (head & 31);
-  return (((hb * 16 + cb) * 4 + j) * 64 + lane) * 4 + e;
+  return ((((hb * 16 + cb) * 2 + (j >> 1)) * 64 + lane) * 8) + (j & 1) * 4 + e;
+}
+// eight float32 accumulator values rounded to bf16 (nearest even), packed for one 16-byte store
+typedef float f32x8v __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ bf16x8 to_bf16x8(f32x4 lo, f32x4 hi) {
+  const f32x8v v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, __builtin_convertvector(v, bf16x8v));
+}
+// the eight float32 values of a 16-byte bf16 piece
+__device__ __forceinline__ void from_bf16x8(bf16x8 p, f32x4& lo, f32x4& hi) {
+  const i32x4 u = __builtin_bit_cast(i32x4, p);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float a = __uint_as_float((uint32_t)u[k] << 16), b = __uint_as_float((uint32_t)u[k] & 0xFFFF0000u);
+    if (k < 2) { lo[2 * k] = a; lo[2 * k + 1] = b; } else { hi[2 * k - 4] = a; hi[2 * k - 3] = b; }
+  }
 }
 
 // ---- How the keys are cut into chunks (one workgroup each).
@@ -229,7 +249,7 @@ __device__ bool balanced_chunk(const int32_t* __restrict__ seq_len, int n_q, int
 // MFMA loop's register allocation does not see it.
 __device__ __noinline__ void exact_chunk(const bf16* __restrict__ q_packed, const unsigned char* __restrict__ kv,
                                          size_t rh0, int j0, int j1, float scale_log2, int n_chunks, int slot,
-                                         float* __restrict__ part_acc, float* __restrict__ part_ml,
+                                         bf16* __restrict__ part_acc, float* __restrict__ part_ml,
                                          float* __restrict__ z, float* __restrict__ lse, unsigned char* smem,
                                          int h_begin, int h_end, bool head_major) {
   float* qs = reinterpret_cast<float*>(smem);   // [ROW]
@@ -279,9 +299,9 @@ __device__ __noinline__ void exact_chunk(const bf16* __restrict__ q_packed, cons
       z[rh * DC + tid + 256] = acc1 / l;
       if (lse != nullptr && tid == 0) lse[rh] = (m + log2f(l)) * kLn2;
     } else {
-      float* blk = part_acc + (size_t)slot * PART_FLOATS;
-      blk[head_major ? h * DC + tid : frag_offset(h, tid)] = acc0;
-      blk[head_major ? h * DC + tid + 256 : frag_offset(h, tid + 256)] = acc1;
+      bf16* blk = part_acc + (size_t)slot * PART_ELEMS;
+      blk[head_major ? h * DC + tid : frag_offset(h, tid)] = (bf16)acc0;
+      blk[head_major ? h * DC + tid + 256 : frag_offset(h, tid + 256)] = (bf16)acc1;
       if (tid == 0) {
         part_ml[((size_t)slot * H + h) * 2 + 0] = m;
         part_ml[((size_t)slot * H + h) * 2 + 1] = l;
@@ -296,7 +316,7 @@ __device__ __noinline__ void exact_chunk(const bf16* __restrict__ q_packed, cons
 __global__ void __launch_bounds__(256)
     decode_attn_fast(const bf16* __restrict__ q_packed, const bf16* __restrict__ cache,
                      const int64_t* __restrict__ seq_off, const int32_t* __restrict__ seq_len, int n_q, int rows,
-                     float scale_log2, int mode, int n_splits, int chunk_len, float* __restrict__ part_acc,
+                     float scale_log2, int mode, int n_splits, int chunk_len, bf16* __restrict__ part_acc,
                      float* __restrict__ part_ml, int2* __restrict__ row_chunks, float* __restrict__ z,
                      float* __restrict__ lse) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
@@ -588,14 +608,16 @@ __global__ void __launch_bounds__(256)
   const f32x16* oacc[16] = {&oc0, &oc1, &oc2, &oc3, &oc4, &oc5, &oc6, &oc7,
                             &oc8, &oc9, &oc10, &oc11, &oc12, &oc13, &oc14, &oc15};
   if (n_chunks > 1) {
-    // ---- partial: 64 stores of 1 KB per wave, straight from the accumulators (layout above)
-    float* blk = part_acc + (size_t)ch.slot * PART_FLOATS + (size_t)w * (PART_FLOATS / 4) + 4 * lane;
+    // ---- partial: 32 stores of 1 KB per wave, straight from the accumulators (layout above)
+    bf16* blk = part_acc + (size_t)ch.slot * PART_ELEMS + (size_t)w * (PART_ELEMS / 4) + 8 * lane;
 #pragma unroll
     for (int cb = 0; cb < 16; ++cb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int jp = 0; jp < 2; ++jp) {
         const f32x16& o = *oacc[cb];
-        *reinterpret_cast<f32x4*>(blk + (cb * 4 + j) * 256) = f32x4{o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]};
+        *reinterpret_cast<bf16x8*>(blk + (cb * 2 + jp) * 512) =
+            to_bf16x8(f32x4{o[8 * jp], o[8 * jp + 1], o[8 * jp + 2], o[8 * jp + 3]},
+                      f32x4{o[8 * jp + 4], o[8 * jp + 5], o[8 * jp + 6], o[8 * jp + 7]});
       }
     return;
   }
@@ -708,7 +730,7 @@ __device__ __forceinline__ bool hsplit_chunk(const int32_t* __restrict__ seq_len
 __global__ void __launch_bounds__(256)
     decode_attn_hsplit(const bf16* __restrict__ q_packed, const bf16* __restrict__ cache,
                        const int64_t* __restrict__ seq_off, const int32_t* __restrict__ seq_len, int n_q, int rows,
-                       float scale_log2, float* __restrict__ part_acc, float* __restrict__ part_ml,
+                       float scale_log2, bf16* __restrict__ part_acc, float* __restrict__ part_ml,
                        int2* __restrict__ row_chunks, float* __restrict__ z, float* __restrict__ lse,
                        int head_major) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
@@ -892,24 +914,27 @@ __global__ void __launch_bounds__(256)
         *reinterpret_cast<f32x4*>(stage + l32 * HS_STAGE + 32 * (4 * w + i) + 8 * j + 4 * g) =
             f32x4{oacc[i][4 * j], oacc[i][4 * j + 1], oacc[i][4 * j + 2], oacc[i][4 * j + 3]};
     __syncthreads();
-    float* prow = part_acc + (size_t)ch.slot * PART_FLOATS + (size_t)head0 * DC + 4 * lane;
+    // each lane rounds 8 consecutive columns of a head row: one 1 KB store per row
+    bf16* prow = part_acc + (size_t)ch.slot * PART_ELEMS + (size_t)head0 * DC + 8 * lane;
 #pragma unroll
     for (int hh = 0; hh < 8; ++hh) {
       const int hl = 8 * w + hh;
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-        __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(stage + hl * HS_STAGE + 256 * c + 4 * lane),
-                                    reinterpret_cast<f32x4*>(prow + (size_t)hl * DC + 256 * c));
+      const float* sr = stage + hl * HS_STAGE + 8 * lane;
+      const bf16x8 v = to_bf16x8(*reinterpret_cast<const f32x4*>(sr), *reinterpret_cast<const f32x4*>(sr + 4));
+      __builtin_nontemporal_store(__builtin_bit_cast(i32x4, v), reinterpret_cast<i32x4*>(prow + (size_t)hl * DC));
     }
   } else {
     // register-order partial: 1 KB stores straight from the accumulators
-    float* blk = part_acc + (size_t)ch.slot * PART_FLOATS + (size_t)hb * (PART_FLOATS / 4) + 4 * lane;
+    bf16* blk = part_acc + (size_t)ch.slot * PART_ELEMS + (size_t)hb * (PART_ELEMS / 4) + 8 * lane;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        __builtin_nontemporal_store(f32x4{oacc[i][4 * j], oacc[i][4 * j + 1], oacc[i][4 * j + 2], oacc[i][4 * j + 3]},
-                                    reinterpret_cast<f32x4*>(blk + ((4 * w + i) * 4 + j) * 256));
+      for (int jp = 0; jp < 2; ++jp) {
+        const bf16x8 v = to_bf16x8(f32x4{oacc[i][8 * jp], oacc[i][8 * jp + 1], oacc[i][8 * jp + 2], oacc[i][8 * jp + 3]},
+                                   f32x4{oacc[i][8 * jp + 4], oacc[i][8 * jp + 5], oacc[i][8 * jp + 6], oacc[i][8 * jp + 7]});
+        __builtin_nontemporal_store(__builtin_bit_cast(i32x4, v),
+                                    reinterpret_cast<i32x4*>(blk + ((4 * w + i) * 2 + jp) * 512));
+      }
   }
   if (w == 0 && g == 0) {
     float* ml = part_ml + ((size_t)ch.slot * H + head) * 2;
@@ -918,27 +943,27 @@ __global__ void __launch_bounds__(256)
   }
 }
 
-// Log-sum-exp merge of decode_attn_fast's split-K partials (register order). One workgroup per
-// (query row, head block hb, col block cb, JN of the 4 row groups j): 32 heads x 8 JN latent
-// columns, each lane owning one head and 4 JN columns (JN = 4 for many rows; JN = 1 spreads a
-// few rows over four times as many workgroups). The row's chunks are the slots
-// base .. base + nck - 1 (every one saw at least one key), as published by the row's first chunk.
+// Log-sum-exp merge of decode_attn_fast's split-K partials (register order, bf16). One workgroup per
+// (query row, head block hb, col block cb, JP of the 2 row-group pairs jp): 32 heads x 16 JP latent
+// columns, each lane owning one head and 8 JP columns (JP = 2 for many rows; JP = 1 spreads a few
+// rows over twice as many workgroups). The row's chunks are the slots base .. base + nck - 1 (every
+// one saw at least one key), as published by the row's first chunk.
 // With M = max_k m_k (m in log2 units), z = sum_k 2^(m_k - M) O_k / sum_k 2^(m_k - M) l_k.
 // One pass: the 4 waves take the chunks round-robin, CU chunks (coalesced 1 KB loads of the
 // partial and its (m, l)) in flight per step, and each wave keeps its own running maximum,
 // rescaling its sums when it grows; the wave sums then meet in LDS against the common maximum.
 // Rows computed as a single chunk were written directly and are skipped.
-template <int JN, bool NT>
-__global__ void __launch_bounds__(256) attn_merge_frag(const float* __restrict__ part_acc,
+template <int JP, bool NT>
+__global__ void __launch_bounds__(256) attn_merge_frag(const bf16* __restrict__ part_acc,
                                                        const float* __restrict__ part_ml,
                                                        const int2* __restrict__ row_chunks,
                                                        float* __restrict__ z, float* __restrict__ lse) {
-  constexpr int CU = JN == 1 ? 16 : 2;   // chunks per step and wave
-  __shared__ f32x4 red[3][JN][64];
+  constexpr int CU = JP == 1 ? 16 : 4;   // chunks per step and wave
+  __shared__ f32x4 red[3][JP][2][64];
   __shared__ float lred[3][64];
   __shared__ float mred[3][64];
   const int bt = blockIdx.y;
-  const int slab = blockIdx.x / (4 / JN), jbase = (blockIdx.x % (4 / JN)) * JN;   // slab = hb * 16 + cb
+  const int slab = blockIdx.x / (2 / JP), jpbase = (blockIdx.x % (2 / JP)) * JP;   // slab = hb * 16 + cb
   const int hb = slab >> 4, cb = slab & 15;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int g = lane >> 5, hl = lane & 31;
@@ -947,11 +972,11 @@ __global__ void __launch_bounds__(256) attn_merge_frag(const float* __restrict__
   const int base = rc.x, nck = rc.y;
   const size_t head = (size_t)32 * hb + hl;
   const float2* ml = reinterpret_cast<const float2*>(part_ml) + (size_t)base * H + head;   // stride H
-  const float* src = part_acc + (size_t)base * PART_FLOATS + (size_t)slab * 1024 + (size_t)jbase * 256 + 4 * lane;
+  const bf16* src = part_acc + (size_t)base * PART_ELEMS + (size_t)slab * 1024 + (size_t)jpbase * 512 + 8 * lane;
   float m_w = -INFINITY, Lsum = 0.0f;
-  f32x4 acc[JN] = {};
+  f32x4 acc[JP][2] = {};
   for (int k0 = wv; k0 < nck; k0 += 4 * CU) {   // chunk k0 exists, so every step sees one
-    f32x4 x[CU][JN];
+    i32x4 x[CU][JP];
     float2 v[CU];
 #pragma unroll
     for (int u = 0; u < CU; ++u) {
@@ -959,9 +984,10 @@ __global__ void __launch_bounds__(256) attn_merge_frag(const float* __restrict__
       v[u] = make_float2(-INFINITY, 0.0f);
       if (kk < nck) {
 #pragma unroll
-        for (int j = 0; j < JN; ++j)
-          x[u][j] = NT ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + (size_t)kk * PART_FLOATS + j * 256))
-                       : *reinterpret_cast<const f32x4*>(src + (size_t)kk * PART_FLOATS + j * 256);
+        for (int j = 0; j < JP; ++j) {
+          const i32x4* p = reinterpret_cast<const i32x4*>(src + (size_t)kk * PART_ELEMS + j * 512);
+          x[u][j] = NT ? __builtin_nontemporal_load(p) : *p;
+        }
         v[u] = ml[(size_t)kk * H];
       }
     }
@@ -971,21 +997,32 @@ __global__ void __launch_bounds__(256) attn_merge_frag(const float* __restrict__
     const float a = exp2f(m_w - mb);   // 0 on the first step (m_w = -inf, mb finite)
     Lsum *= a;
 #pragma unroll
-    for (int j = 0; j < JN; ++j) acc[j] *= a;
+    for (int j = 0; j < JP; ++j) {
+      acc[j][0] *= a;
+      acc[j][1] *= a;
+    }
 #pragma unroll
     for (int u = 0; u < CU; ++u) {
       if (k0 + 4 * u < nck) {
         const float wk = exp2f(v[u].x - mb);
         Lsum = fmaf(wk, v[u].y, Lsum);
 #pragma unroll
-        for (int j = 0; j < JN; ++j) acc[j] += wk * x[u][j];
+        for (int j = 0; j < JP; ++j) {
+          f32x4 lo, hi;
+          from_bf16x8(__builtin_bit_cast(bf16x8, x[u][j]), lo, hi);
+          acc[j][0] += wk * lo;
+          acc[j][1] += wk * hi;
+        }
       }
     }
     m_w = mb;
   }
   if (wv > 0) {
 #pragma unroll
-    for (int j = 0; j < JN; ++j) red[wv - 1][j][lane] = acc[j];
+    for (int j = 0; j < JP; ++j) {
+      red[wv - 1][j][0][lane] = acc[j][0];
+      red[wv - 1][j][1][lane] = acc[j][1];
+    }
     lred[wv - 1][lane] = Lsum;
     mred[wv - 1][lane] = m_w;
   }
@@ -998,21 +1035,30 @@ __global__ void __launch_bounds__(256) attn_merge_frag(const float* __restrict__
     const float a0 = exp2f(m_w - M);
     Lsum *= a0;
 #pragma unroll
-    for (int j = 0; j < JN; ++j) acc[j] *= a0;
+    for (int j = 0; j < JP; ++j) {
+      acc[j][0] *= a0;
+      acc[j][1] *= a0;
+    }
 #pragma unroll
     for (int u = 0; u < 3; ++u) {
       const float au = exp2f(mred[u][lane] - M);
       Lsum = fmaf(au, lred[u][lane], Lsum);
 #pragma unroll
-      for (int j = 0; j < JN; ++j) acc[j] += au * red[u][j][lane];
+      for (int j = 0; j < JP; ++j) {
+        acc[j][0] += au * red[u][j][0][lane];
+        acc[j][1] += au * red[u][j][1][lane];
+      }
     }
     // the two lane halves of a head summed the same chunks: Lsum agrees between them
     const size_t rh = (size_t)bt * H + head;
     const float inv = 1.0f / Lsum;
-    float* dst = z + rh * DC + 32 * cb + 8 * jbase + 4 * g;
+    float* dst = z + rh * DC + 32 * cb + 4 * g;
 #pragma unroll
-    for (int j = 0; j < JN; ++j) *reinterpret_cast<f32x4*>(dst + 8 * j) = acc[j] * inv;
-    if (lse != nullptr && cb == 0 && jbase == 0 && g == 0) lse[rh] = (M + log2f(Lsum)) * kLn2;
+    for (int j = 0; j < JP; ++j) {   // row groups 2 (jpbase + j) and 2 (jpbase + j) + 1
+      *reinterpret_cast<f32x4*>(dst + 16 * (jpbase + j)) = acc[j][0] * inv;
+      *reinterpret_cast<f32x4*>(dst + 16 * (jpbase + j) + 8) = acc[j][1] * inv;
+    }
+    if (lse != nullptr && cb == 0 && jpbase == 0 && g == 0) lse[rh] = (M + log2f(Lsum)) * kLn2;
   }
 }
 
@@ -1021,8 +1067,8 @@ __global__ void __launch_bounds__(256) attn_merge_frag(const float* __restrict__
 // the merge costs no launch of its own, and the weights stream in while the partials are read.
 // One (query row, head, half of the 128 outputs) per workgroup of 8 waves.
 //   merge: the waves take the row's chunks round-robin (every chunk in one step); lane l reads
-//   latent columns 4l .. 4l+3 and 256 + 4l .. +3 (two 1 KB loads per wave and chunk) and keeps a
-//   running maximum; the wave sums meet in LDS against the common maximum,
+//   latent columns 8l .. 8l+7 (one 1 KB load of bf16 per wave and chunk) and keeps a running
+//   maximum; the wave sums meet in LDS against the common maximum,
 //   z = sum_k 2^(m_k - M) O_k / sum_k 2^(m_k - M) l_k. A row computed as one chunk already has its
 //   final z, written by the attention kernel, and is read back.
 //   projection: wave w owns the 8 outputs 64 y + 8 w + j of half y; its lanes load
@@ -1032,7 +1078,7 @@ __global__ void __launch_bounds__(256) attn_merge_frag(const float* __restrict__
 // grid (H, 2, rows), 64 MERGE_WAVES threads.
 constexpr int MERGE_WAVES = 8;
 __global__ void __launch_bounds__(64 * MERGE_WAVES)
-    merge_heads_out_proj(const float* __restrict__ part_acc, const float* __restrict__ part_ml,
+    merge_heads_out_proj(const bf16* __restrict__ part_acc, const float* __restrict__ part_ml,
                          const int2* __restrict__ row_chunks, const bf16* __restrict__ w_uv, float* __restrict__ z,
                          float* __restrict__ lse, bf16* __restrict__ o) {
   constexpr int MW = MERGE_WAVES;
@@ -1055,20 +1101,19 @@ __global__ void __launch_bounds__(64 * MERGE_WAVES)
     for (int c = t; c < DC; c += MW * 64) zs[c] = z[rh * DC + c];
   } else {
     const int base = rc.x, nck = rc.y;
-    const float* src = part_acc + (size_t)base * PART_FLOATS + (size_t)i * DC + 4 * lane;
+    const bf16* src = part_acc + (size_t)base * PART_ELEMS + (size_t)i * DC + 8 * lane;
     const float2* ml = reinterpret_cast<const float2*>(part_ml) + (size_t)base * H + i;   // stride H per chunk
     float m_w = -INFINITY, Lsum = 0.0f;
     f32x4 a0 = {}, a1 = {};
     for (int k0 = w; k0 < nck; k0 += MW * CU) {
-      f32x4 x0[CU], x1[CU];
+      i32x4 x[CU];
       float2 v[CU];
 #pragma unroll
       for (int u = 0; u < CU; ++u) {
         const int kk = k0 + MW * u;
         v[u] = make_float2(-INFINITY, 0.0f);
         if (kk < nck) {
-          x0[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + (size_t)kk * PART_FLOATS));
-          x1[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + (size_t)kk * PART_FLOATS + 256));
+          x[u] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(src + (size_t)kk * PART_ELEMS));
           v[u] = ml[(size_t)kk * H];
         }
       }
@@ -1084,8 +1129,10 @@ __global__ void __launch_bounds__(64 * MERGE_WAVES)
         if (k0 + MW * u < nck) {
           const float wk = exp2f(v[u].x - mb);
           Lsum = fmaf(wk, v[u].y, Lsum);
-          a0 += wk * x0[u];
-          a1 += wk * x1[u];
+          f32x4 lo, hi;
+          from_bf16x8(__builtin_bit_cast(bf16x8, x[u]), lo, hi);
+          a0 += wk * lo;
+          a1 += wk * hi;
         }
       }
       m_w = mb;
@@ -1097,7 +1144,7 @@ __global__ void __launch_bounds__(64 * MERGE_WAVES)
       wl[w] = Lsum;
     }
     __syncthreads();
-    if (t < 128) {
+    if (t < 64) {
       // wave 0 holds chunk 0, so M is finite; a wave without chunks weighs 2^-inf = 0
       float M = wm[0];
 #pragma unroll
@@ -1109,16 +1156,20 @@ __global__ void __launch_bounds__(64 * MERGE_WAVES)
         e[u] = exp2f(wm[u] - M);
         L = fmaf(e[u], wl[u], L);
       }
-      const int hq = t >> 6, l = t & 63;
-      f32x4 acc = e[0] * wacc[0][hq][l];
+      f32x4 acc0 = e[0] * wacc[0][0][t], acc1 = e[0] * wacc[0][1][t];
 #pragma unroll
-      for (int u = 1; u < MW; ++u) acc += e[u] * wacc[u][hq][l];
+      for (int u = 1; u < MW; ++u) {
+        acc0 += e[u] * wacc[u][0][t];
+        acc1 += e[u] * wacc[u][1][t];
+      }
       const float inv = 1.0f / L;
-      const f32x4 zq = acc * inv;
-      const int c = 256 * hq + 4 * l;
-      *reinterpret_cast<f32x4*>(&zs[c]) = zq;
+      const f32x4 z0 = acc0 * inv, z1 = acc1 * inv;
+      const int c = 8 * t;   // this lane's 8 latent columns
+      *reinterpret_cast<f32x4*>(&zs[c]) = z0;
+      *reinterpret_cast<f32x4*>(&zs[c + 4]) = z1;
       if (half == 0) {
-        *reinterpret_cast<f32x4*>(z + rh * DC + c) = zq;
+        *reinterpret_cast<f32x4*>(z + rh * DC + c) = z0;
+        *reinterpret_cast<f32x4*>(z + rh * DC + c + 4) = z1;
         if (lse != nullptr && t == 0) lse[rh] = (M + log2f(L)) * kLn2;
       }
     }
@@ -1177,7 +1228,8 @@ bool attn_fast_supported(const LayerDims& L) {
 // workspace of the MFMA path: partial accumulators, (m, l) pairs, one (first slot, count) per row
 size_t attn_fast_workspace_bytes(const SplitPlan& plan, int rows) {
   if (plan.fast_slots == 0) return 0;
-  return (size_t)plan.fast_slots * ((size_t)fast::PART_FLOATS + 2 * fast::H) * sizeof(float) + (size_t)rows * sizeof(int2);
+  return (size_t)plan.fast_slots * ((size_t)fast::PART_ELEMS * sizeof(__bf16) + 2 * fast::H * sizeof(float)) +
+         (size_t)rows * sizeof(int2);
 }
 
 void attn_fast_plan(int rows, int n_splits, int max_seq_len, SplitPlan* plan) {
@@ -1206,13 +1258,13 @@ bool attn_fast_is_hsplit(const SplitPlan& plan) { return plan.fast_mode == fast:
 namespace {
 // workspace of the MFMA path: partial accumulators, then (m, l) pairs, then (first slot, count) per row
 struct FastParts {
-  float* acc;
+  __bf16* acc;
   float* ml;
   int2* row_chunks;
 };
 FastParts fast_parts(const SplitPlan& plan, void* workspace) {
-  float* acc = (float*)workspace;
-  float* ml = plan.fast_slots > 0 ? acc + (size_t)plan.fast_slots * fast::PART_FLOATS : nullptr;
+  __bf16* acc = (__bf16*)workspace;
+  float* ml = plan.fast_slots > 0 ? reinterpret_cast<float*>(acc + (size_t)plan.fast_slots * fast::PART_ELEMS) : nullptr;
   int2* rc = plan.fast_slots > 0 ? reinterpret_cast<int2*>(ml + (size_t)plan.fast_slots * 2 * fast::H) : nullptr;
   return FastParts{acc, ml, rc};
 }
@@ -1232,7 +1284,7 @@ hipError_t launch_attn_fast(const LayerDims& L, int batch, int n_q, const void* 
                             float* z, float* lse, hipStream_t stream, bool defer_merge) {
   const int rows = batch * n_q;
   const FastParts P = fast_parts(plan, workspace);
-  float* part_acc = P.acc;
+  __bf16* part_acc = P.acc;
   float* part_ml = P.ml;
   int2* row_chunks = P.row_chunks;
   static bool attr_set = false;
@@ -1259,13 +1311,13 @@ hipError_t launch_attn_fast(const LayerDims& L, int batch, int n_q, const void* 
   if (e != hipSuccess || plan.fast_slots == 0) return e;
   if (plan.fast_mode == fast::HSPLIT) {
     if (defer_merge) return hipSuccess;
-    hipLaunchKernelGGL((fast::attn_merge_frag<1, true>), dim3(256, rows), dim3(256), 0, stream, part_acc, part_ml,
+    hipLaunchKernelGGL((fast::attn_merge_frag<1, true>), dim3(128, rows), dim3(256), 0, stream, part_acc, part_ml,
                        row_chunks, z, lse);
-  } else if (rows <= 16) {   // few rows: four workgroups per (row, 32 x 32 block) to keep enough loads in flight
-    hipLaunchKernelGGL((fast::attn_merge_frag<1, false>), dim3(256, rows), dim3(256), 0, stream, part_acc, part_ml,
+  } else if (rows <= 16) {   // few rows: two workgroups per (row, 32 x 32 block) to keep enough loads in flight
+    hipLaunchKernelGGL((fast::attn_merge_frag<1, false>), dim3(128, rows), dim3(256), 0, stream, part_acc, part_ml,
                        row_chunks, z, lse);
   } else {
-    hipLaunchKernelGGL((fast::attn_merge_frag<4, false>), dim3(64, rows), dim3(256), 0, stream, part_acc, part_ml,
+    hipLaunchKernelGGL((fast::attn_merge_frag<2, false>), dim3(64, rows), dim3(256), 0, stream, part_acc, part_ml,
                        row_chunks, z, lse);
   }
   return hipGetLastError();
