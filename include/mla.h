@@ -199,6 +199,30 @@ mla_status mla_decode_step(const mla_config* cfg, int32_t batch, int32_t n_q, co
                            float* lse, void* o, void* stream);
 
 /*
+ * mla_decode_step_noalloc — mla_decode_step for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation. Same arguments,
+ * results, kernels and errors as mla_decode_step, minus the workspace: the split-K partials and the
+ * step's positions go to a scratch array of MLA_NOALLOC_SCRATCH_BYTES that the library holds on
+ * each GPU it runs on (a static device array, resolved once per device on the first call made
+ * with that device current, and held until the process ends). The call allocates and frees
+ * nothing.
+ *  - The array of the current device (hipGetDevice) is used: `stream` must belong to that device.
+ *  - A step whose workspace (mla_decode_step_workspace_size) exceeds MLA_NOALLOC_SCRATCH_BYTES
+ *    returns MLA_ERR_UNSUPPORTED and launches nothing.
+ *  - No part of the array needs to start at zero: every word the step's kernels read is written
+ *    earlier in the same step. The array keeps the last call's contents.
+ *  - All calls on one GPU share its array: calls that overlap in time on one GPU (different
+ *    streams, or different threads without ordering) race and give wrong results. Order them on
+ *    one stream.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES (64u << 20)
+mla_status mla_decode_step_noalloc(const mla_config* cfg, int32_t batch, int32_t n_q, const void* c_new,
+                                   const void* k_rope_new, const void* q_nope, const void* q_rope,
+                                   const void* w_uk, const void* w_uv, void* cache, const int64_t* seq_off,
+                                   const int32_t* seq_len, int32_t max_seq_len, int32_t n_splits,
+                                   void* q_packed, float* z, float* lse, void* o, void* stream);
+
+/*
  * ---- Upstream projections: from the hidden state h to the inputs of the calls above.
  *
  * Bytes of device workspace mla_project_kv_append (d_q = 0) or mla_project_q (its d_q) needs

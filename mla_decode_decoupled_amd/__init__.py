@@ -14,6 +14,7 @@ from .ops import (  # noqa: F401
     mla_out_proj,
     mla_decode_step_workspace_size,
     mla_decode_step,
+    mla_decode_step_noalloc,
     mla_project_workspace_size,
     mla_project_kv_append,
     mla_project_q,

@@ -22,6 +22,8 @@ MLA_ERR_HIP = 4
 MLA_F32 = 0
 MLA_BF16 = 1
 
+MLA_NOALLOC_SCRATCH_BYTES = 64 << 20   # include/mla.h
+
 
 class MlaConfig(ctypes.Structure):
     _fields_ = [
@@ -56,6 +58,8 @@ SIGNATURES = {
     "mla_decode_step_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(MlaConfig), _I32, _I32, _I32, _I32]),
     "mla_decode_step": (ctypes.c_int, [ctypes.POINTER(MlaConfig), _I32, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                        _VP, _VP, _I32, _I32, _VP, ctypes.c_size_t, _VP, _VP, _VP, _VP, _VP]),
+    "mla_decode_step_noalloc": (ctypes.c_int, [ctypes.POINTER(MlaConfig), _I32, _I32, _VP, _VP, _VP, _VP, _VP, _VP,
+                                               _VP, _VP, _VP, _I32, _I32, _VP, _VP, _VP, _VP, _VP]),
     "mla_project_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(MlaConfig), _I32, _I32, _I32]),
     "mla_project_kv_append": (ctypes.c_int, [ctypes.POINTER(MlaConfig), _I32, _I32, _I32, _VP, _VP, _VP, _VP,
                                              ctypes.c_float, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),

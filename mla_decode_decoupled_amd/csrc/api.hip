@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/mla.h"
 #include "kernels.hpp"
 
@@ -264,11 +266,53 @@ size_t mla_decode_step_workspace_size(const mla_config* cfg, int32_t batch, int3
          ((size_t)batch + (size_t)batch * n_q) * sizeof(int32_t);
 }
 
-mla_status mla_decode_step(const mla_config* cfg, int32_t batch, int32_t n_q, const void* c_new, const void* k_rope_new,
-                           const void* q_nope, const void* q_rope, const void* w_uk, const void* w_uv, void* cache,
-                           const int64_t* seq_off, const int32_t* seq_len, int32_t max_seq_len, int32_t n_splits,
-                           void* workspace, size_t workspace_bytes, void* q_packed, float* z, float* lse, void* o,
-                           void* stream) {
+}  // extern "C"
+
+namespace {
+
+// ---- Scratch of mla_decode_step_noalloc, for callers that cannot allocate (graph capture, tight
+// serving loops). One array per GPU the library runs on, held until the process ends. In host code
+// `scratch` is only a stand-in for the symbol, not a device address: the device address of each
+// GPU's copy comes from hipGetSymbolAddress, taken once per device with that device current, and
+// only that address is ever passed to a kernel.
+constexpr size_t kNoallocScratchBytes = (size_t)MLA_NOALLOC_SCRATCH_BYTES;
+constexpr int kNoallocMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kNoallocMaxDevices] = {};
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+namespace {
+
+// device address of the current device's scratch array (resolved on the first call per device)
+mla_status noalloc_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return from_hip(e, "hipGetDevice");
+  if (dev < 0 || dev >= kNoallocMaxDevices)
+    return fail(MLA_ERR_UNSUPPORTED, "device %d: the scratch covers devices 0 .. %d", dev, kNoallocMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return from_hip(e, "hipGetSymbolAddress(scratch)");
+    if (p == nullptr) return fail(MLA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MLA_OK;
+}
+
+// The body of mla_decode_step. With noalloc, the workspace is the library's own scratch array of
+// workspace_bytes (its fixed size): a plan that needs more is rejected instead of reported as a
+// short workspace.
+mla_status decode_step_impl(const mla_config* cfg, int32_t batch, int32_t n_q, const void* c_new,
+                            const void* k_rope_new, const void* q_nope, const void* q_rope, const void* w_uk,
+                            const void* w_uv, void* cache, const int64_t* seq_off, const int32_t* seq_len,
+                            int32_t max_seq_len, int32_t n_splits, void* workspace, size_t workspace_bytes,
+                            void* q_packed, float* z, float* lse, void* o, void* stream, bool noalloc) {
   mla::LayerDims L;
   mla_status s = check_cfg(cfg, &L);
   if (s != MLA_OK) return s;
@@ -287,6 +331,13 @@ mla_status mla_decode_step(const mla_config* cfg, int32_t batch, int32_t n_q, co
   if (s != MLA_OK) return s;
   const size_t attn_bytes = round_up256(attn_workspace_bytes(L, batch, n_q, plan, fast));
   const size_t need = attn_bytes + ((size_t)batch + rows) * sizeof(int32_t);
+  if (noalloc) {
+    if (need > workspace_bytes)
+      return fail(MLA_ERR_UNSUPPORTED, "this step needs %zu bytes of scratch, more than the %zu bytes the library holds",
+                  need, workspace_bytes);
+    s = noalloc_scratch(&workspace);
+    if (s != MLA_OK) return s;
+  }
   if (workspace == nullptr || workspace_bytes < need)
     return fail(MLA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu%s", need, workspace_bytes,
                 workspace ? "" : " (NULL)");
@@ -319,6 +370,29 @@ mla_status mla_decode_step(const mla_config* cfg, int32_t batch, int32_t n_q, co
   e = deferred ? mla::launch_merge_out_proj(L, rows, plan, workspace, w_uv, z, lse, o, st)
                : out_proj_dispatch(cfg, L, rows, z, w_uv, o, st);
   return from_hip(e, "mla_decode_step output projection launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_decode_step(const mla_config* cfg, int32_t batch, int32_t n_q, const void* c_new, const void* k_rope_new,
+                           const void* q_nope, const void* q_rope, const void* w_uk, const void* w_uv, void* cache,
+                           const int64_t* seq_off, const int32_t* seq_len, int32_t max_seq_len, int32_t n_splits,
+                           void* workspace, size_t workspace_bytes, void* q_packed, float* z, float* lse, void* o,
+                           void* stream) {
+  return decode_step_impl(cfg, batch, n_q, c_new, k_rope_new, q_nope, q_rope, w_uk, w_uv, cache, seq_off, seq_len,
+                          max_seq_len, n_splits, workspace, workspace_bytes, q_packed, z, lse, o, stream, false);
+}
+
+mla_status mla_decode_step_noalloc(const mla_config* cfg, int32_t batch, int32_t n_q, const void* c_new,
+                                   const void* k_rope_new, const void* q_nope, const void* q_rope, const void* w_uk,
+                                   const void* w_uv, void* cache, const int64_t* seq_off, const int32_t* seq_len,
+                                   int32_t max_seq_len, int32_t n_splits, void* q_packed, float* z, float* lse,
+                                   void* o, void* stream) {
+  // the scratch is resolved inside, once every argument and the plan's size have been checked
+  return decode_step_impl(cfg, batch, n_q, c_new, k_rope_new, q_nope, q_rope, w_uk, w_uv, cache, seq_off, seq_len,
+                          max_seq_len, n_splits, nullptr, kNoallocScratchBytes, q_packed, z, lse, o, stream, true);
 }
 
 size_t mla_project_workspace_size(const mla_config* cfg, int32_t n_rows, int32_t d_model, int32_t d_q) {

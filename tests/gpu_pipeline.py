@@ -104,8 +104,9 @@ def run_pipeline(hi: HostInputs, n_splits: int = 0, scale: Optional[float] = Non
 
 
 def run_step(hi: HostInputs, n_splits: int = 0, scale: Optional[float] = None, lib_cfg=None,
-             max_len: Optional[int] = None) -> DeviceRun:
-    """The same history and step as run_pipeline, the step as one mla_decode_step call."""
+             max_len: Optional[int] = None, noalloc: bool = False) -> DeviceRun:
+    """The same history and step as run_pipeline, the step as one mla_decode_step call (or, with
+    noalloc, one mla_decode_step_noalloc call, which brings its own scratch)."""
     cfg = hi.cfg
     lc = lib_config(cfg, scale) if lib_cfg is None else lib_cfg
     dt = mla.storage_dtype(lc)
@@ -129,11 +130,16 @@ def run_step(hi: HostInputs, n_splits: int = 0, scale: Optional[float] = None, l
     lse = torch.empty((B, n_q, H), dtype=torch.float32, device="cuda")
     o = torch.empty((R, H, cfg.d_v), dtype=dt, device="cuda")
     max_len = int(lens.max()) if max_len is None else int(max_len)
-    ws = torch.empty(mla.mla_decode_step_workspace_size(lc, B, n_q, max_len, n_splits), dtype=torch.uint8,
-                     device="cuda")
-    mla.mla_decode_step(lc, c_new, k_new, tdev(hi.q_nope.reshape(R, H, cfg.d_nope), dt),
-                        tdev(hi.q_rope.reshape(R, H, cfg.d_rope), dt), tdev(hi.w_uk, dt), tdev(hi.w_uv, dt), cache,
-                        seq_off, seq_len, max_len, q_packed, z, o, lse=lse, n_splits=n_splits, workspace=ws)
+    qn, qr = tdev(hi.q_nope.reshape(R, H, cfg.d_nope), dt), tdev(hi.q_rope.reshape(R, H, cfg.d_rope), dt)
+    wuk, wuv = tdev(hi.w_uk, dt), tdev(hi.w_uv, dt)
+    if noalloc:
+        mla.mla_decode_step_noalloc(lc, c_new, k_new, qn, qr, wuk, wuv, cache, seq_off, seq_len, max_len, q_packed, z,
+                                    o, lse=lse, n_splits=n_splits)
+    else:
+        ws = torch.empty(mla.mla_decode_step_workspace_size(lc, B, n_q, max_len, n_splits), dtype=torch.uint8,
+                         device="cuda")
+        mla.mla_decode_step(lc, c_new, k_new, qn, qr, wuk, wuv, cache, seq_off, seq_len, max_len, q_packed, z, o,
+                            lse=lse, n_splits=n_splits, workspace=ws)
     torch.cuda.synchronize()
     return DeviceRun(cache, seq_off, seq_len, q_packed.view(B, n_q, H, cfg.row), z, lse, o.view(B, n_q, H, cfg.d_v))
 

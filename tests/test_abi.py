@@ -296,3 +296,25 @@ def test_ceilings_library_exports_and_validation():
     assert C.lib.mla_ceiling_lds(0, 256, 10, None, FAKE, None) == 1
     assert C.lib.mla_ceiling_lds(2, 256, 10, FAKE, FAKE, None) == 2
 
+
+def test_decode_step_noalloc_arguments():
+    """The no-allocation step validates like mla_decode_step and rejects, before touching the GPU,
+    a plan whose workspace exceeds the library's scratch."""
+    c = cfg()
+    assert _lib.MLA_NOALLOC_SCRATCH_BYTES == 64 << 20
+
+    def call(c, batch=1, n_q=1, max_len=4097, n_splits=0, c_new=FAKE, o=FAKE):
+        return lib.mla_decode_step_noalloc(c, batch, n_q, c_new, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                           max_len, n_splits, FAKE, FAKE, None, o, None)
+
+    assert call(cfg(reserved=1)) == MLA_ERR_INVALID_ARG
+    assert call(c, c_new=None) == MLA_ERR_INVALID_ARG
+    assert call(c, o=None) == MLA_ERR_INVALID_ARG
+    assert call(c, n_q=8, max_len=4) == MLA_ERR_INVALID_ARG
+    assert call(c, n_splits=999) == MLA_ERR_INVALID_ARG
+    assert call(c, batch=0) == MLA_OK
+    # 16 rows x 256 chunks of fp32 partials: far more than the scratch holds
+    need = lib.mla_decode_step_workspace_size(c, 16, 1, 65536, 256)
+    assert need > _lib.MLA_NOALLOC_SCRATCH_BYTES
+    assert call(c, batch=16, max_len=65536, n_splits=256) == MLA_ERR_UNSUPPORTED
+    assert b"scratch" in lib.mla_last_error()
