@@ -751,6 +751,57 @@ def mfma_peak(args):
                     # the kernel's wall time at the measured clock, per MFMA issued by one SIMD
                     "cycles_per_mfma_per_simd": round(ms * 1e-3 * ghz * 1e9 / per_simd, 2),
                     "ms": round(ms, 3), "median_wave_loop_us": round(us, 1)})
+    # one dependent chain per wave in asm: the accumulator in VGPRs or AGPRs, alone or fed by one
+    # ds_read_b128 per MFMA (the attention kernel's score chain)
+    for variant, name, per_iter in ((100, "chain_vgpr_acc", 8), (101, "chain_agpr_acc", 8),
+                                    (102, "chain_vgpr_acc_lds_fed", 8), (103, "chain_agpr_acc_lds_fed", 8),
+                                    (104, "chain_lds_fed_waits_batched", 12), (105, "chain_one_valu_per_mfma", 8),
+                                    (106, "chain_fed_by_transposed_reads", 8), (107, "two_accumulators_lds_fed", 8),
+                                    (108, "four_accumulators_lds_fed", 8)):
+        waves = n_wg * 4
+        ops = (torch.randn((waves * 64 * 16,), generator=gen, device=dev).to(torch.bfloat16)
+               .view(torch.int32).contiguous())
+        stamps = torch.zeros((waves * 4,), dtype=torch.int64, device=dev)
+        sink = torch.zeros((waves * 64,), dtype=torch.float32, device=dev)
+        iters = 20000
+        C.mfma(1, variant, n_wg, 100, ops, stamps, sink, stream.cuda_stream)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        C.mfma(1, variant, n_wg, iters, ops, stamps, sink, stream.cuda_stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        ghz, cyc, us = _clock_ghz(stamps)
+        per_simd = iters * per_iter
+        flops = waves * per_simd * 32768.0
+        res.append({"variant": name, "waves_per_simd": 1, "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                    "clock_ghz": round(ghz, 3), "cycles_per_mfma_per_simd": round(cyc / per_simd, 2),
+                    "ms": round(ms, 3)})
+    # the same chains with two waves per SIMD (two 4-wave workgroups per CU)
+    for variant, name in ((101, "chain_agpr_acc"), (103, "chain_agpr_acc_lds_fed"), (105, "chain_one_valu_per_mfma"),
+                          (106, "chain_fed_by_transposed_reads")):
+        n2 = 2 * n_wg
+        waves = n2 * 4
+        ops = (torch.randn((waves * 64 * 16,), generator=gen, device=dev).to(torch.bfloat16)
+               .view(torch.int32).contiguous())
+        stamps = torch.zeros((waves * 4,), dtype=torch.int64, device=dev)
+        sink = torch.zeros((waves * 64,), dtype=torch.float32, device=dev)
+        iters = 20000
+        C.mfma(2, variant, n2, 100, ops, stamps, sink, stream.cuda_stream)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        C.mfma(2, variant, n2, iters, ops, stamps, sink, stream.cuda_stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        ghz, cyc, us = _clock_ghz(stamps)
+        per_simd = iters * 8 * 2
+        flops = waves * iters * 8 * 32768.0
+        res.append({"variant": name, "waves_per_simd": 2, "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                    "clock_ghz": round(ghz, 3),
+                    "cycles_per_mfma_per_simd": round(ms * 1e-3 * ghz * 1e9 / per_simd, 2), "ms": round(ms, 3)})
     print(json.dumps({"mfma_peak": res, "instruction": "v_mfma_f32_32x32x16_bf16", "workgroups": n_wg,
                       "note": "32 cycles per MFMA per SIMD is the dense peak (1024 flops/cycle/SIMD)"}), flush=True)
 

@@ -24,7 +24,13 @@ extern "C" {
 /*
  * mla_ceiling_mfma — chip-wide v_mfma_f32_32x32x16_bf16 issue.
  *  waves_per_simd  1 or 2 (workgroups of 4 or 8 waves, one workgroup per CU)
- *  n_acc           independent accumulators per wave: 1, 4 or 8 at one wave per SIMD, 4 or 8 at two
+ *  n_acc           independent accumulators per wave: 1, 4 or 8 at one wave per SIMD, 4 or 8 at two;
+ *                  or, at one wave per SIMD, one dependent chain written in asm: 100 accumulating in
+ *                  VGPRs, 101 in AGPRs, 102 / 103 the same with one ds_read_b128 operand per MFMA,
+ *                  104 LDS-fed with one wait per four MFMAs, 105 one VALU op between MFMAs, 106 each
+ *                  MFMA's operand from two ds_read_b64_tr_b16, 107 / 108 LDS-fed over two / four
+ *                  independent accumulators taken in turn (an iteration issues 8 MFMAs, 12 for 104);
+ *                  with waves_per_simd 2, chains 101, 103, 105 and 106 in two 4-wave workgroups per CU
  *  n_workgroups    workgroups launched (256 = one per CU)
  *  iters           loop iterations; each issues 4 * n_acc MFMAs of 32x32x16 (32768 flops each)
  *  operands        uint32 [n_workgroups * 4 * waves_per_simd * 64 * 8]: per lane the two bf16x8 operands

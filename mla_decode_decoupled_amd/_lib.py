@@ -11,7 +11,9 @@ import ctypes
 import os
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG_DIR, "libmla.so")
+# MLA_LIB_PATH selects another build of the same library (the host-sanitized libmla_asan.so, for the
+# sanitizer run of the C-ABI checks); by default the in-tree libmla.so
+LIB_PATH = os.environ.get("MLA_LIB_PATH") or os.path.join(PKG_DIR, "libmla.so")
 
 MLA_OK = 0
 MLA_ERR_INVALID_ARG = 1

@@ -1,6 +1,6 @@
 """Build libmla.so in-tree with hipcc for gfx950.
 
-Usage: python mla_decode_decoupled_amd/build.py [--debug]
+Usage: python mla_decode_decoupled_amd/build.py [--debug] [--sanitize]
 (run by path: importing the package first would load the library being replaced)
 """
 
@@ -18,6 +18,11 @@ SOURCES = ["api.hip", "generic.hip", "decode_fast.hip", "proj_fast.hip", "proj_g
 # the ceiling microbenchmarks (MFMA issue, HBM streaming) are a library of their own
 CEIL_LIB_PATH = os.path.join(PKG_DIR, "libmla_ceilings.so")
 CEIL_SOURCES = ["ceilings.hip"]
+# a copy of libmla whose host code (argument checks, planning, launch set-up) runs under AddressSanitizer
+# and UndefinedBehaviorSanitizer; the device code is built as usual. Loaded only by the CPU test that
+# runs the C-ABI checks against it (tests/test_abi_sanitized.py), with the sanitizer runtime preloaded.
+ASAN_LIB_PATH = os.path.join(PKG_DIR, "libmla_asan.so")
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-Xarch_host", "-fno-omit-frame-pointer", "-shared-libasan"]
 
 # Packed-FP32 instructions (v_pk_*_f32) are switched off for every device pass: the compiler
 # otherwise forms them from plain float code, and the kernels are validated without them.
@@ -40,16 +45,28 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libmla)")
 
 
-def build(debug: bool = False, verbose: bool = False) -> str:
+def build(debug: bool = False, verbose: bool = False, sanitize: bool = False) -> str:
+    """Build libmla.so and libmla_ceilings.so; with sanitize, also the host-sanitized libmla_asan.so."""
     _build_one(SOURCES, LIB_PATH, debug, verbose)
     _build_one(CEIL_SOURCES, CEIL_LIB_PATH, debug, verbose)
+    if sanitize:
+        _build_one(SOURCES, ASAN_LIB_PATH, debug, verbose, SANITIZE_FLAGS)
     return LIB_PATH
 
 
-def _build_one(sources, lib_path: str, debug: bool, verbose: bool) -> str:
+def asan_runtime() -> str:
+    """Path of the compiler's shared AddressSanitizer runtime (preloaded for libmla_asan.so)."""
+    res = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = res.stdout.strip()
+    if not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("the compiler's shared AddressSanitizer runtime was not found")
+    return path
+
+
+def _build_one(sources, lib_path: str, debug: bool, verbose: bool, extra=()) -> str:
     srcs = [os.path.join(CSRC, s) for s in sources]
     tmp = lib_path + ".tmp"
-    cmd = [hipcc(), *HIP_FLAGS, "-I", os.path.join(PKG_DIR, os.pardir, "include"), "-o", tmp, *srcs]
+    cmd = [hipcc(), *HIP_FLAGS, *extra, "-I", os.path.join(PKG_DIR, os.pardir, "include"), "-o", tmp, *srcs]
     if debug:
         cmd = [c for c in cmd if c != "-O3"] + ["-O1", "-g"]
     if verbose:
@@ -67,5 +84,5 @@ def _build_one(sources, lib_path: str, debug: bool, verbose: bool) -> str:
 
 
 if __name__ == "__main__":
-    path = build(debug="--debug" in sys.argv, verbose=True)
+    path = build(debug="--debug" in sys.argv, verbose=True, sanitize="--sanitize" in sys.argv)
     print(path)

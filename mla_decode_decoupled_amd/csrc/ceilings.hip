@@ -198,6 +198,180 @@ __global__ void __launch_bounds__(256) lds_read(int iters, unsigned int* __restr
   if (x == 0x9e3779b9u) sink[blockIdx.x] = x;
 }
 
+// (d) one wave per SIMD, one dependent chain of v_mfma_f32_32x32x16_bf16, in inline asm so that the
+// accumulator's register file is fixed: VARIANT 0 accumulates in VGPRs, 1 in AGPRs; 2 and 3 do the
+// same with one ds_read_b128 (a fresh 16-byte operand per lane, conflict-free) issued before each
+// MFMA and waited for four MFMAs later, the way the attention kernel feeds its score chain.
+template <int VARIANT>
+__global__ void __launch_bounds__(256) mfma_chain(int iters, const uint32_t* __restrict__ operands,
+                                                  unsigned long long* __restrict__ stamps, float* __restrict__ sink) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int gw = blockIdx.x * 4 + wave;
+  for (int i = threadIdx.x; i < 16384 / 4; i += 256) reinterpret_cast<uint32_t*>(lds)[i] = operands[i & 511];
+  __syncthreads();
+  uint32_t ua[4], ub[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ua[i] = operands[(gw * 64 + lane) * 8 + i];
+    ub[i] = operands[(gw * 64 + lane) * 8 + 4 + i];
+  }
+  const bf16x8 a = __builtin_bit_cast(bf16x8, ua), b = __builtin_bit_cast(bf16x8, ub);
+  const uint32_t la = (uint32_t)(uintptr_t)(lds + wave * 4096 + lane * 16);
+  f32x16 acc = f32x16{};
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+  for (int i = 0; i < iters; ++i) {
+    if (VARIANT == 0) {
+      asm volatile(
+          "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\t"
+          "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\t"
+          "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\t"
+          "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+          : "+v"(acc) : "v"(a), "v"(b));
+    } else if (VARIANT == 1) {
+      asm volatile(
+          "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\t"
+          "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\t"
+          "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\t"
+          "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+          : "+a"(acc) : "v"(a), "v"(b));
+    } else {
+      // ring of four operand slots: the read for MFMA k + 4 goes out right after MFMA k issues
+      typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+      u32x4v r0v, r1v, r2v, r3v;
+#define MLA_CHAIN_BODY(ACC)                                                                                  \
+      asm volatile(                                                                                         \
+          "ds_read_b128 %1, %7 offset:0\n\tds_read_b128 %2, %7 offset:1024\n\t"                             \
+          "ds_read_b128 %3, %7 offset:2048\n\tds_read_b128 %4, %7 offset:3072\n\t"                          \
+          "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %6, %0\n\tds_read_b128 %1, %7 offset:0\n\t" \
+          "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %0, %2, %6, %0\n\tds_read_b128 %2, %7 offset:1024\n\t" \
+          "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %0, %3, %6, %0\n\tds_read_b128 %3, %7 offset:2048\n\t" \
+          "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %0, %4, %6, %0\n\tds_read_b128 %4, %7 offset:3072\n\t" \
+          "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %6, %0\n\t"                              \
+          "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %0, %2, %6, %0\n\t"                              \
+          "s_waitcnt lgkmcnt(1)\n\tv_mfma_f32_32x32x16_bf16 %0, %3, %6, %0\n\t"                              \
+          "s_waitcnt lgkmcnt(0)\n\tv_mfma_f32_32x32x16_bf16 %0, %4, %6, %0"                                    \
+          : ACC(acc), "=&v"(r0v), "=&v"(r1v), "=&v"(r2v), "=&v"(r3v), "=&v"(r3v)                              \
+          : "v"(b), "v"(la)                                                                                   \
+          : "memory")
+      if (VARIANT == 2) {
+        MLA_CHAIN_BODY("+v");
+      } else if (VARIANT == 3) {
+        MLA_CHAIN_BODY("+a");
+      } else if (VARIANT == 4) {
+        // eight slots, the waits batched: one s_waitcnt per four MFMAs
+        u32x4v r4v, r5v, r6v, r7v;
+        asm volatile(
+            "ds_read_b128 %1, %9 offset:0\n\tds_read_b128 %2, %9 offset:1024\n\t"
+            "ds_read_b128 %3, %9 offset:2048\n\tds_read_b128 %4, %9 offset:3072\n\t"
+            "ds_read_b128 %5, %9 offset:0\n\tds_read_b128 %6, %9 offset:1024\n\t"
+            "ds_read_b128 %7, %9 offset:2048\n\tds_read_b128 %8, %9 offset:3072\n\t"
+            "s_waitcnt lgkmcnt(4)\n\t"
+            "v_mfma_f32_32x32x16_bf16 %0, %1, %10, %0\n\tv_mfma_f32_32x32x16_bf16 %0, %2, %10, %0\n\t"
+            "v_mfma_f32_32x32x16_bf16 %0, %3, %10, %0\n\tv_mfma_f32_32x32x16_bf16 %0, %4, %10, %0\n\t"
+            "ds_read_b128 %1, %9 offset:0\n\tds_read_b128 %2, %9 offset:1024\n\t"
+            "ds_read_b128 %3, %9 offset:2048\n\tds_read_b128 %4, %9 offset:3072\n\t"
+            "s_waitcnt lgkmcnt(4)\n\t"
+            "v_mfma_f32_32x32x16_bf16 %0, %5, %10, %0\n\tv_mfma_f32_32x32x16_bf16 %0, %6, %10, %0\n\t"
+            "v_mfma_f32_32x32x16_bf16 %0, %7, %10, %0\n\tv_mfma_f32_32x32x16_bf16 %0, %8, %10, %0\n\t"
+            "s_waitcnt lgkmcnt(0)\n\t"
+            "v_mfma_f32_32x32x16_bf16 %0, %1, %10, %0\n\tv_mfma_f32_32x32x16_bf16 %0, %2, %10, %0\n\t"
+            "v_mfma_f32_32x32x16_bf16 %0, %3, %10, %0\n\tv_mfma_f32_32x32x16_bf16 %0, %4, %10, %0"
+            : "+a"(acc), "=&v"(r0v), "=&v"(r1v), "=&v"(r2v), "=&v"(r3v), "=&v"(r4v), "=&v"(r5v), "=&v"(r6v), "=&v"(r7v)
+            : "v"(la), "v"(b)
+            : "memory");
+      } else if (VARIANT == 5) {
+        // no LDS: one independent VALU op between consecutive MFMAs
+        float t0 = 0.0f;
+        asm volatile(
+            "v_mfma_f32_32x32x16_bf16 %0, %2, %3, %0\n\tv_add_f32 %1, 1.0, %1\n\t"
+            "v_mfma_f32_32x32x16_bf16 %0, %2, %3, %0\n\tv_add_f32 %1, 1.0, %1\n\t"
+            "v_mfma_f32_32x32x16_bf16 %0, %2, %3, %0\n\tv_add_f32 %1, 1.0, %1\n\t"
+            "v_mfma_f32_32x32x16_bf16 %0, %2, %3, %0\n\tv_add_f32 %1, 1.0, %1\n\t"
+            "v_mfma_f32_32x32x16_bf16 %0, %2, %3, %0\n\tv_add_f32 %1, 1.0, %1\n\t"
+            "v_mfma_f32_32x32x16_bf16 %0, %2, %3, %0\n\tv_add_f32 %1, 1.0, %1\n\t"
+            "v_mfma_f32_32x32x16_bf16 %0, %2, %3, %0\n\tv_add_f32 %1, 1.0, %1\n\t"
+            "v_mfma_f32_32x32x16_bf16 %0, %2, %3, %0\n\tv_add_f32 %1, 1.0, %1"
+            : "+a"(acc), "+v"(t0) : "v"(a), "v"(b));
+        if (t0 == 12345.0f) acc[0] += 1.0f;
+      } else if (VARIANT == 7 || VARIANT == 8) {
+        // two (7) or four (8) independent accumulators taken in turn, one ds_read_b128 per MFMA
+        // (the second accumulator lives in v[56:71] / a[16:31], named in the asm)
+        if (VARIANT == 7) {
+          asm volatile(
+              "ds_read_b128 v[40:43], %1 offset:0\n\tds_read_b128 v[44:47], %1 offset:1024\n\t"
+              "ds_read_b128 v[48:51], %1 offset:2048\n\tds_read_b128 v[52:55], %1 offset:3072\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %0, v[40:43], %2, %0\n\tds_read_b128 v[40:43], %1 offset:0\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 a[16:31], v[44:47], %2, a[16:31]\n\tds_read_b128 v[44:47], %1 offset:1024\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %0, v[48:51], %2, %0\n\tds_read_b128 v[48:51], %1 offset:2048\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 a[16:31], v[52:55], %2, a[16:31]\n\tds_read_b128 v[52:55], %1 offset:3072\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %0, v[40:43], %2, %0\n\t"
+              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 a[16:31], v[44:47], %2, a[16:31]\n\t"
+              "s_waitcnt lgkmcnt(1)\n\tv_mfma_f32_32x32x16_bf16 %0, v[48:51], %2, %0\n\t"
+              "s_waitcnt lgkmcnt(0)\n\tv_mfma_f32_32x32x16_bf16 a[16:31], v[52:55], %2, a[16:31]"
+              : "+a"(acc) : "v"(la), "v"(b)
+              : "memory", "v40", "v41", "v42", "v43", "v44", "v45", "v46", "v47", "v48", "v49", "v50", "v51", "v52",
+                "v53", "v54", "v55", "a16", "a17", "a18", "a19", "a20", "a21", "a22", "a23", "a24", "a25", "a26", "a27",
+                "a28", "a29", "a30", "a31");
+        } else {
+          asm volatile(
+              "ds_read_b128 v[40:43], %1 offset:0\n\tds_read_b128 v[44:47], %1 offset:1024\n\t"
+              "ds_read_b128 v[48:51], %1 offset:2048\n\tds_read_b128 v[52:55], %1 offset:3072\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %0, v[40:43], %2, %0\n\tds_read_b128 v[40:43], %1 offset:0\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 a[16:31], v[44:47], %2, a[16:31]\n\tds_read_b128 v[44:47], %1 offset:1024\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 a[32:47], v[48:51], %2, a[32:47]\n\tds_read_b128 v[48:51], %1 offset:2048\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 a[48:63], v[52:55], %2, a[48:63]\n\tds_read_b128 v[52:55], %1 offset:3072\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %0, v[40:43], %2, %0\n\t"
+              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 a[16:31], v[44:47], %2, a[16:31]\n\t"
+              "s_waitcnt lgkmcnt(1)\n\tv_mfma_f32_32x32x16_bf16 a[32:47], v[48:51], %2, a[32:47]\n\t"
+              "s_waitcnt lgkmcnt(0)\n\tv_mfma_f32_32x32x16_bf16 a[48:63], v[52:55], %2, a[48:63]"
+              : "+a"(acc) : "v"(la), "v"(b)
+              : "memory", "v40", "v41", "v42", "v43", "v44", "v45", "v46", "v47", "v48", "v49", "v50", "v51", "v52",
+                "v53", "v54", "v55", "a16", "a17", "a18", "a19", "a20", "a21", "a22", "a23", "a24", "a25", "a26", "a27",
+                "a28", "a29", "a30", "a31", "a32", "a33", "a34", "a35", "a36", "a37", "a38", "a39", "a40", "a41", "a42",
+                "a43", "a44", "a45", "a46", "a47", "a48", "a49", "a50", "a51", "a52", "a53", "a54", "a55", "a56", "a57",
+                "a58", "a59", "a60", "a61", "a62", "a63");
+        }
+      } else {
+        // P.V feeding: two ds_read_b64_tr_b16 (one A operand) per MFMA, ring of four operands in
+        // v[40:55] (named in the asm, declared clobbered)
+        asm volatile(
+            "ds_read_b64_tr_b16 v[40:41], %1 offset:0\n\tds_read_b64_tr_b16 v[42:43], %1 offset:512\n\t"
+            "ds_read_b64_tr_b16 v[44:45], %1 offset:1024\n\tds_read_b64_tr_b16 v[46:47], %1 offset:1536\n\t"
+            "ds_read_b64_tr_b16 v[48:49], %1 offset:2048\n\tds_read_b64_tr_b16 v[50:51], %1 offset:2560\n\t"
+            "ds_read_b64_tr_b16 v[52:53], %1 offset:3072\n\tds_read_b64_tr_b16 v[54:55], %1 offset:3584\n\t"
+            "s_waitcnt lgkmcnt(6)\n\tv_mfma_f32_32x32x16_bf16 %0, v[40:43], %2, %0\n\t"
+            "ds_read_b64_tr_b16 v[40:41], %1 offset:0\n\tds_read_b64_tr_b16 v[42:43], %1 offset:512\n\t"
+            "s_waitcnt lgkmcnt(6)\n\tv_mfma_f32_32x32x16_bf16 %0, v[44:47], %2, %0\n\t"
+            "ds_read_b64_tr_b16 v[44:45], %1 offset:1024\n\tds_read_b64_tr_b16 v[46:47], %1 offset:1536\n\t"
+            "s_waitcnt lgkmcnt(6)\n\tv_mfma_f32_32x32x16_bf16 %0, v[48:51], %2, %0\n\t"
+            "ds_read_b64_tr_b16 v[48:49], %1 offset:2048\n\tds_read_b64_tr_b16 v[50:51], %1 offset:2560\n\t"
+            "s_waitcnt lgkmcnt(6)\n\tv_mfma_f32_32x32x16_bf16 %0, v[52:55], %2, %0\n\t"
+            "ds_read_b64_tr_b16 v[52:53], %1 offset:3072\n\tds_read_b64_tr_b16 v[54:55], %1 offset:3584\n\t"
+            "s_waitcnt lgkmcnt(6)\n\tv_mfma_f32_32x32x16_bf16 %0, v[40:43], %2, %0\n\t"
+            "s_waitcnt lgkmcnt(4)\n\tv_mfma_f32_32x32x16_bf16 %0, v[44:47], %2, %0\n\t"
+            "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %0, v[48:51], %2, %0\n\t"
+            "s_waitcnt lgkmcnt(0)\n\tv_mfma_f32_32x32x16_bf16 %0, v[52:55], %2, %0"
+            : "+a"(acc)
+            : "v"(la - (uint32_t)(lane * 8)), "v"(b)
+            : "memory", "v40", "v41", "v42", "v43", "v44", "v45", "v46", "v47", "v48", "v49", "v50", "v51", "v52",
+              "v53", "v54", "v55");
+      }
+#undef MLA_CHAIN_BODY
+      (void)a;
+    }
+  }
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+  float s = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) s += acc[e];
+  if (lane == 0) {
+    stamp(stamps, 2 * gw, t0, r0);
+    stamp(stamps, 2 * gw + 1, t1, r1);
+  }
+  sink[gw * 64 + lane] = s;
+}
+
 template <int WAVES, int NACC>
 hipError_t launch_mfma(int n_wg, int iters, const uint32_t* ops, unsigned long long* stamps, float* sink,
                        hipStream_t st) {
@@ -224,7 +398,48 @@ int mla_ceiling_mfma(int waves_per_simd, int n_acc, int n_workgroups, int iters,
   else if (waves_per_simd == 1 && n_acc == 1) e = launch_mfma<4, 1>(n_workgroups, iters, ops, stamps, sink, st);
   else if (waves_per_simd == 2 && n_acc == 4) e = launch_mfma<8, 4>(n_workgroups, iters, ops, stamps, sink, st);
   else if (waves_per_simd == 2 && n_acc == 8) e = launch_mfma<8, 8>(n_workgroups, iters, ops, stamps, sink, st);
-  else return 2;
+  else if (waves_per_simd == 2 && n_acc >= 100 && n_acc <= 108) {
+    // the same single-wave chains with two workgroups of 4 waves per CU (two waves per SIMD): the
+    // host passes twice as many workgroups
+    constexpr int kLds = 20 * 1024;
+    const void* fns[9] = {(const void*)mfma_chain<0>, (const void*)mfma_chain<1>, (const void*)mfma_chain<2>,
+                          (const void*)mfma_chain<3>, (const void*)mfma_chain<4>, (const void*)mfma_chain<5>,
+                          (const void*)mfma_chain<6>, (const void*)mfma_chain<7>, (const void*)mfma_chain<8>};
+    e = hipFuncSetAttribute(fns[n_acc - 100], hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+    if (e == hipSuccess) {
+      switch (n_acc) {
+        case 101: hipLaunchKernelGGL(mfma_chain<1>, dim3(n_workgroups), dim3(256), kLds, st, iters, ops, stamps, sink); break;
+        case 103: hipLaunchKernelGGL(mfma_chain<3>, dim3(n_workgroups), dim3(256), kLds, st, iters, ops, stamps, sink); break;
+        case 105: hipLaunchKernelGGL(mfma_chain<5>, dim3(n_workgroups), dim3(256), kLds, st, iters, ops, stamps, sink); break;
+        case 106: hipLaunchKernelGGL(mfma_chain<6>, dim3(n_workgroups), dim3(256), kLds, st, iters, ops, stamps, sink); break;
+        default: return 2;
+      }
+      e = hipGetLastError();
+    }
+  } else if (waves_per_simd == 1 && n_acc >= 100 && n_acc <= 108) {
+    // single-chain variants (see mfma_chain): 100 VGPR accumulator, 101 AGPR, 102/103 the same fed by LDS,
+    // 104 LDS-fed with batched waits, 105 one VALU op per MFMA, 106 fed by transposed reads, 107 / 108
+    // LDS-fed over two / four independent accumulators
+    constexpr int kLds = 96 * 1024;
+    const void* fns[9] = {(const void*)mfma_chain<0>, (const void*)mfma_chain<1>, (const void*)mfma_chain<2>,
+                          (const void*)mfma_chain<3>, (const void*)mfma_chain<4>, (const void*)mfma_chain<5>,
+                          (const void*)mfma_chain<6>, (const void*)mfma_chain<7>, (const void*)mfma_chain<8>};
+    e = hipFuncSetAttribute(fns[n_acc - 100], hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+    if (e == hipSuccess) {
+      switch (n_acc) {
+        case 100: hipLaunchKernelGGL(mfma_chain<0>, dim3(n_workgroups), dim3(256), kLds, st, iters, ops, stamps, sink); break;
+        case 101: hipLaunchKernelGGL(mfma_chain<1>, dim3(n_workgroups), dim3(256), kLds, st, iters, ops, stamps, sink); break;
+        case 102: hipLaunchKernelGGL(mfma_chain<2>, dim3(n_workgroups), dim3(256), kLds, st, iters, ops, stamps, sink); break;
+        case 103: hipLaunchKernelGGL(mfma_chain<3>, dim3(n_workgroups), dim3(256), kLds, st, iters, ops, stamps, sink); break;
+        case 104: hipLaunchKernelGGL(mfma_chain<4>, dim3(n_workgroups), dim3(256), kLds, st, iters, ops, stamps, sink); break;
+        case 105: hipLaunchKernelGGL(mfma_chain<5>, dim3(n_workgroups), dim3(256), kLds, st, iters, ops, stamps, sink); break;
+        case 107: hipLaunchKernelGGL(mfma_chain<7>, dim3(n_workgroups), dim3(256), kLds, st, iters, ops, stamps, sink); break;
+        case 108: hipLaunchKernelGGL(mfma_chain<8>, dim3(n_workgroups), dim3(256), kLds, st, iters, ops, stamps, sink); break;
+        default: hipLaunchKernelGGL(mfma_chain<6>, dim3(n_workgroups), dim3(256), kLds, st, iters, ops, stamps, sink); break;
+      }
+      e = hipGetLastError();
+    }
+  } else return 2;
   return e == hipSuccess ? 0 : 4;
 }
 
