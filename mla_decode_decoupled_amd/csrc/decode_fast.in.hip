@@ -37,6 +37,7 @@
 //   a[0:255]    O^T accumulator, 16 blocks of 32 latent columns x 32 heads, fp32
 //   v[128:255]  latent queries, 32 MFMA B fragments (pinned by physical-register constraints)
 //   v[112:127]  score accumulator S^T, softmax in place
+//   v[64:79]    position part of the queries (4 MFMA B fragments)
 //   v[80:87]    P of the tile being accumulated (two B fragments of 16 keys), carried between
 //               the asm blocks as a pinned value
 //   v[88:111]   operand rings of the two MFMA phases
@@ -75,14 +76,20 @@ constexpr int ES_STRIDE = 256 + 4;      // floats per staged half output row (+ 
 static_assert(TILE_SLOTS % (WAVES * 64) == 0, "tile must split into whole DMA instructions");
 static_assert(ROW_CHUNKS % 8 == 0, "swizzle groups of 8 chunks");
 
-// LDS (160 KB, all of it): four tile buffers, then the position queries laid out chunk-major
-// ([8 chunks of 16 B][128 heads]) so that 16 heads reading the same chunk hit 16 bank groups.
-// The query staging before the loop and the output staging after it reuse the tile buffers;
-// the overflow flags sit in the last kilobyte of the tile area, clear of both stagings.
+// LDS (144 KB): four tile buffers. The query staging before the loop and the output staging after
+// it reuse them; the overflow flags sit in the last kilobyte of the tile area, clear of both
+// stagings. (The 64-dim position part of the queries stays in VGPRs, v[64:79].)
 struct Smem {
   unsigned char tile[NBUF][TILE_BYTES];
-  unsigned char qrope[DR * 2 / 16][H][16];
 };
+// The tile DMA sets M0 once per four 1 KB instructions and steps the LDS address with the
+// instruction's offset field (0, 1024, 2048, 3072), which moves the global address by the same
+// amount: the per-lane global offsets are biased by -1024 (it % 4), plus DMA_BIAS (taken off the
+// base pointer). The offset is an unsigned 32-bit VGPR, so it must stay non-negative for every
+// row it can name, row 0 included (the re-read rows of a tail tile all name one row, possibly
+// row 0): row * ROW_BYTES + 16 chunk >= 0 and DMA_BIAS >= 3072 make it at least DMA_BIAS - 3072.
+constexpr int DMA_BIAS = 4096;
+static_assert(DMA_BIAS >= 3 * 1024, "DMA offsets must stay non-negative for row 0, instruction offset 3072");
 constexpr int FLAGS_OFF = NBUF * TILE_BYTES - 1024;
 static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget");
 static_assert(H * QS_STRIDE <= FLAGS_OFF, "query staging must end before the flags");
@@ -367,25 +374,26 @@ __global__ void __launch_bounds__(256)
   for (int it = 0; it < DMA_PER_WAVE; ++it) {
     const int slot = w * SLOTS_PER_WAVE + it * 64 + lane;
     const int r = slot / ROW_CHUNKS, p = slot % ROW_CHUNKS;
-    dma_off[it] = r * ROW_BYTES + phys_chunk(p, r) * 16;
+    dma_off[it] = r * ROW_BYTES + phys_chunk(p, r) * 16 - (it % 4) * 1024 + DMA_BIAS;
   }
   auto tile_lds = [&](int tile) { return (uint32_t)(uintptr_t)MLA_LDS(unsigned char, sm.tile[tile % NBUF]); };
-  // DMA source of tile `tile` and this lane's nine offsets. Rows of a tail tile past the end
-  // re-read the last valid row (their scores are masked); a tile past the chunk reads qbytes.
+  // DMA source of tile `tile` (less DMA_BIAS) and this lane's nine offsets. Rows of a tail tile
+  // past the end re-read the last valid row (their scores are masked); a tile past the chunk
+  // reads qbytes.
   auto dma_plan = [&](int tile, uint32_t* o) -> const unsigned char* {
     const int key0 = j0 + tile * TILE;
 #pragma unroll
     for (int it = 0; it < DMA_PER_WAVE; ++it) o[it] = dma_off[it];
-    if (tile >= n_tiles) return qbytes;
+    if (tile >= n_tiles) return qbytes - DMA_BIAS;
     if (key0 + TILE > j1) {
       const int last = j1 - 1 - key0;
 #pragma unroll
       for (int it = 0; it < DMA_PER_WAVE; ++it) {
-        const int r = dma_off[it] / ROW_BYTES;
+        const int r = (w * SLOTS_PER_WAVE + it * 64 + lane) / ROW_CHUNKS;
         o[it] = dma_off[it] - (r > last ? r - last : 0) * ROW_BYTES;
       }
     }
-    return kv + (int64_t)key0 * ROW_BYTES;
+    return kv + (int64_t)key0 * ROW_BYTES - DMA_BIAS;
   };
   auto sgpr_ptr = [](const void* p) {
     const uint64_t sb = (uint64_t)(uintptr_t)p;
@@ -411,7 +419,7 @@ __global__ void __launch_bounds__(256)
   // direct global->LDS loads (8 whole cache lines each) into slots QS_STRIDE bytes apart (the
   // 16-byte pad puts the 16 heads of one LDS phase on 16 different bank groups), then reads its
   // fragments. The staging area is the tile buffers, free until the first tile DMA.
-  // Position part: 4 fragments per lane, kept in LDS and read by every score phase.
+  // Position part: 4 fragments per lane, loaded into v[64:79] for every score phase.
   const int qhead = w * 32 + l32;
   const bf16* qrow = q_packed + (rh0 + qhead) * ROW + 8 * g;
   const uint32_t qstage = (uint32_t)(uintptr_t)MLA_LDS(unsigned char, &sm.tile[0][0]) + w * 32 * QS_STRIDE;
@@ -420,9 +428,14 @@ __global__ void __launch_bounds__(256)
 #pragma unroll 4
     for (int i = 0; i < 32; ++i) dma16(qw + i * ROW_BYTES, __builtin_amdgcn_readfirstlane(qstage + i * QS_STRIDE));
   }
-#pragma unroll
-  for (int s = 0; s < DR / 16; ++s)   // chunk 2s + g of the position part, chunk-major layout
-    *reinterpret_cast<bf16x8*>(&sm.qrope[2 * s + g][qhead][0]) = *reinterpret_cast<const bf16x8*>(qrow + DC + 16 * s);
+  i32x4 qrp0, qrp1, qrp2, qrp3;   // position part, dims 16s + 8g .. +7 of head qhead
+  {
+    const i32x4* qp = reinterpret_cast<const i32x4*>(qrow + DC);
+    qrp0 = qp[0];
+    qrp1 = qp[2];
+    qrp2 = qp[4];
+    qrp3 = qp[6];
+  }
   wait_vmcnt_0();   // the staged rows are in
   v16i q0, q1, q2, q3, q4, q5, q6, q7;
   asm volatile(
@@ -472,7 +485,6 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) qk_off[s4] = key * ROW_BYTES + (((2 * s4 + g) ^ swz(key)) & 7) * 16;
   }
-  const uint32_t qr_addr = (uint32_t)(uintptr_t)MLA_LDS(unsigned char, &sm.qrope[g][qhead][0]);
   // values: transpose reads. lane = 16q + L; row = 16s + 8g + 4h + L/4; col = 32cb + 16(q&1) + 4(L&3)
   const int q16 = lane >> 4, L = lane & 15;
   uint32_t pv_off[2][2];  // [cb & 1][h]
@@ -500,7 +512,8 @@ __global__ void __launch_bounds__(256)
 @QK_ASM@
         : "=&{v[112:127]}"(sacc)
         : [k0] "v"(tb + qk_off[0]), [k1] "v"(tb + qk_off[1]), [k2] "v"(tb + qk_off[2]), [k3] "v"(tb + qk_off[3]),
-          [qr] "v"(qr_addr), "{v[128:143]}"(q0), "{v[144:159]}"(q1), "{v[160:175]}"(q2), "{v[176:191]}"(q3),
+          "{v[64:67]}"(qrp0), "{v[68:71]}"(qrp1), "{v[72:75]}"(qrp2), "{v[76:79]}"(qrp3),
+          "{v[128:143]}"(q0), "{v[144:159]}"(q1), "{v[160:175]}"(q2), "{v[176:191]}"(q3),
           "{v[192:207]}"(q4), "{v[208:223]}"(q5), "{v[224:239]}"(q6), "{v[240:255]}"(q7), "{v[80:87]}"(pfr),
           [b] "s"(sbase), [m] "s"(sdst), [o0] "v"(o[0]), [o1] "v"(o[1]), [o2] "v"(o[2]), [o3] "v"(o[3]),
           [o4] "v"(o[4]), [o5] "v"(o[5]), [o6] "v"(o[6]), [o7] "v"(o[7]), [o8] "v"(o[8])

@@ -37,17 +37,14 @@ class Ring:
 
 def qk():
     """Scores of one tile: 36 chained MFMAs (32 latent steps with the query in v[128:255], 4
-    position steps with the query chunks from LDS), the K chunks and position-query chunks
-    streamed through the six-slot ring, plus the nine DMA instructions of a later tile."""
+    position steps with the query's position part in v[64:79]), the K chunks streamed through the
+    six-slot ring, plus the nine DMA instructions of a later tile."""
     L = []
     ring = Ring(L)
     # operand loads in consumption order: (id, slot-use MFMA, instruction)
     loads = []
     for s in range(36):
         loads.append((("A", s), s, f"ds_read_b128 {{r}}, %[k{s % 4}] offset:{(s // 4) * 128}"))
-        if s >= 32:
-            u = s - 32
-            loads.append((("B", s), s, f"ds_read_b128 {{r}}, %[qr] offset:{u * 4096}"))
     nslot = len(RING)
     slot_user = [-1] * nslot          # MFMA that reads the slot's current content
     next_load = 0
@@ -65,25 +62,18 @@ def qk():
             next_load += 1
     fill(-1)
     for s in range(36):
-        need = [("A", s)] + ([("B", s)] if s >= 32 else [])
-        ring.wait(need)
+        ring.wait([("A", s)])
         a_reg = RING[ring.slot_of[("A", s)]]
         a = f"v[{a_reg}:{a_reg + 3}]"
         if s < 32:
             b = f"v[{128 + 4 * s}:{131 + 4 * s}]"
-        else:
-            b_reg = RING[ring.slot_of[("B", s)]]
-            b = f"v[{b_reg}:{b_reg + 3}]"
+        else:   # the position part of the query, held in v[64:79]
+            b = f"v[{64 + 4 * (s - 32)}:{67 + 4 * (s - 32)}]"
         c = "0" if s == 0 else "v[112:127]"
         L.append(f"v_mfma_f32_32x32x16_bf16 v[112:127], {a}, {b}, {c}")
         fill(s)
         if s % 4 == 1:  # one of the 9 DMA instructions of a later tile, every 4 MFMAs
-            it = s // 4
-            if it == 0:
-                L += ["s_mov_b32 m0, %[m]", "s_nop 0"]
-            else:
-                L += ["s_add_u32 m0, m0, 0x400", "s_nop 0"]
-            L.append(f"global_load_lds_dwordx4 %[o{it}], %[b]")
+            L += dma_instr(s // 4)
     assert next_load == len(loads)
     L += ["s_nop 7", "s_nop 7", "s_nop 3"]
     return L
@@ -161,12 +151,21 @@ def qload():
     return L + ["s_waitcnt lgkmcnt(0)"]
 
 
+def dma_instr(it):
+    """DMA instruction `it` (0..8) of a wave's share of a tile: 1 KB at LDS byte M0 + 1024 it. The
+    instruction's offset field moves both the global and the LDS address, so M0 is set once per
+    four instructions (the per-lane global offsets are biased by -1024 (it % 4) to match)."""
+    L = []
+    if it % 4 == 0:
+        L += ["s_mov_b32 m0, %[m]" if it == 0 else "s_add_u32 m0, m0, 0x1000", "s_nop 0"]
+    L.append(f"global_load_lds_dwordx4 %[o{it}], %[b] offset:{(it % 4) * 1024}")
+    return L
+
+
 def dma():
-    L = ["s_mov_b32 m0, %[m]", "s_nop 0"]
+    L = []
     for it in range(9):
-        L.append(f"global_load_lds_dwordx4 %[o{it}], %[b]")
-        if it < 8:
-            L += ["s_add_u32 m0, m0, 0x400", "s_nop 0"]
+        L += dma_instr(it)
     return L
 
 def emit(lines):
