@@ -1078,18 +1078,23 @@ __global__ void __launch_bounds__(256) attn_merge_frag(const bf16* __restrict__ 
 // Log-sum-exp merge of decode_attn_hsplit's head-major partials fused with the output
 // projection o = W_UV,i z ("从零理解 MLA", section "矩阵吸收", output side), for mla_decode_step:
 // the merge costs no launch of its own, and the weights stream in while the partials are read.
-// One (query row, head, half of the 128 outputs) per workgroup of 8 waves.
+// One (query row, head, slice of the 128 outputs) per workgroup of 8 waves; kMergeSlices slices.
 //   merge: the waves take the row's chunks round-robin (every chunk in one step); lane l reads
 //   latent columns 8l .. 8l+7 (one 1 KB load of bf16 per wave and chunk) and keeps a running
 //   maximum; the wave sums meet in LDS against the common maximum,
 //   z = sum_k 2^(m_k - M) O_k / sum_k 2^(m_k - M) l_k. A row computed as one chunk already has its
 //   final z, written by the attention kernel, and is read back.
-//   projection: wave w owns the 8 outputs 64 y + 8 w + j of half y; its lanes load
+//   projection: wave w owns the OPW outputs (128 / kMergeSlices) y + OPW w + j of slice y, in
+//   groups of 8; its lanes load
 //   W_UV,i[v, 8l .. 8l+7] first, then dot them with z[8l .. 8l+7] and reduce across the wave exactly
-//   as out_proj_gemv does, so o is bitwise what out_proj_gemv makes of this z. Half 0 writes z
-//   and lse.
-// grid (H, 2, rows), 64 MERGE_WAVES threads.
+//   as out_proj_gemv does (one 8-output butterfly per group), so o is bitwise what out_proj_gemv
+//   makes of this z. Slice 0 writes z and lse. Every slice merges the partials again: one slice
+//   would read them once, but at one query row (DeepSeek-V3 shape, 4K keys, 43 chunks) the decode
+//   step measured 24.0 us with one slice against 22.5 us with two, the 256 workgroups hiding more
+//   latency than the second read of 5.6 MB costs.
+// grid (H, kMergeSlices, rows), 64 MERGE_WAVES threads.
 constexpr int MERGE_WAVES = 8;
+constexpr int kMergeSlices = 2;
 __global__ void __launch_bounds__(64 * MERGE_WAVES)
     merge_heads_out_proj(const bf16* __restrict__ part_acc, const float* __restrict__ part_ml,
                          const int2* __restrict__ row_chunks, const bf16* __restrict__ w_uv, float* __restrict__ z,
@@ -1097,17 +1102,20 @@ __global__ void __launch_bounds__(64 * MERGE_WAVES)
   constexpr int MW = MERGE_WAVES;
   constexpr int CU = kHsplitChunks / MW;   // chunks per step and wave: every chunk in one step
   constexpr int DV = 128;                  // d_v
+  constexpr int OPW = DV / (kMergeSlices * MW);   // outputs per wave
+  static_assert(OPW % 8 == 0, "whole groups of 8 outputs per wave");
   __shared__ f32x4 wacc[MW][2][64];
   __shared__ float wm[MW], wl[MW];
   __shared__ __attribute__((aligned(16))) float zs[DC];
-  const int i = blockIdx.x, half = blockIdx.y, bt = blockIdx.z;
+  const int i = blockIdx.x, slice = blockIdx.y, bt = blockIdx.z;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const size_t rh = (size_t)bt * H + i;
-  i32x4 wv[8];
+  const int v0 = slice * (DV / kMergeSlices) + OPW * w;   // first output of this wave
+  i32x4 wv[OPW];
   {
-    const bf16* wp = w_uv + ((size_t)i * DV + 64 * half + 8 * w) * DC + 8 * lane;
+    const bf16* wp = w_uv + ((size_t)i * DV + v0) * DC + 8 * lane;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) wv[j] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(wp + (size_t)j * DC));
+    for (int j = 0; j < OPW; ++j) wv[j] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(wp + (size_t)j * DC));
   }
   const int2 rc = row_chunks[bt];
   if (rc.y <= 1) {
@@ -1180,7 +1188,7 @@ __global__ void __launch_bounds__(64 * MERGE_WAVES)
       const int c = 8 * t;   // this lane's 8 latent columns
       *reinterpret_cast<f32x4*>(&zs[c]) = z0;
       *reinterpret_cast<f32x4*>(&zs[c + 4]) = z1;
-      if (half == 0) {
+      if (slice == 0) {
         *reinterpret_cast<f32x4*>(z + rh * DC + c) = z0;
         *reinterpret_cast<f32x4*>(z + rh * DC + c + 4) = z1;
         if (lse != nullptr && t == 0) lse[rh] = (M + log2f(L)) * kLn2;
@@ -1191,44 +1199,47 @@ __global__ void __launch_bounds__(64 * MERGE_WAVES)
     __syncthreads();   // zs complete
     const f32x4 za = *reinterpret_cast<const f32x4*>(&zs[8 * lane]);
     const f32x4 zb = *reinterpret_cast<const f32x4*>(&zs[8 * lane + 4]);
-    float d[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      float wf[8];
+    for (int gi = 0; gi < OPW / 8; ++gi) {
+      float d[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t u = (uint32_t)wv[j][e];
-        wf[2 * e] = __uint_as_float(u << 16);
-        wf[2 * e + 1] = __uint_as_float(u & 0xFFFF0000u);
+      for (int j = 0; j < 8; ++j) {
+        float wf[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t u = (uint32_t)wv[8 * gi + j][e];
+          wf[2 * e] = __uint_as_float(u << 16);
+          wf[2 * e + 1] = __uint_as_float(u & 0xFFFF0000u);
+        }
+        float s = wf[0] * za[0];
+        s = fmaf(wf[1], za[1], s);
+        s = fmaf(wf[2], za[2], s);
+        s = fmaf(wf[3], za[3], s);
+        s = fmaf(wf[4], zb[0], s);
+        s = fmaf(wf[5], zb[1], s);
+        s = fmaf(wf[6], zb[2], s);
+        s = fmaf(wf[7], zb[3], s);
+        d[j] = s;
       }
-      float s = wf[0] * za[0];
-      s = fmaf(wf[1], za[1], s);
-      s = fmaf(wf[2], za[2], s);
-      s = fmaf(wf[3], za[3], s);
-      s = fmaf(wf[4], zb[0], s);
-      s = fmaf(wf[5], zb[1], s);
-      s = fmaf(wf[6], zb[2], s);
-      s = fmaf(wf[7], zb[3], s);
-      d[j] = s;
-    }
-    // reduce-scatter (xor 32: 8 -> 4 outputs per lane, 16: 4 -> 2, 8: 2 -> 1), then xor 4, 2, 1
+      // reduce-scatter (xor 32: 8 -> 4 outputs per lane, 16: 4 -> 2, 8: 2 -> 1), then xor 4, 2, 1
 #pragma unroll
-    for (int m = 32, n = 4; m >= 8; m >>= 1, n >>= 1) {
-      const bool hi = lane & m;
+      for (int m = 32, n = 4; m >= 8; m >>= 1, n >>= 1) {
+        const bool hi = lane & m;
 #pragma unroll
-      for (int j = 0; j < n; ++j) {
-        const float send = hi ? d[j] : d[j + n];
-        const float recv = __shfl_xor(send, m, 64);
-        d[j] = (hi ? d[j + n] : d[j]) + recv;
+        for (int j = 0; j < n; ++j) {
+          const float send = hi ? d[j] : d[j + n];
+          const float recv = __shfl_xor(send, m, 64);
+          d[j] = (hi ? d[j + n] : d[j]) + recv;
+        }
       }
+      float s = d[0];
+      s += __shfl_xor(s, 4, 64);
+      s += __shfl_xor(s, 2, 64);
+      s += __shfl_xor(s, 1, 64);
+      // lane bits 5, 4, 3 -> output bits 2, 1, 0
+      const int j = ((lane >> 5) & 1) * 4 + ((lane >> 4) & 1) * 2 + ((lane >> 3) & 1);
+      if ((lane & 7) == 0) o[rh * DV + v0 + 8 * gi + j] = (bf16)s;
     }
-    float s = d[0];
-    s += __shfl_xor(s, 4, 64);
-    s += __shfl_xor(s, 2, 64);
-    s += __shfl_xor(s, 1, 64);
-    // lane bits 5, 4, 3 -> output bits 2, 1, 0
-    const int j = ((lane >> 5) & 1) * 4 + ((lane >> 4) & 1) * 2 + ((lane >> 3) & 1);
-    if ((lane & 7) == 0) o[rh * DV + 64 * half + 8 * w + j] = (bf16)s;
   }
 }
 
@@ -1287,7 +1298,7 @@ hipError_t launch_merge_out_proj(const LayerDims& L, int rows, const SplitPlan& 
                                  const void* w_uv, float* z, float* lse, void* o, hipStream_t stream) {
   (void)L;
   const FastParts P = fast_parts(plan, const_cast<void*>(workspace));
-  hipLaunchKernelGGL(fast::merge_heads_out_proj, dim3(fast::H, 2, rows), dim3(64 * fast::MERGE_WAVES), 0, stream,
+  hipLaunchKernelGGL(fast::merge_heads_out_proj, dim3(fast::H, fast::kMergeSlices, rows), dim3(64 * fast::MERGE_WAVES), 0, stream,
                      P.acc, P.ml, P.row_chunks, (const bf16*)w_uv, z, lse, (bf16*)o);
   return hipGetLastError();
 }
