@@ -183,10 +183,13 @@ __device__ __forceinline__ void from_bf16x8(bf16x8 p, f32x4& lo, f32x4& hi) {
 // FIXED: the caller's n_splits, chunk k of row bt covers keys [k L, (k + 1) L) with
 //   L = ceil(max_seq_len / n_splits); partial slot bt * n_splits + k.
 // BALANCED (batch * n_q <= kBalanceRows): one grid of kBalanceGrid workgroups over the whole batch.
-//   Every row's visible keys are cut into chunks of Q tiles, Q = max(kMinTiles,
-//   ceil(T / (kBalanceGrid - rows))) for T tiles in all, so no chunk is longer than the share of
-//   one workgroup, whatever the mix of lengths; the chunks of all rows are numbered in row order
-//   and chunk number = workgroup = partial slot.
+//   Q is the smallest bound (at least kMinTiles) for which cutting every row of t tiles into
+//   ceil(t / Q) chunks needs at most kBalanceGrid chunks in all (found by bisection between
+//   ceil(T / kBalanceGrid) and ceil(T / (kBalanceGrid - rows)), T the tiles of all rows), and each
+//   row's tiles are split evenly over its chunks, so no chunk is longer than Q tiles whatever the
+//   mix of lengths; the chunks of all rows are numbered in row order and chunk number =
+//   workgroup = partial slot. (Ragged batch of 64 rows, 1K-8K keys: Q = 41 tiles where
+//   ceil(T / (kBalanceGrid - rows)) gives 48.)
 // PER_ROW: one chunk per row (many rows already fill the chip).
 // HSPLIT (few rows and few keys, the latency-bound case): the BALANCED cut with kHsplitChunks
 //   chunks of at least kHsplitMinTiles tiles, and four workgroups per chunk, one per head block of
@@ -221,8 +224,20 @@ __device__ bool balanced_chunk(const int32_t* __restrict__ seq_len, int n_q, int
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) tsum += __shfl_xor(tsum, o, 64);
+  // q: the smallest bound on a chunk's tiles for which every row cut into ceil(tiles / q) chunks
+  // fits the grid. ceil(T / (grid - rows)) always fits (each row adds at most one partial
+  // chunk), ceil(T / grid) is a lower bound, and the count only falls as q grows: bisect.
   const int64_t share = (tsum + (grid - rows) - 1) / (grid - rows);
-  const int q = (int)max((int64_t)min_tiles, share);
+  int lo = (int)max((int64_t)min_tiles, (tsum + grid - 1) / grid);
+  int hi = (int)max((int64_t)min_tiles, share);
+  while (lo < hi) {   // wave-uniform: every lane holds the same lo, hi and count
+    const int mid = (lo + hi) / 2;
+    int cnt = (tiles[0] + mid - 1) / mid + (tiles[1] + mid - 1) / mid;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
+    if (cnt <= grid) hi = mid; else lo = mid + 1;
+  }
+  const int q = lo;
   bool found = false;
   int carry = 0;
 #pragma unroll
@@ -241,8 +256,11 @@ __device__ bool balanced_chunk(const int32_t* __restrict__ seq_len, int n_q, int
     if (hit) {
       const int src = __ffsll((unsigned long long)hit) - 1;
       const int f = __shfl(first, src, 64), n = __shfl(nck, src, 64), nv = __shfl(nvis[u], src, 64);
+      const int nt = __shfl(tiles[u], src, 64);
       const int k = target - f;
-      *out = Chunk{src + 64 * u, k, n, target, k * q * TILE, min((k + 1) * q * TILE, nv)};
+      // the row's tiles split evenly over its n chunks (sizes differ by at most one tile)
+      const int t0 = (int)((int64_t)k * nt / n), t1 = (int)((int64_t)(k + 1) * nt / n);
+      *out = Chunk{src + 64 * u, k, n, target, t0 * TILE, min(t1 * TILE, nv)};
       found = true;
     }
     carry += __shfl(incl, 63, 64);
