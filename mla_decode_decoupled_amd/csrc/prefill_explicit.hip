@@ -11,9 +11,9 @@
 // pair, and produce the heads' outputs o directly.
 //
 // attn_explicit: one workgroup per (sequence b, head i, block of 128 query rows); 4 waves of 32
-// query rows each walk the visible keys in tiles of 32, the tiles staged in LDS for all 4 waves
-// (global -> registers -> LDS, double-buffered: the next tile's loads are in flight during the
-// current tile's MFMAs). Per wave and tile:
+// query rows each walk the visible keys in tiles of 32, the tiles staged in LDS for all 4 waves by
+// direct 16-byte global -> LDS loads (five per wave and tile) into a ring of four buffers: two tiles
+// in flight while the waves work on two. Per wave and tile:
 //   * scores S^T [32 keys x 32 rows] = K Q^T with 12 MFMA 32x32x16 over the 192 dims; the query
 //     fragments (content part, and the position part rotated on load) stay in registers. The key
 //     rows of the A operand are taken in a permuted order so that each lane's 16 score registers
@@ -41,19 +41,35 @@ constexpr int ROW = DC + DR;          // cache row, 576
 constexpr int BM = 128;               // query rows per workgroup (4 waves x 32)
 constexpr int TK = 32;                // keys per tile
 constexpr float RESCALE = 8.0f;       // log2 units a score may exceed the running reference
-// LDS has 64 banks of 4 bytes. Key rows of 400 bytes (= 144 mod 256) put the 16-byte reads of 16
-// consecutive rows on 16 different bank groups; value rows of 320 bytes (= 64 mod 256) give the
-// transpose reads (4 rows x 64 bytes per 32 lanes) 256 distinct bytes.
-constexpr int KS_STRIDE = DK + 8;     // bf16 per staged key row (400 bytes)
-constexpr int VS_STRIDE = DV + 32;    // bf16 per staged value row (320 bytes)
-constexpr int KS_ELEMS = TK * KS_STRIDE;
-constexpr int VS_ELEMS = TK * VS_STRIDE;
-constexpr int BUF_ELEMS = KS_ELEMS + VS_ELEMS;
-constexpr int LDS_BYTES = 2 * BUF_ELEMS * 2;   // two buffers
-// 16-byte pieces per tile: content keys 32 x 16, position keys 32 x 8, values 32 x 16
-constexpr int PIECES = TK * (DN / 8) + TK * (DR / 8) + TK * (DV / 8);   // 1280
-constexpr int PIECES_PER_THREAD = PIECES / 256;                          // 5
-static_assert(PIECES % 256 == 0, "tile must split evenly over the workgroup");
+// A staged tile: 32 key rows of 384 bytes (content key, then position key: 24 chunks of 16 bytes),
+// then 32 value rows of 256 bytes (16 chunks), unpadded, as the direct loads write 1 KB runs. LDS
+// has 64 banks of 4 bytes; the 16-byte chunks are permuted within each row (an XOR, its own
+// inverse) so that both read patterns are conflict free:
+//   key row r: chunk c sits at (c & ~7) | ((c ^ ((r >> 1) & 7)) & 7). The score reads take one chunk
+//     of 16 keys that run over rows 0-15 or 16-31 (each half once); the 16 rows' (r & 1, (r >> 1) & 7)
+//     are distinct, so their chunks land on 16 distinct groups of 4 banks (a row is 24 chunks,
+//     8 mod 16);
+//   value row r: chunk c sits at c ^ (4 (r & 3)). A transpose read takes 4 consecutive rows x 4
+//     consecutive chunks per 32 lanes, which then cover all 16 bank groups.
+constexpr int KROW = (DK * 2) / 16;   // 24 chunks per key row
+constexpr int VROW = (DV * 2) / 16;   // 16 chunks per value row
+constexpr int K_BYTES = TK * DK * 2;  // 12 KB
+constexpr int BUF_BYTES = K_BYTES + TK * DV * 2;   // 20 KB
+constexpr int NBUF = 4;
+constexpr int LDS_BYTES = NBUF * BUF_BYTES;        // 80 KB: two workgroups per CU fill the 160 KB
+constexpr int SLOTS = BUF_BYTES / 16;              // 1280 chunks per tile
+constexpr int DMA_PER_WAVE = SLOTS / (4 * 64);     // 5 loads of 64 chunks per wave and tile
+static_assert(SLOTS % 256 == 0 && (K_BYTES / 16) % 64 == 0, "every load is all key or all value chunks");
+__device__ __forceinline__ int kchunk(int c, int r) { return (c & ~7) | ((c ^ (r >> 1)) & 7); }
+__device__ __forceinline__ int vchunk(int c, int r) { return c ^ (4 * (r & 3)); }
+// one 16-byte-per-lane direct global -> LDS load: lane l writes LDS bytes lds_base + 16 l
+__device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gaddr), "s"(lds_base)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void wait_vmcnt_5() { __builtin_amdgcn_s_waitcnt(5 | (7 << 4) | (15 << 8)); }
+__device__ __forceinline__ void wait_vmcnt_0() { __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8)); }
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 typedef __bf16 bf16x8e __attribute__((ext_vector_type(8)));
 typedef short i16x4e __attribute__((ext_vector_type(4)));
@@ -81,7 +97,6 @@ __global__ void __launch_bounds__(256, 2) attn_explicit(const bf16* __restrict__
                                                      int n_qb, double base, float scale_log2, bf16* __restrict__ o,
                                                      float* __restrict__ lse) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-  bf16* smem = reinterpret_cast<bf16*>(smem_raw);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 5, l32 = lane & 31;
   // workgroup -> (pair = b * H + i, query block), all blocks of a pair on one XCD, heaviest first
@@ -136,48 +151,55 @@ __global__ void __launch_bounds__(256, 2) attn_explicit(const bf16* __restrict__
     }
   }
 
-  // ---- tile loader: per thread t, two 16-byte pieces of content keys (key t / 16 and 16 + t / 16,
-  // chunk t % 16), one of position keys (key t / 8, chunk t % 8) and two of values (as the content
-  // keys); keys past the sequence re-read its last key (they are masked)
-  static_assert(PIECES_PER_THREAD == 5, "loader layout");
+  // ---- tile loader: load `it` of wave w moves chunks w * 320 + 64 it .. +63 of the tile (lane l one
+  // of them): key chunks first (32 rows x 24), then value chunks (32 rows x 16). A lane reads the
+  // logical chunk that the permutation puts at its LDS position, from a pointer that advances one
+  // tile per load; in the sequence's last, partial tile, keys past its end re-read its last key
+  // (they are masked).
   const size_t kvrow0 = (size_t)b * max_seq_len;
-  const int tk = threadIdx.x >> 4, tc = threadIdx.x & 15;     // content keys / values
-  const int rk = threadIdx.x >> 3, rc = threadIdx.x & 7;      // position keys
-  i32x4 ldA[PIECES_PER_THREAD], ldB[PIECES_PER_THREAD];   // two register sets: tiles t+1 and t+2 in flight
-  // whole tiles advance three base pointers; only the sequence's last, partial tile clamps keys
-  const bf16* kc_p = kc + ((kvrow0 + tk) * H + i) * DN + 8 * tc;
-  const bf16* vv_p = vv + ((kvrow0 + tk) * H + i) * DV + 8 * tc;
-  const bf16* kr_p = cache + (off + rk) * ROW + DC + 8 * rc;
-  const size_t kv_step = (size_t)TK * H * DN;   // one tile of keys in kc / vv
-  auto gload = [&](i32x4 (&ld)[PIECES_PER_THREAD], int tile) {
+  const unsigned char* src[DMA_PER_WAVE];   // this lane's chunk in the next tile to load
+  uint32_t stride[DMA_PER_WAVE];            // bytes from one key to the next (at most 32 KB)
+  int srow[DMA_PER_WAVE];                   // the tile row (key) the lane loads
+#pragma unroll
+  for (int it = 0; it < DMA_PER_WAVE; ++it) {
+    const int slot = w * (SLOTS / 4) + 64 * it + lane;
+    if (slot < K_BYTES / 16) {
+      const int r = slot / KROW, c = kchunk(slot % KROW, r);
+      srow[it] = r;
+      if (c < DN / 8) {   // content key chunk
+        src[it] = reinterpret_cast<const unsigned char*>(kc + ((kvrow0 + r) * H + i) * DN + 8 * c);
+        stride[it] = H * DN * 2;
+      } else {            // position key chunk, straight from the cache row (stored rotated)
+        src[it] = reinterpret_cast<const unsigned char*>(cache + (off + r) * ROW + DC + 8 * (c - DN / 8));
+        stride[it] = ROW * 2;
+      }
+    } else {
+      const int v = slot - K_BYTES / 16, r = v / VROW, c = vchunk(v % VROW, r);
+      srow[it] = r;
+      src[it] = reinterpret_cast<const unsigned char*>(vv + ((kvrow0 + r) * H + i) * DV + 8 * c);
+      stride[it] = H * DV * 2;
+    }
+  }
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)MLA_LDS(unsigned char, smem_raw) +
+                                                       w * (SLOTS / 4) * 16);
+  // loads tile `tile` (the next one: tiles are loaded in order) into buffer `buf`
+  size_t step_bytes[DMA_PER_WAVE];   // one tile of keys
+#pragma unroll
+  for (int it = 0; it < DMA_PER_WAVE; ++it) step_bytes[it] = (size_t)TK * stride[it];
+  auto issue = [&](int tile, int buf) {
     const int j0 = tile * TK;
     if (j0 + TK <= S) {
-      const size_t o = (size_t)tile * kv_step;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        ld[h] = *reinterpret_cast<const i32x4*>(kc_p + o + (size_t)16 * h * H * DN);
-        ld[3 + h] = *reinterpret_cast<const i32x4*>(vv_p + o + (size_t)16 * h * H * DV);
+      for (int it = 0; it < DMA_PER_WAVE; ++it) dma16(src[it], lds0 + buf * BUF_BYTES + 1024 * it);
+    } else {   // the last, partial tile (wave-uniform branch)
+#pragma unroll
+      for (int it = 0; it < DMA_PER_WAVE; ++it) {
+        const int over = max(0, j0 + srow[it] - (S - 1));
+        dma16(src[it] - (size_t)over * stride[it], lds0 + buf * BUF_BYTES + 1024 * it);
       }
-      ld[2] = *reinterpret_cast<const i32x4*>(kr_p + (size_t)j0 * ROW);
-    } else {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int key = min(j0 + tk + 16 * h, S - 1);
-        ld[h] = *reinterpret_cast<const i32x4*>(kc + ((kvrow0 + key) * H + i) * DN + 8 * tc);
-        ld[3 + h] = *reinterpret_cast<const i32x4*>(vv + ((kvrow0 + key) * H + i) * DV + 8 * tc);
-      }
-      ld[2] = *reinterpret_cast<const i32x4*>(cache + (off + min(j0 + rk, S - 1)) * ROW + DC + 8 * rc);
     }
-  };
-  auto lstore = [&](const i32x4 (&ld)[PIECES_PER_THREAD], int buf) {
-    bf16* ks = smem + buf * BUF_ELEMS;
-    bf16* vs = ks + KS_ELEMS;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      *reinterpret_cast<i32x4*>(ks + (tk + 16 * h) * KS_STRIDE + 8 * tc) = ld[h];
-      *reinterpret_cast<i32x4*>(vs + (tk + 16 * h) * VS_STRIDE + 8 * tc) = ld[3 + h];
-    }
-    *reinterpret_cast<i32x4*>(ks + rk * KS_STRIDE + DN + 8 * rc) = ld[2];
+    for (int it = 0; it < DMA_PER_WAVE; ++it) src[it] += step_bytes[it];
   };
 
   f32x16e oacc[4];
@@ -185,63 +207,53 @@ __global__ void __launch_bounds__(256, 2) attn_explicit(const bf16* __restrict__
   for (int c = 0; c < 4; ++c) oacc[c] = f32x16e{};
   float m_run = -INFINITY, l_run = 0.0f;
   const int akey = key_of_row(l32);
+  // LDS read addresses, the same in every buffer (a buffer's offset is a constant of the unrolled
+  // loop below):
+  //   key k-step s reads logical chunk 2 s + g of row akey, at kchunk(2 s + g, akey): for s = 4 u + j
+  //   that is kb[j] + 128 u (the permutation keeps each group of 8 chunks in place);
+  //   value col block c of the transpose reads: row 16 s + 8 g + 4 h + L / 4 (its row & 3 = L / 4),
+  //   logical chunk 4 c + 2 (q & 1) + (L & 3) / 2, byte 8 (L & 1): vb[c] + 256 (16 s + 4 h).
+  const int q = lane >> 4, L = lane & 15;
+  const unsigned char* kb[4];
+  const unsigned char* vb[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    kb[j] = smem_raw + akey * (KROW * 16) + 16 * kchunk(2 * j + g, akey);
+    vb[j] = smem_raw + K_BYTES + (8 * g + (L >> 2)) * (VROW * 16) +
+            16 * vchunk(4 * j + 2 * (q & 1) + ((L & 3) >> 1), L >> 2) + 8 * (L & 1);
+  }
 
-  // Tile t is in LDS buffer t % 2 while the registers hold tiles t + 1 and t + 2 in flight (two
-  // sets, alternating), so a tile's global loads have two iterations to land before they are
-  // stored to LDS at the end of the iteration before its own.
-  auto compute = [&](int t) {
-    const int buf = t & 1;
-    const bf16* ks = smem + buf * BUF_ELEMS;
-    const bf16* vs = ks + KS_ELEMS;
-    // scores of the tile: A = key rows (permuted), B = this wave's query fragments
-    // all 12 key fragments are read before the first MFMA, so the chain waits for one LDS round trip
+  // scores of the tile in buffer `buf`: A = key rows (permuted), B = this wave's query fragments;
+  // register r of the result holds key 16 (r / 8) + 8 g + (r % 8) of the tile
+  auto scores = [&](int buf) {
+    const int bo = buf * BUF_BYTES;
     f32x16e sacc = f32x16e{};
-    const bf16* krow = ks + akey * KS_STRIDE + 8 * g;
     bf16x8e kf[12];
 #pragma unroll
-    for (int s = 0; s < 6; ++s) kf[s] = *reinterpret_cast<const bf16x8e*>(krow + 16 * s);
+    for (int s = 0; s < 6; ++s) kf[s] = *reinterpret_cast<const bf16x8e*>(kb[s & 3] + bo + 128 * (s >> 2));
 #pragma unroll
     for (int s = 0; s < 12; ++s) {
       sacc = mfma(kf[s], qf[s], sacc);
-      if (s + 6 < 12) kf[s + 6] = *reinterpret_cast<const bf16x8e*>(krow + 16 * (s + 6));
+      if (s + 6 < 12) kf[s + 6] = *reinterpret_cast<const bf16x8e*>(kb[(s + 6) & 3] + bo + 128 * ((s + 6) >> 2));
     }
-    // six reads ahead of the chain, then one read behind each MFMA (it reuses the registers the
-    // MFMA has just consumed), then the last six MFMAs
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-#pragma unroll
-    for (int s = 0; s < 6; ++s) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
-    // causal mask and online softmax on the raw scores (the scale is positive, so it is applied in
-    // the exponent); register r holds key 16 (r / 8) + 8 g + (r % 8). Only tiles reaching past the
-    // first position of the wave's rows need the mask.
+    return sacc;
+  };
+  // causal mask of tile t (only tiles reaching past the first position of the wave's rows need it)
+  auto mask = [&](f32x16e& sv, int t) {
     const int j0 = t * TK;
-    float sv[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sv[r] = sacc[r];
-    if (j0 + TK - 1 > wave_pos0) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (j0 + 16 * (r >> 3) + 8 * g + (r & 7) > pos) sv[r] = -INFINITY;
-    }
+    for (int r = 0; r < 16; ++r)
+      if (j0 + 16 * (r >> 3) + 8 * g + (r & 7) > pos) sv[r] = -INFINITY;
+  };
+  auto lane_max = [&](const f32x16e& sv) {
     float mx = sv[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sv[r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
-    // Lazy rescaling: the running reference m_run only moves when a score exceeds it by more than
-    // RESCALE (log2 units), so probabilities stay below 2^RESCALE and the accumulator is rescaled
-    // only on those (rare, mostly early) tiles. Softmax is exact for any reference. Key 0 is
-    // visible to every row, so the first tile always sets a finite reference.
-    if (__any(mx > m_run + RESCALE)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 on the first tile
-      l_run *= alpha;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) oacc[c] *= alpha;
-      m_run = m_new;
-    }
+    return mx;
+  };
+  // P of the tile against the running reference (the scale is positive, so it is applied in the
+  // exponent), packed as the two P.V B fragments; adds the lane's row sums to l_run
+  auto probs = [&](const f32x16e& sv, bf16x8e* pb) {
     int pk[8];
     float psum = 0.0f;
 #pragma unroll
@@ -253,11 +265,13 @@ __global__ void __launch_bounds__(256, 2) attn_explicit(const bf16* __restrict__
     }
     l_run += psum;
     const int pk0[4] = {pk[0], pk[1], pk[2], pk[3]}, pk1[4] = {pk[4], pk[5], pk[6], pk[7]};
-    const bf16x8e pb[2] = {__builtin_bit_cast(bf16x8e, pk0), __builtin_bit_cast(bf16x8e, pk1)};
-    // O^T += V^T P^T: A fragment of col block c, key step s = value rows 16 s + 8 g .. +7 of column
-    // 32 c + l32, gathered by two transpose reads (lane L of a 16-lane group points at row
-    // 16 s + 8 g + 4 h + L / 4, columns 32 c + 16 (q & 1) + 4 (L & 3) .. +3, q = lane / 16)
-    const int q = lane >> 4, L = lane & 15;
+    pb[0] = __builtin_bit_cast(bf16x8e, pk0);
+    pb[1] = __builtin_bit_cast(bf16x8e, pk1);
+  };
+  // O^T += V^T P^T for the tile in buffer `buf`: A fragment of col block c, key step s = value rows
+  // 16 s + 8 g .. +7 of column 32 c + l32, gathered by two transpose reads
+  auto pv = [&](int buf, const bf16x8e* pb) {
+    const int bo = buf * BUF_BYTES;
     bf16x8e vf[2][4];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
@@ -266,8 +280,8 @@ __global__ void __launch_bounds__(256, 2) attn_explicit(const bf16* __restrict__
         i16x4e hv[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const bf16* p = vs + (16 * s + 8 * g + 4 * h + (L >> 2)) * VS_STRIDE + 32 * c + 16 * (q & 1) + 4 * (L & 3);
-          hv[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4e*)MLA_LDS(bf16, p));
+          const unsigned char* p = vb[c] + bo + (VROW * 16) * (16 * s + 4 * h);
+          hv[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4e*)MLA_LDS(unsigned char, p));
         }
         vf[s][c] = __builtin_bit_cast(bf16x8e, hv);
       }
@@ -275,26 +289,80 @@ __global__ void __launch_bounds__(256, 2) attn_explicit(const bf16* __restrict__
     for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int c = 0; c < 4; ++c) oacc[c] = mfma(vf[s][c], pb[s], oacc[c]);
-    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
   };
-  gload(ldA, 0);
-  if (n_tiles > 1) gload(ldB, 1);
-  lstore(ldA, 0);
-  __syncthreads();
-  for (int t = 0; t < n_tiles; t += 2) {
-    // even tile: set A is free (tile t was stored), set B holds tile t + 1
-    if (t + 2 < n_tiles) gload(ldA, t + 2);
-    compute(t);
+  // Lazy rescaling: the running reference m_run only moves when a score exceeds it by more than
+  // RESCALE (log2 units), so probabilities stay below 2^RESCALE and the accumulator is rescaled
+  // only on those (rare, mostly early) tiles. Softmax is exact for any reference. Key 0 is visible
+  // to every row, so the first tile always sets a finite reference.
+  auto rescale_to = [&](float mx) {
+    if (__any(mx > m_run + RESCALE)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 on the first tile
+      l_run *= alpha;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) oacc[c] *= alpha;
+      m_run = m_new;
+    }
+  };
+
+  // Software pipeline, per iteration t: the score MFMAs of tile t + 1 run with the exponentials of
+  // tile t between them; then the P.V MFMAs of tile t run with tile t + 1's row maxima between
+  // them; then the reference moves if tile t + 1 needs it. Tile t sits in buffer t % 4, tiles t + 2
+  // and t + 3 load into the other two. The last iteration scores a resident buffer once more and
+  // discards it (its maximum is taken as -inf). The loop is unrolled by the 4 buffers so that every
+  // LDS address is a per-lane base plus a constant.
+  issue(0, 0);
+  if (n_tiles > 1) issue(1, 1);
+  if (n_tiles > 2) {
+    issue(2, 2);
+    __builtin_amdgcn_s_waitcnt(10 | (7 << 4) | (15 << 8));   // tile 0 landed, tiles 1-2 may not have
+  } else if (n_tiles > 1) {
+    wait_vmcnt_5();
+  } else {
+    wait_vmcnt_0();
+  }
+  lds_barrier();
+  f32x16e scur = scores(0);
+  if (TK - 1 > wave_pos0) mask(scur, 0);
+  {
+    float mx = lane_max(scur);
+    rescale_to(fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2);
+  }
+  auto step = [&](int t, int buf) {
+    // tile t + 1 landed everywhere (tile t + 2 may still load); every wave is past iteration t - 1,
+    // so the buffer of tile t - 1 is free for tile t + 3
+    if (t + 2 < n_tiles) wait_vmcnt_5(); else wait_vmcnt_0();
+    lds_barrier();
+    if (t + 3 < n_tiles) issue(t + 3, (buf + 3) & 3);
+    f32x16e snext = scores((buf + 1) & 3);
+    bf16x8e pb[2];
+    probs(scur, pb);
+    // the 12 MFMAs with their 12 key reads and the 56 VALU operations of the exponentials form one
+    // block, left to the scheduler (fixed patterns of 3 or 5 VALU operations per MFMA measured
+    // slower). The empty asm keeps the exponentials in this block: without it they sink past the
+    // branch below, next to their use in P.V, and nothing runs between the score MFMAs.
+    asm volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(l_run));
+    if ((t + 1) * TK + TK - 1 > wave_pos0 && t + 1 < n_tiles) mask(snext, t + 1);
+    pv(buf, pb);
+    float mx = lane_max(snext);
+    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
+    rescale_to(t + 1 < n_tiles ? mx : -INFINITY);
+    scur = snext;
+  };
+  for (int t = 0; t < n_tiles; t += 4) {
+    step(t, 0);
     if (t + 1 >= n_tiles) break;
-    lstore(ldB, (t + 1) & 1);   // buffer (t + 1) % 2 was last read in iteration t - 1
-    __syncthreads();
-    // odd tile: set B is free, set A holds tile t + 2
-    if (t + 3 < n_tiles) gload(ldB, t + 3);
-    compute(t + 1);
+    step(t + 1, 1);
     if (t + 2 >= n_tiles) break;
-    lstore(ldA, t & 1);
-    __syncthreads();
+    step(t + 2, 2);
+    if (t + 3 >= n_tiles) break;
+    step(t + 3, 3);
   }
   // ---- output: o[row][32 c + 8 r4 + 4 g + e] = O^T / l, four consecutive values per store
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
