@@ -69,6 +69,12 @@ __device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_base) {
 }
 __device__ __forceinline__ void wait_vmcnt_5() { __builtin_amdgcn_s_waitcnt(5 | (7 << 4) | (15 << 8)); }
 __device__ __forceinline__ void wait_vmcnt_0() { __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8)); }
+// the max of v over lanes l and l ^ 32: v_permlane32_swap exchanges lanes 32-63 of its first
+// operand with lanes 0-31 of its second, so with v in both the pair holds v[l] and v[l ^ 32]
+__device__ __forceinline__ float half_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 typedef __bf16 bf16x8e __attribute__((ext_vector_type(8)));
@@ -326,7 +332,7 @@ __global__ void __launch_bounds__(256, 2) attn_explicit(const bf16* __restrict__
   if (TK - 1 > wave_pos0) mask(scur, 0);
   {
     float mx = lane_max(scur);
-    rescale_to(fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2);
+    rescale_to(half_max(mx) * scale_log2);
   }
   auto step = [&](int t, int buf) {
     // tile t + 1 landed everywhere (tile t + 2 may still load); every wave is past iteration t - 1,
@@ -351,7 +357,7 @@ __global__ void __launch_bounds__(256, 2) attn_explicit(const bf16* __restrict__
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
+    mx = half_max(mx) * scale_log2;
     rescale_to(t + 1 < n_tiles ? mx : -INFINITY);
     scur = snext;
   };
