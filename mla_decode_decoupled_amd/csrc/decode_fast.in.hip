@@ -1329,15 +1329,11 @@ hipError_t launch_attn_fast(const LayerDims& L, int batch, int n_q, const void* 
   __bf16* part_acc = P.acc;
   float* part_ml = P.ml;
   int2* row_chunks = P.row_chunks;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)fast::decode_attn_fast, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)sizeof(fast::Smem));
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void*)fast::decode_attn_hsplit, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)sizeof(fast::SmemH));
+  static std::atomic<uint32_t> lds_set{0};
+  {
+    const hipError_t e = ensure_lds_limit(lds_set, {{(const void*)fast::decode_attn_fast, (int)sizeof(fast::Smem)},
+                                                    {(const void*)fast::decode_attn_hsplit, (int)sizeof(fast::SmemH)}});
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   if (plan.fast_mode == fast::HSPLIT) {
     hipLaunchKernelGGL(fast::decode_attn_hsplit, dim3(plan.fast_grid_x), dim3(256), sizeof(fast::SmemH), stream,

@@ -5,7 +5,32 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <initializer_list>
+
 namespace mla {
+
+// Raises the dynamic-LDS limit of kernels that need more than the default, once per device (the
+// attribute belongs to the device's context): `done` holds one bit per device, set only after every
+// hipFuncSetAttribute succeeded. Two threads making the first call on a device at once both set
+// the attribute, which is harmless. Devices past the 32nd set it on every call.
+struct LdsLimit {
+  const void* fn;
+  int bytes;
+};
+inline hipError_t ensure_lds_limit(std::atomic<uint32_t>& done, std::initializer_list<LdsLimit> fns) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint32_t bit = dev >= 0 && dev < 32 ? 1u << dev : 0u;
+  if (bit != 0 && (done.load(std::memory_order_acquire) & bit) != 0) return hipSuccess;
+  for (const LdsLimit& f : fns) {
+    e = hipFuncSetAttribute(f.fn, hipFuncAttributeMaxDynamicSharedMemorySize, f.bytes);
+    if (e != hipSuccess) return e;
+  }
+  done.fetch_or(bit, std::memory_order_release);
+  return hipSuccess;
+}
 
 struct LayerDims {
   int n_heads, d_nope, d_latent, d_rope, d_v;

@@ -608,29 +608,19 @@ hipError_t linear(const T* x, int ldx, int M, int K, const Seg2& s, hipStream_t 
     const bool vec = K % 8 == 0 && ldx % 8 == 0 && aligned16(x) && aligned16(s.w1) && (s.n == s.n1 || aligned16(s.w2));
     if constexpr (sizeof(Ty) == 2) {
       if (vec && M >= WM && K % WK == 0 && staged_ok(s)) {
-        static bool wide_attr_set = false;
-        if (!wide_attr_set) {
-          const hipError_t e = hipFuncSetAttribute((const void*)lin_gemm_wide<false>,
-                                                   hipFuncAttributeMaxDynamicSharedMemorySize, WIDE_LDS);
-          if (e != hipSuccess) return e;
-          wide_attr_set = true;
-        }
+        static std::atomic<uint32_t> wide_lds_set{0};
+        const hipError_t e = ensure_lds_limit(wide_lds_set, {{(const void*)lin_gemm_wide<false>, WIDE_LDS}});
+        if (e != hipSuccess) return e;
         hipLaunchKernelGGL((lin_gemm_wide<false>), dim3((s.n + WN - 1) / WN, (M + WM - 1) / WM), dim3(256), WIDE_LDS,
                            stream, x, ldx, M, K, s, SeqRows{nullptr, nullptr, 0});
         return hipGetLastError();
       }
     }
     if (vec && M >= kGemmMinRows && K % TK == 0) {
-      static bool attr_set = false;
-      if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)lin_gemm<Ty, false, false>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, GEMM_LDS);
-        if (e == hipSuccess)
-          e = hipFuncSetAttribute((const void*)lin_gemm<Ty, false, sizeof(Ty) == 2>,
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, GEMM_LDS);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-      }
+      static std::atomic<uint32_t> lds_set{0};
+      const hipError_t e = ensure_lds_limit(lds_set, {{(const void*)lin_gemm<Ty, false, false>, GEMM_LDS},
+                                                      {(const void*)lin_gemm<Ty, false, sizeof(Ty) == 2>, GEMM_LDS}});
+      if (e != hipSuccess) return e;
       const dim3 grid((s.n + TN - 1) / TN, (M + TM - 1) / TM);
       if (sizeof(Ty) == 2 && staged_ok(s))
         hipLaunchKernelGGL((lin_gemm<Ty, false, sizeof(Ty) == 2>), grid, dim3(256), GEMM_LDS, stream, x, ldx, M, K, s,
@@ -759,12 +749,10 @@ template hipError_t launch_linear<__bf16>(const void*, int, int, int, const void
 hipError_t launch_kv_expand(int batch, int max_seq_len, int n_out, int d_latent, int row, const void* cache,
                             const int64_t* seq_off, const int32_t* seq_len, const void* w_uk, const void* w_uv,
                             void* kc, void* vv, hipStream_t stream) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)lin::lin_gemm_wide<true>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, lin::WIDE_LDS);
+  static std::atomic<uint32_t> lds_set{0};
+  {
+    const hipError_t e = ensure_lds_limit(lds_set, {{(const void*)lin::lin_gemm_wide<true>, lin::WIDE_LDS}});
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   lin::Seg2 s{w_uk, w_uv, kc, vv, n_out, 2 * n_out, n_out, n_out};
   lin::SeqRows sq{seq_len, seq_off, (int64_t)max_seq_len * n_out};

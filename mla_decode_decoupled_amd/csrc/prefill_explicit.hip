@@ -407,12 +407,9 @@ hipError_t launch_prefill_explicit(const LayerDims& L, int batch, int n_q, const
   hipError_t e = launch_kv_expand(batch, max_seq_len, H * xp::DN, xp::DC, xp::ROW, cache, seq_off, seq_len, w_uk,
                                   w_uv, kc, vv, stream);
   if (e != hipSuccess) return e;
-  static bool attr_set = false;
-  if (!attr_set) {
-    e = hipFuncSetAttribute((const void*)xp::attn_explicit, hipFuncAttributeMaxDynamicSharedMemorySize, xp::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint32_t> lds_set{0};
+  e = ensure_lds_limit(lds_set, {{(const void*)xp::attn_explicit, xp::LDS_BYTES}});
+  if (e != hipSuccess) return e;
   const int n_qb = (n_q + xp::BM - 1) / xp::BM;
   hipLaunchKernelGGL(xp::attn_explicit, dim3(batch * H * n_qb), dim3(256), xp::LDS_BYTES, stream, (const bf16*)q_nope,
                      (const bf16*)q_rope, (const bf16*)cache, seq_off, seq_len, (const bf16*)kc, (const bf16*)vv, H, n_q,

@@ -289,12 +289,10 @@ __global__ void __launch_bounds__(256) out_proj_gemm(const float* __restrict__ z
 
 hipError_t launch_absorb_q_gemm(const LayerDims& L, int n_rows, const void* q_nope, const void* q_rope,
                                 const int32_t* q_pos, const void* w_uk, void* q_packed, hipStream_t stream) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm::absorb_q_gemm, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       gemm::ABSORB_LDS);
+  static std::atomic<uint32_t> lds_set{0};
+  {
+    const hipError_t e = ensure_lds_limit(lds_set, {{(const void*)gemm::absorb_q_gemm, gemm::ABSORB_LDS}});
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   // the quarters of a row tile, then the row tiles of one head, run together
   const dim3 grid(4, (n_rows + gemm::BM - 1) / gemm::BM, gemm::H);
@@ -306,15 +304,11 @@ hipError_t launch_absorb_q_gemm(const LayerDims& L, int n_rows, const void* q_no
 hipError_t launch_out_proj_gemm(const LayerDims& L, int n_rows, const float* z, const void* w_uv, void* o,
                                 hipStream_t stream) {
   (void)L;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm::out_proj_gemm<128>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       gemm::outp_lds<128>());
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void*)gemm::out_proj_gemm<64>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              gemm::outp_lds<64>());
+  static std::atomic<uint32_t> lds_set{0};
+  {
+    const hipError_t e = ensure_lds_limit(lds_set, {{(const void*)gemm::out_proj_gemm<128>, gemm::outp_lds<128>()},
+                                                    {(const void*)gemm::out_proj_gemm<64>, gemm::outp_lds<64>()}});
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   // row tiles (and output halves) of one head run together
   const int tiles = (n_rows + gemm::BM - 1) / gemm::BM;
