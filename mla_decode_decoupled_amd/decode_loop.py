@@ -1,4 +1,4 @@
-"""Multi-step, multi-layer decode driver over the library's calls.
+"""Multi-step, multi-layer decode loop over the library's calls.
 
 A stack of MLA attention layers is run token by token the way the pages run their check of the
 absorbed form ("从零理解 MLA", the decode loop after the decoupled-RoPE code: every step appends
