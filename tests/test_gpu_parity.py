@@ -174,6 +174,21 @@ def test_ragged_batch_balanced_chunks():
         _check_outputs(run, hi, b, heads=[0, 31, 32, 63, 64, 95, 96, 127])
 
 
+def test_ragged_batch_plan_extremes():
+    """The balanced chunk plan on an extreme length mix: 40 rows, among them single-key rows, rows one
+    key either side of a tile boundary and rows of 4097, 12345 and 20000 keys, so that the bisected
+    chunk bound cuts the long rows into many evenly split chunks while short rows take one (a row
+    whose keys all fit one chunk writes z directly). Every row against the oracle, at both ends of
+    every 32-head block."""
+    cfg = CONFIGS[2]
+    lens = [1, 2, 31, 32, 33, 63, 64, 65, 20000, 1, 96, 97, 12345, 1, 5, 4097, 128, 129, 1, 3,
+            200, 33, 1, 700, 31, 1000, 1, 2, 64, 65, 160, 1, 4, 999, 1, 300, 32, 1, 77, 2048]
+    hi = host_inputs(cfg, lens=lens)
+    run = run_pipeline(hi)
+    for b in range(len(lens)):
+        _check_outputs(run, hi, b, heads=[0, 31, 32, 63, 64, 95, 96, 127])
+
+
 @pytest.mark.slow
 def test_long_context_128k_sampled():
     cfg = CONFIGS[3]
