@@ -196,6 +196,8 @@ __device__ __forceinline__ void from_bf16x8(bf16x8 p, f32x4& lo, f32x4& hi) {
 //   32 heads (decode_attn_hsplit).
 enum ChunkMode { FIXED = 0, BALANCED = 1, PER_ROW = 2, HSPLIT = 3 };
 constexpr int kBalanceGrid = 256;
+constexpr int kXcds = 8;   // MI355X: workgroup i runs on XCD i % 8
+static_assert(kBalanceGrid % kXcds == 0, "the balanced grid splits evenly over the XCDs");
 constexpr int kBalanceRows = 128;
 constexpr int kMinTiles = 4;
 constexpr int kHsplitChunks = 64;
@@ -364,7 +366,11 @@ __global__ void __launch_bounds__(256)
     Chunk* shared_ch = reinterpret_cast<Chunk*>(smem_raw + FLAGS_OFF + 64);
     if (w == 0) {
       Chunk c;
-      const bool found = balanced_chunk(seq_len, n_q, rows, (int)blockIdx.x, kBalanceGrid, kMinTiles, &c);
+      // Workgroups are dealt to the 8 XCDs in turn; numbering the chunks so that XCD x takes the 32
+      // consecutive chunks 32x .. 32x + 31 puts the few workgroups of one row on one XCD, where they
+      // share the row's 147 KB of queries through its L2 instead of each fetching them from HBM.
+      const int target = (int)(blockIdx.x % kXcds) * (kBalanceGrid / kXcds) + (int)(blockIdx.x / kXcds);
+      const bool found = balanced_chunk(seq_len, n_q, rows, target, kBalanceGrid, kMinTiles, &c);
       if (lane == 0) {
         if (!found) c.nck = 0;
         *shared_ch = c;
