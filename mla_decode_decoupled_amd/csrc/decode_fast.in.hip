@@ -209,6 +209,19 @@ struct Chunk {
   int bt, k, nck, slot, j0, j1;
 };
 
+// Inclusive prefix sum over the 64 lanes of a wave by DPP: row shifts by 1, 2, 4 and 8 scan each row
+// of 16 lanes, then the broadcasts of lane 15 (into rows 1 and 3) and lane 31 (into rows 2 and 3)
+// carry the row totals across; no LDS round trip, unlike a shuffle. Lane 63 ends with the total.
+__device__ __forceinline__ int wave_scan_incl(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);   // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);   // row_bcast:31
+  return v;
+}
+
 // BALANCED plan over `grid` chunks of at least `min_tiles` tiles, computed by every lane of wave 0
 // for all rows (rows <= 128: two per lane): the chunk numbered `target`. Returns false when
 // `target` lies past the last chunk.
@@ -216,27 +229,29 @@ __device__ bool balanced_chunk(const int32_t* __restrict__ seq_len, int n_q, int
                                int min_tiles, Chunk* out) {
   const int lane = threadIdx.x & 63;
   int nvis[2], tiles[2];
-  int64_t tsum = 0;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int r = lane + 64 * u;
-    nvis[u] = r < rows ? seq_len[r / n_q] - n_q + (r % n_q) + 1 : 0;
+    const int b = n_q == 1 ? r : r / n_q, i = n_q == 1 ? 0 : r % n_q;   // one query row: no division
+    nvis[u] = r < rows ? seq_len[b] - n_q + i + 1 : 0;
     tiles[u] = (nvis[u] + TILE - 1) / TILE;
-    tsum += tiles[u];
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) tsum += __shfl_xor(tsum, o, 64);
+  // T, exactly: a lane's two rows hold under 2^27 tiles, so its count splits into 16-bit halves whose
+  // sums over the wave fit 32 bits
+  const int lsum = tiles[0] + tiles[1];
+  const int64_t tsum = ((int64_t)__builtin_amdgcn_readlane(wave_scan_incl(lsum >> 16), 63) << 16) +
+                       __builtin_amdgcn_readlane(wave_scan_incl(lsum & 0xFFFF), 63);
   // q: the smallest bound on a chunk's tiles for which every row cut into ceil(tiles / q) chunks
   // fits the grid. ceil(T / (grid - rows)) always fits (each row adds at most one partial
   // chunk), ceil(T / grid) is a lower bound, and the count only falls as q grows: bisect.
   const int64_t share = (tsum + (grid - rows) - 1) / (grid - rows);
   int lo = (int)max((int64_t)min_tiles, (tsum + grid - 1) / grid);
   int hi = (int)max((int64_t)min_tiles, share);
-  while (lo < hi) {   // wave-uniform: every lane holds the same lo, hi and count
+  while (lo < hi) {   // wave-uniform: lo, hi and the count (read from lane 63) are scalars
     const int mid = (lo + hi) / 2;
-    int cnt = (tiles[0] + mid - 1) / mid + (tiles[1] + mid - 1) / mid;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
+    // at most grid + rows chunks for any mid >= lo, so the sum cannot overflow
+    const int cnt = __builtin_amdgcn_readlane(
+        wave_scan_incl((tiles[0] + mid - 1) / mid + (tiles[1] + mid - 1) / mid), 63);
     if (cnt <= grid) hi = mid; else lo = mid + 1;
   }
   const int q = lo;
@@ -245,27 +260,22 @@ __device__ bool balanced_chunk(const int32_t* __restrict__ seq_len, int n_q, int
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int nck = (tiles[u] + q - 1) / q;
-    int incl = nck;   // inclusive prefix over the 64 lanes of this round
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int v = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += v;
-    }
+    const int incl = wave_scan_incl(nck);   // inclusive prefix over the 64 lanes of this round
     const int first = carry + incl - nck;
     const int r = lane + 64 * u;
     const bool mine = r < rows && target >= first && target < first + nck;
     const uint64_t hit = __ballot(mine);
     if (hit) {
-      const int src = __ffsll((unsigned long long)hit) - 1;
-      const int f = __shfl(first, src, 64), n = __shfl(nck, src, 64), nv = __shfl(nvis[u], src, 64);
-      const int nt = __shfl(tiles[u], src, 64);
+      const int src = __ffsll((unsigned long long)hit) - 1;   // wave-uniform
+      const int f = __builtin_amdgcn_readlane(first, src), n = __builtin_amdgcn_readlane(nck, src);
+      const int nv = __builtin_amdgcn_readlane(nvis[u], src), nt = __builtin_amdgcn_readlane(tiles[u], src);
       const int k = target - f;
       // the row's tiles split evenly over its n chunks (sizes differ by at most one tile)
       const int t0 = (int)((int64_t)k * nt / n), t1 = (int)((int64_t)(k + 1) * nt / n);
       *out = Chunk{src + 64 * u, k, n, target, t0 * TILE, min(t1 * TILE, nv)};
       found = true;
     }
-    carry += __shfl(incl, 63, 64);
+    carry += __builtin_amdgcn_readlane(incl, 63);
   }
   return found;
 }
