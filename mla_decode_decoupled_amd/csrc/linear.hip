@@ -268,11 +268,14 @@ constexpr int GEMM_LDS = 2 * 2 * TM * SROW * 2;   // two buffers of the A and B 
 
 // Per-sequence rows (SEQ form): blockIdx.z is a sequence b whose M = len[b] rows start at row
 // off[b] of x; its outputs start y_bstride elements further per b. The row tile is blockIdx.x
-// and the column tile blockIdx.y in this form.
+// and the column tile blockIdx.y in this form. With head_stride > 0 (lin_gemm_wide only) a
+// segment's outputs are stored head-major instead: its columns in blocks of 128, block h of row m
+// at h * head_stride + 128 m, so that one head's rows are contiguous.
 struct SeqRows {
   const int32_t* len;
   const int64_t* off;
   int64_t y_bstride;
+  int64_t head_stride = 0;
 };
 
 // grid (ceil(n / 128), ceil(M / 128)), or (ceil(M / 128), ceil(n / 128), sequences) in the SEQ form;
@@ -544,7 +547,13 @@ __global__ void __launch_bounds__(256, 2) lin_gemm_wide(const bf16* __restrict__
     const int m = m0 + r, n = n0 + 8 * c;
     if (m < M && n < s.n) {
       const i32x4 v = *reinterpret_cast<const i32x4*>(Cs + r * WCS + 8 * c);
-      bf16* dst = n < s.n1 ? (bf16*)s.y1 + (size_t)m * s.ldy1 + n : (bf16*)s.y2 + (size_t)m * s.ldy2 + (n - s.n1);
+      bf16* dst;
+      if (SEQ && sq.head_stride > 0) {   // the tile's 128 columns are one head: one contiguous 64 KB block
+        const int nn = n < s.n1 ? n : n - s.n1;
+        dst = (n < s.n1 ? (bf16*)s.y1 : (bf16*)s.y2) + (size_t)(nn >> 7) * sq.head_stride + (size_t)m * 128 + (nn & 127);
+      } else {
+        dst = n < s.n1 ? (bf16*)s.y1 + (size_t)m * s.ldy1 + n : (bf16*)s.y2 + (size_t)m * s.ldy2 + (n - s.n1);
+      }
       *reinterpret_cast<i32x4*>(dst) = v;
     }
   }
@@ -746,7 +755,8 @@ template hipError_t launch_linear<__bf16>(const void*, int, int, int, const void
 
 // K_C = C W_UK^T and V = C W_UV^T for every key of every sequence (the explicit form's key and
 // value reconstruction): per sequence b the latents are the first d_latent columns of its cache
-// rows seq_off[b] .. seq_off[b] + seq_len[b] - 1; outputs kc / vv [batch][max_seq_len][H * 128].
+// rows seq_off[b] .. seq_off[b] + seq_len[b] - 1; outputs kc / vv head-major,
+// [batch][H][max_seq_len][128], so that the attention's key/value tiles of one head are contiguous.
 hipError_t launch_kv_expand(int batch, int max_seq_len, int n_out, int d_latent, int row, const void* cache,
                             const int64_t* seq_off, const int32_t* seq_len, const void* w_uk, const void* w_uv,
                             void* kc, void* vv, hipStream_t stream) {
@@ -756,7 +766,7 @@ hipError_t launch_kv_expand(int batch, int max_seq_len, int n_out, int d_latent,
     if (e != hipSuccess) return e;
   }
   lin::Seg2 s{w_uk, w_uv, kc, vv, n_out, 2 * n_out, n_out, n_out};
-  lin::SeqRows sq{seq_len, seq_off, (int64_t)max_seq_len * n_out};
+  lin::SeqRows sq{seq_len, seq_off, (int64_t)max_seq_len * n_out, (int64_t)max_seq_len * 128};
   // n_out = H * 128 and the workspace rows keep every staged 16-byte store aligned; d_latent = 512
   // is a whole number of K steps
   const dim3 grid((max_seq_len + lin::WM - 1) / lin::WM, (2 * n_out + lin::WN - 1) / lin::WN, batch);

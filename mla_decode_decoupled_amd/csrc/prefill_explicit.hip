@@ -162,7 +162,7 @@ __global__ void __launch_bounds__(256, 2) attn_explicit(const bf16* __restrict__
   // logical chunk that the permutation puts at its LDS position, from a pointer that advances one
   // tile per load; in the sequence's last, partial tile, keys past its end re-read its last key
   // (they are masked).
-  const size_t kvrow0 = (size_t)b * max_seq_len;
+  const size_t hrow0 = ((size_t)b * H + i) * max_seq_len;   // key 0 of this (sequence, head) in kc / vv
   const unsigned char* src[DMA_PER_WAVE];   // this lane's chunk in the next tile to load
   uint32_t stride[DMA_PER_WAVE];            // bytes from one key to the next (at most 32 KB)
   int srow[DMA_PER_WAVE];                   // the tile row (key) the lane loads
@@ -173,8 +173,8 @@ __global__ void __launch_bounds__(256, 2) attn_explicit(const bf16* __restrict__
       const int r = slot / KROW, c = kchunk(slot % KROW, r);
       srow[it] = r;
       if (c < DN / 8) {   // content key chunk
-        src[it] = reinterpret_cast<const unsigned char*>(kc + ((kvrow0 + r) * H + i) * DN + 8 * c);
-        stride[it] = H * DN * 2;
+        src[it] = reinterpret_cast<const unsigned char*>(kc + (hrow0 + r) * DN + 8 * c);
+        stride[it] = DN * 2;
       } else {            // position key chunk, straight from the cache row (stored rotated)
         src[it] = reinterpret_cast<const unsigned char*>(cache + (off + r) * ROW + DC + 8 * (c - DN / 8));
         stride[it] = ROW * 2;
@@ -182,8 +182,8 @@ __global__ void __launch_bounds__(256, 2) attn_explicit(const bf16* __restrict__
     } else {
       const int v = slot - K_BYTES / 16, r = v / VROW, c = vchunk(v % VROW, r);
       srow[it] = r;
-      src[it] = reinterpret_cast<const unsigned char*>(vv + ((kvrow0 + r) * H + i) * DV + 8 * c);
-      stride[it] = H * DV * 2;
+      src[it] = reinterpret_cast<const unsigned char*>(vv + (hrow0 + r) * DV + 8 * c);
+      stride[it] = DV * 2;
     }
   }
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)MLA_LDS(unsigned char, smem_raw) +
