@@ -6,6 +6,7 @@ Usage: python mla_decode_decoupled_amd/build.py [--debug] [--sanitize]
 
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import shutil
 import subprocess
@@ -63,12 +64,7 @@ def asan_runtime() -> str:
     return path
 
 
-def _build_one(sources, lib_path: str, debug: bool, verbose: bool, extra=()) -> str:
-    srcs = [os.path.join(CSRC, s) for s in sources]
-    tmp = lib_path + ".tmp"
-    cmd = [hipcc(), *HIP_FLAGS, *extra, "-I", os.path.join(PKG_DIR, os.pardir, "include"), "-o", tmp, *srcs]
-    if debug:
-        cmd = [c for c in cmd if c != "-O3"] + ["-O1", "-g"]
+def _run(cmd, verbose: bool) -> None:
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -79,7 +75,26 @@ def _build_one(sources, lib_path: str, debug: bool, verbose: bool, extra=()) -> 
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if err.strip() and verbose:
         print(err, file=sys.stderr)
+
+
+def _build_one(sources, lib_path: str, debug: bool, verbose: bool, extra=()) -> str:
+    """Compile the sources to objects in parallel, then link the library."""
+    flags = [*HIP_FLAGS, *extra, "-I", os.path.join(PKG_DIR, os.pardir, "include")]
+    if debug:
+        flags = [f for f in flags if f != "-O3"] + ["-O1", "-g"]
+    compile_flags = [f for f in flags if f != "-shared"]
+    obj_dir = lib_path + ".objs"
+    os.makedirs(obj_dir, exist_ok=True)
+    objs = [os.path.join(obj_dir, os.path.splitext(s)[0] + ".o") for s in sources]
+    cmds = [[hipcc(), *compile_flags, "-c", os.path.join(CSRC, s), "-o", o]
+            for s, o in zip(sources, objs)]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 1)) as pool:
+        for f in [pool.submit(_run, c, verbose) for c in cmds]:
+            f.result()
+    tmp = lib_path + ".tmp"
+    _run([hipcc(), *flags, "-o", tmp, *objs], verbose)
     os.replace(tmp, lib_path)
+    shutil.rmtree(obj_dir, ignore_errors=True)
     return lib_path
 
 
