@@ -41,6 +41,9 @@ constexpr int ROW = DC + DR;          // cache row, 576
 constexpr int BM = 128;               // query rows per workgroup (4 waves x 32)
 constexpr int TK = 32;                // keys per tile
 constexpr float RESCALE = 8.0f;       // log2 units a score may exceed the running reference
+// a lane's probability sum up to which no score can have moved the reference: 2^RESCALE / 2, half the
+// bound, so that the rounding of the hardware exponential never hides a score just past the limit
+constexpr float kRescaleSum = 128.0f;
 // A staged tile: 32 key rows of 384 bytes (content key, then position key: 24 chunks of 16 bytes),
 // then 32 value rows of 256 bytes (16 chunks), unpadded, as the direct loads write 1 KB runs. LDS
 // has 64 banks of 4 bytes; the 16-byte chunks are permuted within each row (an XOR, its own
@@ -258,7 +261,7 @@ __global__ void __launch_bounds__(256, 2) attn_explicit(const bf16* __restrict__
     return mx;
   };
   // P of the tile against the running reference (the scale is positive, so it is applied in the
-  // exponent), packed as the two P.V B fragments; adds the lane's row sums to l_run
+  // exponent), packed as the two P.V B fragments; returns the sum of the lane's 16 probabilities
   auto probs = [&](const f32x16e& sv, bf16x8e* pb) {
     int pk[8];
     float psum = 0.0f;
@@ -269,10 +272,10 @@ __global__ void __launch_bounds__(256, 2) attn_explicit(const bf16* __restrict__
       psum += p0 + p1;
       pk[r / 2] = __builtin_bit_cast(int, __builtin_convertvector((f32x2e){p0, p1}, bf16x2e));
     }
-    l_run += psum;
     const int pk0[4] = {pk[0], pk[1], pk[2], pk[3]}, pk1[4] = {pk[4], pk[5], pk[6], pk[7]};
     pb[0] = __builtin_bit_cast(bf16x8e, pk0);
     pb[1] = __builtin_bit_cast(bf16x8e, pk1);
+    return psum;
   };
   // O^T += V^T P^T for the tile in buffer `buf`: A fragment of col block c, key step s = value rows
   // 16 s + 8 g .. +7 of column 32 c + l32, gathered by two transpose reads
@@ -300,6 +303,12 @@ __global__ void __launch_bounds__(256, 2) attn_explicit(const bf16* __restrict__
   // RESCALE (log2 units), so probabilities stay below 2^RESCALE and the accumulator is rescaled
   // only on those (rare, mostly early) tiles. Softmax is exact for any reference. Key 0 is visible
   // to every row, so the first tile always sets a finite reference.
+  // A tile's maximum is only needed when it may move the reference: if the sum of a lane's 16
+  // probabilities against the current reference is at most kRescaleSum (< 2^RESCALE), none of them
+  // reaches 2^RESCALE, so no score exceeds the reference by more than RESCALE and the rule would not
+  // move it. Only a larger sum (rare) computes the maximum, applies the rule, and recomputes the
+  // probabilities against the moved reference: the references, and so the results, are those of
+  // taking every tile's maximum.
   auto rescale_to = [&](float mx) {
     if (__any(mx > m_run + RESCALE)) {
       const float m_new = fmaxf(m_run, mx);
@@ -342,7 +351,13 @@ __global__ void __launch_bounds__(256, 2) attn_explicit(const bf16* __restrict__
     if (t + 3 < n_tiles) issue(t + 3, (buf + 3) & 3);
     f32x16e snext = scores((buf + 1) & 3);
     bf16x8e pb[2];
-    probs(scur, pb);
+    float psum = probs(scur, pb);
+    if (__any(psum > kRescaleSum)) {   // may move the reference (rare): the exact rule
+      const float m_old = m_run;
+      rescale_to(half_max(lane_max(scur)) * scale_log2);
+      if (m_run != m_old) psum = probs(scur, pb);
+    }
+    l_run += psum;
     // the 12 MFMAs with their 12 key reads and the 56 VALU operations of the exponentials form one
     // block, left to the scheduler (fixed patterns of 3 or 5 VALU operations per MFMA measured
     // slower). The empty asm keeps the exponentials in this block: without it they sink past the
@@ -350,15 +365,9 @@ __global__ void __launch_bounds__(256, 2) attn_explicit(const bf16* __restrict__
     asm volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(l_run));
     if ((t + 1) * TK + TK - 1 > wave_pos0 && t + 1 < n_tiles) mask(snext, t + 1);
     pv(buf, pb);
-    float mx = lane_max(snext);
+    // the 16 transpose reads first, then the 8 MFMAs: their LDS latency is not waited out one by one
     __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-    }
-    mx = half_max(mx) * scale_log2;
-    rescale_to(t + 1 < n_tiles ? mx : -INFINITY);
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     scur = snext;
   };
   for (int t = 0; t < n_tiles; t += 4) {

@@ -81,3 +81,38 @@ def test_explicit_prefill_chunked_prefill_workload():
     s = assert_close(o, np32(run.o), "bf16", "explicit vs absorbed o (all rows and heads)")
     s2 = assert_close(lse, np32(run.lse), "bf16", "explicit vs absorbed lse (all rows and heads)")
     print("explicit vs absorbed:", s, s2)
+
+
+def test_explicit_prefill_reference_moves():
+    """Scores that climb tile by tile, so that the running reference moves again and again. All
+    query rows share one content query; the latent rows of tiles 0-4 are built to score about
+    -50, -40, -30, -20 and -10 (natural units) against every head's absorbed query, the later tiles
+    are ordinary. Each tile's maximum then exceeds the reference by more than the lazy-rescale
+    limit (8 in log2 units), five moves in all, while the outputs and log-sum-exps come from the
+    ordinary tiles (the early keys weigh e^-40 and less), so the bf16 bar still applies."""
+    from mla_workloads.generate import round_bf16
+    lens, n_q, H = [320], 8, 4
+    cfg = _small_cfg(210, H, n_q, lens)
+    hi = host_inputs(cfg, lens=lens)
+    hi.q_nope[0][:] = hi.q_nope[0][0]
+    q_abs = O.absorb_query(hi.q_nope[0][:1], hi.w_uk)[0]             # [H, d_c]
+    d = sum(q_abs[i] / float(q_abs[i] @ q_abs[i]) for i in range(H))   # q_abs[i] . d ~ 1 for every head
+    c = hi.c[0].copy()
+    for t in range(5):
+        target = -(50.0 - 10.0 * t) / cfg.softmax_scale
+        c[32 * t:32 * (t + 1)] = 0.1 * c[32 * t:32 * (t + 1)] + target * d
+    hi.c[0] = round_bf16(c)
+    run = run_pipeline(hi)
+    o, lse = _run_explicit(hi, run)
+    ref = O.explicit_attention(hi.c[0], hi.k_pre[0], hi.q_nope[0], hi.q_rope[0], hi.w_uk, hi.w_uv,
+                               scale=cfg.softmax_scale, base=cfg.rope_base)
+    # the construction holds: each of the first five tiles tops the one before by more than the limit
+    s_tile = np.array([[float((q_abs[i] @ hi.c[0][32 * t:32 * (t + 1)].T).max()) for t in range(6)]
+                       for i in range(H)]) * cfg.softmax_scale * np.log2(np.e)
+    assert np.all(np.diff(s_tile, axis=1) > 8.0), s_tile
+    s1 = assert_close(o[0], ref["o"], "bf16", "explicit o")
+    s2 = assert_close(lse[0], ref["lse"], "bf16", "explicit lse")
+    # the absorbed path on the same inputs: its fixed reference (the first tile's maximum) overflows,
+    # and the exact fallback recomputes the chunks
+    s3 = assert_close(np32(run.o[0]), ref["o"], "bf16", "absorbed o")
+    print(f"tile maxima (log2, content part) {np.round(s_tile[0], 1)}: explicit o {s1}, lse {s2}; absorbed o {s3}")
