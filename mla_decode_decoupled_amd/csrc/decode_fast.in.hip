@@ -20,10 +20,11 @@
 //     (below), so that each lane's 16 score registers are exactly the keys its P.V operand needs;
 //   * softmax per head in log2 units against a fixed reference: m_ref is the head's max over the
 //     chunk's first tile and probabilities are 2^(s - m_ref). Softmax is exact for any reference,
-//     so the accumulator is never rescaled. A score above m_ref + 64 sets a flag; after the loop
-//     the workgroup then recomputes its chunk with exact_chunk(), a slow VALU online softmax
-//     (correct for any input, never taken on realistic scores). Keys more than 126 below the
-//     reference lose weight under 2^-126 relative to the first tile's largest key;
+//     so the accumulator is never rescaled. A score above m_ref + 64 makes its probability, and
+//     so the lane's running sum of probabilities, exceed 2^64; a sum above that after the loop
+//     sets a flag, and the workgroup then recomputes its chunk with exact_chunk(), a slow VALU
+//     online softmax (correct for any input, never taken on realistic scores). Keys more than 126
+//     below the reference lose weight under 2^-126 relative to the first tile's largest key;
 //   * P (bf16) stays in registers: O^T[512 x 32 heads] += V^T P^T with 32 MFMAs, the B operand
 //     straight from the softmax registers and V^T read from the row-major tile with the gfx950
 //     transpose read ds_read_b64_tr_b16. No wave waits for another wave's probabilities.
@@ -70,6 +71,7 @@ constexpr int WAVES = 4;
 constexpr int SLOTS_PER_WAVE = TILE_SLOTS / WAVES;        // 576
 constexpr int DMA_PER_WAVE = SLOTS_PER_WAVE / 64;         // 9 instructions
 constexpr float HEADROOM = 64.0f;       // log2 units: P values stay <= 2^64
+constexpr float kSumLimit = 0x1p64f;    // 2^HEADROOM: a probability sum above it may hide one above it
 constexpr int QS_STRIDE = 1024 + 16;    // bytes per staged query row (latent part + pad)
 constexpr int ES_STRIDE = 256 + 4;      // floats per staged half output row (+ pad)
 
@@ -482,7 +484,6 @@ __global__ void __launch_bounds__(256)
   issue_tile(0);
   issue_tile(1);   // past the chunk when it has one tile: then a harmless read of qbytes
 
-  bool ovf = false;   // this wave saw a score far above its reference (uniform)
 
   // O^T accumulators: latent col block cb (32 columns) x this wave's 32 heads, 16 fp32 each,
   // zeroed in AGPRs by MFMAs of zero operands (a plain zero initialisation would be built in
@@ -582,18 +583,16 @@ __global__ void __launch_bounds__(256)
   // interleaved; leaves P of tile t+1 in v[80:87].
   auto pv_softmax = [&](int tile, f32x16& sacc) {
     const uint32_t tb = tile_lds(tile);
-    float mx;
     asm volatile(
 @PVSM_ASM@
         : [o0] "+a"(oc0), [o1] "+a"(oc1), [o2] "+a"(oc2), [o3] "+a"(oc3), [o4] "+a"(oc4), [o5] "+a"(oc5),
           [o6] "+a"(oc6), [o7] "+a"(oc7), [o8] "+a"(oc8), [o9] "+a"(oc9), [o10] "+a"(oc10), [o11] "+a"(oc11),
-          [o12] "+a"(oc12), [o13] "+a"(oc13), [o14] "+a"(oc14), [o15] "+a"(oc15), [l] "+v"(l_run), [mx] "=&v"(mx),
+          [o12] "+a"(oc12), [o13] "+a"(oc13), [o14] "+a"(oc14), [o15] "+a"(oc15), [l] "+v"(l_run),
           "+{v[112:127]}"(sacc), "+{v[80:87]}"(pfr)
         : [v00] "v"(tb + pv_off[0][0]), [v01] "v"(tb + pv_off[0][1]), [v10] "v"(tb + pv_off[1][0]),
           [v11] "v"(tb + pv_off[1][1]), [sc] "s"(scale_log2), [nm] "v"(-m_ref)
         : "v88", "v89", "v90", "v91", "v92", "v93", "v94", "v95", "v96", "v97", "v98", "v99", "v100", "v101",
           "v102", "v103", "v104", "v105", "v106", "v107", "v108", "v109", "v110", "v111", "memory");
-    ovf |= __any(mx * scale_log2 > m_ref + HEADROOM);
   };
 
   // ---- the loop. Iteration t >= 0: P.V of tile t fused with the softmax of tile t+1 (its scores
@@ -625,7 +624,11 @@ __global__ void __launch_bounds__(256)
 
   // A score far above the reference makes later probabilities overflow (inf / NaN in the
   // accumulator, harmless to the hardware); the loop still runs to its end, and the chunk is then
-  // recomputed by the exact path. The flags meet in LDS once, after the loop.
+  // recomputed by the exact path. Every probability is at most the lane's sum l_run, so a sum of at
+  // most 2^HEADROOM proves that no score exceeded the reference by more than HEADROOM; a larger (or
+  // non-finite) sum sends the chunk to the exact path, which is correct for any input. The flags
+  // meet in LDS once, after the loop.
+  const bool ovf = __any(!(l_run <= kSumLimit));
   int* flags = reinterpret_cast<int*>(smem_raw + FLAGS_OFF);
   if (lane == 0) flags[w] = ovf ? 1 : 0;
   __syncthreads();

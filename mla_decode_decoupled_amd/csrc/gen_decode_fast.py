@@ -85,10 +85,6 @@ def pv():
     six-slot ring. The softmax of the next tile (scores in v[112:127]) is interleaved; its P goes
     to v[80:83] once the first key step no longer reads them and to v[84:87] after the last MFMA."""
     sm = []
-    sm.append("v_max3_f32 %[mx], v112, v113, v114")
-    for r in range(3, 15, 2):
-        sm.append(f"v_max3_f32 %[mx], %[mx], v{112+r}, v{113+r}")
-    sm.append("v_max_f32 %[mx], %[mx], v127")
     for r in range(16):  # x = s * scale - m_ref
         sm.append(f"v_fma_f32 v{112+r}, v{112+r}, %[sc], %[nm]")
     for r in range(16):
