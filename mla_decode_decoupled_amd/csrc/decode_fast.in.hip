@@ -413,22 +413,16 @@ __global__ void __launch_bounds__(256)
     dma_off[it] = r * ROW_BYTES + phys_chunk(p, r) * 16 - (it % 4) * 1024 + DMA_BIAS;
   }
   auto tile_lds = [&](int tile) { return (uint32_t)(uintptr_t)MLA_LDS(unsigned char, sm.tile[tile % NBUF]); };
-  // DMA source of tile `tile` (less DMA_BIAS) and this lane's nine offsets. Rows of a tail tile
-  // past the end re-read the last valid row (their scores are masked); a tile past the chunk
-  // reads qbytes.
-  auto dma_plan = [&](int tile, uint32_t* o) -> const unsigned char* {
-    const int key0 = j0 + tile * TILE;
-#pragma unroll
-    for (int it = 0; it < DMA_PER_WAVE; ++it) o[it] = dma_off[it];
+  // Where tile `tile` is read from (less DMA_BIAS), with the lane's offsets dma_off. A partial last
+  // tile of a chunk of two or more tiles is moved back to end at the chunk's last key: its first
+  // tail_shift rows repeat keys of the tile before, and their scores are masked. The move keeps
+  // every read inside the chunk and the same for all lanes, so the loop passes dma_off to the DMA
+  // untouched. (A chunk shorter than one tile cannot move back; its one tile re-reads its last key
+  // instead, with per-lane offsets, in the prologue.) A tile past the chunk reads qbytes.
+  const int tail_shift = n_tiles >= 2 ? j0 + n_tiles * TILE - j1 : 0;
+  auto tile_src = [&](int tile) -> const unsigned char* {
     if (tile >= n_tiles) return qbytes - DMA_BIAS;
-    if (key0 + TILE > j1) {
-      const int last = j1 - 1 - key0;
-#pragma unroll
-      for (int it = 0; it < DMA_PER_WAVE; ++it) {
-        const int r = (w * SLOTS_PER_WAVE + it * 64 + lane) / ROW_CHUNKS;
-        o[it] = dma_off[it] - (r > last ? r - last : 0) * ROW_BYTES;
-      }
-    }
+    const int key0 = j0 + tile * TILE - (tile == n_tiles - 1 ? tail_shift : 0);
     return kv + (int64_t)key0 * ROW_BYTES - DMA_BIAS;
   };
   auto sgpr_ptr = [](const void* p) {
@@ -439,7 +433,17 @@ __global__ void __launch_bounds__(256)
   // stand-alone tile DMA (prologue): nine 1 KB instructions per wave into the tile's buffer
   auto issue_tile = [&](int tile) {
     uint32_t o[DMA_PER_WAVE];
-    const uint64_t sbase = sgpr_ptr(dma_plan(tile, o));
+#pragma unroll
+    for (int it = 0; it < DMA_PER_WAVE; ++it) o[it] = dma_off[it];
+    if (n_tiles == 1 && tile == 0 && j1 - j0 < TILE) {   // lone partial tile: rows past the end re-read the last key
+      const int last = j1 - 1 - j0;
+#pragma unroll
+      for (int it = 0; it < DMA_PER_WAVE; ++it) {
+        const int r = (w * SLOTS_PER_WAVE + it * 64 + lane) / ROW_CHUNKS;
+        o[it] = dma_off[it] - (r > last ? r - last : 0) * ROW_BYTES;
+      }
+    }
+    const uint64_t sbase = sgpr_ptr(tile_src(tile));
     const uint32_t sdst = __builtin_amdgcn_readfirstlane(tile_lds(tile) + (w * SLOTS_PER_WAVE) * 16);
     asm volatile(
 @DMA_ASM@
@@ -539,9 +543,8 @@ __global__ void __launch_bounds__(256)
   // finished reading before the barrier that opened this iteration.
   auto scores = [&](int tile, f32x16& sacc) {
     const uint32_t tb = tile_lds(tile);
-    const int dt = tile + 2;
-    uint32_t o[DMA_PER_WAVE];
-    const uint64_t sbase = sgpr_ptr(dma_plan(dt, o));
+    const int dt = tile + 2;   // at least 2: never the lone partial tile
+    const uint64_t sbase = sgpr_ptr(tile_src(dt));
     const uint32_t sdst = __builtin_amdgcn_readfirstlane(tile_lds(dt) + (w * SLOTS_PER_WAVE) * 16);
     asm volatile(
 @QK_ASM@
@@ -550,8 +553,9 @@ __global__ void __launch_bounds__(256)
           "{v[64:67]}"(qrp0), "{v[68:71]}"(qrp1), "{v[72:75]}"(qrp2), "{v[76:79]}"(qrp3),
           "{v[128:143]}"(q0), "{v[144:159]}"(q1), "{v[160:175]}"(q2), "{v[176:191]}"(q3),
           "{v[192:207]}"(q4), "{v[208:223]}"(q5), "{v[224:239]}"(q6), "{v[240:255]}"(q7), "{v[80:87]}"(pfr),
-          [b] "s"(sbase), [m] "s"(sdst), [o0] "v"(o[0]), [o1] "v"(o[1]), [o2] "v"(o[2]), [o3] "v"(o[3]),
-          [o4] "v"(o[4]), [o5] "v"(o[5]), [o6] "v"(o[6]), [o7] "v"(o[7]), [o8] "v"(o[8])
+          [b] "s"(sbase), [m] "s"(sdst), [o0] "v"(dma_off[0]), [o1] "v"(dma_off[1]), [o2] "v"(dma_off[2]),
+          [o3] "v"(dma_off[3]), [o4] "v"(dma_off[4]), [o5] "v"(dma_off[5]), [o6] "v"(dma_off[6]),
+          [o7] "v"(dma_off[7]), [o8] "v"(dma_off[8])
         : "v88", "v89", "v90", "v91", "v92", "v93", "v94", "v95", "v96", "v97", "v98", "v99", "v100", "v101",
           "v102", "v103", "v104", "v105", "v106", "v107", "v108", "v109", "v110", "v111", "memory", "m0");
   };
@@ -612,11 +616,10 @@ __global__ void __launch_bounds__(256)
     if (tile + 1 >= n_tiles) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[r] = -INFINITY;   // no next tile: the fused softmax adds 0
-    } else if (j0 + (tile + 2) * TILE > j1) {               // partial next tile: mask keys past the end
-      const int key0 = j0 + (tile + 1) * TILE;
+    } else if (tile + 2 == n_tiles && tail_shift > 0) {   // the moved-back last tile: mask its repeated keys
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (key0 + key_of_reg(r, g) >= j1) sacc[r] = -INFINITY;
+        if (key_of_reg(r, g) < tail_shift) sacc[r] = -INFINITY;
     }
     pv_softmax(tile, sacc);
   }
