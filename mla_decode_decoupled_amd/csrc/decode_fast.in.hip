@@ -513,6 +513,7 @@ __global__ void __launch_bounds__(256)
   }
 
   float m_ref = -INFINITY;  // per lane: head 32w + l32 (both lane halves agree); set by the first tile
+  float neg_mref = INFINITY;
   float l_run = 0.0f;       // per lane: sum over this lane's half of the keys
   v8i pfr;                  // P of the tile being accumulated: bf16 pairs, keys 16s + 8g + e
 
@@ -581,6 +582,8 @@ __global__ void __launch_bounds__(256)
                          ((uint32_t)__builtin_bit_cast(unsigned short, (bf16)p1) << 16));
     }
     l_run += psum;
+    neg_mref = -m_ref;
+    asm volatile("" : "+v"(neg_mref));   // kept, not recomputed from m_ref in every tile
   };
 
   // P.V of tile t (P in v[80:87]) with the softmax of tile t+1 (scores in v[112:127])
@@ -594,7 +597,7 @@ __global__ void __launch_bounds__(256)
           [o12] "+a"(oc12), [o13] "+a"(oc13), [o14] "+a"(oc14), [o15] "+a"(oc15), [l] "+v"(l_run),
           "+{v[112:127]}"(sacc), "+{v[80:87]}"(pfr)
         : [v00] "v"(tb + pv_off[0][0]), [v01] "v"(tb + pv_off[0][1]), [v10] "v"(tb + pv_off[1][0]),
-          [v11] "v"(tb + pv_off[1][1]), [sc] "s"(scale_log2), [nm] "v"(-m_ref)
+          [v11] "v"(tb + pv_off[1][1]), [sc] "s"(scale_log2), [nm] "v"(neg_mref)
         : "v88", "v89", "v90", "v91", "v92", "v93", "v94", "v95", "v96", "v97", "v98", "v99", "v100", "v101",
           "v102", "v103", "v104", "v105", "v106", "v107", "v108", "v109", "v110", "v111", "memory");
   };
