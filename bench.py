@@ -109,13 +109,18 @@ TRAFFIC_SOURCES = [os.path.join(ROOT, "mla_decode_decoupled_amd", "csrc", f)
                    for f in ("api.hip", "generic.hip", "decode_fast.hip", "prefill_explicit.hip", "linear.hip")]
 
 
-def sources_sha() -> str:
-    """Hash of the sources that decide what the attention kernels read and write."""
+def sources_sha(paths=None) -> str:
+    """Hash of the code of the sources that decide what the attention kernels read and write: their
+    text with the comments, trailing blanks and empty lines taken out, so that a comment edit keeps the
+    records valid and any change to the code does not."""
     import hashlib
+    import re
     h = hashlib.sha256()
-    for f in TRAFFIC_SOURCES:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+    for f in TRAFFIC_SOURCES if paths is None else paths:
+        with open(f, encoding="utf-8") as fh:
+            text = re.sub(r"/\*.*?\*/", "", fh.read(), flags=re.S)
+        lines = (re.sub(r"//.*$", "", line).rstrip() for line in text.splitlines())
+        h.update("\n".join(line for line in lines if line).encode())
     return h.hexdigest()[:16]
 
 

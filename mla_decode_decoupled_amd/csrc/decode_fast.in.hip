@@ -88,8 +88,9 @@ struct Smem {
 // instruction's offset field (0, 1024, 2048, 3072), which moves the global address by the same
 // amount: the per-lane global offsets are biased by -1024 (it % 4), plus DMA_BIAS (taken off the
 // base pointer). The offset is an unsigned 32-bit VGPR, so it must stay non-negative for every
-// row it can name, row 0 included (the re-read rows of a tail tile all name one row, possibly
-// row 0): row * ROW_BYTES + 16 chunk >= 0 and DMA_BIAS >= 3072 make it at least DMA_BIAS - 3072.
+// row it can name, row 0 included (the re-read rows of a chunk shorter than one tile all name its
+// last row, possibly row 0): row * ROW_BYTES + 16 chunk >= 0 and DMA_BIAS >= 3072 make it at least
+// DMA_BIAS - 3072.
 constexpr int DMA_BIAS = 4096;
 static_assert(DMA_BIAS >= 3 * 1024, "DMA offsets must stay non-negative for row 0, instruction offset 3072");
 constexpr int FLAGS_OFF = NBUF * TILE_BYTES - 1024;
@@ -561,8 +562,9 @@ __global__ void __launch_bounds__(256)
           "v102", "v103", "v104", "v105", "v106", "v107", "v108", "v109", "v110", "v111", "memory", "m0");
   };
 
-  // softmax of the chunk's first tile in C++: fixes the reference, masks keys past the end of a
-  // tail tile, and leaves P in the B-operand registers.
+  // softmax of the chunk's first tile in C++: fixes the reference, masks the rows past the end of a
+  // chunk shorter than one tile (the only first tile that can be partial), and leaves P in the
+  // B-operand registers.
   auto softmax_first = [&](f32x16 sacc) {
     float tmax = -INFINITY;
 #pragma unroll

@@ -36,3 +36,19 @@ def test_traffic_records_parse():
         got = bench.recorded_traffic(r["workload"], r["call"], r["n_splits"], cold=True)
         assert got == (r["traffic_bytes_per_call"] if r["source_sha"] == sha else None)
         assert bench.recorded_traffic(r["workload"], r["call"], r["n_splits"], cold=False) is None
+
+
+def test_source_hash_follows_code_not_comments(tmp_path):
+    """The records' key hashes the code only: a comment or blank-line edit keeps it, a code edit changes it."""
+    sys.path.insert(0, ROOT)
+    import bench
+
+    code = "int f(int a) {\n  return a + 1;\n}\n"
+    a = tmp_path / "a.hip"
+    a.write_text(code)
+    b = tmp_path / "b.hip"
+    b.write_text("// header\n/* a block\n   comment */\nint f(int a) {   \n\n  return a + 1;  // one more\n}\n")
+    c = tmp_path / "c.hip"
+    c.write_text(code.replace("a + 1", "a + 2"))
+    assert bench.sources_sha([str(a)]) == bench.sources_sha([str(b)])
+    assert bench.sources_sha([str(a)]) != bench.sources_sha([str(c)])
