@@ -114,6 +114,21 @@ def test_split_count_does_not_change_results(cid, n_splits):
         assert dz <= 2e-3 and rel <= 5e-3
 
 
+@pytest.mark.parametrize("n_splits", [2, 3])
+def test_fast_kernel_chunk_tails(n_splits):
+    """The 128-head MFMA kernel with a caller's split count (chunks of ceil(100 / n_splits) keys) on
+    lengths whose chunks end in every way a chunk can: a partial last tile of a chunk of two tiles,
+    which moves back to end at the chunk's last key and masks the rows it repeats (33 keys: a
+    31-row repeat); a chunk shorter than one tile, whose one tile re-reads its last key; exact tiles.
+    All heads and outputs against the oracle."""
+    lens = [100, 90, 33, 64, 65]
+    cfg = MLAConfig(**{**CONFIGS[1].__dict__, "batch": len(lens)})
+    hi = host_inputs(cfg, lens=lens)
+    run = run_pipeline(hi, n_splits=n_splits)
+    for b in range(len(lens)):
+        _check_outputs(run, hi, b)
+
+
 def test_ragged_batch_sampled():
     cfg = CONFIGS[2]
     hi = host_inputs(cfg)
