@@ -9,7 +9,8 @@
 // both contractions.
 //
 // One workgroup (4 waves, one per SIMD) takes one (query row, split chunk) and walks the chunk
-// in tiles of 32 keys. Wave w owns heads 32w..32w+31 from end to end:
+// in tiles of 32 keys. Wave w scores heads 32w..32w+31 and accumulates latent columns
+// 128w..128w+127 of all 128 heads:
 //   * tiles stream HBM -> LDS with direct 16-byte global_load_lds into four buffers, two tiles in
 //     flight while two are being computed on. The global addresses are permuted so that LDS holds
 //     an XOR-swizzled layout (16-byte chunk c of row r sits at c ^ f(r) within its group of 8),
@@ -25,23 +26,27 @@
 //     sets a flag, and the workgroup then recomputes its chunk with exact_chunk(), a slow VALU
 //     online softmax (correct for any input, never taken on realistic scores). Keys more than 126
 //     below the reference lose weight under 2^-126 relative to the first tile's largest key;
-//   * P (bf16) stays in registers: O^T[512 x 32 heads] += V^T P^T with 32 MFMAs, the B operand
-//     straight from the softmax registers and V^T read from the row-major tile with the gfx950
-//     transpose read ds_read_b64_tr_b16. No wave waits for another wave's probabilities.
-// The loop is software-pipelined with one barrier per tile (the tile buffers are shared):
+//   * P (bf16) goes through LDS: each wave stores the B fragments of its 32 heads (2 KB) into one
+//     of two P buffers, and every wave reads all four head blocks' fragments back. Then
+//     O^T[128 columns x 128 heads] += V^T P^T with 32 MFMAs per wave: V^T is read from the
+//     row-major tile with the gfx950 transpose read ds_read_b64_tr_b16, and each V^T fragment
+//     feeds the four head blocks' MFMAs (each P fragment the four column blocks'), so a wave reads
+//     16 KB of operands from LDS per tile for P.V instead of the 32 KB of V^T that all 512 columns
+//     of its own heads would take.
+// The loop is software-pipelined with one barrier per tile (the tile and P buffers are shared):
 // iteration t computes the scores of tile t+1 (and issues the DMA of tile t+3), then runs the
 // P.V MFMAs of tile t with the softmax VALU work of tile t+1 interleaved between them, so the
-// exponentials hide under the MFMAs. The chunk result is either final (one chunk: z = O / l,
-// lse) or a split-K partial (O, m, l) that attn_merge_frag combines by log-sum-exp.
+// exponentials hide under the MFMAs, and stores P of tile t+1 for the next iteration. The chunk
+// result is either final (one chunk: z = O / l, lse) or a split-K partial (O, m, l) that
+// attn_merge_frag combines by log-sum-exp.
 //
 // Register plan (per lane, 512 = 256 VGPRs + 256 AGPRs with one wave per SIMD):
-//   a[0:255]    O^T accumulator, 16 blocks of 32 latent columns x 32 heads, fp32
+//   a[0:255]    O^T accumulator, 16 blocks (4 column blocks x 4 head blocks) of 32 latent
+//               columns x 32 heads, fp32
 //   v[128:255]  latent queries, 32 MFMA B fragments (pinned by physical-register constraints)
-//   v[112:127]  score accumulator S^T, softmax in place
+//   v[112:127]  score accumulator S^T, softmax in place, then P packed in place (v[112:119])
 //   v[64:79]    position part of the queries (4 MFMA B fragments)
-//   v[80:87]    P of the tile being accumulated (two B fragments of 16 keys), carried between
-//               the asm blocks as a pinned value
-//   v[88:111]   operand rings of the two MFMA phases
+//   v[80:111]   operand slots of the two MFMA phases (the score phase uses v[88:111])
 //   v[0:79]     everything the compiler allocates (addresses, softmax state, DMA offsets)
 // The two MFMA phases are inline asm because at this occupancy the compiler's allocator spills
 // whatever split it picks. Hazards it cannot see inside asm are handled explicitly: LDS operands
@@ -73,16 +78,21 @@ constexpr int DMA_PER_WAVE = SLOTS_PER_WAVE / 64;         // 9 instructions
 constexpr float HEADROOM = 64.0f;       // log2 units: P values stay <= 2^64
 constexpr float kSumLimit = 0x1p64f;    // 2^HEADROOM: a probability sum above it may hide one above it
 constexpr int QS_STRIDE = 1024 + 16;    // bytes per staged query row (latent part + pad)
-constexpr int ES_STRIDE = 256 + 4;      // floats per staged half output row (+ pad)
+constexpr int ES_STRIDE = 128 + 4;      // floats per staged output row slice (+ pad)
 
 static_assert(TILE_SLOTS % (WAVES * 64) == 0, "tile must split into whole DMA instructions");
 static_assert(ROW_CHUNKS % 8 == 0, "swizzle groups of 8 chunks");
 
-// LDS (144 KB): four tile buffers. The query staging before the loop and the output staging after
-// it reuse them; the overflow flags sit in the last kilobyte of the tile area, clear of both
-// stagings. (The 64-dim position part of the queries stays in VGPRs, v[64:79].)
+// LDS (160 KB): four tile buffers (144 KB), then two P buffers, each P of one tile for all 128
+// heads, [head block][key step][lane][8 bf16] (8 KB), written by the wave that scored the head
+// block and read by every wave. The query staging before the loop and the output staging after
+// it reuse the tile buffers; the overflow flags, the chunk plan and the output's per-head sums sit
+// in the last kilobyte of the tile area, clear of both stagings. (The 64-dim position part of the
+// queries stays in VGPRs, v[64:79].)
+constexpr int PBUF_BYTES = 4 * 2 * 64 * 16;
 struct Smem {
   unsigned char tile[NBUF][TILE_BYTES];
+  unsigned char pbuf[2][PBUF_BYTES];
 };
 // The tile DMA sets M0 once per four 1 KB instructions and steps the LDS address with the
 // instruction's offset field (0, 1024, 2048, 3072), which moves the global address by the same
@@ -516,7 +526,11 @@ __global__ void __launch_bounds__(256)
   float m_ref = -INFINITY;  // per lane: head 32w + l32 (both lane halves agree); set by the first tile
   float neg_mref = INFINITY;
   float l_run = 0.0f;       // per lane: sum over this lane's half of the keys
-  v8i pfr;                  // P of the tile being accumulated: bf16 pairs, keys 16s + 8g + e
+  // P buffers: lane l reads B fragment (head block hb, key step s) at pb + (2 hb + s) KB and writes
+  // its own head block's two fragments at pw (+ 1 KB for the second key step)
+  const uint32_t pbuf_lds = (uint32_t)(uintptr_t)MLA_LDS(unsigned char, &sm.pbuf[0][0]) + 16 * lane;
+  auto p_read = [&](int tile) { return pbuf_lds + (tile & 1) * PBUF_BYTES; };
+  auto p_write = [&](int tile) { return pbuf_lds + (tile & 1) * PBUF_BYTES + w * 2048; };
 
   // per-lane LDS byte offsets
   // scores: A operand row l32 = key pi(l32), logical chunk 2s + g -> phys (s/4)*8 + ((2(s%4)+g) ^ swz(key))
@@ -526,9 +540,11 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) qk_off[s4] = key * ROW_BYTES + (((2 * s4 + g) ^ swz(key)) & 7) * 16;
   }
-  // values: transpose reads. lane = 16q + L; row = 16s + 8g + 4h + L/4; col = 32cb + 16(q&1) + 4(L&3)
+  // values: transpose reads of this wave's column blocks cb = 4w + db. lane = 16q + L;
+  // row = 16s + 8g + 4h + L/4; col = 32cb + 16(q&1) + 4(L&3). Chunk group cb/2 = 2w + db/2: the
+  // wave's 256 bytes are in the offsets, db/2 in the instruction's offset field.
   const int q16 = lane >> 4, L = lane & 15;
-  uint32_t pv_off[2][2];  // [cb & 1][h]
+  uint32_t pv_off[2][2];  // [db & 1][h]
 #pragma unroll
   for (int cbo = 0; cbo < 2; ++cbo)
 #pragma unroll
@@ -536,7 +552,7 @@ __global__ void __launch_bounds__(256)
       const int row = 8 * g + 4 * h + (L >> 2);
       const int clow = 4 * cbo + 2 * (q16 & 1) + ((L >> 1) & 1);  // logical chunk & 7
       const int ph = (clow ^ swz(row)) & 7;
-      pv_off[cbo][h] = row * ROW_BYTES + ph * 16 + (L & 1) * 8;
+      pv_off[cbo][h] = row * ROW_BYTES + w * 256 + ph * 16 + (L & 1) * 8;
     }
 
   // Scores of one tile into v[112:127]. The same asm block issues the DMA of the tile two
@@ -554,17 +570,18 @@ __global__ void __launch_bounds__(256)
         : [k0] "v"(tb + qk_off[0]), [k1] "v"(tb + qk_off[1]), [k2] "v"(tb + qk_off[2]), [k3] "v"(tb + qk_off[3]),
           "{v[64:67]}"(qrp0), "{v[68:71]}"(qrp1), "{v[72:75]}"(qrp2), "{v[76:79]}"(qrp3),
           "{v[128:143]}"(q0), "{v[144:159]}"(q1), "{v[160:175]}"(q2), "{v[176:191]}"(q3),
-          "{v[192:207]}"(q4), "{v[208:223]}"(q5), "{v[224:239]}"(q6), "{v[240:255]}"(q7), "{v[80:87]}"(pfr),
+          "{v[192:207]}"(q4), "{v[208:223]}"(q5), "{v[224:239]}"(q6), "{v[240:255]}"(q7),
           [b] "s"(sbase), [m] "s"(sdst), [o0] "v"(dma_off[0]), [o1] "v"(dma_off[1]), [o2] "v"(dma_off[2]),
           [o3] "v"(dma_off[3]), [o4] "v"(dma_off[4]), [o5] "v"(dma_off[5]), [o6] "v"(dma_off[6]),
           [o7] "v"(dma_off[7]), [o8] "v"(dma_off[8])
-        : "v88", "v89", "v90", "v91", "v92", "v93", "v94", "v95", "v96", "v97", "v98", "v99", "v100", "v101",
-          "v102", "v103", "v104", "v105", "v106", "v107", "v108", "v109", "v110", "v111", "memory", "m0");
+        : "v80", "v81", "v82", "v83", "v84", "v85", "v86", "v87", "v88", "v89", "v90", "v91", "v92", "v93", "v94",
+          "v95", "v96", "v97", "v98", "v99", "v100", "v101", "v102", "v103", "v104", "v105", "v106", "v107", "v108",
+          "v109", "v110", "v111", "memory", "m0");
   };
 
   // softmax of the chunk's first tile in C++: fixes the reference, masks the rows past the end of a
-  // chunk shorter than one tile (the only first tile that can be partial), and leaves P in the
-  // B-operand registers.
+  // chunk shorter than one tile (the only first tile that can be partial), and stores P (the
+  // lane's two B fragments) to this wave's part of P buffer 0.
   auto softmax_first = [&](f32x16 sacc) {
     float tmax = -INFINITY;
 #pragma unroll
@@ -576,20 +593,25 @@ __global__ void __launch_bounds__(256)
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
     m_ref = tmax;
     float psum = 0.0f;
+    i32x4 pf[2];
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
       const float p0 = exp2f(sacc[r] - m_ref), p1 = exp2f(sacc[r + 1] - m_ref);
       psum += p0 + p1;
-      pfr[r / 2] = (int)((uint32_t)__builtin_bit_cast(unsigned short, (bf16)p0) |
-                         ((uint32_t)__builtin_bit_cast(unsigned short, (bf16)p1) << 16));
+      pf[r / 8][(r / 2) % 4] = (int)((uint32_t)__builtin_bit_cast(unsigned short, (bf16)p0) |
+                                     ((uint32_t)__builtin_bit_cast(unsigned short, (bf16)p1) << 16));
     }
+    unsigned char* pw = &sm.pbuf[0][0] + w * 2048 + 16 * lane;   // p_write(0)
+    *reinterpret_cast<i32x4*>(pw) = pf[0];
+    *reinterpret_cast<i32x4*>(pw + 1024) = pf[1];
     l_run += psum;
     neg_mref = -m_ref;
     asm volatile("" : "+v"(neg_mref));   // kept, not recomputed from m_ref in every tile
   };
 
-  // P.V of tile t (P in v[80:87]) with the softmax of tile t+1 (scores in v[112:127])
-  // interleaved; leaves P of tile t+1 in v[80:87].
+  // P.V of tile t (P of all heads in P buffer t & 1) with the softmax of tile t+1 (scores in
+  // v[112:127]) interleaved; stores P of tile t+1 to this wave's part of P buffer (t + 1) & 1, which
+  // every wave finished reading (tile t-1) before the barrier that opened this iteration.
   auto pv_softmax = [&](int tile, f32x16& sacc) {
     const uint32_t tb = tile_lds(tile);
     asm volatile(
@@ -597,11 +619,13 @@ __global__ void __launch_bounds__(256)
         : [o0] "+a"(oc0), [o1] "+a"(oc1), [o2] "+a"(oc2), [o3] "+a"(oc3), [o4] "+a"(oc4), [o5] "+a"(oc5),
           [o6] "+a"(oc6), [o7] "+a"(oc7), [o8] "+a"(oc8), [o9] "+a"(oc9), [o10] "+a"(oc10), [o11] "+a"(oc11),
           [o12] "+a"(oc12), [o13] "+a"(oc13), [o14] "+a"(oc14), [o15] "+a"(oc15), [l] "+v"(l_run),
-          "+{v[112:127]}"(sacc), "+{v[80:87]}"(pfr)
+          "+{v[112:127]}"(sacc)
         : [v00] "v"(tb + pv_off[0][0]), [v01] "v"(tb + pv_off[0][1]), [v10] "v"(tb + pv_off[1][0]),
-          [v11] "v"(tb + pv_off[1][1]), [sc] "s"(scale_log2), [nm] "v"(neg_mref)
-        : "v88", "v89", "v90", "v91", "v92", "v93", "v94", "v95", "v96", "v97", "v98", "v99", "v100", "v101",
-          "v102", "v103", "v104", "v105", "v106", "v107", "v108", "v109", "v110", "v111", "memory");
+          [v11] "v"(tb + pv_off[1][1]), [sc] "s"(scale_log2), [nm] "v"(neg_mref), [pb] "v"(p_read(tile)),
+          [pw] "v"(p_write(tile + 1))
+        : "v80", "v81", "v82", "v83", "v84", "v85", "v86", "v87", "v88", "v89", "v90", "v91", "v92", "v93", "v94",
+          "v95", "v96", "v97", "v98", "v99", "v100", "v101", "v102", "v103", "v104", "v105", "v106", "v107", "v108",
+          "v109", "v110", "v111", "memory");
   };
 
   // ---- the loop. Iteration t >= 0: P.V of tile t fused with the softmax of tile t+1 (its scores
@@ -663,46 +687,57 @@ __global__ void __launch_bounds__(256)
       ml[1] = l_run;
     }
   }
+  // accumulator db * 4 + hb: latent columns 32 (4w + db) .. +31 x heads 32 hb .. 32 hb + 31
   const f32x16* oacc[16] = {&oc0, &oc1, &oc2, &oc3, &oc4, &oc5, &oc6, &oc7,
                             &oc8, &oc9, &oc10, &oc11, &oc12, &oc13, &oc14, &oc15};
   if (n_chunks > 1) {
-    // ---- partial: 32 stores of 1 KB per wave, straight from the accumulators (layout above)
-    bf16* blk = part_acc + (size_t)ch.slot * PART_ELEMS + (size_t)w * (PART_ELEMS / 4) + 8 * lane;
+    // ---- partial: 32 stores of 1 KB per wave, straight from the accumulators (layout above:
+    // head block hb, column block cb, half jp, lane)
+    bf16* blk = part_acc + (size_t)ch.slot * PART_ELEMS + 8 * lane;
 #pragma unroll
-    for (int cb = 0; cb < 16; ++cb)
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int jp = 0; jp < 2; ++jp) {
-        const f32x16& o = *oacc[cb];
-        *reinterpret_cast<bf16x8*>(blk + (cb * 2 + jp) * 512) =
-            to_bf16x8(f32x4{o[8 * jp], o[8 * jp + 1], o[8 * jp + 2], o[8 * jp + 3]},
-                      f32x4{o[8 * jp + 4], o[8 * jp + 5], o[8 * jp + 6], o[8 * jp + 7]});
-      }
+      for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+        for (int jp = 0; jp < 2; ++jp) {
+          const f32x16& o = *oacc[db * 4 + hb];
+          *reinterpret_cast<bf16x8*>(blk + (size_t)hb * (PART_ELEMS / 4) + ((4 * w + db) * 2 + jp) * 512) =
+              to_bf16x8(f32x4{o[8 * jp], o[8 * jp + 1], o[8 * jp + 2], o[8 * jp + 3]},
+                        f32x4{o[8 * jp + 4], o[8 * jp + 5], o[8 * jp + 6], o[8 * jp + 7]});
+        }
     return;
   }
 
-  // ---- z = O / l of this wave's 32 heads, through this wave's own slice of LDS, one half of the
-  // columns at a time: written straight from the accumulator layout, every store would touch 32
-  // rows; transposed, each store writes 1 KB of one head's row. No other wave touches the slice.
-  const float inv = 1.0f / l_run;
+  // ---- z = O / l: this wave holds latent columns 128w .. 128w+127 of every head. Each head's sum
+  // l comes from the wave that scored it, through LDS. One head block at a time goes through this
+  // wave's own slice of LDS: written straight from the accumulator layout, every store would touch
+  // 32 rows; transposed, each store writes the wave's 512 bytes of two heads' rows.
+  float* lsh = reinterpret_cast<float*>(smem_raw + FLAGS_OFF + 256);   // [H], clear of the flags and plan
+  if (g == 0) lsh[qhead] = l_run;
+  __syncthreads();
+  float inv[4];
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb) inv[hb] = 1.0f / lsh[32 * hb + l32];
   float* stage = reinterpret_cast<float*>(smem_raw) + w * 32 * ES_STRIDE;   // [32 heads][ES_STRIDE]
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
+  for (int hb = 0; hb < 4; ++hb) {
     float* row = stage + l32 * ES_STRIDE + 4 * g;
 #pragma unroll
-    for (int cb = 0; cb < 8; ++cb)
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const f32x16& o = *oacc[8 * half + cb];
-        *reinterpret_cast<f32x4*>(row + 32 * cb + 8 * j) =
-            f32x4{o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]} * inv;
+        const f32x16& o = *oacc[db * 4 + hb];
+        *reinterpret_cast<f32x4*>(row + 32 * db + 8 * j) =
+            f32x4{o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]} * inv[hb];
       }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's writes land before its reads
 #pragma unroll 4
-    for (int i = 0; i < 32; ++i) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(stage + i * ES_STRIDE + 4 * lane);
-      *reinterpret_cast<f32x4*>(z + (rh0 + w * 32 + i) * DC + 256 * half + 4 * lane) = v;
+    for (int i = 0; i < 16; ++i) {
+      const int hr = 2 * i + g;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(stage + hr * ES_STRIDE + 4 * l32);
+      *reinterpret_cast<f32x4*>(z + (rh0 + 32 * hb + hr) * DC + 128 * w + 4 * l32) = v;
     }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads done before the next half's writes
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads done before the next block's writes
   }
 }
 

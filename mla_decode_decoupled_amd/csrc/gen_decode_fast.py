@@ -7,7 +7,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROW_BYTES = 1152
 P_STRIDE = 80
 
-RING = list(range(88, 112, 4))   # six 4-register operand slots, v[88:111], shared by both phases
+RING = list(range(88, 112, 4))   # six 4-register operand slots of the score phase, v[88:111]
 
 
 class Ring:
@@ -80,10 +80,13 @@ def qk():
 
 
 def pv():
-    """P.V of one tile for the wave's own 32 heads: 32 MFMAs (2 key steps x 16 latent column
-    blocks), B = P from v[80:87], A = V^T fragments from the tile by transpose reads through the
-    six-slot ring. The softmax of the next tile (scores in v[112:127]) is interleaved; its P goes
-    to v[80:83] once the first key step no longer reads them and to v[84:87] after the last MFMA."""
+    """P.V of one tile for the wave's 128 latent columns (column blocks 4w .. 4w+3) and all 128
+    heads: 32 MFMAs (2 key steps x 4 column blocks x 4 head blocks). A = V^T fragments from the tile
+    by transpose reads, each feeding the 4 MFMAs of its column block; B = the P fragments of all four
+    waves from the LDS P buffer (%[pb]), each feeding 4 MFMAs. Operands stream through eight
+    4-register slots, v[80:111]. The softmax of the next tile (scores in v[112:127]) is interleaved;
+    its P is packed in place into v[112:119] and stored to this wave's part of the other P buffer
+    (%[pw]) after the last MFMA."""
     sm = []
     for r in range(16):  # x = s * scale - m_ref
         sm.append(f"v_fma_f32 v{112+r}, v{112+r}, %[sc], %[nm]")
@@ -91,53 +94,74 @@ def pv():
         sm.append(f"v_exp_f32 v{112+r}, v{112+r}")
     for r in range(16):
         sm.append(f"v_add_f32 %[l], %[l], v{112+r}")
-    cvt0 = [f"v_cvt_pk_bf16_f32 v{80+j}, v{112+2*j}, v{113+2*j}" for j in range(4)]
-    cvt1 = [f"v_cvt_pk_bf16_f32 v{84+j}, v{120+2*j}, v{121+2*j}" for j in range(4)]
-    L = []
-    ring = Ring(L)
-    order = [(s, cb) for s in range(2) for cb in range(16)]
-    loads = []
-    for i, (s, cb) in enumerate(order):
-        base = s * 16 * ROW_BYTES + (cb >> 1) * 128
-        loads.append(((s, cb), i, [f"ds_read_b64_tr_b16 {{r0}}, %[v{cb & 1}0] offset:{base}",
-                                   f"ds_read_b64_tr_b16 {{r1}}, %[v{cb & 1}1] offset:{base}"]))
-    nslot = len(RING)
-    slot_user = [-1] * nslot
-    next_load = 0
+    # in place: v[112+j] <- (v[112+2j], v[113+2j]); for j >= 1 the destination was a source of an
+    # earlier pack, so the order j = 0..7 never overwrites an unread value
+    sm += [f"v_cvt_pk_bf16_f32 v{112+j}, v{112+2*j}, v{113+2*j}" for j in range(8)]
+    order = [(s, db, hb) for s in range(2) for db in range(4) for hb in range(4)]
+    ops = []                       # operands in order of first use
+    last_use = {}
+    for i, (s, db, hb) in enumerate(order):
+        for op in (("A", s, db), ("B", s, hb)):
+            if op not in last_use:
+                ops.append(op)
+            last_use[op] = i
 
-    def fill(after_mfma):
-        nonlocal next_load
-        while next_load < len(loads):
-            slot = next_load % nslot
-            if slot_user[slot] > after_mfma:
+    def instrs(op, r):
+        if op[0] == "A":
+            _, s, db = op
+            base = s * 16 * ROW_BYTES + (db >> 1) * 128
+            return [f"ds_read_b64_tr_b16 v[{r}:{r + 1}], %[v{db & 1}0] offset:{base}",
+                    f"ds_read_b64_tr_b16 v[{r + 2}:{r + 3}], %[v{db & 1}1] offset:{base}"]
+        _, s, hb = op
+        return [f"ds_read_b128 v[{r}:{r + 3}], %[pb] offset:{(2 * hb + s) * 1024}"]
+
+    L = []
+    slots = list(range(80, 112, 4))
+    holder = {r: None for r in slots}      # slot -> operand it holds
+    where = {}                             # operand -> slot
+    issued = []                            # LDS instructions in issue order (operand of each)
+    waited = [-1]
+    nxt = [0]
+
+    def fill(done):                        # MFMAs 0 .. done have issued
+        while nxt[0] < len(ops):
+            free = [r for r in slots if holder[r] is None or last_use[holder[r]] <= done]
+            if not free:
                 return
-            lid, user, ins = loads[next_load]
-            r = RING[slot]
-            instrs = [ins[0].format(r0=f"v[{r}:{r + 1}]"), ins[1].format(r1=f"v[{r + 2}:{r + 3}]")]
-            # two instructions per fragment: record both so the waits count them
-            ring.issue(("x", lid), slot, instrs[:1])
-            ring.issue(lid, slot, instrs[1:])
-            slot_user[slot] = user
-            next_load += 1
-    n_mfma = len(order)
+            r = free[0]
+            op = ops[nxt[0]]
+            holder[r] = op
+            where[op] = r
+            for ins in instrs(op, r):
+                L.append(ins)
+                issued.append(op)
+            nxt[0] += 1
+
+    def wait(ops_needed):
+        idx = max(len(issued) - 1 - issued[::-1].index(op) for op in ops_needed)
+        if idx > waited[0]:
+            L.append(f"s_waitcnt lgkmcnt({len(issued) - 1 - idx})")
+            waited[0] = idx
+
+    n = len(order)
     spread = 28
-    per = [0] * n_mfma
+    per = [0] * n
     for i in range(len(sm)):
         per[i * spread // len(sm)] += 1
     q = list(sm)
     fill(-1)
-    for i, (s, cb) in enumerate(order):
-        ring.wait([(s, cb)])
-        a_reg = RING[ring.slot_of[(s, cb)]]
-        b = "v[80:83]" if s == 0 else "v[84:87]"
-        L.append(f"v_mfma_f32_32x32x16_bf16 %[o{cb}], v[{a_reg}:{a_reg + 3}], {b}, %[o{cb}]")
+    for i, (s, db, hb) in enumerate(order):
+        a, b = ("A", s, db), ("B", s, hb)
+        wait([a, b])
+        ra, rb = where[a], where[b]
+        acc = db * 4 + hb
+        L.append(f"v_mfma_f32_32x32x16_bf16 %[o{acc}], v[{ra}:{ra + 3}], v[{rb}:{rb + 3}], %[o{acc}]")
         for _ in range(per[i]):
             L.append(q.pop(0))
-        if i >= spread:                   # the first key step is done with v[80:83]
-            L.append(cvt0[i - spread])
         fill(i)
-    assert not q and next_load == len(loads)
-    L += ["s_nop 7"] + cvt1           # v[84:87] was read by the last MFMA
+    assert not q and nxt[0] == len(ops)
+    # P of the next tile to this wave's part of the other buffer: 16 bytes per lane per key step
+    L += ["ds_write_b128 %[pw], v[112:115] offset:0", "ds_write_b128 %[pw], v[116:119] offset:1024", "s_nop 1"]
     return L
 
 
