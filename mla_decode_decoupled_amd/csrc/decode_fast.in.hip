@@ -107,6 +107,8 @@ constexpr int FLAGS_OFF = NBUF * TILE_BYTES - 1024;
 static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget");
 static_assert(H * QS_STRIDE <= FLAGS_OFF, "query staging must end before the flags");
 static_assert(H * ES_STRIDE * 4 <= FLAGS_OFF, "output staging must end before the flags");
+constexpr int LSUM_OFF = FLAGS_OFF + 256;   // per-head sums for z = O / l, after the flags and the plan
+static_assert(LSUM_OFF + H * 4 <= NBUF * TILE_BYTES, "per-head sums must stay in the tile area");
 
 typedef int v16i __attribute__((vector_size(64)));
 typedef int v8i __attribute__((vector_size(32)));
@@ -386,6 +388,7 @@ __global__ void __launch_bounds__(256)
     const int bt = blockIdx.x;
     ch = Chunk{bt, 0, 1, 0, 0, seq_len[bt / n_q] - n_q + (bt % n_q) + 1};
   } else {
+    static_assert(FLAGS_OFF + 64 + sizeof(Chunk) <= LSUM_OFF, "the plan must end before the per-head sums");
     Chunk* shared_ch = reinterpret_cast<Chunk*>(smem_raw + FLAGS_OFF + 64);
     if (w == 0) {
       Chunk c;
@@ -712,7 +715,7 @@ __global__ void __launch_bounds__(256)
   // l comes from the wave that scored it, through LDS. One head block at a time goes through this
   // wave's own slice of LDS: written straight from the accumulator layout, every store would touch
   // 32 rows; transposed, each store writes the wave's 512 bytes of two heads' rows.
-  float* lsh = reinterpret_cast<float*>(smem_raw + FLAGS_OFF + 256);   // [H], clear of the flags and plan
+  float* lsh = reinterpret_cast<float*>(smem_raw + LSUM_OFF);   // [H]
   if (g == 0) lsh[qhead] = l_run;
   __syncthreads();
   float inv[4];
