@@ -223,7 +223,9 @@ def test_chunked_prefill_sampled():
     run = run_pipeline(hi)
     _check_cache(run, hi, 1)
     _check_qpacked(run, hi, 1, rows=[0, 1, 1000, 2047])
-    _check_outputs(run, hi, 1, heads=[0, 127], rows=[0, 1, 1000, 2047])
+    # both ends of every 32-head block: wave w of the attention kernel scores heads 32w .. 32w + 31,
+    # and every wave writes its 128 latent columns of all heads' z
+    _check_outputs(run, hi, 1, heads=[0, 31, 32, 63, 64, 95, 96, 127], rows=[0, 1, 1000, 2047])
     _check_outputs(run, hi, 0, heads=[64], rows=[2047, 5])
 
 
