@@ -578,7 +578,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(W, args.cpu_seconds)
+        cpu = cpu_baseline(W, args.cpu_seconds, explicit=args.explicit)
 
     out = {
         "metric": "MLA decode tokens/s + achieved HBM GB/s (H=128, d_c=512, S=4K-128K)",
@@ -618,9 +618,11 @@ def main():
 # ---------------------------------------------------------------------------------------------------
 # CPU baseline: the fp64 oracle on the host cores
 
-def cpu_baseline(W, budget_s):
+def cpu_baseline(W, budget_s, explicit=False):
     """The fp64 non-absorbed oracle on the host cores over a bounded sample of the same workload:
-    all cores of this process's affinity mask (BLAS threads pinned to that count), plus one thread."""
+    all cores of this process's affinity mask (BLAS threads pinned to that count), plus one thread.
+    The oracle's outputs for the heads it evaluates are also compared with the GPU's result of the
+    last timed call on the same inputs (z, or o for the explicit path): the run's own parity check."""
     import numpy as np
 
     import oracle as O
@@ -637,6 +639,10 @@ def cpu_baseline(W, budget_s):
     qn = W.qn_host[b * n_q:(b + 1) * n_q]
     qr = W.qr_host[b * n_q:(b + 1) * n_q]
     rows = list(range(n_q)) if n_q <= 4 else [0, n_q // 2, n_q - 1]
+    # the GPU's result for sequence 0's sampled rows (every copy holds the same inputs)
+    key = "o" if explicit else "z"
+    gpu = (W.o[b * n_q:(b + 1) * n_q] if explicit else W.z[b]).float().cpu().numpy()[rows]
+    checked = {}   # head -> (abs error max, squared error sum, squared reference sum)
 
     def sample(seconds):
         # head evaluations of sequence 0's query rows, cycling over the heads in groups of 8
@@ -645,8 +651,12 @@ def cpu_baseline(W, budget_s):
         while (time.perf_counter() - t0) < seconds:
             h0 = done % H
             hs = list(range(h0, min(H, h0 + 8)))
-            O.explicit_attention(W.c_host[b], W.k_host[b], qn, qr, W.wuk_host, W.wuv_host, scale=cfg.softmax_scale,
-                                 base=cfg.rope_base, heads=hs, rows=rows)
+            ref = O.explicit_attention(W.c_host[b], W.k_host[b], qn, qr, W.wuk_host, W.wuv_host,
+                                       scale=cfg.softmax_scale, base=cfg.rope_base, heads=hs, rows=rows)[key]
+            if hs[0] not in checked:
+                for j, h in enumerate(hs):
+                    d = gpu[:, h].astype(np.float64) - ref[:, j]
+                    checked[h] = (float(np.abs(d).max()), float((d * d).sum()), float((ref[:, j] ** 2).sum()))
             done += len(hs)
         el = time.perf_counter() - t0
         return (done / H) * len(rows) / el, done, el
@@ -674,7 +684,14 @@ def cpu_baseline(W, budget_s):
     v_all, done, el = limited(cores, sample, budget_s)
     v_one, done1, el1 = limited(1, sample, max(2.0, budget_s / 4))
     tiny_one = limited(1, tiny_full)
-    return {"value": round(v_all, 4), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+    tol = {"abs": 1e-5, "rel_l2": 1e-5} if cfg.dtype == "f32" else {"abs": 2e-2, "rel_l2": 1e-2}
+    max_abs = max(v[0] for v in checked.values())
+    rel = (sum(v[1] for v in checked.values()) / max(sum(v[2] for v in checked.values()), 1e-300)) ** 0.5
+    parity = {"output": key, "sequence": b, "rows": [int(r) for r in rows], "heads_checked": len(checked),
+              "max_abs_err": float(f"{max_abs:.3e}"), "rel_l2_err": float(f"{rel:.3e}"), "tolerance": tol,
+              "pass": bool(max_abs <= tol["abs"] and rel <= tol["rel_l2"]),
+              "against": "the GPU result of the last timed call on the same inputs"}
+    return {"value": round(v_all, 4), "unit": "tokens/s", "cores": int(cores), "kind": "oracle", "parity": parity,
             "sample": f"{cfg.name}: sequence 0 ({int(W.lens[0])} keys), {len(rows)} query row(s), {done} head "
                       f"evaluations ({done / H:.1f} x all {H} heads) in {el:.1f} s of the fp64 non-absorbed oracle "
                       f"on {cores} threads; tokens/s = whole-token equivalents / s",

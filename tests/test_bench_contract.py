@@ -1,6 +1,7 @@
 """CPU checks of bench.py's command-line contract that need no GPU: the build runs on one GPU, so any
-other --gpus value ends the run with a message and a failing status before a device is touched, and
-the traffic records it reads are keyed by the current kernel sources."""
+other --gpus value ends the run with a message and a failing status before a device is touched; the
+traffic records it reads are keyed by the current kernel sources; and the CPU-baseline leg's parity
+field compares the oracle's outputs with the result it is handed."""
 
 import json
 import os
@@ -52,3 +53,51 @@ def test_source_hash_follows_code_not_comments(tmp_path):
     c.write_text(code.replace("a + 1", "a + 2"))
     assert bench.sources_sha([str(a)]) == bench.sources_sha([str(b)])
     assert bench.sources_sha([str(a)]) != bench.sources_sha([str(c)])
+
+
+def _host_workload(cid):
+    """The host half of bench.Workload for workload `cid` (inputs drawn, nothing on a device)."""
+    import numpy as np
+    import torch
+
+    from mla_workloads import get_config
+    from mla_workloads import generate as G
+
+    cfg = get_config(cid)
+    lens = G.seq_lens(cfg)
+    B, n_q, H = cfg.batch, cfg.n_q, cfg.n_heads
+
+    class W:
+        pass
+
+    W.cfg, W.lens, W.B, W.n_q, W.H, W.R = cfg, lens, B, n_q, H, B * n_q
+    W.c_host = [G.cache_latent(cfg, b, int(lens[b])) for b in range(B)]
+    W.k_host = [G.cache_rope_pre(cfg, b, int(lens[b])) for b in range(B)]
+    W.qn_host = np.stack([G.query_nope(cfg, b) for b in range(B)]).reshape(B * n_q, H, cfg.d_nope)
+    W.qr_host = np.stack([G.query_rope_pre(cfg, b) for b in range(B)]).reshape(B * n_q, H, cfg.d_rope)
+    W.wuk_host, W.wuv_host = G.weight_uk(cfg), G.weight_uv(cfg)
+    W.z = torch.zeros((B, n_q, H, cfg.d_latent), dtype=torch.float32)
+    W.o = torch.zeros((B * n_q, H, cfg.d_v), dtype=torch.float32)
+    return W
+
+
+def test_cpu_baseline_parity_field():
+    """The CPU-baseline leg compares the oracle's outputs for the heads it evaluates with the device
+    result it is handed (here a host tensor): a result equal to the oracle's passes, every head is
+    checked, and a result off by more than the tolerance in one element fails."""
+    sys.path.insert(0, ROOT)
+    import bench
+    import oracle as O
+
+    W = _host_workload(0)
+    cfg = W.cfg
+    ref = O.explicit_attention(W.c_host[0], W.k_host[0], W.qn_host, W.qr_host, W.wuk_host, W.wuv_host,
+                               scale=cfg.softmax_scale, base=cfg.rope_base)
+    import torch
+
+    W.z[0] = torch.from_numpy(ref["z"].astype("float32"))
+    out = bench.cpu_baseline(W, 0.3)["parity"]
+    assert out["pass"] and out["heads_checked"] == cfg.n_heads and out["max_abs_err"] < 1e-6
+    W.z[0, 0, cfg.n_heads - 1, 3] += 1e-3
+    out = bench.cpu_baseline(W, 0.3)["parity"]
+    assert not out["pass"] and out["max_abs_err"] > 5e-4
