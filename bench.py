@@ -177,7 +177,8 @@ def roofline_of(bytes_, flops, ms, traffic=None, kernel="mla_decode_attn"):
         achieved, peak, unit, bound = flops / s / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s", "mfma"
     return {"kernel": kernel, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4), "traffic": traffic, "algorithmic_bytes_per_launch": int(bytes_),
-            "algorithmic_flops_per_launch": int(flops), "avg_launch_ms": round(ms, 6)}
+            "algorithmic_flops_per_launch": int(flops), "avg_launch_ms": round(ms, 6),
+            "gbs": round(bytes_ / s / 1e9, 2), "tflops": round(flops / s / 1e12, 2)}
 
 
 class Workload:
