@@ -96,6 +96,8 @@ def parse():
                     help="measure chip-wide bf16 MFMA issue (1 and 2 waves per SIMD) and the clock it ran at")
     ap.add_argument("--lds-ceiling", action="store_true",
                     help="measure LDS read throughput per CU for ds_read_b128 and ds_read_b64_tr_b16")
+    ap.add_argument("--phase-stamps", action="store_true",
+                    help="per-phase time of the attention kernels' workgroups (diagnostic build libmla_stamps.so)")
     ap.add_argument("--stream-ceiling", action="store_true",
                     help="measure read-only HBM streaming: vector loads, and the attention kernel's LDS tile ring")
     return ap.parse_args()
@@ -423,6 +425,108 @@ def attn_only(args):
           flush=True)
 
 
+def stamp_summary(st, cycles_only=False):
+    """Per-workgroup phases of one launch from the stamp array (uint64 [workgroups, 16], see
+    include/mla_stamps.h): medians and spreads in µs, each workgroup's cycles at its own clock."""
+    import numpy as np
+
+    act = st[(st[:, 5] != 0) & (st[:, 0] != 0) & ((st[:, 13] == 1) | (st[:, 13] == 2))]
+    if len(act) == 0:
+        return None
+    kern = int(act[0, 13])
+    real_us = (act[:, 9].astype(np.float64) - act[:, 8]) / 100.0           # 100 MHz counter
+    cyc = act[:, 5].astype(np.float64) - act[:, 0]
+    ghz = cyc / (real_us * 1e3)
+    phases = {"chunk_plan": (0, 1), "queries_to_registers": (1, 2), "first_tiles_issued": (2, 3),
+              "tile_loop": (3, 4), "stores_to_exit": (4, 5), "workgroup_total": (0, 5)}
+    if kern == 2:
+        phases = {"chunk_plan": (0, 1), "queries_and_first_tiles_landed": (1, 3), "tile_loop": (3, 4),
+                  "stores_to_exit": (4, 5), "workgroup_total": (0, 5)}
+    out = {"kernel": "decode_attn_fast" if kern == 1 else "decode_attn_hsplit", "workgroups": int(len(act)),
+           "clock_ghz_median": round(float(np.median(ghz)), 3)}
+    for name, (a, b) in phases.items():
+        us = (act[:, b].astype(np.float64) - act[:, a]) / (ghz * 1e3)
+        out[name + "_us"] = {"median": round(float(np.median(us)), 2), "p10": round(float(np.percentile(us, 10)), 2),
+                             "p90": round(float(np.percentile(us, 90)), 2)}
+    tiles = act[:, 10].astype(np.float64)
+    loop_cyc = act[:, 4].astype(np.float64) - act[:, 3]
+    per_tile = loop_cyc[tiles > 0] / tiles[tiles > 0]
+    out["tiles_per_workgroup"] = {"median": float(np.median(tiles)), "min": int(tiles.min()), "max": int(tiles.max())}
+    out["cycles_per_tile_median"] = round(float(np.median(per_tile)), 1)
+    r0, r1 = act[:, 8].astype(np.float64), act[:, 9].astype(np.float64)
+    out["start_spread_us"] = round(float(r0.max() - r0.min()) / 100.0, 2)
+    out["end_spread_us"] = round(float(r1.max() - r1.min()) / 100.0, 2)
+    out["first_start_to_last_end_us"] = round(float(r1.max() - r0.min()) / 100.0, 2)
+    return out
+
+
+def phase_stamps(args):
+    """--phase-stamps: mla_decode_attn on each workload through the phase-stamp build of the library
+    (libmla_stamps.so: the same kernels with per-workgroup clock stamps, include/mla_stamps.h), and
+    where the workgroups' time goes: chunk plan, query staging, first tiles, the tile loop (and its
+    cycles per tile), the output stores, and the spread of the workgroups' start and end times."""
+    import ctypes
+
+    import numpy as np
+
+    path = os.path.join(ROOT, "mla_decode_decoupled_amd", "libmla_stamps.so")
+    if "mla_decode_decoupled_amd" in sys.modules:
+        raise SystemExit("--phase-stamps must load the stamp build before the library")
+    os.environ["MLA_LIB_PATH"] = path
+    import torch
+
+    import mla_decode_decoupled_amd as mla
+
+    lib = ctypes.CDLL(path)
+    lib.mla_phase_stamps_bytes.restype = ctypes.c_size_t
+    lib.mla_phase_stamps_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    nbytes = lib.mla_phase_stamps_bytes()
+    host = np.zeros(nbytes // 8, dtype=np.uint64)
+    dev = _device()
+    res = []
+    for cid in [int(x) for x in args.per_configs.split(",") if x.strip()]:
+        W = Workload(cid, dev, max(2, args.steps), args.hot)
+        cfg, lc = W.cfg, W.lc
+        B, n_q, H = W.B, W.n_q, W.H
+        ws = torch.empty(max(16, mla.mla_decode_attn_workspace_size(lc, B, n_q, W.max_len, cfg.n_splits)),
+                         dtype=torch.uint8, device=dev)
+        qps = []
+        for (_, wuk, _, qn, qr) in W.copies:
+            qp = torch.empty_like(W.q_packed)
+            mla.mla_absorb_q(lc, qn, qr, W.q_pos, wuk, qp)
+            qps.append(qp.view(B, n_q, H, W.row))
+
+        def attn(i):
+            c = i % W.n_copies
+            mla.mla_decode_attn(lc, qps[c], W.copies[c][0], W.seq_off, W.seq_len, W.max_len, W.z, W.lse,
+                                n_splits=cfg.n_splits, workspace=ws)
+
+        for i in range(max(1, args.warmup)):
+            attn(i)
+        torch.cuda.synchronize()
+        runs = []
+        for i in range(args.steps):
+            if lib.mla_phase_stamps_clear() != 0:
+                raise RuntimeError("mla_phase_stamps_clear failed")
+            attn(i)
+            torch.cuda.synchronize()
+            if lib.mla_phase_stamps_read(host.ctypes.data, nbytes) != 0:
+                raise RuntimeError("mla_phase_stamps_read failed")
+            summ = stamp_summary(host.reshape(-1, 16))
+            if summ is not None:
+                runs.append(summ)
+        # the median call by its first-start-to-last-end span
+        runs.sort(key=lambda r: r["first_start_to_last_end_us"])
+        entry = {"workload": cfg.name, "call": "mla_decode_attn", "calls": len(runs),
+                 "median_call": runs[len(runs) // 2] if runs else None,
+                 "span_us_all_calls": [r["first_start_to_last_end_us"] for r in runs]}
+        res.append(entry)
+        del qps, ws, W
+        torch.cuda.empty_cache()
+    print(json.dumps({"phase_stamps": res, "library": "libmla_stamps.so",
+                      "note": "each call's stamps read back after it; one call per cold copy"}), flush=True)
+
+
 # ---------------------------------------------------------------------------------------------------
 # the headline step
 
@@ -435,7 +539,7 @@ def main():
     modes = {"copy_calibration": copy_calibration, "decode_loop": decode_loop, "merged_wo_check": merged_wo_check,
              "a16_check": a16_check, "mfma_peak": mfma_peak, "stream_ceiling": stream_ceiling,
              "lds_ceiling": lds_ceiling,
-             "attn_only": attn_only, "prefill_crossover": prefill_crossover}
+             "attn_only": attn_only, "prefill_crossover": prefill_crossover, "phase_stamps": phase_stamps}
     for name, fn in modes.items():
         if getattr(args, name):
             fn(args)

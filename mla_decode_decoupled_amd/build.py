@@ -24,6 +24,10 @@ CEIL_SOURCES = ["ceilings.hip"]
 # runs the C-ABI checks against it (tests/test_abi_sanitized.py), with the sanitizer runtime preloaded.
 ASAN_LIB_PATH = os.path.join(PKG_DIR, "libmla_asan.so")
 SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-Xarch_host", "-fno-omit-frame-pointer", "-shared-libasan"]
+# a copy of libmla whose attention kernels also record per-workgroup phase stamps
+# (include/mla_stamps.h); loaded only by bench.py --phase-stamps
+STAMPS_LIB_PATH = os.path.join(PKG_DIR, "libmla_stamps.so")
+STAMPS_FLAGS = ["-DMLA_PHASE_STAMPS"]
 
 # Packed-FP32 instructions (v_pk_*_f32) are switched off for every device pass: the compiler
 # otherwise forms them from plain float code, and the kernels are validated without them.
@@ -47,9 +51,11 @@ def hipcc() -> str:
 
 
 def build(debug: bool = False, verbose: bool = False, sanitize: bool = False) -> str:
-    """Build libmla.so and libmla_ceilings.so; with sanitize, also the host-sanitized libmla_asan.so."""
+    """Build libmla.so, libmla_ceilings.so and the phase-stamp build libmla_stamps.so; with sanitize,
+    also the host-sanitized libmla_asan.so."""
     _build_one(SOURCES, LIB_PATH, debug, verbose)
     _build_one(CEIL_SOURCES, CEIL_LIB_PATH, debug, verbose)
+    _build_one(SOURCES, STAMPS_LIB_PATH, debug, verbose, STAMPS_FLAGS)
     if sanitize:
         _build_one(SOURCES, ASAN_LIB_PATH, debug, verbose, SANITIZE_FLAGS)
     return LIB_PATH

@@ -138,6 +138,33 @@ __device__ __forceinline__ int key_of_reg(int rr, int g) { return key_of_row(8 *
 // accesses across the barrier.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Phase stamps, compiled only into the diagnostic build (-DMLA_PHASE_STAMPS, libmla_stamps.so):
+// thread 0 of each workgroup records the shader clock counter (s_memtime) at the phase boundaries
+// of the attention kernels, the 100 MHz counter (s_memrealtime) at entry and exit, and what its
+// chunk was. Slots: 0 entry, 1 chunk known, 2 queries in registers (128-head kernel), 3 first tiles
+// issued (head-split kernel: queries and first tiles landed), 4 loop done, 5 exit with every store
+// completed; 8 and 9 entry and exit on the 100 MHz counter; 10 tiles, 11 query row, 12 chunk index,
+// 13 kernel (1 the 128-head kernel, 2 the head-split kernel). In the library proper the macros
+// expand to nothing.
+#ifdef MLA_PHASE_STAMPS
+constexpr int kStampSlots = 16;
+constexpr int kStampMaxWorkgroups = 8192;
+__device__ unsigned long long g_phase_stamps[kStampMaxWorkgroups][kStampSlots];
+__device__ __forceinline__ void phase_stamp(int slot, unsigned long long v) {
+  const unsigned wg = blockIdx.x + blockIdx.y * gridDim.x;
+  if (threadIdx.x == 0 && wg < (unsigned)kStampMaxWorkgroups) g_phase_stamps[wg][slot] = v;
+}
+#define MLA_STAMP(slot) phase_stamp(slot, __builtin_amdgcn_s_memtime())
+#define MLA_STAMP_REAL(slot) phase_stamp(slot, __builtin_amdgcn_s_memrealtime())
+#define MLA_STAMP_VAL(slot, v) phase_stamp(slot, (unsigned long long)(v))
+#define MLA_STAMP_DRAIN() asm volatile("s_waitcnt vmcnt(0)" ::: "memory")
+#else
+#define MLA_STAMP(slot) ((void)0)
+#define MLA_STAMP_REAL(slot) ((void)0)
+#define MLA_STAMP_VAL(slot, v) ((void)0)
+#define MLA_STAMP_DRAIN() ((void)0)
+#endif
+
 // one 16-byte-per-lane direct global->LDS load: lane l writes LDS bytes lds_base + 16 l
 __device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gaddr), "s"(lds_base)
@@ -375,6 +402,9 @@ __global__ void __launch_bounds__(256)
   Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 5, l32 = lane & 31;
+  MLA_STAMP(0);
+  MLA_STAMP_REAL(8);
+  MLA_STAMP_VAL(13, 1);
 
   // ---- this workgroup's chunk
   Chunk ch;
@@ -409,6 +439,10 @@ __global__ void __launch_bounds__(256)
   const int bt = ch.bt, j0 = ch.j0, j1 = ch.j1, n_chunks = ch.nck;
   const int b = bt / n_q;
   const size_t rh0 = (size_t)bt * H;
+  MLA_STAMP(1);
+  MLA_STAMP_VAL(10, (j1 - j0 + TILE - 1) / TILE);
+  MLA_STAMP_VAL(11, bt);
+  MLA_STAMP_VAL(12, ch.k);
   // every row's first chunk publishes where the row's partials are (first slot, count; count 1
   // means the row is written directly), so the merge never reads an entry of an earlier call
   if (row_chunks != nullptr && ch.k == 0 && threadIdx.x == 0) row_chunks[bt] = make_int2(ch.slot, n_chunks);
@@ -499,8 +533,10 @@ __global__ void __launch_bounds__(256)
       : [a] "v"(qstage + l32 * QS_STRIDE + 16 * g)
       : "memory");
   lds_barrier();   // every wave holds its fragments: the staging area is free for the tiles
+  MLA_STAMP(2);
   issue_tile(0);
   issue_tile(1);   // past the chunk when it has one tile: then a harmless read of qbytes
+  MLA_STAMP(3);
 
 
   // O^T accumulators: latent col block cb (32 columns) x this wave's 32 heads, 16 fp32 each,
@@ -656,6 +692,7 @@ __global__ void __launch_bounds__(256)
     pv_softmax(tile, sacc);
   }
   wait_vmcnt_0();   // the trailing DMAs (past the chunk) have landed; LDS is free
+  MLA_STAMP(4);
 
   // A score far above the reference makes later probabilities overflow (inf / NaN in the
   // accumulator, harmless to the hardware); the loop still runs to its end, and the chunk is then
@@ -708,6 +745,9 @@ __global__ void __launch_bounds__(256)
               to_bf16x8(f32x4{o[8 * jp], o[8 * jp + 1], o[8 * jp + 2], o[8 * jp + 3]},
                         f32x4{o[8 * jp + 4], o[8 * jp + 5], o[8 * jp + 6], o[8 * jp + 7]});
         }
+    MLA_STAMP_DRAIN();
+    MLA_STAMP(5);
+    MLA_STAMP_REAL(9);
     return;
   }
 
@@ -742,6 +782,9 @@ __global__ void __launch_bounds__(256)
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads done before the next block's writes
   }
+  MLA_STAMP_DRAIN();
+  MLA_STAMP(5);
+  MLA_STAMP_REAL(9);
 }
 
 // ---- Head-split kernel for few query rows and short histories (latency-bound decode).
@@ -838,6 +881,9 @@ __global__ void __launch_bounds__(256)
   const int wg = blockIdx.x;
   const int hb = (wg >> 3) & 3, cidx = ((wg >> 5) << 3) | (wg & 7);
   const int head0 = 32 * hb;
+  MLA_STAMP(0);
+  MLA_STAMP_REAL(8);
+  MLA_STAMP_VAL(13, 2);
 
   // DMA plan as in decode_attn_fast: slot (row r, physical chunk p) <- logical chunk phys_chunk(p, r)
   uint32_t dma_off[DMA_PER_WAVE];
@@ -875,6 +921,10 @@ __global__ void __launch_bounds__(256)
   const int bt = ch.bt, j0 = ch.j0, j1 = ch.j1, n_chunks = ch.nck;
   const int b = bt / n_q;
   const size_t rh0 = (size_t)bt * H;
+  MLA_STAMP(1);
+  MLA_STAMP_VAL(10, (j1 - j0 + TILE - 1) / TILE);
+  MLA_STAMP_VAL(11, bt);
+  MLA_STAMP_VAL(12, ch.k);
   if (row_chunks != nullptr && ch.k == 0 && hb == 0 && threadIdx.x == 0) row_chunks[bt] = make_int2(ch.slot, n_chunks);
   const int n_tiles = (j1 - j0 + TILE - 1) / TILE;
   const unsigned char* kv = reinterpret_cast<const unsigned char*>(cache + (b == 0 ? off0 : seq_off[b]) * (int64_t)ROW);
@@ -898,6 +948,7 @@ __global__ void __launch_bounds__(256)
     wait_vmcnt_9();
   }
   lds_barrier();
+  MLA_STAMP(3);
   // B operand of the scores: head l32, dims 16s + 8g .. +7 for this wave's k-steps s = 9w + u
   bf16x8e qf[9];
 #pragma unroll
@@ -975,6 +1026,7 @@ __global__ void __launch_bounds__(256)
   int* flags = reinterpret_cast<int*>(&sm.exch[0][0][0][0]);
   const bool wave_ovf = __any(ovf);
   lds_barrier();   // every wave is done with the exchange area
+  MLA_STAMP(4);
   if (lane == 0) flags[w] = wave_ovf ? 1 : 0;
   __syncthreads();
   if ((flags[0] | flags[1] | flags[2] | flags[3]) != 0) {
@@ -996,6 +1048,9 @@ __global__ void __launch_bounds__(256)
         *reinterpret_cast<f32x4*>(zr + 32 * (4 * w + i) + 8 * j) =
             f32x4{oacc[i][4 * j], oacc[i][4 * j + 1], oacc[i][4 * j + 2], oacc[i][4 * j + 3]} * inv;
     if (lse != nullptr && w == 0 && g == 0) lse[rh0 + head] = (m_ref + log2f(l_run)) * kLn2;
+    MLA_STAMP_DRAIN();
+    MLA_STAMP(5);
+    MLA_STAMP_REAL(9);
     return;
   }
   if (head_major) {
@@ -1037,6 +1092,9 @@ __global__ void __launch_bounds__(256)
     ml[0] = m_ref;
     ml[1] = l_run;
   }
+  MLA_STAMP_DRAIN();
+  MLA_STAMP(5);
+  MLA_STAMP_REAL(9);
 }
 
 // Log-sum-exp merge of decode_attn_fast's split-K partials (register order, bf16). One workgroup per
@@ -1427,3 +1485,29 @@ hipError_t launch_attn_fast(const LayerDims& L, int batch, int n_q, const void* 
 }
 
 }  // namespace mla
+
+#ifdef MLA_PHASE_STAMPS
+// Host side of the phase stamps (diagnostic build only; declared in include/mla_stamps.h).
+#include "mla.h"
+#include "mla_stamps.h"
+
+extern "C" {
+
+size_t mla_phase_stamps_bytes(void) { return sizeof(mla::fast::g_phase_stamps); }
+
+int mla_phase_stamps_clear(void) {
+  void* dev = nullptr;   // the device address of the array (its name in host code is only a stand-in)
+  if (hipGetSymbolAddress(&dev, HIP_SYMBOL(mla::fast::g_phase_stamps)) != hipSuccess) return MLA_ERR_HIP;
+  return hipMemset(dev, 0, sizeof(mla::fast::g_phase_stamps)) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int mla_phase_stamps_read(void* host_dst, size_t bytes) {
+  if (host_dst == nullptr || bytes < sizeof(mla::fast::g_phase_stamps)) return MLA_ERR_INVALID_ARG;
+  return hipMemcpyFromSymbol(host_dst, HIP_SYMBOL(mla::fast::g_phase_stamps), sizeof(mla::fast::g_phase_stamps), 0,
+                             hipMemcpyDeviceToHost) == hipSuccess
+             ? MLA_OK
+             : MLA_ERR_HIP;
+}
+
+}  // extern "C"
+#endif

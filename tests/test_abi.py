@@ -318,3 +318,29 @@ def test_decode_step_noalloc_arguments():
     assert need > _lib.MLA_NOALLOC_SCRATCH_BYTES
     assert call(c, batch=16, max_len=65536, n_splits=256) == MLA_ERR_UNSUPPORTED
     assert b"scratch" in lib.mla_last_error()
+
+
+STAMPS_HEADER = os.path.join(os.path.dirname(HEADER), "mla_stamps.h")
+
+
+def test_stamps_library_exports_and_validation():
+    """The phase-stamp build exports every call of mla.h and of mla_stamps.h, reports the size of its
+    stamp array, and rejects a null or short destination before touching the device."""
+    import ctypes
+
+    path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "mla_decode_decoupled_amd",
+                        "libmla_stamps.so")
+    lib = ctypes.CDLL(path)
+    names = set(re.findall(r"^\s*(?:int|size_t)\s+(mla_\w+)\s*\(", open(STAMPS_HEADER).read(), re.M))
+    assert names == {"mla_phase_stamps_bytes", "mla_phase_stamps_clear", "mla_phase_stamps_read"}
+    main = set(re.findall(r"^\s*(?:mla_status|size_t|int|const char\s*\*)\s+(mla_\w+)\s*\(", open(HEADER).read(), re.M))
+    assert main
+    for n in names | main:
+        assert hasattr(lib, n), n
+    lib.mla_phase_stamps_bytes.restype = ctypes.c_size_t
+    lib.mla_phase_stamps_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    n = lib.mla_phase_stamps_bytes()
+    assert n == 8192 * 16 * 8
+    assert lib.mla_phase_stamps_read(None, n) == MLA_ERR_INVALID_ARG
+    buf = ctypes.create_string_buffer(16)
+    assert lib.mla_phase_stamps_read(buf, 16) == MLA_ERR_INVALID_ARG

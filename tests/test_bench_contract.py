@@ -101,3 +101,31 @@ def test_cpu_baseline_parity_field():
     W.z[0, 0, cfg.n_heads - 1, 3] += 1e-3
     out = bench.cpu_baseline(W, 0.3)["parity"]
     assert not out["pass"] and out["max_abs_err"] > 5e-4
+
+
+def test_stamp_summary_phases():
+    """bench.py's reading of the phase stamps (slot layout of include/mla_stamps.h) on two synthetic
+    workgroups at 2 GHz: phase lengths, cycles per tile, and the start and end spreads on the 100 MHz
+    counter; inactive workgroups (exit slot 0) are left out."""
+    import numpy as np
+
+    sys.path.insert(0, ROOT)
+    import bench
+
+    st = np.zeros((8192, 16), dtype=np.uint64)
+    for wg, (start, tiles) in enumerate([(1000, 10), (1100, 20)]):
+        t0 = 5_000_000
+        cyc = [t0, t0 + 2000, t0 + 6000, t0 + 10000, t0 + 10000 + 3000 * tiles, t0 + 12000 + 3000 * tiles]
+        st[wg, :6] = cyc
+        st[wg, 8] = start
+        st[wg, 9] = start + (cyc[5] - cyc[0]) // 20          # 2 GHz against 100 MHz: 20 cycles a tick
+        st[wg, 10], st[wg, 11], st[wg, 12], st[wg, 13] = tiles, 0, wg, 1
+    st[2, 0], st[2, 13] = 7, 1                               # started, never finished: left out
+    out = bench.stamp_summary(st)
+    assert out["workgroups"] == 2 and out["kernel"] == "decode_attn_fast"
+    assert abs(out["clock_ghz_median"] - 2.0) < 1e-9
+    assert out["chunk_plan_us"]["median"] == 1.0 and out["queries_to_registers_us"]["median"] == 2.0
+    assert out["cycles_per_tile_median"] == 3000.0
+    assert out["start_spread_us"] == 1.0
+    # ends: 1000 + (42000 / 20) and 1100 + (72000 / 20) ticks
+    assert out["end_spread_us"] == round(((1100 + 3600) - (1000 + 2100)) / 100.0, 2)
