@@ -425,7 +425,7 @@ def attn_only(args):
           flush=True)
 
 
-def stamp_summary(st, cycles_only=False):
+def stamp_summary(st):
     """Per-workgroup phases of one launch from the stamp array (uint64 [workgroups, 16], see
     include/mla_stamps.h): medians and spreads in µs, each workgroup's cycles at its own clock."""
     import numpy as np
