@@ -194,10 +194,10 @@ __device__ __forceinline__ void wait_vmcnt_27() {
 // For mla_decode_step, decode_attn_hsplit stores them head-major instead, [head][col], so that one
 // head's 1 KB row per chunk is contiguous for merge_heads_out_proj, which merges and projects one
 // head per workgroup. The head-split kernel writes its (few, latency-bound) partials with
-// nontemporal stores, which shortens the write-back at the end of the kernel, and attn_merge_frag
-// reads them nontemporally too (cached by the merge, the lines would slow the next call's
-// stores); the big kernel's partials go through the caches both ways, where the merge finds part
-// of them.
+// nontemporal stores, which shortens the write-back at the end of the kernel; the big kernel's
+// go through the caches (nontemporal stores measured slower on the ragged batch). attn_merge_frag
+// reads every partial nontemporally: cached by the merge, the lines would slow the next call's
+// stores.
 constexpr int PART_ELEMS = H * DC;   // bf16 values per (query row, chunk)
 __device__ __forceinline__ int frag_offset(int head, int col) {
   const int cb = col >> 5, j = (col >> 3) & 3, g = (col >> 2) & 1, e = col & 3;
@@ -1107,7 +1107,7 @@ __global__ void __launch_bounds__(256)
 // partial and its (m, l)) in flight per step, and each wave keeps its own running maximum,
 // rescaling its sums when it grows; the wave sums then meet in LDS against the common maximum.
 // Rows computed as a single chunk were written directly and are skipped.
-template <int JP, bool NT>
+template <int JP>
 __global__ void __launch_bounds__(256) attn_merge_frag(const bf16* __restrict__ part_acc,
                                                        const float* __restrict__ part_ml,
                                                        const int2* __restrict__ row_chunks,
@@ -1140,7 +1140,7 @@ __global__ void __launch_bounds__(256) attn_merge_frag(const bf16* __restrict__ 
 #pragma unroll
         for (int j = 0; j < JP; ++j) {
           const i32x4* p = reinterpret_cast<const i32x4*>(src + (size_t)kk * PART_ELEMS + j * 512);
-          x[u][j] = NT ? __builtin_nontemporal_load(p) : *p;
+          x[u][j] = __builtin_nontemporal_load(p);
         }
         v[u] = ml[(size_t)kk * H];
       }
@@ -1472,13 +1472,13 @@ hipError_t launch_attn_fast(const LayerDims& L, int batch, int n_q, const void* 
   if (e != hipSuccess || plan.fast_slots == 0) return e;
   if (plan.fast_mode == fast::HSPLIT) {
     if (defer_merge) return hipSuccess;
-    hipLaunchKernelGGL((fast::attn_merge_frag<1, true>), dim3(128, rows), dim3(256), 0, stream, part_acc, part_ml,
+    hipLaunchKernelGGL((fast::attn_merge_frag<1>), dim3(128, rows), dim3(256), 0, stream, part_acc, part_ml,
                        row_chunks, z, lse);
   } else if (rows <= 16) {   // few rows: two workgroups per (row, 32 x 32 block) to keep enough loads in flight
-    hipLaunchKernelGGL((fast::attn_merge_frag<1, false>), dim3(128, rows), dim3(256), 0, stream, part_acc, part_ml,
+    hipLaunchKernelGGL((fast::attn_merge_frag<1>), dim3(128, rows), dim3(256), 0, stream, part_acc, part_ml,
                        row_chunks, z, lse);
   } else {
-    hipLaunchKernelGGL((fast::attn_merge_frag<2, false>), dim3(64, rows), dim3(256), 0, stream, part_acc, part_ml,
+    hipLaunchKernelGGL((fast::attn_merge_frag<2>), dim3(64, rows), dim3(256), 0, stream, part_acc, part_ml,
                        row_chunks, z, lse);
   }
   return hipGetLastError();
