@@ -129,6 +129,21 @@ def test_fast_kernel_chunk_tails(n_splits):
         _check_outputs(run, hi, b)
 
 
+def test_fast_kernel_causal_rows_with_fixed_splits():
+    """Several causal query rows per sequence with a caller's split count on the 128-head kernel:
+    40 new rows on 300 and 137 keys in chunks of 100 keys, so every row of the first sequence has
+    three chunks (the last one ending in a partial tile), while the rows of the second see 98 to 137
+    keys: its first rows fit one chunk (z written directly, their second chunk has no keys and does
+    nothing) and its later rows take two (partials and the merge). All rows and heads against the
+    oracle."""
+    lens = [300, 137]
+    cfg = MLAConfig(**{**CONFIGS[1].__dict__, "cid": 260, "batch": len(lens), "n_q": 40})
+    hi = host_inputs(cfg, lens=lens)
+    run = run_pipeline(hi, n_splits=3)
+    for b in range(len(lens)):
+        _check_outputs(run, hi, b)
+
+
 def test_ragged_batch_sampled():
     cfg = CONFIGS[2]
     hi = host_inputs(cfg)
